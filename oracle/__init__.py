@@ -1,0 +1,206 @@
+"""CPU oracle for the dense matrix-unit GEMM path -- test infrastructure only.
+
+Only the test suite, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product library never loads it and
+has no fallback to it.  It shares no code with the HIP path.
+
+The arithmetic lives in ``oracle.c`` (plain C, FP64, exact decoding); this
+module loads it with ctypes and marshals numpy arrays.  What each function
+computes, and the page passages it follows, is documented in ``oracle.c``.
+The two error metrics below are the definitions used on the page "Tensor
+Cores: Matrix Instructions, Swizzling and FP8, Measured", Step 2 (relative
+error = RMS of the error over RMS of the value) and Step 5 ("total" versus
+"from the sums" errors against an FP64 product).
+
+Every function here is pinned by ``tests/test_oracle_*.py``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+E4M3 = 0
+E5M2 = 1
+B_ROW_MAJOR = 0
+B_COL_MAJOR = 1
+SCALE_TENSOR = 0
+SCALE_BLOCK = 1
+FMAX = {E4M3: 448.0, E5M2: 57344.0}
+
+
+def build(force: bool = False) -> str:
+    """Compile oracle.c into liboracle.so with gcc (no fast-math, no FMA
+    contraction) and return its path."""
+    if force or not os.path.exists(_LIB_PATH) or (
+        os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC)
+    ):
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        cmd = [
+            "gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
+            "-std=c11", "-shared", "-fPIC", _SRC, "-o", tmp, "-lm",
+        ]
+        subprocess.check_call(cmd)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        build()
+        L = ctypes.CDLL(_LIB_PATH)
+        p = ctypes.c_void_p
+        i64 = ctypes.c_int64
+        i32 = ctypes.c_int
+        L.orc_decode_bf16_array.argtypes = [p, i64, p]
+        L.orc_decode_fp8_array.argtypes = [p, i64, i32, p]
+        L.orc_encode_bf16_array.argtypes = [p, i64, p]
+        L.orc_encode_fp8_array.argtypes = [p, i64, i32, p]
+        L.orc_quantize_fp8.argtypes = [p, i64, i64, i64, i32, i64, i64, p, i64, p]
+        L.orc_quantize_fp8.restype = i32
+        L.orc_gemm_bf16.argtypes = [p, i64, p, i64, i32, p, i64, i64, i64, i64, p, i64, p, p]
+        L.orc_gemm_bf16.restype = i32
+        L.orc_gemm_fp8.argtypes = [p, i64, i32, p, i64, i32, p, p, i32, p, i64, i64, i64,
+                                   i64, p, i64, p, p]
+        L.orc_gemm_fp8.restype = i32
+        _lib = L
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def decode_bf16(h) -> np.ndarray:
+    h = np.ascontiguousarray(h, dtype=np.uint16)
+    out = np.empty(h.shape, dtype=np.float64)
+    lib().orc_decode_bf16_array(_ptr(h), h.size, _ptr(out))
+    return out
+
+
+def decode_fp8(v, fmt: int) -> np.ndarray:
+    v = np.ascontiguousarray(v, dtype=np.uint8)
+    out = np.empty(v.shape, dtype=np.float64)
+    lib().orc_decode_fp8_array(_ptr(v), v.size, fmt, _ptr(out))
+    return out
+
+
+def encode_bf16(x) -> np.ndarray:
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(x.shape, dtype=np.uint16)
+    lib().orc_encode_bf16_array(_ptr(x), x.size, _ptr(out))
+    return out
+
+
+def encode_fp8(x, fmt: int) -> np.ndarray:
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(x.shape, dtype=np.uint8)
+    lib().orc_encode_fp8_array(_ptr(x), x.size, fmt, _ptr(out))
+    return out
+
+
+def quantize_fp8(X, fmt: int, block_rows: int | None = None, block_cols: int | None = None):
+    """Return (Q uint8 like X, scales float32 [rows/br][cols/bc]).  Block
+    (None, None) means one block for the whole tensor."""
+    X = np.ascontiguousarray(X, dtype=np.float32)
+    rows, cols = X.shape
+    br = rows if block_rows is None else block_rows
+    bc = cols if block_cols is None else block_cols
+    Q = np.empty((rows, cols), dtype=np.uint8)
+    scales = np.empty((rows // br, cols // bc), dtype=np.float32)
+    rc = lib().orc_quantize_fp8(_ptr(X), rows, cols, cols, fmt, br, bc, _ptr(Q), cols,
+                                _ptr(scales))
+    if rc != 0:
+        raise ValueError("orc_quantize_fp8: bad arguments")
+    return Q, scales
+
+
+def _rows_arg(rows, M):
+    if rows is None:
+        return None, M
+    r = np.ascontiguousarray(rows, dtype=np.int64)
+    return r, r.size
+
+
+def gemm_bf16(A, B, b_layout: int, C=None, rows=None):
+    """FP64 D = A*B + C (selected rows) and S = sum_k |a*b|.  A: [M][K] uint16
+    BF16 codes.  B: [K][N] (row-major) or [N][K] (column-major) uint16."""
+    A = np.ascontiguousarray(A, dtype=np.uint16)
+    B = np.ascontiguousarray(B, dtype=np.uint16)
+    M, K = A.shape
+    N = B.shape[1] if b_layout == B_ROW_MAJOR else B.shape[0]
+    assert (B.shape[0] if b_layout == B_ROW_MAJOR else B.shape[1]) == K
+    if C is not None:
+        C = np.ascontiguousarray(C, dtype=np.float32)
+        assert C.shape == (M, N)
+    r, nr = _rows_arg(rows, M)
+    D = np.empty((nr, N), dtype=np.float64)
+    S = np.empty((nr, N), dtype=np.float64)
+    rc = lib().orc_gemm_bf16(_ptr(A), K, _ptr(B), B.shape[1], b_layout, _ptr(C), N, M, N, K,
+                             _ptr(r), nr, _ptr(D), _ptr(S))
+    if rc != 0:
+        raise ValueError("orc_gemm_bf16: bad arguments")
+    return D, S
+
+
+def gemm_fp8(A, B, fmt_a: int, fmt_b: int, sa, sb, scale_mode: int, C=None, rows=None):
+    """FP64 scaled FP8 product (selected rows) and S = sum |a sa| |b sb|.
+    A: [M][K] uint8, B: [N][K] uint8 (column-major B)."""
+    A = np.ascontiguousarray(A, dtype=np.uint8)
+    B = np.ascontiguousarray(B, dtype=np.uint8)
+    M, K = A.shape
+    N = B.shape[0]
+    assert B.shape[1] == K
+    sa = np.ascontiguousarray(sa, dtype=np.float32)
+    sb = np.ascontiguousarray(sb, dtype=np.float32)
+    if C is not None:
+        C = np.ascontiguousarray(C, dtype=np.float32)
+        assert C.shape == (M, N)
+    r, nr = _rows_arg(rows, M)
+    D = np.empty((nr, N), dtype=np.float64)
+    S = np.empty((nr, N), dtype=np.float64)
+    rc = lib().orc_gemm_fp8(_ptr(A), K, fmt_a, _ptr(B), K, fmt_b, _ptr(sa), _ptr(sb),
+                            scale_mode, _ptr(C), N, M, N, K, _ptr(r), nr, _ptr(D), _ptr(S))
+    if rc != 0:
+        raise ValueError("orc_gemm_fp8: bad arguments")
+    return D, S
+
+
+# ------------------------------------------------------------------ metrics
+
+def rel_rms(D, D_ref) -> float:
+    """Relative RMS error: sqrt(sum (D - D_ref)^2) / sqrt(sum D_ref^2)."""
+    D = np.asarray(D, dtype=np.float64)
+    D_ref = np.asarray(D_ref, dtype=np.float64)
+    return float(np.sqrt(np.sum((D - D_ref) ** 2)) / np.sqrt(np.sum(D_ref ** 2)))
+
+
+def bound_ratio(D, D_ref, S) -> float:
+    """max |D - D_ref| / S elementwise (S = sum_k |a_ik b_kj|); the FP32-output
+    acceptance bound is bound_ratio <= 1e-5."""
+    D = np.asarray(D, dtype=np.float64)
+    err = np.abs(D - D_ref)
+    S = np.asarray(S, dtype=np.float64)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        r = np.where(S > 0, err / np.where(S > 0, S, 1.0), np.where(err > 0, np.inf, 0.0))
+    return float(np.max(r)) if r.size else 0.0
+
+
+def within_bound(D, D_ref, S, bf16_out: bool, rel: float = 1e-5) -> np.ndarray:
+    """Per-element acceptance: |D - D_ref| <= rel*S (FP32 out), plus
+    2^-8*|D_ref| for BF16 output."""
+    D = np.asarray(D, dtype=np.float64)
+    tol = rel * np.asarray(S, dtype=np.float64)
+    if bf16_out:
+        tol = tol + 2.0 ** -8 * np.abs(D_ref)
+    return np.abs(D - D_ref) <= tol

@@ -1,0 +1,323 @@
+/*
+ * CPU oracle for the dense matrix-unit GEMM path (test infrastructure only).
+ *
+ * This file is the plain, slow, obviously-correct definition that the HIP
+ * kernels are checked against.  Nothing in the product library links it; only
+ * the test suite, the smoke check and the CPU-baseline leg of the benchmark
+ * load it.  It shares no source, header, table or helper with the GPU path.
+ *
+ * Sources for what is computed (cited by page title and section):
+ *  - "Tensor Cores: Matrix Instructions, Swizzling and FP8, Measured"
+ *    (vidyal.ai), Step 1: an MMA instruction computes D = A*B + C; Step 2:
+ *    B stored N x K, inputs rounded to BF16, FP32 results, error measured
+ *    against an FP64 product; Step 5: FP8 E4M3 inputs with an FP32
+ *    accumulator, promotion of partial sums per block of K.
+ *  - "Tensor Cores" chapter (ai-infra-handbooks), section "Precision: FP16,
+ *    BF16, TF32, FP8": bit splits BF16 1/8/7, E4M3 1/4/3, E5M2 1/5/2; FP8 GEMMs
+ *    carry per-tensor, per-row or per-block scaling factors.
+ *  - "Tensor cores and low precision" (learn-kernels.com), opening
+ *    paragraphs: E4M3 has no infinity and a largest normal of 448, E5M2 keeps
+ *    IEEE specials and reaches 57,344; a tensor is scaled so its largest
+ *    values sit near that maximum, cast down, and the scale is removed after
+ *    the multiply.
+ *
+ * Readings where the pages leave a step open (each also listed in the design
+ * notes): E4M3 is the OCP "FN" variant (no Inf, NaN = S.1111.111); FP8 encode
+ * saturates to +-max instead of producing Inf/NaN; the quantizer multiplies by
+ * m = fl32(FMAX/amax) and stores the dequantisation factor s = fl32(amax/FMAX);
+ * an all-zero block uses m = s = 1; a block holding a NaN has amax = NaN, one
+ * holding an Inf (and no NaN) has amax = +Inf; NaN encodes to 0x7F/0xFF.
+ *
+ * Everything is FP64 with exact decoding.  Each output element is summed in
+ * increasing k order; no blocking or reordering of the sums.
+ * Build: gcc -O2 -fopenmp -ffp-contract=off (never -ffast-math).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORC_FMT_E4M3 0
+#define ORC_FMT_E5M2 1
+#define ORC_B_ROW_MAJOR 0 /* B(k,j) at B[k*ldb + j] */
+#define ORC_B_COL_MAJOR 1 /* B(k,j) at B[j*ldb + k], i.e. B stored N x K */
+#define ORC_SCALE_TENSOR 0
+#define ORC_SCALE_BLOCK 1
+#define ORC_BLOCK 128
+
+/* ---------------------------------------------------------------- decoders */
+
+/* BF16 is the upper half of an IEEE binary32 (1 sign, 8 exponent, 7 fraction
+ * bits); widening is exact. */
+double orc_decode_bf16(uint16_t h) {
+  uint32_t u = (uint32_t)h << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return (double)f;
+}
+
+/* FP8 E4M3 (OCP FN, exponent bias 7) and E5M2 (IEEE-like, bias 15), decoded
+ * from the sign/exponent/mantissa fields. */
+double orc_decode_fp8(uint8_t v, int fmt) {
+  int s = v >> 7;
+  double sign = s ? -1.0 : 1.0;
+  if (fmt == ORC_FMT_E4M3) {
+    int e = (v >> 3) & 15, m = v & 7;
+    if (e == 15 && m == 7) return NAN;
+    if (e == 0) return sign * ldexp((double)m, -9);        /* m/8 * 2^(1-7) */
+    return sign * ldexp((double)(8 + m), e - 10);          /* (1+m/8) * 2^(e-7) */
+  } else {
+    int e = (v >> 2) & 31, m = v & 3;
+    if (e == 31) return m == 0 ? sign * INFINITY : NAN;
+    if (e == 0) return sign * ldexp((double)m, -16);       /* m/4 * 2^(1-15) */
+    return sign * ldexp((double)(4 + m), e - 17);          /* (1+m/4) * 2^(e-15) */
+  }
+}
+
+void orc_decode_bf16_array(const uint16_t* h, int64_t n, double* out) {
+  for (int64_t i = 0; i < n; i++) out[i] = orc_decode_bf16(h[i]);
+}
+
+void orc_decode_fp8_array(const uint8_t* v, int64_t n, int fmt, double* out) {
+  for (int64_t i = 0; i < n; i++) out[i] = orc_decode_fp8(v[i], fmt);
+}
+
+/* ---------------------------------------------------------------- encoders */
+
+/* Round a finite, non-negative double a to the grid of a binary format with
+ * `mbits` fraction bits and smallest normal exponent `emin` (no upper limit),
+ * ties to even.  Works on values: the quantum of a's binade (or of the
+ * subnormal range) divides a exactly in FP64, and rint() rounds half to even
+ * in the default rounding mode. */
+static double round_to_grid(double a, int mbits, int emin) {
+  if (a == 0.0) return 0.0;
+  int e2;
+  frexp(a, &e2);          /* a = f * 2^e2, f in [0.5, 1) */
+  int E = e2 - 1;         /* a in [2^E, 2^(E+1)) */
+  if (E < emin) E = emin; /* subnormal range shares the smallest normal quantum */
+  double q = ldexp(1.0, E - mbits);
+  return rint(a / q) * q;
+}
+
+/* FP32 -> BF16, round to nearest even; overflow goes to Inf (BF16 has Inf);
+ * NaN becomes the quiet NaN 0x7FC0 with the input's sign; no flush to zero. */
+uint16_t orc_encode_bf16(float x) {
+  uint32_t u;
+  memcpy(&u, &x, sizeof u);
+  uint16_t sign = (uint16_t)((u >> 16) & 0x8000u);
+  if (isnan(x)) return (uint16_t)(sign | 0x7FC0u);
+  double a = fabs((double)x);
+  if (isinf(x)) return (uint16_t)(sign | 0x7F80u);
+  double v = round_to_grid(a, 7, -126);
+  if (v >= ldexp(1.0, 128)) return (uint16_t)(sign | 0x7F80u);
+  /* v is exactly a BF16 value, hence exactly an FP32 value whose low 16 bits
+   * are zero. */
+  float fv = (float)v;
+  uint32_t w;
+  memcpy(&w, &fv, sizeof w);
+  return (uint16_t)(sign | (w >> 16));
+}
+
+/* FP32 -> FP8 with round to nearest even and saturation: magnitudes at or
+ * above the format's largest finite value (Inf included) become +-max. */
+uint8_t orc_encode_fp8(float x, int fmt) {
+  uint32_t u;
+  memcpy(&u, &x, sizeof u);
+  uint8_t sign = (uint8_t)((u >> 24) & 0x80u);
+  if (isnan(x)) return (uint8_t)(sign | 0x7F);
+  const int mbits = fmt == ORC_FMT_E4M3 ? 3 : 2;
+  const int bias = fmt == ORC_FMT_E4M3 ? 7 : 15;
+  const int emin = 1 - bias;
+  const double fmax = fmt == ORC_FMT_E4M3 ? 448.0 : 57344.0;
+  const uint8_t maxcode = fmt == ORC_FMT_E4M3 ? 0x7E : 0x7B;
+  double a = fabs((double)x);
+  if (a >= fmax) return (uint8_t)(sign | maxcode);
+  double v = round_to_grid(a, mbits, emin);
+  if (v == 0.0) return sign;
+  /* Recover the fields of the representable value v. */
+  int e2;
+  frexp(v, &e2);
+  int E = e2 - 1;
+  int efield, mfield;
+  if (E < emin) {
+    efield = 0;
+    mfield = (int)(v / ldexp(1.0, emin - mbits));
+  } else {
+    efield = E + bias;
+    mfield = (int)(v / ldexp(1.0, E - mbits)) - (1 << mbits);
+  }
+  return (uint8_t)(sign | (efield << mbits) | mfield);
+}
+
+void orc_encode_bf16_array(const float* x, int64_t n, uint16_t* out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; i++) out[i] = orc_encode_bf16(x[i]);
+}
+
+void orc_encode_fp8_array(const float* x, int64_t n, int fmt, uint8_t* out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; i++) out[i] = orc_encode_fp8(x[i], fmt);
+}
+
+/* ---------------------------------------------------------------- quantize */
+
+/* Per-block FP8 quantisation: amax over the block, m = fl32(FMAX/amax),
+ * q = encode(fl32(x*m)), stored scale s = fl32(amax/FMAX) so x ~ decode(q)*s.
+ * Blocks are block_rows x block_cols; scales are row-major
+ * [rows/block_rows][cols/block_cols].  Returns 0, or -1 on bad arguments. */
+int orc_quantize_fp8(const float* X, int64_t rows, int64_t cols, int64_t ldx, int fmt,
+                     int64_t block_rows, int64_t block_cols, uint8_t* Q, int64_t ldq,
+                     float* scales) {
+  if (rows <= 0 || cols <= 0 || block_rows <= 0 || block_cols <= 0) return -1;
+  if (rows % block_rows || cols % block_cols || ldx < cols || ldq < cols) return -1;
+  if (fmt != ORC_FMT_E4M3 && fmt != ORC_FMT_E5M2) return -1;
+  const float fmax = fmt == ORC_FMT_E4M3 ? 448.0f : 57344.0f;
+  const int64_t nbr = rows / block_rows, nbc = cols / block_cols;
+#pragma omp parallel for collapse(2) schedule(dynamic)
+  for (int64_t bi = 0; bi < nbr; bi++) {
+    for (int64_t bj = 0; bj < nbc; bj++) {
+      float amax = 0.0f;
+      int has_nan = 0;
+      for (int64_t r = bi * block_rows; r < (bi + 1) * block_rows; r++)
+        for (int64_t c = bj * block_cols; c < (bj + 1) * block_cols; c++) {
+          float x = X[r * ldx + c];
+          if (isnan(x)) has_nan = 1;
+          else if (fabsf(x) > amax) amax = fabsf(x);
+        }
+      if (has_nan) amax = NAN;
+      float m, s;
+      if (amax == 0.0f) {
+        m = 1.0f;
+        s = 1.0f;
+      } else {
+        m = fmax / amax;
+        s = amax / fmax;
+      }
+      for (int64_t r = bi * block_rows; r < (bi + 1) * block_rows; r++)
+        for (int64_t c = bj * block_cols; c < (bj + 1) * block_cols; c++) {
+          float y = X[r * ldx + c] * m;
+          Q[r * ldq + c] = orc_encode_fp8(y, fmt);
+        }
+      scales[bi * nbc + bj] = s;
+    }
+  }
+  return 0;
+}
+
+/* ---------------------------------------------------------------- GEMMs */
+
+/* Selected rows of D = A*B + C in FP64, plus S = sum_k |a_ik * b_kj| (the
+ * magnitude that the tolerance scales with).  A is M x K row-major BF16, B is
+ * K x N given row-major or column-major (= stored N x K).  C (FP32 M x N,
+ * row-major) may be NULL.  rows == NULL means all M rows.  Outputs D and S are
+ * [nrows][N] row-major doubles (S may be NULL). */
+int orc_gemm_bf16(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, int b_layout,
+                  const float* C, int64_t ldc, int64_t M, int64_t N, int64_t K,
+                  const int64_t* rows, int64_t nrows, double* D, double* S) {
+  if (M <= 0 || N <= 0 || K <= 0) return -1;
+  if (b_layout != ORC_B_ROW_MAJOR && b_layout != ORC_B_COL_MAJOR) return -1;
+  if (!rows) nrows = M;
+  double* tab = (double*)malloc(65536 * sizeof(double));
+  if (!tab) return -2;
+  for (int h = 0; h < 65536; h++) tab[h] = orc_decode_bf16((uint16_t)h);
+  int bad = 0;
+#pragma omp parallel for schedule(dynamic)
+  for (int64_t r = 0; r < nrows; r++) {
+    int64_t i = rows ? rows[r] : r;
+    if (i < 0 || i >= M) { bad = 1; continue; }
+    double* d = D + r * N;
+    double* s = S ? S + r * N : NULL;
+    if (b_layout == ORC_B_COL_MAJOR) {
+      for (int64_t j = 0; j < N; j++) {
+        double acc = 0.0, sacc = 0.0;
+        for (int64_t k = 0; k < K; k++) {
+          double p = tab[A[i * lda + k]] * tab[B[j * ldb + k]];
+          acc += p;
+          sacc += fabs(p);
+        }
+        d[j] = acc;
+        if (s) s[j] = sacc;
+      }
+    } else {
+      for (int64_t j = 0; j < N; j++) d[j] = 0.0;
+      if (s) for (int64_t j = 0; j < N; j++) s[j] = 0.0;
+      for (int64_t k = 0; k < K; k++) {
+        double a = tab[A[i * lda + k]];
+        const uint16_t* brow = B + k * ldb;
+        for (int64_t j = 0; j < N; j++) {
+          double p = a * tab[brow[j]];
+          d[j] += p;
+          if (s) s[j] += fabs(p);
+        }
+      }
+    }
+    if (C)
+      for (int64_t j = 0; j < N; j++) d[j] += (double)C[i * ldc + j];
+  }
+  free(tab);
+  return bad ? -1 : 0;
+}
+
+/* Selected rows of the scaled FP8 product.  A is M x K row-major, B is stored
+ * N x K (column-major B), both FP8 codes in formats fmt_a / fmt_b.
+ *  per-tensor: D = sa[0]*sb[0]*sum_k a_ik b_jk + C
+ *  per-block:  D = sum_kb sa[i][kb]*sb[j/128][kb]*(sum_{k in kb} a_ik b_jk) + C,
+ *              sa is [M][K/128], sb is [ceil(N/128)][K/128], both row-major;
+ *              each 128-wide partial sum is formed first and then scaled
+ *              (promotion of per-block partial sums).
+ * S receives sum |a*scale_a| * |b*scale_b| over k. */
+int orc_gemm_fp8(const uint8_t* A, int64_t lda, int fmt_a, const uint8_t* B, int64_t ldb,
+                 int fmt_b, const float* sa, const float* sb, int scale_mode, const float* C,
+                 int64_t ldc, int64_t M, int64_t N, int64_t K, const int64_t* rows,
+                 int64_t nrows, double* D, double* S) {
+  if (M <= 0 || N <= 0 || K <= 0) return -1;
+  if (scale_mode != ORC_SCALE_TENSOR && scale_mode != ORC_SCALE_BLOCK) return -1;
+  if (scale_mode == ORC_SCALE_BLOCK && K % ORC_BLOCK) return -1;
+  if (!rows) nrows = M;
+  double ta[256], tb[256];
+  for (int v = 0; v < 256; v++) {
+    ta[v] = orc_decode_fp8((uint8_t)v, fmt_a);
+    tb[v] = orc_decode_fp8((uint8_t)v, fmt_b);
+  }
+  const int64_t nkb = K / ORC_BLOCK;
+  int bad = 0;
+#pragma omp parallel for schedule(dynamic)
+  for (int64_t r = 0; r < nrows; r++) {
+    int64_t i = rows ? rows[r] : r;
+    if (i < 0 || i >= M) { bad = 1; continue; }
+    for (int64_t j = 0; j < N; j++) {
+      const uint8_t* arow = A + i * lda;
+      const uint8_t* bcol = B + j * ldb;
+      double out, sabs;
+      if (scale_mode == ORC_SCALE_TENSOR) {
+        double acc = 0.0, sacc = 0.0;
+        for (int64_t k = 0; k < K; k++) {
+          double p = ta[arow[k]] * tb[bcol[k]];
+          acc += p;
+          sacc += fabs(p);
+        }
+        double sc = (double)sa[0] * (double)sb[0];
+        out = acc * sc;
+        sabs = sacc * fabs(sc);
+      } else {
+        out = 0.0;
+        sabs = 0.0;
+        for (int64_t kb = 0; kb < nkb; kb++) {
+          double part = 0.0, spart = 0.0;
+          for (int64_t k = kb * ORC_BLOCK; k < (kb + 1) * ORC_BLOCK; k++) {
+            double p = ta[arow[k]] * tb[bcol[k]];
+            part += p;
+            spart += fabs(p);
+          }
+          double sc = (double)sa[i * nkb + kb] * (double)sb[(j / ORC_BLOCK) * nkb + kb];
+          out += part * sc;
+          sabs += spart * fabs(sc);
+        }
+      }
+      if (C) out += (double)C[i * ldc + j];
+      D[r * N + j] = out;
+      if (S) S[r * N + j] = sabs;
+    }
+  }
+  return bad ? -1 : 0;
+}
