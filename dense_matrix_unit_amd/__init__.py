@@ -1,0 +1,219 @@
+"""dense_matrix_unit_amd -- MFMA GEMM (BF16 / scaled FP8) for AMD MI355X.
+
+Thin Python binding over the C ABI of ``libdmu.so`` (``include/dmu.h``): the
+functions below only check tensor metadata and marshal pointers, leading
+dimensions and the current HIP stream; every step of the computation runs in
+the library's HIP kernels.  Tensors must live on the GPU (PyTorch is used for
+device memory and streams only).  There is no fallback: if the library is
+missing, importing the binding raises.
+
+BF16 operands are passed as ``torch.bfloat16`` (or ``torch.uint16``/``int16``
+bit patterns); FP8 operands as ``torch.uint8`` codes (or torch float8
+tensors).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libdmu.so")
+
+DMU_OK = 0
+DMU_ERR_INVALID_ARG = -1
+DMU_ERR_UNSUPPORTED = -2
+DMU_ERR_HIP = -3
+OUT_F32 = 0
+OUT_BF16 = 1
+B_ROW_MAJOR = 0
+B_COL_MAJOR = 1
+E4M3 = 0
+E5M2 = 1
+SCALE_TENSOR = 0
+SCALE_BLOCK = 1
+PROBE_BF16_16X16X32 = 0
+PROBE_BF16_32X32X16 = 1
+PROBE_FP8_16X16X128 = 2
+PROBE_FP8_32X32X64 = 3
+
+# (name, restype, argtypes) of every exported C symbol
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_I = ctypes.c_int
+SYMBOLS = {
+    "gemm_bf16": (_I, [_P, _I64, _P, _I64, _I, _P, _I64, _P, _I64, _I, _I64, _I64, _I64, _P]),
+    "gemm_fp8_scaled": (_I, [_P, _I64, _I, _P, _I64, _I, _P, _P, _I, _P, _I64, _P, _I64, _I,
+                             _I64, _I64, _I64, _P]),
+    "quantize_fp8": (_I, [_P, _I64, _I64, _I64, _I, _I64, _I64, _P, _I64, _P, _P]),
+    "dmu_status_string": (ctypes.c_char_p, [_I]),
+    "dmu_version": (_I, []),
+    "dmu_probe_mfma": (_I, [_I, _I, _I, _P, _P, _P, _P, _P]),
+    "dmu_probe_lds_load": (_I, [_P, _P, _I, _I, _P]),
+}
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libdmu.so and declare its C signatures (no GPU needed)."""
+    global _lib
+    if _lib is not None and path == LIB_PATH:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(
+            "libdmu.so is not built (%s); run `python -m dense_matrix_unit_amd.build`" % path)
+    L = ctypes.CDLL(path)
+    for name, (res, args) in SYMBOLS.items():
+        f = getattr(L, name)
+        f.restype = res
+        f.argtypes = args
+    if path == LIB_PATH:
+        _lib = L
+    return L
+
+
+class DmuError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        msg = load_library().dmu_status_string(status).decode()
+        super().__init__("%s: %s (status %d)" % (fn, msg, status))
+        self.status = status
+
+
+def _check(fn: str, rc: int):
+    if rc != DMU_OK:
+        raise DmuError(fn, rc)
+
+
+def _torch():
+    import torch
+
+    return torch
+
+
+def _stream(stream=None):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dev_ptr(t, name):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError("%s must be a GPU tensor" % name)
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _ld(t, name):
+    """Leading dimension (elements) of a 2-D row-major tensor."""
+    if t.dim() != 2 or (t.stride(1) != 1 and t.size(1) > 1):
+        raise ValueError("%s must be 2-D with unit column stride" % name)
+    return t.stride(0)
+
+
+def _check_dtype(t, allowed, name):
+    if t.dtype not in allowed:
+        raise TypeError("%s has dtype %s; expected one of %s" % (name, t.dtype, allowed))
+
+
+def gemm_bf16(A, B, out, b_layout: int = B_COL_MAJOR, C=None, stream=None):
+    """out = A @ B (+ C).  A: [M, K] BF16.  B: [K, N] BF16 if b_layout is
+    B_ROW_MAJOR, or [N, K] (B stored N x K) if B_COL_MAJOR.  out: [M, N] float32
+    or bfloat16.  C: optional [M, N] float32."""
+    torch = _torch()
+    bf = (torch.bfloat16, torch.int16, torch.uint16)
+    _check_dtype(A, bf, "A")
+    _check_dtype(B, bf, "B")
+    _check_dtype(out, (torch.float32, torch.bfloat16), "out")
+    M, K = A.shape
+    N = B.shape[1] if b_layout == B_ROW_MAJOR else B.shape[0]
+    if (B.shape[0] if b_layout == B_ROW_MAJOR else B.shape[1]) != K:
+        raise ValueError("inner dimensions differ")
+    if tuple(out.shape) != (M, N):
+        raise ValueError("out has shape %s, expected %s" % (tuple(out.shape), (M, N)))
+    cptr, ldc = None, 0
+    if C is not None:
+        _check_dtype(C, (torch.float32,), "C")
+        if tuple(C.shape) != (M, N):
+            raise ValueError("C shape")
+        cptr, ldc = _dev_ptr(C, "C"), _ld(C, "C")
+    rc = load_library().gemm_bf16(
+        _dev_ptr(A, "A"), _ld(A, "A"), _dev_ptr(B, "B"), _ld(B, "B"), b_layout, cptr, ldc,
+        _dev_ptr(out, "out"), _ld(out, "out"),
+        OUT_F32 if out.dtype == torch.float32 else OUT_BF16, M, N, K, _stream(stream))
+    _check("gemm_bf16", rc)
+    return out
+
+
+def _fp8_ptr(t, name):
+    torch = _torch()
+    _check_dtype(t, (torch.uint8, torch.float8_e4m3fn, torch.float8_e5m2), name)
+    return _dev_ptr(t, name)
+
+
+def gemm_fp8_scaled(A, B, scale_a, scale_b, out, fmt_a: int = E4M3, fmt_b: int = E4M3,
+                    scale_mode: int = SCALE_TENSOR, C=None, stream=None):
+    """out = (A*scale_a) @ (B*scale_b)^T (+ C).  A: [M, K] FP8 codes, B: [N, K]
+    FP8 codes (B stored N x K).  scale_a/scale_b: float32 device tensors, one
+    element each (SCALE_TENSOR) or [M, K/128] and [ceil(N/128), K/128]
+    (SCALE_BLOCK)."""
+    torch = _torch()
+    _check_dtype(out, (torch.float32, torch.bfloat16), "out")
+    M, K = A.shape
+    N = B.shape[0]
+    if B.shape[1] != K or tuple(out.shape) != (M, N):
+        raise ValueError("shape mismatch")
+    _check_dtype(scale_a, (torch.float32,), "scale_a")
+    _check_dtype(scale_b, (torch.float32,), "scale_b")
+    if scale_mode == SCALE_BLOCK:
+        if tuple(scale_a.shape) != (M, K // 128) or tuple(scale_b.shape) != ((N + 127) // 128, K // 128):
+            raise ValueError("block scale shapes")
+        if not (scale_a.is_contiguous() and scale_b.is_contiguous()):
+            raise ValueError("block scales must be contiguous")
+    elif scale_a.numel() < 1 or scale_b.numel() < 1:
+        raise ValueError("per-tensor scales need one element")
+    cptr, ldc = None, 0
+    if C is not None:
+        _check_dtype(C, (torch.float32,), "C")
+        cptr, ldc = _dev_ptr(C, "C"), _ld(C, "C")
+    rc = load_library().gemm_fp8_scaled(
+        _fp8_ptr(A, "A"), _ld(A, "A"), fmt_a, _fp8_ptr(B, "B"), _ld(B, "B"), fmt_b,
+        _dev_ptr(scale_a, "scale_a"), _dev_ptr(scale_b, "scale_b"), scale_mode, cptr, ldc,
+        _dev_ptr(out, "out"), _ld(out, "out"),
+        OUT_F32 if out.dtype == torch.float32 else OUT_BF16, M, N, K, _stream(stream))
+    _check("gemm_fp8_scaled", rc)
+    return out
+
+
+def quantize_fp8(X, Q, scales, fmt: int = E4M3, block=None, stream=None):
+    """Q, scales = FP8 quantisation of X (float32 [rows, cols]).  block: None
+    (one scale for the tensor), (1, 128) or (128, 128).  Q: uint8 [rows, cols];
+    scales: float32 [rows/br, cols/bc] (dequantisation factors)."""
+    torch = _torch()
+    _check_dtype(X, (torch.float32,), "X")
+    rows, cols = X.shape
+    br, bc = (rows, cols) if block is None else block
+    if tuple(Q.shape) != (rows, cols):
+        raise ValueError("Q shape")
+    if scales.numel() < (rows // br) * (cols // bc) or not scales.is_contiguous():
+        raise ValueError("scales must be contiguous with one element per block")
+    _check_dtype(scales, (torch.float32,), "scales")
+    rc = load_library().quantize_fp8(
+        _dev_ptr(X, "X"), rows, cols, _ld(X, "X"), fmt, br, bc, _fp8_ptr(Q, "Q"), _ld(Q, "Q"),
+        _dev_ptr(scales, "scales"), _stream(stream))
+    _check("quantize_fp8", rc)
+    return Q, scales
+
+
+def probe_mfma(kind: int, A, B, C, D, fmt_a: int = E4M3, fmt_b: int = E4M3, stream=None):
+    """Run one matrix instruction (see include/dmu_probe.h)."""
+    rc = load_library().dmu_probe_mfma(kind, fmt_a, fmt_b, _dev_ptr(A, "A"), _dev_ptr(B, "B"),
+                                       _dev_ptr(C, "C"), _dev_ptr(D, "D"), _stream(stream))
+    _check("dmu_probe_mfma", rc)
+    return D
+
+
+def probe_lds_load(src, dst, mode: int, oob_from: int = 64, stream=None):
+    rc = load_library().dmu_probe_lds_load(_dev_ptr(src, "src"), _dev_ptr(dst, "dst"), mode,
+                                           oob_from, _stream(stream))
+    _check("dmu_probe_lds_load", rc)
+    return dst

@@ -1,0 +1,137 @@
+// C-ABI front end of libdmu: argument validation and kernel dispatch.
+// Semantics and error behaviour of each entry point are documented in
+// include/dmu.h and include/dmu_probe.h.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/dmu.h"
+#include "../../include/dmu_probe.h"
+#include "dmu_internal.h"
+
+namespace {
+
+constexpr int64_t kMaxTileBytes = (int64_t)1 << 31;  // 32-bit buffer offsets inside a tile
+constexpr int kTileRows = 256;                        // largest workgroup tile edge
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+int finish(hipError_t e) { return e == hipSuccess ? DMU_OK : DMU_ERR_HIP; }
+
+// Common checks of D = A*B (+C): sizes, output type, C and D.
+int check_out(const float* C, int64_t ldc, const void* D, int64_t ldd, int d_dtype, int64_t M,
+              int64_t N) {
+  if (!D || M < 1 || N < 1 || M > INT32_MAX || N > INT32_MAX) return DMU_ERR_INVALID_ARG;
+  if (d_dtype != DMU_OUT_F32 && d_dtype != DMU_OUT_BF16) return DMU_ERR_INVALID_ARG;
+  const int64_t osz = d_dtype == DMU_OUT_F32 ? 4 : 2;
+  if (ldd < N || !aligned(D, 16) || (ldd * osz) % 16) return DMU_ERR_INVALID_ARG;
+  if (C) {
+    if (ldc < N || !aligned(C, 16) || (ldc * 4) % 16) return DMU_ERR_INVALID_ARG;
+    if ((const void*)C == D && (d_dtype != DMU_OUT_F32 || ldc != ldd)) return DMU_ERR_INVALID_ARG;
+  }
+  return DMU_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gemm_bf16(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, int b_layout,
+              const float* C, int64_t ldc, void* D, int64_t ldd, int d_dtype, int64_t M,
+              int64_t N, int64_t K, void* stream) {
+  int rc = check_out(C, ldc, D, ldd, d_dtype, M, N);
+  if (rc) return rc;
+  if (!A || !B || K < 8 || K % 8 || K > INT32_MAX) return DMU_ERR_INVALID_ARG;
+  if (b_layout != DMU_B_ROW_MAJOR && b_layout != DMU_B_COL_MAJOR) return DMU_ERR_INVALID_ARG;
+  if (lda < K || (lda * 2) % 16 || !aligned(A, 16) || !aligned(B, 16)) return DMU_ERR_INVALID_ARG;
+  if (b_layout == DMU_B_ROW_MAJOR ? ldb < N : ldb < K) return DMU_ERR_INVALID_ARG;
+  if ((ldb * 2) % 16) return DMU_ERR_INVALID_ARG;
+  if (kTileRows * lda * 2 >= kMaxTileBytes) return DMU_ERR_UNSUPPORTED;
+  if (b_layout == DMU_B_COL_MAJOR ? kTileRows * ldb * 2 >= kMaxTileBytes
+                                  : K * ldb * 2 >= kMaxTileBytes)
+    return DMU_ERR_UNSUPPORTED;
+  dmu::GemmArgs a{A, B, C, D, lda, ldb, ldc, ldd, M, N, K, nullptr, nullptr,
+                  d_dtype == DMU_OUT_BF16};
+  (void)hipGetLastError();
+  return finish(dmu::launch_gemm_bf16(a, b_layout == DMU_B_COL_MAJOR, (hipStream_t)stream));
+}
+
+int gemm_fp8_scaled(const uint8_t* A, int64_t lda, int fmt_a, const uint8_t* B, int64_t ldb,
+                    int fmt_b, const float* scale_a, const float* scale_b, int scale_mode,
+                    const float* C, int64_t ldc, void* D, int64_t ldd, int d_dtype, int64_t M,
+                    int64_t N, int64_t K, void* stream) {
+  int rc = check_out(C, ldc, D, ldd, d_dtype, M, N);
+  if (rc) return rc;
+  if (!A || !B || !scale_a || !scale_b) return DMU_ERR_INVALID_ARG;
+  if (fmt_a != DMU_FP8_E4M3 && fmt_a != DMU_FP8_E5M2) return DMU_ERR_INVALID_ARG;
+  if (fmt_b != DMU_FP8_E4M3 && fmt_b != DMU_FP8_E5M2) return DMU_ERR_INVALID_ARG;
+  if (scale_mode != DMU_SCALE_TENSOR && scale_mode != DMU_SCALE_BLOCK) return DMU_ERR_INVALID_ARG;
+  if (K < 16 || K > INT32_MAX || K % (scale_mode == DMU_SCALE_BLOCK ? 128 : 16))
+    return DMU_ERR_INVALID_ARG;
+  if (lda < K || ldb < K || lda % 16 || ldb % 16) return DMU_ERR_INVALID_ARG;
+  if (!aligned(A, 16) || !aligned(B, 16) || !aligned(scale_a, 4) || !aligned(scale_b, 4))
+    return DMU_ERR_INVALID_ARG;
+  if (kTileRows * lda >= kMaxTileBytes || kTileRows * ldb >= kMaxTileBytes)
+    return DMU_ERR_UNSUPPORTED;
+  if (scale_mode == DMU_SCALE_BLOCK && kTileRows * (K / 128) * 4 >= kMaxTileBytes)
+    return DMU_ERR_UNSUPPORTED;
+  dmu::GemmArgs a{A, B, C, D, lda, ldb, ldc, ldd, M, N, K, scale_a, scale_b,
+                  d_dtype == DMU_OUT_BF16};
+  (void)hipGetLastError();
+  return finish(dmu::launch_gemm_fp8(a, fmt_a, fmt_b, scale_mode == DMU_SCALE_BLOCK,
+                                     (hipStream_t)stream));
+}
+
+int quantize_fp8(const float* X, int64_t rows, int64_t cols, int64_t ldx, int fmt,
+                 int64_t block_rows, int64_t block_cols, uint8_t* Q, int64_t ldq, float* scales,
+                 void* stream) {
+  if (!X || !Q || !scales || rows < 1 || cols < 1) return DMU_ERR_INVALID_ARG;
+  if (fmt != DMU_FP8_E4M3 && fmt != DMU_FP8_E5M2) return DMU_ERR_INVALID_ARG;
+  if (ldx < cols || ldq < cols || ldx % 4 || ldq % 16) return DMU_ERR_INVALID_ARG;
+  if (!aligned(X, 16) || !aligned(Q, 16) || !aligned(scales, 4)) return DMU_ERR_INVALID_ARG;
+  if (block_rows < 1 || block_cols < 1 || rows % block_rows || cols % block_cols)
+    return DMU_ERR_INVALID_ARG;
+  const bool tensor = block_rows == rows && block_cols == cols;
+  const bool row128 = block_rows == 1 && block_cols == 128;
+  const bool blk128 = block_rows == 128 && block_cols == 128;
+  if (!tensor && !row128 && !blk128) return DMU_ERR_UNSUPPORTED;
+  if (tensor && cols % 4) return DMU_ERR_UNSUPPORTED;
+  if ((rows / block_rows) * (cols / block_cols) > INT32_MAX) return DMU_ERR_UNSUPPORTED;
+  (void)hipGetLastError();
+  return finish(dmu::launch_quantize_fp8(X, rows, cols, ldx, fmt, block_rows, block_cols, Q, ldq,
+                                         scales, (hipStream_t)stream));
+}
+
+const char* dmu_status_string(int status) {
+  switch (status) {
+    case DMU_OK:
+      return "DMU_OK";
+    case DMU_ERR_INVALID_ARG:
+      return "DMU_ERR_INVALID_ARG: null pointer, bad size, alignment, leading dimension or enum";
+    case DMU_ERR_UNSUPPORTED:
+      return "DMU_ERR_UNSUPPORTED: valid request outside what this library implements";
+    case DMU_ERR_HIP:
+      return "DMU_ERR_HIP: the HIP runtime reported an error at launch";
+    default:
+      return "unknown dmu status";
+  }
+}
+
+int dmu_version(void) { return (1 << 16) | 0; }
+
+int dmu_probe_mfma(int kind, int fmt_a, int fmt_b, const void* A, const void* B,
+                   const float* C, float* D, void* stream) {
+  if (!A || !B || !C || !D || kind < 0 || kind > 3) return DMU_ERR_INVALID_ARG;
+  if (fmt_a < 0 || fmt_a > 1 || fmt_b < 0 || fmt_b > 1) return DMU_ERR_INVALID_ARG;
+  (void)hipGetLastError();
+  return finish(dmu::launch_probe_mfma(kind, fmt_a, fmt_b, A, B, C, D, (hipStream_t)stream));
+}
+
+int dmu_probe_lds_load(const void* src, void* dst, int mode, int oob_from, void* stream) {
+  if (!src || !dst || (mode != 0 && mode != 1) || oob_from < 0 || oob_from > 64)
+    return DMU_ERR_INVALID_ARG;
+  if (!aligned(src, 16) || !aligned(dst, 16)) return DMU_ERR_INVALID_ARG;
+  (void)hipGetLastError();
+  return finish(dmu::launch_probe_lds(src, dst, mode, oob_from, (hipStream_t)stream));
+}
+
+}  // extern "C"

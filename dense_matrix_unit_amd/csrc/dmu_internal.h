@@ -1,0 +1,37 @@
+// Host-side declarations shared between the C-ABI front end (dmu_api.cpp) and
+// the kernel translation units.  Not part of the public interface.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dmu {
+
+struct GemmArgs {
+  const void* A;
+  const void* B;
+  const float* C;
+  void* D;
+  int64_t lda, ldb, ldc, ldd;  // elements
+  int64_t M, N, K;
+  const float* sa;  // FP8 scales (device)
+  const float* sb;
+  int out_bf16;  // 1: D is BF16, 0: FP32
+};
+
+enum GemmKind { kBF16 = 0, kFP8Tensor = 1, kFP8Block = 2 };
+
+// Launchers: argument checking is done by the caller; these only pick a
+// kernel configuration and launch it.  They return a hipError_t.
+hipError_t launch_gemm_bf16(const GemmArgs& a, int b_col_major, hipStream_t s);
+hipError_t launch_gemm_fp8(const GemmArgs& a, int fmt_a, int fmt_b, int block_scaled,
+                           hipStream_t s);
+hipError_t launch_quantize_fp8(const float* X, int64_t rows, int64_t cols, int64_t ldx, int fmt,
+                               int64_t br, int64_t bc, uint8_t* Q, int64_t ldq, float* scales,
+                               hipStream_t s);
+
+hipError_t launch_probe_mfma(int kind, int fa, int fb, const void* A, const void* B,
+                             const float* C, float* D, hipStream_t s);
+hipError_t launch_probe_lds(const void* src, void* dst, int mode, int oob_from, hipStream_t s);
+
+}  // namespace dmu

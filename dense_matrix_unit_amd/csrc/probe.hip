@@ -1,0 +1,146 @@
+// One-instruction probes of the gfx950 matrix unit and of the direct
+// global -> LDS copy.  They exist so the test suite can pin the lane/register
+// layouts the GEMM kernels rely on, the way the page "Tensor Cores: Matrix
+// Instructions, Swizzling and FP8, Measured" (vidyal.ai), Step 1, checks one
+// mma.sync against the CPU with small-integer inputs, and Step 5 probes how
+// many bits the accumulator keeps (C = 2^e plus a product of 1).
+//
+// Layouts assumed (and therefore tested) for one wave of 64 lanes, with
+// g = lane / rows-per-group:
+//  * 16x16xK MFMA (K = 32 bf16 or 128 fp8): lane l supplies row l%16 of A and
+//    column l%16 of B, holding the K-run [g*K/4, (g+1)*K/4) with g = l/16;
+//    result register v of lane l is D[4*(l/16) + v][l%16].
+//  * 32x32xK MFMA (K = 16 bf16 or 64 fp8): lane l supplies row l%32 of A and
+//    column l%32 of B, holding the K-run [g*K/2, (g+1)*K/2) with g = l/32;
+//    result register v of lane l is D[8*(v/4) + 4*(l/32) + v%4][l%32].
+#include "dmu_device.h"
+#include "dmu_internal.h"
+
+namespace dmu {
+namespace {
+
+// A: [M][K] row-major, B: [N][K] row-major (B stored N x K), C/D: [M][N] FP32.
+template <int KIND, int FA, int FB>
+__global__ void probe_mfma_kernel(const void* Av, const void* Bv, const float* C, float* D) {
+  const int l = threadIdx.x;
+  if constexpr (KIND == 0) {  // bf16 16x16x32
+    const uint16_t* A = (const uint16_t*)Av;
+    const uint16_t* B = (const uint16_t*)Bv;
+    bf16x8_t a, b;
+    for (int p = 0; p < 8; ++p) {
+      a[p] = __builtin_bit_cast(__bf16, A[(l % 16) * 32 + 8 * (l / 16) + p]);
+      b[p] = __builtin_bit_cast(__bf16, B[(l % 16) * 32 + 8 * (l / 16) + p]);
+    }
+    f32x4_t c;
+    for (int v = 0; v < 4; ++v) c[v] = C[(4 * (l / 16) + v) * 16 + l % 16];
+    const f32x4_t d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    for (int v = 0; v < 4; ++v) D[(4 * (l / 16) + v) * 16 + l % 16] = d[v];
+  } else if constexpr (KIND == 1) {  // bf16 32x32x16
+    const uint16_t* A = (const uint16_t*)Av;
+    const uint16_t* B = (const uint16_t*)Bv;
+    bf16x8_t a, b;
+    for (int p = 0; p < 8; ++p) {
+      a[p] = __builtin_bit_cast(__bf16, A[(l % 32) * 16 + 8 * (l / 32) + p]);
+      b[p] = __builtin_bit_cast(__bf16, B[(l % 32) * 16 + 8 * (l / 32) + p]);
+    }
+    f32x16_t c;
+    for (int v = 0; v < 16; ++v) c[v] = C[(8 * (v / 4) + 4 * (l / 32) + v % 4) * 32 + l % 32];
+    const f32x16_t d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    for (int v = 0; v < 16; ++v) D[(8 * (v / 4) + 4 * (l / 32) + v % 4) * 32 + l % 32] = d[v];
+  } else if constexpr (KIND == 2) {  // fp8 16x16x128
+    const uint8_t* A = (const uint8_t*)Av;
+    const uint8_t* B = (const uint8_t*)Bv;
+    i32x8_t a, b;
+    for (int w = 0; w < 8; ++w) {
+      uint32_t x = 0, y = 0;
+      for (int q = 0; q < 4; ++q) {
+        x |= (uint32_t)A[(l % 16) * 128 + 32 * (l / 16) + 4 * w + q] << (8 * q);
+        y |= (uint32_t)B[(l % 16) * 128 + 32 * (l / 16) + 4 * w + q] << (8 * q);
+      }
+      a[w] = (int)x;
+      b[w] = (int)y;
+    }
+    f32x4_t c;
+    for (int v = 0; v < 4; ++v) c[v] = C[(4 * (l / 16) + v) * 16 + l % 16];
+    const f32x4_t d =
+        __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, FA, FB, 0, 0, 0, 0);
+    for (int v = 0; v < 4; ++v) D[(4 * (l / 16) + v) * 16 + l % 16] = d[v];
+  } else {  // fp8 32x32x64
+    const uint8_t* A = (const uint8_t*)Av;
+    const uint8_t* B = (const uint8_t*)Bv;
+    i32x8_t a, b;
+    for (int w = 0; w < 8; ++w) {
+      uint32_t x = 0, y = 0;
+      for (int q = 0; q < 4; ++q) {
+        x |= (uint32_t)A[(l % 32) * 64 + 32 * (l / 32) + 4 * w + q] << (8 * q);
+        y |= (uint32_t)B[(l % 32) * 64 + 32 * (l / 32) + 4 * w + q] << (8 * q);
+      }
+      a[w] = (int)x;
+      b[w] = (int)y;
+    }
+    f32x16_t c;
+    for (int v = 0; v < 16; ++v) c[v] = C[(8 * (v / 4) + 4 * (l / 32) + v % 4) * 32 + l % 32];
+    const f32x16_t d =
+        __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FA, FB, 0, 0, 0, 0);
+    for (int v = 0; v < 16; ++v) D[(8 * (v / 4) + 4 * (l / 32) + v % 4) * 32 + l % 32] = d[v];
+  }
+}
+
+// One wave copies 64 x 16 bytes (mode 0) or 64 x 4 bytes (mode 1) from src to
+// LDS with buffer loads that write LDS directly, then dumps 2 KiB of LDS to
+// dst.  Lanes >= oob_from get an out-of-range offset (they must write zeros).
+__global__ void probe_lds_kernel(const uint8_t* src, uint8_t* dst, int mode, int oob_from) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2048];
+  const int l = threadIdx.x;
+  for (int i = l; i < 2048 / 4; i += 64) ((uint32_t*)lds)[i] = 0xA5A5A5A5u;
+  __syncthreads();
+  const int sz = mode == 0 ? 16 : 4;
+  const __amdgpu_buffer_rsrc_t r = make_rsrc(src, 64 * sz);
+  const uint32_t voff = l < oob_from ? (uint32_t)(l * sz) : kOOB;
+  if (mode == 0)
+    buffer_load_lds16(r, lds, voff, 0);
+  else
+    buffer_load_lds4(r, lds, voff, 0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int i = l; i < 2048 / 4; i += 64) ((uint32_t*)dst)[i] = ((uint32_t*)lds)[i];
+}
+
+template <int KIND>
+hipError_t probe_fmt(int fa, int fb, const void* A, const void* B, const float* C, float* D,
+                     hipStream_t s) {
+#define DMU_PROBE_LAUNCH(FA, FB) \
+  hipLaunchKernelGGL((probe_mfma_kernel<KIND, FA, FB>), dim3(1), dim3(64), 0, s, A, B, C, D)
+  if (fa == 0 && fb == 0) DMU_PROBE_LAUNCH(0, 0);
+  else if (fa == 0 && fb == 1) DMU_PROBE_LAUNCH(0, 1);
+  else if (fa == 1 && fb == 0) DMU_PROBE_LAUNCH(1, 0);
+  else DMU_PROBE_LAUNCH(1, 1);
+#undef DMU_PROBE_LAUNCH
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_probe_mfma(int kind, int fa, int fb, const void* A, const void* B,
+                             const float* C, float* D, hipStream_t s) {
+  switch (kind) {
+    case 0:
+      hipLaunchKernelGGL((probe_mfma_kernel<0, 0, 0>), dim3(1), dim3(64), 0, s, A, B, C, D);
+      return hipGetLastError();
+    case 1:
+      hipLaunchKernelGGL((probe_mfma_kernel<1, 0, 0>), dim3(1), dim3(64), 0, s, A, B, C, D);
+      return hipGetLastError();
+    case 2:
+      return probe_fmt<2>(fa, fb, A, B, C, D, s);
+    default:
+      return probe_fmt<3>(fa, fb, A, B, C, D, s);
+  }
+}
+
+hipError_t launch_probe_lds(const void* src, void* dst, int mode, int oob_from, hipStream_t s) {
+  hipLaunchKernelGGL(probe_lds_kernel, dim3(1), dim3(64), 0, s, (const uint8_t*)src,
+                     (uint8_t*)dst, mode, oob_from);
+  return hipGetLastError();
+}
+
+}  // namespace dmu

@@ -1,0 +1,230 @@
+// FP32 -> FP8 (E4M3 / E5M2) quantisation with one scale per block, for gfx950.
+//
+// What is computed (page "Tensor cores and low precision", learn-kernels.com,
+// paragraph on rescaling before the cast; "Tensor Cores" chapter,
+// ai-infra-handbooks, "Precision" section on per-tensor / per-block scaling
+// factors): for each block, amax = max |x|, m = FMAX / amax, every element is
+// encoded as the saturating round-to-nearest-even FP8 value of the FP32
+// product x*m, and the dequantisation factor s = amax / FMAX is stored.
+//
+// Kernels (all HBM-bound streaming; every value is read once per pass):
+//  * per tensor: (1) clear the amax slot, (2) grid-wide amax with one atomic
+//    max per workgroup on the bit pattern of |x| (for non-negative floats the
+//    integer order is the numeric order, and any NaN pattern sorts above
+//    +Inf, so a NaN anywhere yields a NaN amax), (3) encode, (4) replace amax
+//    by the scale.  The amax slot is scales[0] itself.
+//  * 1 x 128 blocks: 32 lanes per block (16 bytes per lane), half-wave max.
+//  * 128 x 128 blocks: one 256-thread workgroup per block keeps its 64 values
+//    per thread in registers between the amax and the encode (one HBM read).
+#include "dmu_device.h"
+#include "dmu_internal.h"
+
+namespace dmu {
+namespace {
+
+template <int FMT>
+struct Fp8Fmt;
+template <>
+struct Fp8Fmt<0> {  // E4M3 (OCP FN)
+  static constexpr int kMant = 3, kBias = 7;
+  static constexpr uint32_t kMaxBits = 0x43E00000u;  // 448.0f
+  static constexpr uint32_t kMaxCode = 0x7E;
+  static constexpr float kMax = 448.0f;
+};
+template <>
+struct Fp8Fmt<1> {  // E5M2
+  static constexpr int kMant = 2, kBias = 15;
+  static constexpr uint32_t kMaxBits = 0x47600000u;  // 57344.0f
+  static constexpr uint32_t kMaxCode = 0x7B;
+  static constexpr float kMax = 57344.0f;
+};
+
+// Saturating round-to-nearest-even FP32 -> FP8 on the bit pattern.
+template <int FMT>
+__device__ __forceinline__ uint32_t encode_fp8(float y) {
+  using F = Fp8Fmt<FMT>;
+  const uint32_t u = __float_as_uint(y);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7FFFFFFFu;
+  if (a > 0x7F800000u) return sign | 0x7Fu;         // NaN
+  if (a >= F::kMaxBits) return sign | F::kMaxCode;  // saturate (Inf included)
+  constexpr uint32_t kMinNormal = (uint32_t)(127 + 1 - F::kBias) << 23;
+  constexpr int kDrop = 23 - F::kMant;
+  if (a >= kMinNormal) {
+    // keep kMant fraction bits, round half to even, re-bias the exponent
+    const uint32_t r = (a + ((1u << (kDrop - 1)) - 1u) + ((a >> kDrop) & 1u)) >> kDrop;
+    return sign | (r - ((uint32_t)(127 - F::kBias) << F::kMant));
+  }
+  if (a < 0x00800000u) return sign;  // zero or FP32 subnormal: far below half an FP8 step
+  // FP8 subnormal: count multiples of 2^(1 - bias - mant), round half to even
+  const int e = (int)(a >> 23);
+  const uint32_t sig = (a & 0x007FFFFFu) | 0x00800000u;
+  const int shift = 150 + 1 - F::kBias - F::kMant - e;
+  if (shift > 24) return sign;
+  const uint32_t n = (sig + (1u << (shift - 1)) - 1u + ((sig >> shift) & 1u)) >> shift;
+  return sign | n;
+}
+
+__device__ __forceinline__ uint32_t abs_bits(float x) { return __float_as_uint(x) & 0x7FFFFFFFu; }
+
+__device__ __forceinline__ uint32_t wave_max(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, 64));
+  return v;
+}
+
+__device__ __forceinline__ uint32_t half_wave_max(uint32_t v) {
+#pragma unroll
+  for (int o = 16; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, 64));
+  return v;
+}
+
+// m = FMAX / amax (or 1 for an all-zero block), IEEE division.
+template <int FMT>
+__device__ __forceinline__ float mult_from_amax(float amax) {
+  return amax == 0.0f ? 1.0f : Fp8Fmt<FMT>::kMax / amax;
+}
+template <int FMT>
+__device__ __forceinline__ float scale_from_amax(float amax) {
+  return amax == 0.0f ? 1.0f : amax / Fp8Fmt<FMT>::kMax;
+}
+
+template <int FMT>
+__device__ __forceinline__ uint32_t encode4(f32x4_t x, float m) {
+  return encode_fp8<FMT>(x[0] * m) | (encode_fp8<FMT>(x[1] * m) << 8) |
+         (encode_fp8<FMT>(x[2] * m) << 16) | (encode_fp8<FMT>(x[3] * m) << 24);
+}
+
+// ---- per tensor -----------------------------------------------------------
+
+__global__ void clear_slot(float* s) { *(uint32_t*)s = 0u; }
+
+__global__ __launch_bounds__(256) void amax_tensor(const float* X, int64_t rows, int64_t cols4,
+                                                   int64_t ldx, float* slot) {
+  const int64_t total = rows * cols4;
+  uint32_t m = 0;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * 256) {
+    const int64_t r = i / cols4, c = i - r * cols4;
+    const f32x4_t v = *(const f32x4_t*)(X + r * ldx + 4 * c);
+    m = max(m, max(max(abs_bits(v[0]), abs_bits(v[1])), max(abs_bits(v[2]), abs_bits(v[3]))));
+  }
+  m = wave_max(m);
+  __shared__ uint32_t red[4];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t b = max(max(red[0], red[1]), max(red[2], red[3]));
+    atomicMax((unsigned int*)slot, b);
+  }
+}
+
+template <int FMT>
+__global__ __launch_bounds__(256) void encode_tensor(const float* X, int64_t rows, int64_t cols4,
+                                                     int64_t ldx, uint8_t* Q, int64_t ldq,
+                                                     const float* slot) {
+  const float m = mult_from_amax<FMT>(*slot);
+  const int64_t total = rows * cols4;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * 256) {
+    const int64_t r = i / cols4, c = i - r * cols4;
+    const f32x4_t v = *(const f32x4_t*)(X + r * ldx + 4 * c);
+    *(uint32_t*)(Q + r * ldq + 4 * c) = encode4<FMT>(v, m);
+  }
+}
+
+template <int FMT>
+__global__ void finalize_tensor(float* slot) {
+  *slot = scale_from_amax<FMT>(*slot);
+}
+
+// ---- 1 x 128 blocks -------------------------------------------------------
+// 32 lanes own one block (4 values each); a 256-thread workgroup covers 8.
+template <int FMT>
+__global__ __launch_bounds__(256) void quant_1x128(const float* X, int64_t rows, int64_t nbc,
+                                                   int64_t ldx, uint8_t* Q, int64_t ldq,
+                                                   float* scales) {
+  const int64_t blk = (int64_t)blockIdx.x * 8 + (threadIdx.x >> 5);
+  const bool valid = blk < rows * nbc;
+  const int lane = threadIdx.x & 31;
+  int64_t r = 0, cb = 0;
+  f32x4_t v = {0.f, 0.f, 0.f, 0.f};
+  if (valid) {
+    r = blk / nbc;
+    cb = blk - r * nbc;
+    v = *(const f32x4_t*)(X + r * ldx + cb * 128 + 4 * lane);
+  }
+  uint32_t m = max(max(abs_bits(v[0]), abs_bits(v[1])), max(abs_bits(v[2]), abs_bits(v[3])));
+  m = half_wave_max(m);
+  if (valid) {
+    const float amax = __uint_as_float(m);
+    *(uint32_t*)(Q + r * ldq + cb * 128 + 4 * lane) = encode4<FMT>(v, mult_from_amax<FMT>(amax));
+    if (lane == 0) scales[blk] = scale_from_amax<FMT>(amax);
+  }
+}
+
+// ---- 128 x 128 blocks -----------------------------------------------------
+template <int FMT>
+__global__ __launch_bounds__(256) void quant_128x128(const float* X, int64_t nbc, int64_t ldx,
+                                                     uint8_t* Q, int64_t ldq, float* scales) {
+  const int64_t bi = blockIdx.x / nbc, bj = blockIdx.x - (blockIdx.x / nbc) * nbc;
+  const int t = threadIdx.x, c4 = t & 31, r0 = t >> 5;  // rows r0, r0+8, ... ; float4 column c4
+  const float* base = X + (bi * 128) * ldx + bj * 128 + 4 * c4;
+  f32x4_t v[16];
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    v[i] = *(const f32x4_t*)(base + (int64_t)(r0 + 8 * i) * ldx);
+    m = max(m, max(max(abs_bits(v[i][0]), abs_bits(v[i][1])),
+                   max(abs_bits(v[i][2]), abs_bits(v[i][3]))));
+  }
+  m = wave_max(m);
+  __shared__ uint32_t red[4];
+  if ((t & 63) == 0) red[t >> 6] = m;
+  __syncthreads();
+  m = max(max(red[0], red[1]), max(red[2], red[3]));
+  const float amax = __uint_as_float(m);
+  const float mult = mult_from_amax<FMT>(amax);
+  uint8_t* qb = Q + (bi * 128) * ldq + bj * 128 + 4 * c4;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) *(uint32_t*)(qb + (int64_t)(r0 + 8 * i) * ldq) = encode4<FMT>(v[i], mult);
+  if (t == 0) scales[blockIdx.x] = scale_from_amax<FMT>(amax);
+}
+
+template <int FMT>
+hipError_t launch_fmt(const float* X, int64_t rows, int64_t cols, int64_t ldx, int64_t br,
+                      int64_t bc, uint8_t* Q, int64_t ldq, float* scales, hipStream_t s) {
+  if (br == rows && bc == cols) {
+    const int64_t cols4 = cols / 4, total = rows * cols4;
+    int64_t grid = (total + 255) / 256;
+    if (grid > 2048) grid = 2048;  // 8 resident workgroups per CU on 256 CUs
+    hipLaunchKernelGGL(clear_slot, dim3(1), dim3(1), 0, s, scales);
+    hipLaunchKernelGGL(amax_tensor, dim3((unsigned)grid), dim3(256), 0, s, X, rows, cols4, ldx,
+                       scales);
+    int64_t egrid = (total + 255) / 256;
+    if (egrid > 8192) egrid = 8192;
+    hipLaunchKernelGGL(encode_tensor<FMT>, dim3((unsigned)egrid), dim3(256), 0, s, X, rows,
+                       cols4, ldx, Q, ldq, scales);
+    hipLaunchKernelGGL(finalize_tensor<FMT>, dim3(1), dim3(1), 0, s, scales);
+  } else if (br == 1 && bc == 128) {
+    const int64_t nbc = cols / 128, nblk = rows * nbc;
+    hipLaunchKernelGGL(quant_1x128<FMT>, dim3((unsigned)((nblk + 7) / 8)), dim3(256), 0, s, X,
+                       rows, nbc, ldx, Q, ldq, scales);
+  } else {
+    const int64_t nbc = cols / 128, nblk = (rows / 128) * nbc;
+    hipLaunchKernelGGL(quant_128x128<FMT>, dim3((unsigned)nblk), dim3(256), 0, s, X, nbc, ldx, Q,
+                       ldq, scales);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_quantize_fp8(const float* X, int64_t rows, int64_t cols, int64_t ldx, int fmt,
+                               int64_t br, int64_t bc, uint8_t* Q, int64_t ldq, float* scales,
+                               hipStream_t s) {
+  if (fmt == 0) return launch_fmt<0>(X, rows, cols, ldx, br, bc, Q, ldq, scales, s);
+  return launch_fmt<1>(X, rows, cols, ldx, br, bc, Q, ldq, scales, s);
+}
+
+}  // namespace dmu

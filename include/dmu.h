@@ -1,0 +1,150 @@
+/*
+ * dmu.h -- dense matrix-unit GEMM library for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI.  Every pointer argument is a DEVICE pointer (memory the caller
+ * allocated on the GPU, e.g. a torch tensor's data_ptr()); the caller owns all
+ * buffers and the library keeps no reference after a call returns.  `stream`
+ * is a hipStream_t passed as void* (NULL = the default stream).  Every call
+ * only validates its arguments on the host, enqueues its kernels on `stream`
+ * and returns without synchronising; a nonzero status means nothing was
+ * enqueued (or, for DMU_ERR_HIP, that the launch itself failed).  Faults
+ * inside a kernel surface at the caller's next synchronisation.  Calls are
+ * thread-safe; the library holds no mutable global state.
+ *
+ * Matrices are dense with a leading dimension counted in elements: element
+ * (r, c) of a row-major matrix X lives at X[r * ldx + c].  Every pointer must
+ * be 16-byte aligned and every leading dimension times the element size must
+ * be a multiple of 16 bytes.
+ *
+ * What is computed follows the pages on tensor-core GEMMs:
+ *  - "Tensor Cores: Matrix Instructions, Swizzling and FP8, Measured"
+ *    (vidyal.ai), Step 1 (a matrix instruction computes D = A*B + C), Step 2
+ *    (B stored N x K as PyTorch stores nn.Linear weights, BF16 inputs, FP32
+ *    accumulation), Step 5 (FP8 E4M3 inputs, FP32 accumulator, promotion of
+ *    partial sums to FP32 per block of K);
+ *  - "Tensor Cores" chapter (ai-infra-handbooks), section "Precision: FP16,
+ *    BF16, TF32, FP8" (FP16/BF16 in, FP32 accumulate; FP8 GEMMs carry
+ *    per-tensor, per-row or per-block scale factors);
+ *  - "Tensor cores and low precision" (learn-kernels.com), paragraphs on E4M3
+ *    and E5M2 and on scaling before the cast (a tensor is scaled so that its
+ *    largest values sit near 448 or 57,344, cast to FP8, and the scale is
+ *    removed after the multiply).
+ */
+#ifndef DMU_H
+#define DMU_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by every entry point. */
+#define DMU_OK 0
+#define DMU_ERR_INVALID_ARG (-1) /* null pointer, bad size, alignment or enum */
+#define DMU_ERR_UNSUPPORTED (-2) /* valid request this library does not implement */
+#define DMU_ERR_HIP (-3)         /* the HIP runtime reported an error at launch */
+
+/* Output element type of D. */
+#define DMU_OUT_F32 0  /* IEEE binary32 */
+#define DMU_OUT_BF16 1 /* bfloat16, rounded to nearest even from the FP32 result */
+
+/* Storage of the K x N operand B. */
+#define DMU_B_ROW_MAJOR 0 /* B(k, n) at B[k * ldb + n] */
+#define DMU_B_COL_MAJOR 1 /* B(k, n) at B[n * ldb + k]: B stored N x K ("TN") */
+
+/* FP8 encodings (OCP 8-bit floating point). */
+#define DMU_FP8_E4M3 0 /* 1/4/3 bits, bias 7, largest finite 448, no Inf, NaN = S.1111.111 */
+#define DMU_FP8_E5M2 1 /* 1/5/2 bits, bias 15, largest finite 57344, IEEE Inf/NaN */
+
+/* Scale granularity of gemm_fp8_scaled. */
+#define DMU_SCALE_TENSOR 0 /* one FP32 scale per operand */
+#define DMU_SCALE_BLOCK 1  /* A: one scale per 1 x 128 row segment; B: per 128 x 128 block */
+
+/*
+ * gemm_bf16: D = A * B (+ C), BF16 inputs, FP32 accumulation.
+ *
+ *   A  : M x K BF16 (uint16 bit patterns), row-major, leading dimension lda.
+ *   B  : K x N BF16, layout `b_layout` (DMU_B_ROW_MAJOR or DMU_B_COL_MAJOR),
+ *        leading dimension ldb.
+ *   C  : optional M x N FP32 addend, row-major, ldc (NULL = no addend).  C may
+ *        be the same memory as D when d_dtype is DMU_OUT_F32 and ldc == ldd.
+ *   D  : M x N output, row-major, ldd, type `d_dtype` (DMU_OUT_F32 or
+ *        DMU_OUT_BF16).
+ *   M, N >= 1; K >= 8 and K % 8 == 0.
+ * Each D element is the FP32 sum over k of the exact products a_ik * b_kj
+ * (summation order unspecified), plus C, rounded once to the output type.
+ * Errors: DMU_ERR_INVALID_ARG for null A/B/D, non-positive sizes, K % 8 != 0,
+ * lda < K, ldb < (row-major ? N : K), ldc/ldd < N, a misaligned pointer or
+ * leading dimension, or an unknown enum value.
+ */
+int gemm_bf16(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, int b_layout,
+              const float* C, int64_t ldc, void* D, int64_t ldd, int d_dtype, int64_t M,
+              int64_t N, int64_t K, void* stream);
+
+/*
+ * gemm_fp8_scaled: D = dequantised(A) * dequantised(B) (+ C) with FP8 inputs
+ * and FP32 accumulation.
+ *
+ *   A       : M x K FP8 codes (format fmt_a), row-major, lda.
+ *   B       : K x N operand stored N x K (column-major B), FP8 codes (fmt_b),
+ *             leading dimension ldb (bytes per stored row).
+ *   scale_a, scale_b : FP32 dequantisation factors (x ~ decode(code) * scale),
+ *             device pointers:
+ *     DMU_SCALE_TENSOR: one float each;
+ *       D = (sum_k a_ik b_jk) * scale_a[0] * scale_b[0] (+ C).
+ *     DMU_SCALE_BLOCK : scale_a is [M][K/128] row-major (one per 1 x 128 row
+ *       segment of A), scale_b is [ceil(N/128)][K/128] row-major (one per
+ *       128 x 128 block of the stored N x K matrix);
+ *       D = sum_kb scale_a[i][kb] * scale_b[j/128][kb] * (sum_{k in kb} a_ik b_jk)
+ *       (+ C): every 128-wide partial sum is formed from zero in the matrix
+ *       unit and then promoted into the FP32 accumulator with its scales.
+ *   C, D    : as for gemm_bf16.
+ *   M, N >= 1; K % 16 == 0 (DMU_SCALE_TENSOR) or K % 128 == 0 (DMU_SCALE_BLOCK).
+ * Errors: DMU_ERR_INVALID_ARG as for gemm_bf16, plus null scales or an
+ * unknown format / scale mode.
+ */
+int gemm_fp8_scaled(const uint8_t* A, int64_t lda, int fmt_a, const uint8_t* B, int64_t ldb,
+                    int fmt_b, const float* scale_a, const float* scale_b, int scale_mode,
+                    const float* C, int64_t ldc, void* D, int64_t ldd, int d_dtype, int64_t M,
+                    int64_t N, int64_t K, void* stream);
+
+/*
+ * quantize_fp8: FP32 -> FP8 with one scale per block.
+ *
+ *   X      : rows x cols FP32, row-major, ldx.
+ *   fmt    : DMU_FP8_E4M3 (FMAX = 448) or DMU_FP8_E5M2 (FMAX = 57344).
+ *   block_rows x block_cols : the scaling block.  Supported: (rows, cols) =
+ *            one per-tensor scale; (1, 128) = per row segment; (128, 128).
+ *            rows % block_rows == 0 and cols % block_cols == 0.
+ *   Q      : rows x cols FP8 codes, row-major, ldq.
+ *   scales : [rows/block_rows][cols/block_cols] FP32, row-major.
+ * For each block: amax = max |x|; m = FMAX / amax and s = amax / FMAX, both
+ * IEEE FP32 divisions; q = saturating round-to-nearest-even FP8 encoding of the
+ * FP32 product x * m (magnitudes >= FMAX, Inf included, become +-FMAX; FP8
+ * subnormals are kept; -0 stays -0); the stored scale is s, the factor that
+ * dequantises (x ~ decode(q) * s), which is what gemm_fp8_scaled takes.
+ * An all-zero block gets m = s = 1.  A block holding a NaN gets amax = NaN
+ * (scale NaN, codes NaN); one holding an Inf and no NaN gets amax = +Inf
+ * (scale +Inf, finite inputs encode to +-0, infinite ones to NaN).  The result
+ * is bit-exact and independent of launch configuration.
+ * The per-tensor mode writes amax into scales[0] as scratch before it writes
+ * the final scale there, and needs no other workspace.
+ * Errors: DMU_ERR_INVALID_ARG for null pointers, bad sizes, leading dimensions
+ * or alignment, an unknown format; DMU_ERR_UNSUPPORTED for other block shapes.
+ */
+int quantize_fp8(const float* X, int64_t rows, int64_t cols, int64_t ldx, int fmt,
+                 int64_t block_rows, int64_t block_cols, uint8_t* Q, int64_t ldq, float* scales,
+                 void* stream);
+
+/* Human-readable text for a status code (static storage, never NULL). */
+const char* dmu_status_string(int status);
+
+/* Library ABI version: (major << 16) | minor. */
+int dmu_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DMU_H */

@@ -1,0 +1,52 @@
+/*
+ * dmu_probe.h -- diagnostic entry points of libdmu (gfx950).
+ *
+ * One-instruction probes used by the test suite to pin the hardware facts the
+ * GEMM kernels rely on, in the manner of the page "Tensor Cores: Matrix
+ * Instructions, Swizzling and FP8, Measured" (vidyal.ai): Step 1 checks a
+ * single matrix instruction against the CPU with small-integer inputs (exact
+ * in the input format), and Step 5 probes how many bits the accumulator keeps
+ * by adding a product of 1 to C = 2^e.  All pointers are device pointers owned
+ * by the caller; calls enqueue on `stream` (a hipStream_t as void*) and return
+ * without synchronising.
+ */
+#ifndef DMU_PROBE_H
+#define DMU_PROBE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DMU_PROBE_BF16_16X16X32 0 /* v_mfma_f32_16x16x32_bf16 */
+#define DMU_PROBE_BF16_32X32X16 1 /* v_mfma_f32_32x32x16_bf16 */
+#define DMU_PROBE_FP8_16X16X128 2 /* v_mfma_f32_16x16x128_f8f6f4 */
+#define DMU_PROBE_FP8_32X32X64 3  /* v_mfma_f32_32x32x64_f8f6f4 */
+
+/*
+ * Run ONE matrix instruction of `kind` on a single wave: D = A * B + C with
+ * A [m][k] row-major, B given as [n][k] row-major (B stored N x K), C and D
+ * [m][n] row-major FP32, where (m, n, k) is the instruction's shape.  Elements
+ * are BF16 bit patterns (kinds 0, 1) or FP8 codes in formats fmt_a / fmt_b
+ * (0 = E4M3, 1 = E5M2; kinds 2, 3).  Fragments are loaded with the layout the
+ * GEMM kernels assume (documented in probe.hip); a wrong assumption shows up
+ * as a wrong D.  Returns DMU_OK or DMU_ERR_INVALID_ARG / DMU_ERR_HIP.
+ */
+int dmu_probe_mfma(int kind, int fmt_a, int fmt_b, const void* A, const void* B,
+                   const float* C, float* D, void* stream);
+
+/*
+ * Copy 64 x 16 bytes (mode 0) or 64 x 4 bytes (mode 1) from src into LDS with
+ * one buffer load per lane that writes LDS directly (lane l's bytes are
+ * expected at LDS offset l*size), lanes >= oob_from using an out-of-range
+ * offset (expected to write zeros), after filling 2 KiB of LDS with 0xA5;
+ * then write those 2 KiB of LDS to dst (2048 bytes).
+ */
+int dmu_probe_lds_load(const void* src, void* dst, int mode, int oob_from, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DMU_PROBE_H */

@@ -1,0 +1,108 @@
+"""The C-ABI library loads on the CPU host, exports every function the public
+headers declare, and rejects bad arguments before launching anything (every
+call below fails validation, so no GPU is touched)."""
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+import dense_matrix_unit_amd as dmu
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M):
+            names.add(m.group(1))
+    return names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = dmu.load_library()
+    names = declared_functions()
+    assert {"gemm_bf16", "gemm_fp8_scaled", "quantize_fp8", "dmu_status_string"} <= names
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in dmu.SYMBOLS, n
+
+
+def test_status_strings_and_version():
+    lib = dmu.load_library()
+    assert lib.dmu_version() >> 16 == 1
+    for s in (0, -1, -2, -3, 7):
+        assert lib.dmu_status_string(s)
+    assert b"INVALID" in lib.dmu_status_string(-1)
+
+
+FAKE = 1 << 20  # aligned, never dereferenced: every call below is rejected first
+
+
+def call_bf16(**kw):
+    a = dict(A=FAKE, lda=64, B=FAKE, ldb=64, b_layout=1, C=None, ldc=0, D=FAKE, ldd=64,
+             d_dtype=0, M=64, N=64, K=64, stream=None)
+    a.update(kw)
+    return dmu.load_library().gemm_bf16(*a.values())
+
+
+@pytest.mark.parametrize("kw", [
+    dict(A=None), dict(B=None), dict(D=None), dict(M=0), dict(N=-1), dict(K=0), dict(K=12),
+    dict(lda=32), dict(ldb=32), dict(ldd=32), dict(b_layout=2), dict(d_dtype=5),
+    dict(A=FAKE + 2), dict(D=FAKE + 8), dict(lda=68), dict(C=FAKE, ldc=8),
+    dict(C=FAKE, ldc=64, d_dtype=1), dict(b_layout=0, ldb=60),
+])
+def test_gemm_bf16_rejects(kw):
+    assert call_bf16(**kw) == dmu.DMU_ERR_INVALID_ARG
+
+
+def test_gemm_bf16_unsupported_huge_ld():
+    assert call_bf16(lda=1 << 23, K=64) == dmu.DMU_ERR_UNSUPPORTED
+
+
+def call_fp8(**kw):
+    a = dict(A=FAKE, lda=128, fa=0, B=FAKE, ldb=128, fb=0, sa=FAKE, sb=FAKE, mode=0, C=None,
+             ldc=0, D=FAKE, ldd=64, d_dtype=1, M=64, N=64, K=128, stream=None)
+    a.update(kw)
+    return dmu.load_library().gemm_fp8_scaled(*a.values())
+
+
+@pytest.mark.parametrize("kw", [
+    dict(A=None), dict(sa=None), dict(sb=None), dict(fa=2), dict(fb=-1), dict(mode=3),
+    dict(K=8), dict(K=136, mode=1, lda=144, ldb=144), dict(lda=120), dict(ldb=136),
+    dict(sa=FAKE + 2), dict(M=0),
+])
+def test_gemm_fp8_rejects(kw):
+    assert call_fp8(**kw) == dmu.DMU_ERR_INVALID_ARG
+
+
+def call_quant(**kw):
+    a = dict(X=FAKE, rows=256, cols=256, ldx=256, fmt=0, br=1, bc=128, Q=FAKE, ldq=256,
+             scales=FAKE, stream=None)
+    a.update(kw)
+    return dmu.load_library().quantize_fp8(*a.values())
+
+
+@pytest.mark.parametrize("kw", [
+    dict(X=None), dict(Q=None), dict(scales=None), dict(rows=0), dict(fmt=2), dict(ldx=128),
+    dict(ldq=200), dict(br=3), dict(bc=100), dict(X=FAKE + 4), dict(ldx=258),
+])
+def test_quantize_rejects(kw):
+    assert call_quant(**kw) == dmu.DMU_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kw", [dict(br=2, bc=128), dict(br=1, bc=64), dict(br=256, bc=128)])
+def test_quantize_unsupported_blocks(kw):
+    assert call_quant(**kw) == dmu.DMU_ERR_UNSUPPORTED
+
+
+def test_python_binding_rejects_cpu_tensors():
+    import torch
+
+    A = torch.zeros(64, 64, dtype=torch.bfloat16)
+    with pytest.raises(TypeError):
+        dmu.gemm_bf16(A, A, torch.zeros(64, 64))

@@ -1,0 +1,90 @@
+"""quantize_fp8 (HIP) must equal the oracle bit for bit: codes and scales."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import dense_matrix_unit_amd as dmu
+from dense_matrix_unit_amd import workloads as wl
+from gpu_helpers import dev
+
+pytestmark = pytest.mark.gpu
+FMTS = [dmu.E4M3, dmu.E5M2]
+BLOCKS = [None, (1, 128), (128, 128)]
+
+
+def nan_code(q):
+    return (q & 0x7F) == 0x7F
+
+
+def run_quant(X, fmt, block, ldq_pad=0):
+    rows, cols = X.shape
+    br, bc = (rows, cols) if block is None else block
+    Qbig = torch.full((rows, cols + ldq_pad), 0x5A, dtype=torch.uint8, device="cuda")
+    Q = Qbig[:, :cols]
+    s = torch.full(((rows // br) * (cols // bc),), -7.0, dtype=torch.float32, device="cuda")
+    dmu.quantize_fp8(dev(X) if not isinstance(X, torch.Tensor) else X, Q, s, fmt, block)
+    torch.cuda.synchronize()
+    if ldq_pad:
+        assert torch.all(Qbig[:, cols:] == 0x5A)
+    return Q.cpu().numpy(), s.cpu().numpy().reshape(rows // br, cols // bc)
+
+
+def compare(X, fmt, block, Q, s):
+    Qr, sr = oracle.quantize_fp8(X, fmt, *(block or (None, None)))
+    both_nan = nan_code(Q) & nan_code(Qr)           # NaN sign is unspecified
+    assert np.array_equal(np.where(both_nan, 0, Q), np.where(both_nan, 0, Qr))
+    nan_s = np.isnan(s) & np.isnan(sr)
+    assert np.array_equal(np.where(nan_s, 0, s).view(np.uint32), np.where(nan_s, 0, sr).view(np.uint32))
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("block", BLOCKS)
+def test_bit_exact_small(fmt, block):
+    X, _ = wl.normal_with_outlier_rows((384, 640), 3, frac=0.02)
+    Q, s = run_quant(X, fmt, block)
+    compare(X, fmt, block, Q, s)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("block", BLOCKS)
+def test_bit_exact_wide_range_and_strides(fmt, block):
+    # magnitudes over many binades so FP8 subnormals, ties and saturation occur
+    rng = np.random.default_rng(5)
+    X = (rng.standard_normal((256, 384)) * 2.0 ** rng.integers(-30, 30, (256, 384))).astype(np.float32)
+    X[0, :8] = [0.0, -0.0, 1e-40, -1e-45, 3e38, -3e38, 2.0 ** -20, 448.0]
+    Xbig = np.zeros((256, 400), np.float32)
+    Xbig[:, :384] = X
+    Xt = dev(Xbig)[:, :384]
+    Q, s = run_quant(Xt, fmt, block, ldq_pad=16)
+    compare(X, fmt, block, Q, s)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_special_blocks(fmt):
+    X = wl.normal((128, 512), 4)
+    X[0, 3] = np.nan            # block (0,0) of 1x128: NaN
+    X[1, 130] = np.inf          # block (1,1): Inf
+    X[2, 256:384] = 0.0         # block (2,2): all zero
+    X[2, 300] = -0.0
+    X[3, 384:512] = -2.5        # all equal
+    for block in [(1, 128), (128, 128), None]:
+        Q, s = run_quant(X, fmt, block)
+        compare(X, fmt, block, Q, s)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_per_tensor_4096(fmt):
+    X = wl.normal((4096, 4096), wl.SEED_A)
+    Q, s = run_quant(X, fmt, None)
+    compare(X, fmt, None, Q, s)
+
+
+def test_block_sizes_of_block_scaled_workload():
+    Xa, _ = wl.normal_with_outlier_rows((8192, 7168), wl.SEED_A)
+    Q, s = run_quant(Xa, dmu.E4M3, (1, 128))
+    compare(Xa, dmu.E4M3, (1, 128), Q, s)
+    del Xa, Q, s
+    Xb = wl.normal((7168, 7168), wl.SEED_B)
+    Q, s = run_quant(Xb, dmu.E4M3, (128, 128))
+    compare(Xb, dmu.E4M3, (128, 128), Q, s)
