@@ -1,0 +1,352 @@
+#!/usr/bin/env python3
+"""Benchmark of the dense matrix-unit GEMM path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--legs all|headline|name,...]
+
+Headline (the JSON line's `value`): gemm_bf16 at M = N = K = 4096, A row-major,
+B stored N x K, BF16 output, inputs N(0,1) rounded to BF16, in TFLOP/s.  A
+"step" is one launch of that GEMM; K steps are timed between two device
+synchronisations, each launch also bracketed by HIP events on the stream it
+runs on.  The other workloads (B row-major, FP8 per-tensor E4M3/E5M2, the
+block-scaled 8192x7168x7168 GEMM and its quantizers, the LLM-shaped sweep,
+256^3) are timed the same way in the same process and reported under "legs".
+
+Operands are resident in HBM before timing starts.  The 4096^3 legs rotate
+over several operand copies whose total exceeds the 256 MB Infinity Cache, so
+successive launches do not find their operands in the last-level cache.
+
+`cpu_baseline` times the CPU oracle (FP64, all host threads) on a bounded
+sample of the headline workload: blocks of 256 output rows until 10 s have
+passed or the whole product is done.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6  # 256 CU x 4096 FLOP/clk x 2.4 GHz (published 2.5 PFLOP/s dense)
+PEAK_FP8_TFLOPS = 5033.2   # 256 CU x 8192 FLOP/clk x 2.4 GHz (published 5.0 PFLOP/s dense)
+PEAK_HBM_GBS = 8000.0
+METRIC = "GEMM TFLOP/s and % of MFMA peak, 4096³ BF16 and FP8 E4M3, 1×MI355X"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = ["dense_matrix_unit_amd/csrc/gemm.hip", "dense_matrix_unit_amd/csrc/dmu_device.h"]
+
+
+def log(msg):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def time_launches(torch, launch, steps, warmup):
+    """Run `launch(i)` warmup times, then time `steps` launches.  Returns the
+    wall-clock time per launch between two synchronisations and the per-launch
+    HIP-event durations (same stream as the kernels)."""
+    for i in range(warmup):
+        launch(i)
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record()
+        launch(i)
+        ends[i].record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    d = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    return {"wall_ms": (t1 - t0) * 1e3 / steps, "event_mean_ms": statistics.fmean(d),
+            "event_median_ms": statistics.median(d)}
+
+
+class Bench:
+    def __init__(self, args):
+        import torch
+
+        import dense_matrix_unit_amd as dmu
+        from dense_matrix_unit_amd import workloads as wl
+
+        self.torch, self.dmu, self.wl, self.args = torch, dmu, wl, args
+        dmu.load_library()  # raises if the HIP library is not built
+        self.dev = torch.device("cuda:0")
+
+    # ---- input helpers (harness step: FP32 sources -> BF16, untimed)
+    def normal_bf16(self, shape, seed):
+        t = self.torch.from_numpy(self.wl.normal(shape, seed)).to(self.dev)
+        return t.to(self.torch.bfloat16)
+
+    def normal_f32(self, shape, seed):
+        return self.torch.from_numpy(self.wl.normal(shape, seed)).to(self.dev)
+
+    def copies(self, t, n):
+        return [t] + [t.clone() for _ in range(n - 1)]
+
+    # ---- legs
+    def gemm_bf16_leg(self, M, N, K, layout, steps, warmup, copies=1, out_f32=False,
+                      seed_dist="normal", B=None):
+        torch, dmu = self.torch, self.dmu
+        bshape = (N, K) if layout == dmu.B_COL_MAJOR else (K, N)
+        if seed_dist == "uniform":
+            A = torch.from_numpy(self.wl.uniform_pm1((M, K), 1)).to(self.dev).to(torch.bfloat16)
+            B = torch.from_numpy(self.wl.uniform_pm1(bshape, 2)).to(self.dev).to(torch.bfloat16)
+        else:
+            A = self.normal_bf16((M, K), 1)
+            if B is None:
+                B = self.normal_bf16(bshape, 2)
+        As, Bs = self.copies(A, copies), self.copies(B, copies)
+        outs = [torch.empty((M, N), dtype=torch.float32 if out_f32 else torch.bfloat16,
+                            device=self.dev) for _ in range(min(copies, 2))]
+
+        def launch(i):
+            dmu.gemm_bf16(As[i % copies], Bs[i % copies], outs[i % len(outs)], layout)
+
+        t = time_launches(torch, launch, steps, warmup)
+        flop = 2.0 * M * N * K
+        bytes_ = 2.0 * (M * K + N * K) + (4.0 if out_f32 else 2.0) * M * N
+        return self.report(t, flop, bytes_, PEAK_BF16_TFLOPS, copies)
+
+    def fp8_operands(self, M, N, K, fmt, block=None):
+        torch, dmu = self.torch, self.dmu
+        if block:
+            Xa, _ = self.wl.normal_with_outlier_rows((M, K), 1)
+            Xa = torch.from_numpy(Xa).to(self.dev)
+        else:
+            Xa = self.normal_f32((M, K), 1)
+        Xb = self.normal_f32((N, K), 2)
+        Qa = torch.empty((M, K), dtype=torch.uint8, device=self.dev)
+        Qb = torch.empty((N, K), dtype=torch.uint8, device=self.dev)
+        if block:
+            sa = torch.empty((M, K // 128), dtype=torch.float32, device=self.dev)
+            sb = torch.empty(((N + 127) // 128, K // 128), dtype=torch.float32, device=self.dev)
+            dmu.quantize_fp8(Xa, Qa, sa, fmt, (1, 128))
+            dmu.quantize_fp8(Xb, Qb, sb, fmt, (128, 128))
+        else:
+            sa = torch.empty(1, dtype=torch.float32, device=self.dev)
+            sb = torch.empty(1, dtype=torch.float32, device=self.dev)
+            dmu.quantize_fp8(Xa, Qa, sa, fmt)
+            dmu.quantize_fp8(Xb, Qb, sb, fmt)
+        return Xa, Xb, Qa, Qb, sa, sb
+
+    def gemm_fp8_leg(self, M, N, K, fmt, steps, warmup, copies=1, block=False):
+        torch, dmu = self.torch, self.dmu
+        Xa, Xb, Qa, Qb, sa, sb = self.fp8_operands(M, N, K, fmt, block)
+        del Xa, Xb
+        Qas, Qbs = self.copies(Qa, copies), self.copies(Qb, copies)
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=self.dev)
+        mode = dmu.SCALE_BLOCK if block else dmu.SCALE_TENSOR
+
+        def launch(i):
+            dmu.gemm_fp8_scaled(Qas[i % copies], Qbs[i % copies], sa, sb, out, fmt, fmt, mode)
+
+        t = time_launches(torch, launch, steps, warmup)
+        flop = 2.0 * M * N * K
+        bytes_ = 1.0 * (M * K + N * K) + 2.0 * M * N + 4.0 * (sa.numel() + sb.numel())
+        return self.report(t, flop, bytes_, PEAK_FP8_TFLOPS, copies)
+
+    def quantize_leg(self, rows, cols, fmt, block, steps, warmup, outliers=False):
+        torch, dmu = self.torch, self.dmu
+        if outliers:
+            X, _ = self.wl.normal_with_outlier_rows((rows, cols), 1)
+            X = torch.from_numpy(X).to(self.dev)
+        else:
+            X = self.normal_f32((rows, cols), 1)
+        Q = torch.empty((rows, cols), dtype=torch.uint8, device=self.dev)
+        br, bc = (rows, cols) if block is None else block
+        s = torch.empty(((rows // br) * (cols // bc),), dtype=torch.float32, device=self.dev)
+
+        def launch(i):
+            dmu.quantize_fp8(X, Q, s, fmt, block)
+
+        t = time_launches(torch, launch, steps, warmup)
+        bytes_ = 5.0 * rows * cols + 4.0 * s.numel()
+        ms = t["event_mean_ms"]
+        return {"ms": round(ms, 5), "GB_per_s": round(bytes_ / ms / 1e6, 1),
+                "pct_hbm_peak": round(100 * bytes_ / ms / 1e6 / PEAK_HBM_GBS, 1),
+                "algorithmic_MB": round(bytes_ / 1e6, 2), "wall_ms": round(t["wall_ms"], 5)}
+
+    @staticmethod
+    def report(t, flop, bytes_, peak, copies):
+        ms = t["event_mean_ms"]
+        tf = flop / ms / 1e9
+        return {"ms": round(ms, 5), "median_ms": round(t["event_median_ms"], 5),
+                "wall_ms": round(t["wall_ms"], 5), "TFLOP_per_s": round(tf, 1),
+                "pct_peak": round(100 * tf / peak, 1),
+                "GB_per_s_algorithmic": round(bytes_ / ms / 1e6, 1),
+                "operand_copies": copies}
+
+
+def cpu_baseline(A_bf16, B_bf16, budget_s=10.0):
+    """Time the CPU oracle on 256-row blocks of the headline GEMM."""
+    import numpy as np
+
+    import oracle
+
+    import torch
+
+    A = A_bf16.cpu().view(torch.int16).numpy().view(np.uint16)
+    B = B_bf16.cpu().view(torch.int16).numpy().view(np.uint16)
+    M, K = A.shape
+    N = B.shape[0]
+    done, t0 = 0, time.perf_counter()
+    while done < M and time.perf_counter() - t0 < budget_s:
+        oracle.gemm_bf16(A, B, oracle.B_COL_MAJOR, rows=np.arange(done, min(M, done + 256)))
+        done = min(M, done + 256)
+    dt = time.perf_counter() - t0
+    return {"value": round(2.0 * done * N * K / dt / 1e12, 5), "unit": "TFLOP/s",
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": "rows 0..%d of the 4096^3 BF16 product (FP64 sums, exact decoding), %.1f s"
+                      % (done - 1, dt)}
+
+
+def traffic_for(kernel_key, launch_ms):
+    """HBM bytes per launch measured with rocprofv3 counters (profiles/traffic.json),
+    valid only while the kernel source is unchanged."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)[kernel_key]
+    except (OSError, KeyError, ValueError):
+        return None
+    if rec.get("source_sha256") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--legs", default="all", help="all | headline | comma list of leg names")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="only run a device copy of this many MiB (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the GEMM shards without communication; see the design notes). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calib_copy_bytes_read": n * 4, "calib_copy_bytes_written": n * 4}))
+        return
+
+    b = Bench(args)
+    dmu = b.dmu
+    names = None if args.legs == "all" else set(args.legs.split(","))
+    want = lambda name: names is None or name in names
+    S, W = args.steps, args.warmup
+    S4, W4 = max(S // 4, 10), max(W // 4, 5)
+
+    # ---- headline: exactly S timed launches of the 4096^3 BF16 GEMM
+    log("headline gemm_bf16 4096^3 (B N x K, BF16 out): %d warmup + %d timed launches" % (W, S))
+    A = b.normal_bf16((4096, 4096), 1)
+    B = b.normal_bf16((4096, 4096), 2)
+    As, Bs = b.copies(A, 6), b.copies(B, 6)
+    out = torch.empty((4096, 4096), dtype=torch.bfloat16, device="cuda")
+
+    def launch(i):
+        dmu.gemm_bf16(As[i % 6], Bs[i % 6], out, dmu.B_COL_MAJOR)
+
+    t = time_launches(torch, launch, S, W)
+    flop = 2.0 * 4096 ** 3
+    value = flop / (t["wall_ms"] * 1e-3) / 1e12
+    achieved = flop / (t["event_mean_ms"] * 1e-3) / 1e12
+    log("headline: %.1f TFLOP/s wall, %.1f TFLOP/s per kernel (%.1f%% of peak)"
+        % (value, achieved, 100 * achieved / PEAK_BF16_TFLOPS))
+    del As, Bs, out
+
+    legs = {}
+    if want("bf16_4096_nn"):
+        legs["bf16_4096_nn"] = b.gemm_bf16_leg(4096, 4096, 4096, dmu.B_ROW_MAJOR, S, W, copies=6)
+        log("bf16 4096 B row-major: %s" % legs["bf16_4096_nn"])
+    for name, fmt in (("fp8_e4m3_4096", dmu.E4M3), ("fp8_e5m2_4096", dmu.E5M2)):
+        if want(name):
+            legs[name] = b.gemm_fp8_leg(4096, 4096, 4096, fmt, S, W, copies=10)
+            log("%s: %s" % (name, legs[name]))
+    if want("quantize_e4m3_4096_tensor"):
+        legs["quantize_e4m3_4096_tensor"] = b.quantize_leg(4096, 4096, dmu.E4M3, None, S, W)
+        log("quantize 4096^2: %s" % legs["quantize_e4m3_4096_tensor"])
+    if want("fp8_block_8192x7168x7168"):
+        legs["fp8_block_8192x7168x7168"] = b.gemm_fp8_leg(8192, 7168, 7168, dmu.E4M3, S4, W4,
+                                                           block=True)
+        log("block-scaled: %s" % legs["fp8_block_8192x7168x7168"])
+    if want("quantize_block"):
+        legs["quantize_e4m3_8192x7168_1x128"] = b.quantize_leg(8192, 7168, dmu.E4M3, (1, 128),
+                                                                S4, W4, outliers=True)
+        legs["quantize_e4m3_7168x7168_128x128"] = b.quantize_leg(7168, 7168, dmu.E4M3,
+                                                                  (128, 128), S4, W4)
+        log("block quantizers: %s %s" % (legs["quantize_e4m3_8192x7168_1x128"],
+                                        legs["quantize_e4m3_7168x7168_128x128"]))
+    if want("llm_28672x8192"):
+        Bllm = b.normal_bf16((28672, 8192), 2)
+        for M in (16, 128, 1024, 8192):
+            legs["bf16_llm_M%d_N28672_K8192" % M] = b.gemm_bf16_leg(
+                M, 28672, 8192, dmu.B_COL_MAJOR, S if M < 1024 else S4, W4, B=Bllm)
+            log("llm M=%d: %s" % (M, legs["bf16_llm_M%d_N28672_K8192" % M]))
+        del Bllm
+    if want("bf16_256"):
+        legs["bf16_256_f32out"] = b.gemm_bf16_leg(256, 256, 256, dmu.B_ROW_MAJOR, S, W,
+                                                  out_f32=True, seed_dist="uniform")
+        log("256^3: %s" % legs["bf16_256_f32out"])
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        cpu = cpu_baseline(A, B)
+        log("cpu baseline: %s" % cpu)
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": S,
+        "warmup": W,
+        "ms_per_step": round(t["wall_ms"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded N(0,1) FP32 sources rounded to BF16 (PCG64 seeds 1, 2)",
+        "config": {"workload": "gemm_bf16 M=N=K=4096, A row-major, B stored N x K, FP32 "
+                               "accumulate, BF16 out", "M": 4096, "N": 4096, "K": 4096,
+                   "operand_copies": 6},
+        "pct_peak": round(100 * value / PEAK_BF16_TFLOPS, 1),
+        "fp8_e4m3_4096": legs.get("fp8_e4m3_4096"),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic_for("gemm_bf16_4096_tn", t["event_mean_ms"]),
+                     "kernel": "gemm_kernel<kBF16, B col-major, 256x256>",
+                     "kernel_ms": round(t["event_mean_ms"], 5)},
+        "cpu_baseline": cpu,
+        "legs": legs,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -62,6 +62,8 @@ def lib():
         p = ctypes.c_void_p
         i64 = ctypes.c_int64
         i32 = ctypes.c_int
+        L.orc_num_threads.argtypes = []
+        L.orc_num_threads.restype = i32
         L.orc_decode_bf16_array.argtypes = [p, i64, p]
         L.orc_decode_fp8_array.argtypes = [p, i64, i32, p]
         L.orc_encode_bf16_array.argtypes = [p, i64, p]
@@ -75,6 +77,10 @@ def lib():
         L.orc_gemm_fp8.restype = i32
         _lib = L
     return _lib
+
+
+def num_threads() -> int:
+    return int(lib().orc_num_threads())
 
 
 def _ptr(a):

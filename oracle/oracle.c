@@ -33,6 +33,7 @@
  * Build: gcc -O2 -fopenmp -ffp-contract=off (never -ffast-math).
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -44,6 +45,9 @@
 #define ORC_SCALE_TENSOR 0
 #define ORC_SCALE_BLOCK 1
 #define ORC_BLOCK 128
+
+/* Number of OpenMP threads the oracle's parallel loops use. */
+int orc_num_threads(void) { return omp_get_max_threads(); }
 
 /* ---------------------------------------------------------------- decoders */
 
