@@ -13,22 +13,29 @@
 // per-tensor/per-row/per-block FP8 scaling factors).
 //
 // Structure (three-level tiling: workgroup tile staged in LDS, wave tile held
-// in accumulator registers, one MFMA per 32x32 sub-tile):
+// in accumulator registers, one MFMA per sub-tile):
 //  * a 256-thread workgroup (4 waves, one per SIMD) owns a BM x BN tile of D;
-//    each wave owns a (BM/2) x (BN/2) quarter as 32x32 MFMA sub-tiles;
-//  * K advances in slices of 128 bytes per row (64 BF16 or 128 FP8 values);
-//    two LDS stages: while the MFMAs consume one slice, the next slice is being
-//    copied into the other stage;
+//    each wave owns a (BM/2) x (BN/2) quarter as 32x32 (or 16x16) sub-tiles;
+//  * K advances in slices of RB bytes per row (RB = 64: 32 BF16 or 64 FP8
+//    values; RB = 128 for the staging paths that need it), held in an S-stage
+//    ring of LDS buffers: the copy of slice k+S-1 is issued while slice k is
+//    multiplied, so global-memory latency is covered by S-1 slices of MFMA
+//    work;
 //  * A and column-major B are copied global -> LDS by buffer loads that write
 //    LDS directly (no VGPR round trip); a row-major B slice goes through VGPRs
 //    and is transposed 8x8 in registers so that LDS always holds K-contiguous
 //    rows;
-//  * LDS rows are 128 bytes = eight 16-byte chunks; chunk c of row r is stored
-//    at position c ^ ((r ^ (r >> 3)) & 7).  A wave's 16-byte fragment reads
-//    (32 consecutive rows, one chunk column) then hit every bank once per 8 or
-//    16 lanes.  The same XOR is applied when the slice is written, so no
-//    padding is needed (the XOR-swizzle idea of the vidyal.ai page, Step 3,
-//    re-derived for 128-byte rows and 16-byte reads);
+//  * LDS rows are RB bytes of 16-byte chunks; chunk c of row r is stored at
+//    position c ^ f(r), with f(r) = (r ^ (r >> 3)) & 7 for 128-byte rows and
+//    ((r >> 1) ^ (r >> 2)) & 3 for 64-byte rows.  A wave's 16-byte fragment
+//    reads (consecutive rows, one chunk column) then touch every bank exactly
+//    once per 8 lanes (32 four-byte banks) and per 16 lanes (64 banks).  The
+//    same XOR is applied when the slice is written, so no padding is needed
+//    (the XOR-swizzle idea of the vidyal.ai page, Step 3, re-derived for these
+//    row widths and 16-byte reads);
+//  * within a slice, the LDS reads of MFMA step s+1 and the next slice's
+//    copies are issued before the MFMAs of step s; half of the last step's
+//    MFMAs run after the slice barrier, behind the next slice's first reads;
 //  * out-of-range rows and the K tail are fetched as zeros by giving their
 //    buffer loads an out-of-range offset;
 //  * workgroup ids are remapped so that the tiles one XCD runs together share
@@ -40,9 +47,19 @@ namespace dmu {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kRowBytes = 128;  // bytes of K per tile row per stage
 
-__device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
+// LDS position of logical 16-byte chunk c in row r for RB-byte rows.
+template <int RB>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (RB == 128) return (r ^ (r >> 3)) & 7;
+  else return ((r >> 1) ^ (r >> 2)) & 3;
+}
+
+// s_waitcnt immediate for gfx9-family: vmcnt(N) and lgkmcnt(0), expcnt free.
+template <int N>
+constexpr int waitcnt_vm_lgkm0() {
+  return (N & 0xF) | ((N >> 4) << 14) | (0x7 << 4);
+}
 
 // Workgroup -> output tile.  Workgroups are dispatched to the 8 XCDs round
 // robin (id % 8); give each XCD a contiguous run of logical tile ids, and walk
@@ -70,13 +87,17 @@ __device__ __forceinline__ f32x16_t mfma_fp8_32x32x64(const i32x8_t& a, const i3
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FA, FB, 0, 0, 0, 0);
 }
 
+__device__ __forceinline__ i32x8_t cat(const i32x4_t& lo, const i32x4_t& hi) {
+  return i32x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
 // D[row][col .. col+3] = x (+ C), masked to the matrix.
 __device__ __forceinline__ void store4(const GemmArgs& p, int64_t row, int64_t col, f32x4_t x) {
   if (row >= p.M || col >= p.N) return;
   const bool full = col + 3 < p.N;
   if (p.C) {
     const float* c = p.C + row * p.ldc + col;
-    if (full && ((p.ldc & 3) == 0)) {
+    if (full) {
       x += *(const f32x4_t*)c;
     } else {
       for (int r = 0; r < 4; ++r)
@@ -104,41 +125,49 @@ __device__ __forceinline__ void store4(const GemmArgs& p, int64_t row, int64_t c
   }
 }
 
-template <int KIND, int FA, int FB, bool BROW, int BM, int BN, int kGroupM>
-__global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p) {
+template <int KIND, int FA, int FB, bool BROW, int BM, int BN, int RB, int S, int kGroupM>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_kernel(
+    GemmArgs p) {
   constexpr int ESZ = KIND == kBF16 ? 2 : 1;
+  constexpr int CPR = RB / 16;  // 16-byte chunks per LDS row
   constexpr int WM = BM / 2, WN = BN / 2;
-  constexpr int TM = WM / 32, TN = WN / 32;
-  constexpr int A_BYTES = BM * kRowBytes, B_BYTES = BN * kRowBytes;
+  constexpr int TM = WM / 32, TN = WN / 32;      // 32x32 sub-tiles per wave
+  constexpr int TM16 = WM / 16, TN16 = WN / 16;  // 16x16 sub-tiles (block-scaled FP8)
+  constexpr int A_BYTES = BM * RB, B_BYTES = BN * RB;
   constexpr int SA_BYTES = KIND == kFP8Block ? BM * 4 : 0;
   constexpr int STAGE = A_BYTES + B_BYTES + SA_BYTES;
-  constexpr int NSTEP = KIND == kBF16 ? 4 : 2;  // MFMA K-steps per slice
-  static_assert(BM % 64 == 0 && BN % 64 == 0, "tile");
-  static_assert(!BROW || (KIND == kBF16 && BN == 256), "row-major B staging layout");
-  static_assert(KIND != kFP8Block || BM == kThreads, "block-scale staging layout");
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE];
+  constexpr int NSTEP = KIND == kBF16 ? RB / 32 : RB / 64;  // MFMA K-steps per slice
+  constexpr int NLA = BM * CPR / kThreads;                 // A copies per thread per slice
+  constexpr int NLB = BROW ? 8 : BN * CPR / kThreads;      // B copies per thread per slice
+  constexpr int NL = NLA + NLB + (KIND == kFP8Block ? 1 : 0);
+  static_assert(BM % 64 == 0 && BN % 64 == 0 && (BM * CPR) % kThreads == 0, "tile");
+  static_assert(!BROW || (KIND == kBF16 && BN == 256 && RB == 128 && S == 2),
+                "row-major B staging");
+  static_assert(KIND != kFP8Block || (BM == kThreads && RB == 128 && WN <= 128), "block scales");
+  static_assert(S >= 2 && NL * (S - 2) < 64, "vmcnt range");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[S * STAGE];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int swave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, kept scalar
+  const int wm = swave >> 1, wn = swave & 1;
+  const int rl = lane & 31, hl = lane >> 5;
   const int tiles_m = (int)((p.M + BM - 1) / BM), tiles_n = (int)((p.N + BN - 1) / BN);
   int tm, tn;
   tile_coords<kGroupM>(tiles_m, tiles_n, tm, tn);
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
   const int64_t kbytes = p.K * ESZ;
-  const int nkt = (int)((kbytes + kRowBytes - 1) / kRowBytes);
-  const bool tail = (kbytes % kRowBytes) != 0;
+  const int nkt = (int)((kbytes + RB - 1) / RB);
 
   // ---- A: global -> LDS descriptors (rows beyond M read as zeros)
   const int rowsA = (int)min((int64_t)BM, p.M - m0);
   const uint32_t ldaB = (uint32_t)(p.lda * ESZ);
   const __amdgpu_buffer_rsrc_t rA =
       make_rsrc((const uint8_t*)p.A + m0 * p.lda * ESZ, (int64_t)(rowsA - 1) * ldaB + kbytes);
-  uint32_t voffA[BM / 32];
-  uint32_t cA[BM / 32];
+  uint32_t voffA[NLA], cA[NLA];
 #pragma unroll
-  for (int it = 0; it < BM / 32; ++it) {
-    const int q = it * kThreads + tid, row = q >> 3;
-    const uint32_t c = (uint32_t)(((q & 7) ^ swz(row)) << 4);
+  for (int it = 0; it < NLA; ++it) {
+    const int q = it * kThreads + tid, row = q / CPR;
+    const uint32_t c = (uint32_t)(((q % CPR) ^ swz<RB>(row)) << 4);
     cA[it] = c;
     voffA[it] = row < rowsA ? (uint32_t)row * ldaB + c : kOOB;
   }
@@ -147,9 +176,8 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p) {
   const int rowsB = (int)min((int64_t)BN, p.N - n0);
   const uint32_t ldbB = (uint32_t)(p.ldb * ESZ);
   __amdgpu_buffer_rsrc_t rB;
-  constexpr int NB_IT = BROW ? 1 : BN / 32;
-  uint32_t voffB[NB_IT];
-  uint32_t cB[NB_IT];
+  constexpr int NBV = BROW ? 1 : NLB;
+  uint32_t voffB[NBV], cB[NBV];
   // row-major B: thread owns an 8 (k) x 8 (n) block of the slice
   const int kb8 = tid >> 5, nb8 = tid & 31;
   bool colok = true;
@@ -161,9 +189,9 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p) {
   } else {
     rB = make_rsrc((const uint8_t*)p.B + n0 * p.ldb * ESZ, (int64_t)(rowsB - 1) * ldbB + kbytes);
 #pragma unroll
-    for (int it = 0; it < NB_IT; ++it) {
-      const int q = it * kThreads + tid, row = q >> 3;
-      const uint32_t c = (uint32_t)(((q & 7) ^ swz(row)) << 4);
+    for (int it = 0; it < NLB; ++it) {
+      const int q = it * kThreads + tid, row = q / CPR;
+      const uint32_t c = (uint32_t)(((q % CPR) ^ swz<RB>(row)) << 4);
       cB[it] = c;
       voffB[it] = row < rowsB ? (uint32_t)row * ldbB + c : kOOB;
     }
@@ -178,45 +206,72 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p) {
     voffSA = tid < rowsA ? (uint32_t)tid * (uint32_t)nkb * 4 : kOOB;
   }
 
-  u32x4_t breg[8];  // row-major B staging registers
+  u32x4_t breg[BROW ? 8 : 1];  // row-major B staging registers
 
-  auto issue_loads = [&](int kt, int stage) __attribute__((always_inline)) {
-    uint8_t* sA = smem + stage * STAGE;
+  // Copy K slice `kt` into LDS stage `st`.  With active == false every lane
+  // gets an out-of-range offset (slices after the last one), so the
+  // instruction stream is the same on every iteration.
+  auto issue_loads = [&](int kt, int st, bool active) __attribute__((always_inline)) {
+    uint8_t* sA = smem + st * STAGE;
     uint8_t* sB = sA + A_BYTES;
-    const uint32_t koff = (uint32_t)kt * kRowBytes;
-    const bool partial = tail && kt == nkt - 1;
+    // chunks at byte position >= klim along K are fetched as zeros: the K
+    // tail of the last slice, or everything when inactive
+    const uint32_t koff = active ? (uint32_t)kt * RB : 0u;
+    const uint32_t klim = active ? (uint32_t)kbytes : 0u;
 #pragma unroll
-    for (int it = 0; it < BM / 32; ++it) {
-      uint32_t v = voffA[it];
-      if (partial && koff + cA[it] >= (uint32_t)kbytes) v = kOOB;
-      buffer_load_lds16(rA, sA + (it * kThreads + wave * 64) * 16, v, koff);
+    for (int it = 0; it < NLA; ++it) {
+      const uint32_t v = koff + cA[it] < klim ? voffA[it] : kOOB;
+      buffer_load_lds16(rA, sA + (it * kThreads + swave * 64) * 16, v, koff);
     }
     if constexpr (BROW) {
       const int k0 = kt * 64 + kb8 * 8;
-      const bool ok = colok && k0 < p.K;
-      const uint32_t soff = (uint32_t)kt * 64u * (uint32_t)p.ldb * 2u;
+      const bool ok = active && colok && k0 < p.K;
+      const uint32_t soff = active ? (uint32_t)kt * 64u * (uint32_t)p.ldb * 2u : 0u;
 #pragma unroll
       for (int i = 0; i < 8; ++i)
         breg[i] = buffer_load16(rB, ok ? voffB[0] + (uint32_t)(i * p.ldb * 2) : kOOB, soff);
     } else {
 #pragma unroll
-      for (int it = 0; it < NB_IT; ++it) {
-        uint32_t v = voffB[it];
-        if (partial && koff + cB[it] >= (uint32_t)kbytes) v = kOOB;
-        buffer_load_lds16(rB, sB + (it * kThreads + wave * 64) * 16, v, koff);
+      for (int it = 0; it < NLB; ++it) {
+        const uint32_t v = koff + cB[it] < klim ? voffB[it] : kOOB;
+        buffer_load_lds16(rB, sB + (it * kThreads + swave * 64) * 16, v, koff);
       }
     }
     if constexpr (KIND == kFP8Block) {
       uint8_t* sSA = sB + B_BYTES;
-      buffer_load_lds4(rSA, sSA + wave * 256, voffSA, (uint32_t)kt * 4);
+      buffer_load_lds4(rSA, sSA + swave * 256, active ? voffSA : kOOB,
+                       active ? (uint32_t)kt * 4 : 0u);
+    }
+  };
+
+  // Copy number idx (0 <= idx < NLA + NLB) of slice kt into stage st; the
+  // same copies issue_loads makes, one at a time, so they can be spread
+  // between MFMAs.
+  auto issue_one = [&](int kt, int st, bool active, int idx) __attribute__((always_inline)) {
+    uint8_t* sA = smem + st * STAGE;
+    uint8_t* sB = sA + A_BYTES;
+    const uint32_t koff = active ? (uint32_t)kt * RB : 0u;
+    const uint32_t klim = active ? (uint32_t)kbytes : 0u;
+    if (idx < NLA) {
+      const uint32_t v = koff + cA[idx] < klim ? voffA[idx] : kOOB;
+      buffer_load_lds16(rA, sA + (idx * kThreads + swave * 64) * 16, v, koff);
+    } else if constexpr (BROW) {
+      const int i = idx - NLA;
+      const bool ok = active && colok && kt * 64 + kb8 * 8 < p.K;
+      const uint32_t soff = active ? (uint32_t)kt * 64u * (uint32_t)p.ldb * 2u : 0u;
+      breg[i] = buffer_load16(rB, ok ? voffB[0] + (uint32_t)(i * p.ldb * 2) : kOOB, soff);
+    } else {
+      const int it = idx - NLA;
+      const uint32_t v = koff + cB[it] < klim ? voffB[it] : kOOB;
+      buffer_load_lds16(rB, sB + (it * kThreads + swave * 64) * 16, v, koff);
     }
   };
 
   // row-major B: transpose the thread's 8x8 block in registers and store the
   // eight 16-byte K-chunks (one per n) into the swizzled K-contiguous layout.
-  auto store_brow = [&](int stage) __attribute__((always_inline)) {
+  auto store_brow = [&](int st) __attribute__((always_inline)) {
     if constexpr (BROW) {
-      uint8_t* sB = smem + stage * STAGE + A_BYTES;
+      uint8_t* sB = smem + st * STAGE + A_BYTES;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         u32x4_t w;
@@ -226,140 +281,215 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p) {
           w[q] = (j & 1) ? ((lo >> 16) | (hi & 0xFFFF0000u)) : ((lo & 0xFFFFu) | (hi << 16));
         }
         const int n = nb8 * 8 + j;
-        *(u32x4_t*)(sB + n * kRowBytes + ((kb8 ^ swz(n)) << 4)) = w;
+        *(u32x4_t*)(sB + n * RB + ((kb8 ^ swz<RB>(n)) << 4)) = w;
       }
     }
   };
 
-  f32x16_t acc[TM][TN];
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j) acc[i][j] = f32x16_t{};
+  // 16-byte LDS read of logical chunk c of tile row `row`.
+  auto lds16 = [&](const uint8_t* base, int row, int c) __attribute__((always_inline)) -> i32x4_t {
+    return *(const i32x4_t*)(base + row * RB + ((c ^ swz<RB>(row)) << 4));
+  };
 
-  const int rl = lane & 31, hl = lane >> 5;
-
-  issue_loads(0, 0);
-  __builtin_amdgcn_s_waitcnt(0);
-  store_brow(0);
+  // ---- prologue: slices 0 .. S-2 in flight, wait for slice 0
+#pragma unroll
+  for (int t = 0; t < S - 1; ++t) issue_loads(t, t, t < nkt);
+  if constexpr (BROW) {
+    __builtin_amdgcn_s_waitcnt(0);
+    store_brow(0);
+  } else {
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<NL * (S - 2)>());
+  }
   __syncthreads();
 
-  for (int kt = 0; kt < nkt; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nkt) issue_loads(kt + 1, cur ^ 1);
-    const uint8_t* sA = smem + cur * STAGE;
-    const uint8_t* sB = sA + A_BYTES;
-
-    if constexpr (KIND == kBF16) {
+  if constexpr (KIND == kBF16 || KIND == kFP8Tensor) {
+    constexpr int CPL = KIND == kBF16 ? 1 : 2;  // 16-byte chunks per lane per step
+    f32x16_t acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) acc[i][j] = f32x16_t{};
+    i32x4_t fa[2][TM][CPL], fb[2][TN][CPL];
+    auto load_step = [&](int st, int s, int buf) __attribute__((always_inline)) {
+      const uint8_t* sA = smem + st * STAGE;
+      const uint8_t* sB = sA + A_BYTES;
+      const int c = (2 * s + hl) * CPL;
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int h = 0; h < CPL; ++h) fa[buf][i][h] = lds16(sA, wm * WM + i * 32 + rl, c + h);
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int h = 0; h < CPL; ++h) fb[buf][j][h] = lds16(sB, wn * WN + j * 32 + rl, c + h);
+    };
+    // The B fragment is the instruction's first operand, so each accumulator
+    // holds a transposed 32x32 sub-tile (see the epilogue).
+    auto mfma_one = [&](int buf, int i, int j) __attribute__((always_inline)) {
+      if constexpr (KIND == kBF16)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            __builtin_bit_cast(bf16x8_t, fb[buf][j][0]),
+            __builtin_bit_cast(bf16x8_t, fa[buf][i][0]), acc[i][j], 0, 0, 0);
+      else
+        acc[i][j] = mfma_fp8_32x32x64<FB, FA>(cat(fb[buf][j][0], fb[buf][j][1]),
+                                              cat(fa[buf][i][0], fa[buf][i][1]), acc[i][j]);
+    };
+    // With two or more steps per slice, the fragment buffers alternate within
+    // the slice and the last step ends on buffer 1, so the next slice's first
+    // reads (buffer 0) can overlap the second half of the last step.  With
+    // one step per slice all MFMAs are issued before the barrier and the
+    // next slice's fragments are read after it.
+    constexpr bool kSplitLast = NSTEP >= 2;
+    // The next slice's copies are spread between this slice's MFMAs (one
+    // every R MFMAs, all before the barrier): a burst of copies would stall
+    // the wave at issue while the matrix pipe idles.
+    constexpr int NLD = NLA + NLB;
+    constexpr int PRE = (NSTEP - 1) * TM * TN + (kSplitLast ? TM / 2 : TM) * TN;
+    constexpr int R = PRE / NLD < 2 ? PRE / NLD : 2;
+    static_assert(R >= 1, "every copy is issued before the slice barrier");
+    load_step(0, 0, 0);
+    int st = 0;
+    for (int kt = 0; kt < nkt; ++kt) {
+      const int ld_st = st == 0 ? S - 1 : st - 1;  // stage of slice kt+S-1
+      const int nx_st = st == S - 1 ? 0 : st + 1;  // stage of slice kt+1
+      const bool act = kt + S - 1 < nkt;
 #pragma unroll
       for (int s = 0; s < NSTEP; ++s) {
-        bf16x8_t a[TM], b[TN];
-        const int c = 2 * s + hl;
+        const int buf = s & 1;
+        __builtin_amdgcn_sched_barrier(0);
+        if (s + 1 < NSTEP) load_step(st, s + 1, buf ^ 1);
+        __builtin_amdgcn_sched_barrier(0);
+        const int iend = (s + 1 < NSTEP || !kSplitLast) ? TM : TM / 2;
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
-          const int row = wm * WM + i * 32 + rl;
-          a[i] = *(const bf16x8_t*)(sA + row * kRowBytes + ((c ^ swz(row)) << 4));
-        }
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          const int row = wn * WN + j * 32 + rl;
-          b[j] = *(const bf16x8_t*)(sB + row * kRowBytes + ((c ^ swz(row)) << 4));
-        }
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-          for (int j = 0; j < TN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
-      }
-    } else {
-      // FP8: 32 bytes (two chunks) of K per lane per step
-      auto frag = [&](const uint8_t* base, int row, int s) __attribute__((always_inline)) -> i32x8_t {
-        const int c = 4 * s + 2 * hl;
-        const i32x4_t lo = *(const i32x4_t*)(base + row * kRowBytes + ((c ^ swz(row)) << 4));
-        const i32x4_t hi =
-            *(const i32x4_t*)(base + row * kRowBytes + (((c + 1) ^ swz(row)) << 4));
-        return i32x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      };
-      if constexpr (KIND == kFP8Tensor) {
-#pragma unroll
-        for (int s = 0; s < NSTEP; ++s) {
-          i32x8_t a[TM], b[TN];
-#pragma unroll
-          for (int i = 0; i < TM; ++i) a[i] = frag(sA, wm * WM + i * 32 + rl, s);
-#pragma unroll
-          for (int j = 0; j < TN; ++j) b[j] = frag(sB, wn * WN + j * 32 + rl, s);
-#pragma unroll
-          for (int i = 0; i < TM; ++i)
-#pragma unroll
-            for (int j = 0; j < TN; ++j) acc[i][j] = mfma_fp8_32x32x64<FB, FA>(b[j], a[i], acc[i][j]);
-        }
-      } else {
-        // per-block scales: partial = sum over this 128-wide K block, from zero
-        const float* sSA = (const float*)(sB + B_BYTES);
-        // a wave whose columns all lie beyond N has no scale row to read
-        const int64_t ncol0 = n0 + wn * WN;
-        const int nblk = __builtin_amdgcn_readfirstlane((int)(ncol0 >> 7));
-        const float sbv = ncol0 < p.N ? p.sb[(int64_t)nblk * nkb + kt] : 0.0f;
-        i32x8_t a0[TM], a1[TM], b0[TN], b1[TN];
-#pragma unroll
-        for (int i = 0; i < TM; ++i) {
-          a0[i] = frag(sA, wm * WM + i * 32 + rl, 0);
-          a1[i] = frag(sA, wm * WM + i * 32 + rl, 1);
-        }
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          b0[j] = frag(sB, wn * WN + j * 32 + rl, 0);
-          b1[j] = frag(sB, wn * WN + j * 32 + rl, 1);
-        }
-#pragma unroll
-        for (int i = 0; i < TM; ++i) {
-          // lane holds row (i*32 + lane%32) of the sub-tile: one A scale per lane
-          const float sc = sSA[wm * WM + i * 32 + rl] * sbv;
+          if (i >= iend) continue;
 #pragma unroll
           for (int j = 0; j < TN; ++j) {
-            f32x16_t part = mfma_fp8_32x32x64<FB, FA>(b0[j], a0[i], f32x16_t{});
-            part = mfma_fp8_32x32x64<FB, FA>(b1[j], a1[i], part);
-#pragma unroll
-            for (int v = 0; v < 16; ++v) acc[i][j][v] = __builtin_fmaf(part[v], sc, acc[i][j][v]);
+            mfma_one(buf, i, j);
+            const int g = (s * TM + i) * TN + j;
+            if (g % R == R - 1 && g / R < NLD) {
+              __builtin_amdgcn_sched_barrier(0);
+              issue_one(kt + S - 1, ld_st, act, g / R);
+              __builtin_amdgcn_sched_barrier(0);
+            }
           }
         }
       }
-    }
-
-    if (kt + 1 < nkt) {
-      __builtin_amdgcn_s_waitcnt(0);
-      store_brow(cur ^ 1);
-    }
-    __syncthreads();
-  }
-
-  // ---- epilogue: scale, add C, round, store.  MFMAs were issued with the
-  // B fragment as the instruction's first operand, so the accumulator holds
-  // the transposed sub-tile: lane l, register 4q+r is D[row = l%32]
-  // [col = 8q + 4*(l/32) + r] -- four consecutive columns of one row.
-  float alpha = 1.0f;
-  if constexpr (KIND == kFP8Tensor) alpha = p.sa[0] * p.sb[0];
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<NL * (S - 2)>());
+      store_brow(ld_st);  // row-major B: registers of slice kt+1 -> LDS (S == 2)
+      __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);
+      // next slice's first reads (zeros after the last slice)
+      load_step(nx_st, 0, 0);
+      if constexpr (kSplitLast) {
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int i = 0; i < TM; ++i) {
-    const int64_t row = m0 + wm * WM + i * 32 + rl;
+        for (int i = TM / 2; i < TM; ++i)
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int64_t col = n0 + wn * WN + j * 32 + 8 * q + 4 * hl;
-        f32x4_t x = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
-                     acc[i][j][4 * q + 3]};
-        if constexpr (KIND == kFP8Tensor) x *= alpha;
-        store4(p, row, col, x);
+          for (int j = 0; j < TN; ++j) mfma_one((NSTEP - 1) & 1, i, j);  // rest of this slice
       }
+      st = nx_st;
+    }
+
+    // ---- epilogue: scale, add C, round, store.  Lane l, register 4q+r of a
+    // transposed 32x32 accumulator is D[row = l%32][col = 8q + 4*(l/32) + r].
+    // Written straight to memory that is 16 B per lane spread over 32 rows;
+    // instead each wave passes one 32-row band at a time through its own LDS
+    // region, and reads it back so that every store covers whole row
+    // segments (32 lanes x 16 B of FP32, or x 8 B of BF16, per row).  Rows
+    // are padded by 16 bytes, which makes both the band writes (16 lanes at
+    // the same column of 16 rows) and the row reads bank-conflict free.
+    constexpr int ROWW = WN + 4;  // padded band row, in floats
+    static_assert(4 * 32 * ROWW * 4 <= S * STAGE, "epilogue bands fit in LDS");
+    static_assert(WN % 4 == 0 && 64 % (WN / 4) == 0, "band read shape");
+    float alpha = 1.0f;
+    if constexpr (KIND == kFP8Tensor) alpha = p.sa[0] * p.sb[0];
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();  // every wave is done reading the K-slice stages
+    float* band = (float*)smem + swave * 32 * ROWW;
+    constexpr int LPR = WN / 4;       // lanes per band row on the read side
+    constexpr int RPI = 64 / LPR;     // band rows per read instruction
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          f32x4_t x = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                       acc[i][j][4 * q + 3]};
+          if constexpr (KIND == kFP8Tensor) x *= alpha;
+          *(f32x4_t*)(band + rl * ROWW + j * 32 + 8 * q + 4 * hl) = x;
+        }
+#pragma unroll
+      for (int it = 0; it < 32 / RPI; ++it) {
+        const int br = it * RPI + lane / LPR, bc = (lane % LPR) * 4;
+        const f32x4_t x = *(const f32x4_t*)(band + br * ROWW + bc);
+        store4(p, m0 + wm * WM + i * 32 + br, n0 + wn * WN + bc, x);
+      }
+    }
+  } else {
+    // Per-block scales.  One 16x16x128 MFMA covers the whole 128-wide K block
+    // of a 16x16 sub-tile, so each partial sum is formed from zero and then
+    // promoted into the FP32 accumulator with its two scales.
+    f32x4_t acc[TM16][TN16];
+#pragma unroll
+    for (int i = 0; i < TM16; ++i)
+#pragma unroll
+      for (int j = 0; j < TN16; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const int r16 = lane & 15, g16 = lane >> 4;
+    // a wave whose columns all lie beyond N has no scale row to read
+    const int64_t ncol0 = n0 + wn * WN;
+    const int nblk = __builtin_amdgcn_readfirstlane((int)(ncol0 >> 7));
+    const bool colvalid = ncol0 < p.N;
+    int st = 0;
+    for (int kt = 0; kt < nkt; ++kt) {
+      const int ld_st = st == 0 ? S - 1 : st - 1;
+      issue_loads(kt + S - 1, ld_st, kt + S - 1 < nkt);
+      const uint8_t* sA = smem + st * STAGE;
+      const uint8_t* sB = sA + A_BYTES;
+      const float* sSA = (const float*)(sB + B_BYTES);
+      const float sbv = colvalid ? p.sb[(int64_t)nblk * nkb + kt] : 0.0f;
+      i32x8_t a[TM16], b[TN16];
+#pragma unroll
+      for (int i = 0; i < TM16; ++i)
+        a[i] = cat(lds16(sA, wm * WM + i * 16 + r16, 2 * g16),
+                   lds16(sA, wm * WM + i * 16 + r16, 2 * g16 + 1));
+#pragma unroll
+      for (int j = 0; j < TN16; ++j)
+        b[j] = cat(lds16(sB, wn * WN + j * 16 + r16, 2 * g16),
+                   lds16(sB, wn * WN + j * 16 + r16, 2 * g16 + 1));
+#pragma unroll
+      for (int i = 0; i < TM16; ++i) {
+        // lane holds row (i*16 + lane%16) of the sub-tile: one A scale per lane
+        const float sc = sSA[wm * WM + i * 16 + r16] * sbv;
+#pragma unroll
+        for (int j = 0; j < TN16; ++j) {
+          const f32x4_t part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              b[j], a[i], f32x4_t{0.f, 0.f, 0.f, 0.f}, FB, FA, 0, 0, 0, 0);
+#pragma unroll
+          for (int v = 0; v < 4; ++v) acc[i][j][v] = __builtin_fmaf(part[v], sc, acc[i][j][v]);
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<NL * (S - 2)>());
+      __syncthreads();
+      st = st == S - 1 ? 0 : st + 1;
+    }
+    // Lane l, register r of a transposed 16x16 accumulator is
+    // D[row = l%16][col = 4*(l/16) + r].
+#pragma unroll
+    for (int i = 0; i < TM16; ++i) {
+      const int64_t row = m0 + wm * WM + i * 16 + r16;
+#pragma unroll
+      for (int j = 0; j < TN16; ++j) store4(p, row, n0 + wn * WN + j * 16 + 4 * g16, acc[i][j]);
     }
   }
 }
 
-template <int KIND, int FA, int FB, bool BROW, int BM, int BN, int G>
+template <int KIND, int FA, int FB, bool BROW, int BM, int BN, int RB, int S, int G>
 hipError_t launch(const GemmArgs& a, hipStream_t s) {
   const int64_t tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_kernel<KIND, FA, FB, BROW, BM, BN, G>), dim3((unsigned)tiles),
+  hipLaunchKernelGGL((gemm_kernel<KIND, FA, FB, BROW, BM, BN, RB, S, G>), dim3((unsigned)tiles),
                      dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
@@ -367,14 +497,14 @@ hipError_t launch(const GemmArgs& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_gemm_bf16(const GemmArgs& a, int b_col_major, hipStream_t s) {
-  if (b_col_major) return launch<kBF16, 0, 0, false, 256, 256, 4>(a, s);
-  return launch<kBF16, 0, 0, true, 256, 256, 4>(a, s);
+  if (b_col_major) return launch<kBF16, 0, 0, false, 256, 256, 128, 2, 4>(a, s);
+  return launch<kBF16, 0, 0, true, 256, 256, 128, 2, 4>(a, s);
 }
 
 template <int FA, int FB>
 static hipError_t launch_fp8_fmt(const GemmArgs& a, int block_scaled, hipStream_t s) {
-  if (block_scaled) return launch<kFP8Block, FA, FB, false, 256, 256, 4>(a, s);
-  return launch<kFP8Tensor, FA, FB, false, 256, 256, 4>(a, s);
+  if (block_scaled) return launch<kFP8Block, FA, FB, false, 256, 128, 128, 3, 4>(a, s);
+  return launch<kFP8Tensor, FA, FB, false, 256, 256, 128, 2, 4>(a, s);
 }
 
 hipError_t launch_gemm_fp8(const GemmArgs& a, int fmt_a, int fmt_b, int block_scaled,
