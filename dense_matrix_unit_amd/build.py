@@ -18,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdmu.so")
-SOURCES = ["dmu_api.cpp", "gemm.hip", "quantize.hip", "probe.hip"]
+SOURCES = ["dmu_api.cpp", "gemm.hip", "gemm_skinny.hip", "quantize.hip", "probe.hip"]
 HEADERS = ["dmu_device.h", "dmu_internal.h"]
 
 

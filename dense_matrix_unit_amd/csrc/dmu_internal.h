@@ -24,6 +24,9 @@ enum GemmKind { kBF16 = 0, kFP8Tensor = 1, kFP8Block = 2 };
 // Launchers: argument checking is done by the caller; these only pick a
 // kernel configuration and launch it.  They return a hipError_t.
 hipError_t launch_gemm_bf16(const GemmArgs& a, int b_col_major, hipStream_t s);
+// Skinny-M BF16 path (M <= 128, B stored N x K): HBM-bound streaming of B.
+bool skinny_applies(const GemmArgs& a);
+hipError_t launch_gemm_bf16_skinny(const GemmArgs& a, hipStream_t s);
 hipError_t launch_gemm_fp8(const GemmArgs& a, int fmt_a, int fmt_b, int block_scaled,
                            hipStream_t s);
 hipError_t launch_quantize_fp8(const float* X, int64_t rows, int64_t cols, int64_t ldx, int fmt,

@@ -497,6 +497,7 @@ hipError_t launch(const GemmArgs& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_gemm_bf16(const GemmArgs& a, int b_col_major, hipStream_t s) {
+  if (b_col_major && skinny_applies(a)) return launch_gemm_bf16_skinny(a, s);
   if (b_col_major) return launch<kBF16, 0, 0, false, 256, 256, 128, 2, 4>(a, s);
   return launch<kBF16, 0, 0, true, 256, 256, 128, 2, 4>(a, s);
 }

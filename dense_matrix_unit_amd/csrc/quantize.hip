@@ -96,27 +96,66 @@ __device__ __forceinline__ uint32_t encode4(f32x4_t x, float m) {
 }
 
 // ---- per tensor -----------------------------------------------------------
+// Both passes walk rows: workgroup b takes rows b, b + grid, ...; inside a row
+// each thread takes float4 columns t, t + 256, ..., four at a time so that
+// several loads are in flight per thread.  No per-element division.
 
 __global__ void clear_slot(float* s) { *(uint32_t*)s = 0u; }
 
-__global__ __launch_bounds__(256) void amax_tensor(const float* X, int64_t rows, int64_t cols4,
-                                                   int64_t ldx, float* slot) {
-  const int64_t total = rows * cols4;
-  uint32_t m = 0;
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total;
-       i += (int64_t)gridDim.x * 256) {
-    const int64_t r = i / cols4, c = i - r * cols4;
-    const f32x4_t v = *(const f32x4_t*)(X + r * ldx + 4 * c);
-    m = max(m, max(max(abs_bits(v[0]), abs_bits(v[1])), max(abs_bits(v[2]), abs_bits(v[3]))));
-  }
+__device__ __forceinline__ uint32_t amax4(const f32x4_t& v) {
+  return max(max(abs_bits(v[0]), abs_bits(v[1])), max(abs_bits(v[2]), abs_bits(v[3])));
+}
+
+// Workgroup max -> one atomic max on the slot.  Device-scope atomics on one
+// address are serialised across the XCDs, so the flat pass uses few, large
+// workgroups (one per CU).
+template <int NT>
+__device__ __forceinline__ void amax_commit(uint32_t m, float* slot) {
   m = wave_max(m);
-  __shared__ uint32_t red[4];
+  __shared__ uint32_t red[NT / 64];
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
   __syncthreads();
   if (threadIdx.x == 0) {
-    const uint32_t b = max(max(red[0], red[1]), max(red[2], red[3]));
+    uint32_t b = 0;
+    for (int w = 0; w < NT / 64; ++w) b = max(b, red[w]);
     atomicMax((unsigned int*)slot, b);
   }
+}
+
+// Contiguous tensor (ldx == cols): flat grid-stride walk, 8 float4 loads in
+// flight per thread.
+__global__ __launch_bounds__(1024) void amax_flat(const f32x4_t* X, int64_t n4, float* slot) {
+  uint32_t m = 0;
+  const int64_t stride = (int64_t)gridDim.x * 1024;
+  int64_t i = (int64_t)blockIdx.x * 1024 + threadIdx.x;
+  for (; i + 7 * stride < n4; i += 8 * stride) {
+    f32x4_t v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = __builtin_nontemporal_load(X + i + u * stride);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) m = max(m, amax4(v[u]));
+  }
+  for (; i < n4; i += stride) m = max(m, amax4(X[i]));
+  amax_commit<1024>(m, slot);
+}
+
+// Strided rows.
+__global__ __launch_bounds__(256) void amax_tensor(const float* X, int64_t rows, int64_t cols4,
+                                                   int64_t ldx, float* slot) {
+  uint32_t m = 0;
+  for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
+    const float* row = X + r * ldx;
+    int64_t c = threadIdx.x;
+    for (; c + 768 < cols4; c += 1024) {
+      f32x4_t v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = *(const f32x4_t*)(row + 4 * (c + 256 * u));
+#pragma unroll
+      for (int u = 0; u < 4; ++u) m = max(m, amax4(v[u]));
+    }
+    for (; c < cols4; c += 256) m = max(m, amax4(*(const f32x4_t*)(row + 4 * c)));
+  }
+  amax_commit<256>(m, slot);
 }
 
 template <int FMT>
@@ -124,12 +163,19 @@ __global__ __launch_bounds__(256) void encode_tensor(const float* X, int64_t row
                                                      int64_t ldx, uint8_t* Q, int64_t ldq,
                                                      const float* slot) {
   const float m = mult_from_amax<FMT>(*slot);
-  const int64_t total = rows * cols4;
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total;
-       i += (int64_t)gridDim.x * 256) {
-    const int64_t r = i / cols4, c = i - r * cols4;
-    const f32x4_t v = *(const f32x4_t*)(X + r * ldx + 4 * c);
-    *(uint32_t*)(Q + r * ldq + 4 * c) = encode4<FMT>(v, m);
+  for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
+    const float* row = X + r * ldx;
+    uint8_t* qrow = Q + r * ldq;
+    int64_t c = threadIdx.x;
+    for (; c + 768 < cols4; c += 1024) {
+      f32x4_t v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = *(const f32x4_t*)(row + 4 * (c + 256 * u));
+#pragma unroll
+      for (int u = 0; u < 4; ++u) *(uint32_t*)(qrow + 4 * (c + 256 * u)) = encode4<FMT>(v[u], m);
+    }
+    for (; c < cols4; c += 256)
+      *(uint32_t*)(qrow + 4 * c) = encode4<FMT>(*(const f32x4_t*)(row + 4 * c), m);
   }
 }
 
@@ -139,27 +185,36 @@ __global__ void finalize_tensor(float* slot) {
 }
 
 // ---- 1 x 128 blocks -------------------------------------------------------
-// 32 lanes own one block (4 values each); a 256-thread workgroup covers 8.
+// 32 lanes own one block (4 values each); a 256-thread workgroup covers 8
+// blocks per round and does kRounds rounds, loads of all rounds issued first.
+constexpr int kRounds = 4;
 template <int FMT>
 __global__ __launch_bounds__(256) void quant_1x128(const float* X, int64_t rows, int64_t nbc,
                                                    int64_t ldx, uint8_t* Q, int64_t ldq,
                                                    float* scales) {
-  const int64_t blk = (int64_t)blockIdx.x * 8 + (threadIdx.x >> 5);
-  const bool valid = blk < rows * nbc;
   const int lane = threadIdx.x & 31;
-  int64_t r = 0, cb = 0;
-  f32x4_t v = {0.f, 0.f, 0.f, 0.f};
-  if (valid) {
-    r = blk / nbc;
-    cb = blk - r * nbc;
-    v = *(const f32x4_t*)(X + r * ldx + cb * 128 + 4 * lane);
+  const int64_t nblk = rows * nbc;
+  f32x4_t v[kRounds];
+  int64_t blk[kRounds], r[kRounds], cb[kRounds];
+#pragma unroll
+  for (int u = 0; u < kRounds; ++u) {
+    blk[u] = ((int64_t)blockIdx.x * kRounds + u) * 8 + (threadIdx.x >> 5);
+    v[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    r[u] = blk[u] / nbc;
+    cb[u] = blk[u] - r[u] * nbc;
+    if (blk[u] < nblk) v[u] = *(const f32x4_t*)(X + r[u] * ldx + cb[u] * 128 + 4 * lane);
   }
-  uint32_t m = max(max(abs_bits(v[0]), abs_bits(v[1])), max(abs_bits(v[2]), abs_bits(v[3])));
-  m = half_wave_max(m);
-  if (valid) {
-    const float amax = __uint_as_float(m);
-    *(uint32_t*)(Q + r * ldq + cb * 128 + 4 * lane) = encode4<FMT>(v, mult_from_amax<FMT>(amax));
-    if (lane == 0) scales[blk] = scale_from_amax<FMT>(amax);
+#pragma unroll
+  for (int u = 0; u < kRounds; ++u) {
+    uint32_t m = max(max(abs_bits(v[u][0]), abs_bits(v[u][1])),
+                     max(abs_bits(v[u][2]), abs_bits(v[u][3])));
+    m = half_wave_max(m);
+    if (blk[u] < nblk) {
+      const float amax = __uint_as_float(m);
+      *(uint32_t*)(Q + r[u] * ldq + cb[u] * 128 + 4 * lane) =
+          encode4<FMT>(v[u], mult_from_amax<FMT>(amax));
+      if (lane == 0) scales[blk[u]] = scale_from_amax<FMT>(amax);
+    }
   }
 }
 
@@ -195,21 +250,23 @@ template <int FMT>
 hipError_t launch_fmt(const float* X, int64_t rows, int64_t cols, int64_t ldx, int64_t br,
                       int64_t bc, uint8_t* Q, int64_t ldq, float* scales, hipStream_t s) {
   if (br == rows && bc == cols) {
-    const int64_t cols4 = cols / 4, total = rows * cols4;
-    int64_t grid = (total + 255) / 256;
-    if (grid > 2048) grid = 2048;  // 8 resident workgroups per CU on 256 CUs
+    const int64_t cols4 = cols / 4;
+    const int64_t grid = rows < 2048 ? rows : 2048;  // 8 workgroups per CU on 256 CUs
+    const int64_t agrid = rows < 512 ? rows : 512;   // strided amax: fewer atomics
     hipLaunchKernelGGL(clear_slot, dim3(1), dim3(1), 0, s, scales);
-    hipLaunchKernelGGL(amax_tensor, dim3((unsigned)grid), dim3(256), 0, s, X, rows, cols4, ldx,
-                       scales);
-    int64_t egrid = (total + 255) / 256;
-    if (egrid > 8192) egrid = 8192;
-    hipLaunchKernelGGL(encode_tensor<FMT>, dim3((unsigned)egrid), dim3(256), 0, s, X, rows,
+    if (ldx == cols)
+      hipLaunchKernelGGL(amax_flat, dim3(256), dim3(1024), 0, s, (const f32x4_t*)X, rows * cols4,
+                         scales);
+    else
+      hipLaunchKernelGGL(amax_tensor, dim3((unsigned)agrid), dim3(256), 0, s, X, rows, cols4, ldx,
+                         scales);
+    hipLaunchKernelGGL(encode_tensor<FMT>, dim3((unsigned)grid), dim3(256), 0, s, X, rows,
                        cols4, ldx, Q, ldq, scales);
     hipLaunchKernelGGL(finalize_tensor<FMT>, dim3(1), dim3(1), 0, s, scales);
   } else if (br == 1 && bc == 128) {
     const int64_t nbc = cols / 128, nblk = rows * nbc;
-    hipLaunchKernelGGL(quant_1x128<FMT>, dim3((unsigned)((nblk + 7) / 8)), dim3(256), 0, s, X,
-                       rows, nbc, ldx, Q, ldq, scales);
+    hipLaunchKernelGGL(quant_1x128<FMT>, dim3((unsigned)((nblk + 8 * kRounds - 1) / (8 * kRounds))),
+                       dim3(256), 0, s, X, rows, nbc, ldx, Q, ldq, scales);
   } else {
     const int64_t nbc = cols / 128, nblk = (rows / 128) * nbc;
     hipLaunchKernelGGL(quant_128x128<FMT>, dim3((unsigned)nblk), dim3(256), 0, s, X, nbc, ldx, Q,

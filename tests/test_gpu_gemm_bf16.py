@@ -130,3 +130,15 @@ def test_accuracy_vs_k(K):
     print("K=%d rel-RMS sums %.3e total %.3e" % (K, oracle.rel_rms(D, Dref),
                                                  oracle.rel_rms(D, total_ref)))
     assert oracle.rel_rms(D, Dref) < 1e-5
+
+
+@pytest.mark.parametrize("out_dtype", OUTS)
+@pytest.mark.parametrize("shape", [(1, 113, 8), (5, 1000, 264), (33, 250, 520), (100, 3000, 1032),
+                                   (128, 224, 4096), (16, 2000, 8192)])
+def test_skinny_m(out_dtype, shape):
+    # M <= 128 with B stored N x K takes the bandwidth-bound skinny kernel
+    M, N, K = shape
+    A = bf16(wl.normal((M, K), 31))
+    B = bf16(wl.normal((N, K), 32))
+    C = wl.normal((M, N), 33)
+    check(A, B, dmu.B_COL_MAJOR, out_dtype, C=C, what="skinny %s" % (shape,))
