@@ -4,9 +4,10 @@
 //
 // Such a product does little arithmetic per byte of B, so its bound is HBM
 // bandwidth, not the matrix unit: the page "How Blackwell's Tensor Memory
-// Actually Works" (thesoftwarefrontier.com), section on decode, makes the
-// point that small batches leave the matrix instruction's M dimension mostly
-// empty and the cost sits in streaming the weights.  The design therefore
+// Actually Works" (thesoftwarefrontier.com), section "What this does to
+// serving economics", makes the point that a decode step is a GEMM whose M
+// (the batch) is skinny, so most of the matrix instruction's M dimension is
+// empty and the cost sits in reading the weights.  The design therefore
 // aims to keep B streaming at full bandwidth and treats the MFMAs as cheap:
 //  * a workgroup of 7 waves owns 112 columns of D (16 per wave), so N = 28672
 //    gives exactly 256 workgroups, one per CU;

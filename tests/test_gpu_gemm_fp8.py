@@ -1,5 +1,17 @@
 """Parity of gemm_fp8_scaled (HIP) against the FP64 oracle, per-tensor and
-per-block (A: 1 x 128, B: 128 x 128) scales, E4M3 and E5M2."""
+per-block (A: 1 x 128, B: 128 x 128) scales, E4M3 and E5M2.
+
+Tolerance: the FP32-accumulation bound 1e-5 * sum|ab| (+ 2^-8 |D| for BF16
+output) plus a term for the matrix unit's own FP8 arithmetic.  gfx950's FP8
+MFMAs sum the products inside one instruction on a grid tied to the largest
+product (2^p + 2^(p-13) is exact, 2^p + 2^(p-14) is not; pinned by
+test_gpu_probe.py::test_fp8_mfma_inner_sum_keeps_14_bits), the ~14-bit
+behaviour the vidyal.ai page measures for Ada's FP8 instruction in Step 5.
+Each instruction can therefore be off by about 2^-13 of its largest product;
+the test allows 2^-12 x (sum over the instruction's K blocks of the largest
+|a*b| in the block, with its scales): twice the worst case measured on random
+data, and orders of magnitude below what a dropped term or a wrong index
+produces."""
 import numpy as np
 import pytest
 import torch
@@ -7,7 +19,7 @@ import torch
 import oracle
 import dense_matrix_unit_amd as dmu
 from dense_matrix_unit_amd import workloads as wl
-from gpu_helpers import assert_within_bound, dev, empty_padded, out_to_f64, padded, round_out
+from gpu_helpers import dev, empty_padded, out_to_f64, padded, round_out
 
 pytestmark = pytest.mark.gpu
 FMT_PAIRS = [(0, 0), (0, 1), (1, 0), (1, 1)]
@@ -24,6 +36,30 @@ def run_fp8(A, B, fa, fb, sa, sb, mode, out_dtype, C=None):
     return out_to_f64(out)
 
 
+def block_max_term(A, B, fa, fb, sa, sb, mode, rows=None):
+    """sum over K blocks of max_k |a_ik b_jk| (dequantised): 64-wide blocks for
+    the per-tensor kernel's 32x32x64 MFMA, 128-wide for the block-scaled
+    kernel's 16x16x128."""
+    blk = 64 if mode == dmu.SCALE_TENSOR else 128
+    Ad = oracle.decode_fp8(A, fa)
+    if rows is not None:
+        Ad = Ad[rows]
+    Bd = oracle.decode_fp8(B, fb)
+    M, K = Ad.shape
+    N = Bd.shape[0]
+    out = np.zeros((M, N))
+    for b in range(0, K, blk):
+        for r0 in range(0, M, 16):
+            p = np.abs(Ad[r0:r0 + 16, None, b:b + blk] * Bd[None, :, b:b + blk]).max(axis=2)
+            if mode == dmu.SCALE_TENSOR:
+                p = p * (float(np.ravel(sa)[0]) * float(np.ravel(sb)[0]))
+            else:
+                ra = np.arange(M)[r0:r0 + 16] if rows is None else np.asarray(rows)[r0:r0 + 16]
+                p = p * sa[ra, b // 128][:, None] * np.repeat(sb[:, b // 128], 128)[None, :N]
+            out[r0:r0 + 16] += p
+    return out
+
+
 def check(A, B, fa, fb, sa, sb, mode, out_dtype, C=None, rows=None, what=""):
     D = run_fp8(A, B, fa, fb, sa, sb, mode, out_dtype, C)
     Dref, S = oracle.gemm_fp8(A, B, fa, fb, sa, sb, mode, C=C, rows=rows)
@@ -31,7 +67,14 @@ def check(A, B, fa, fb, sa, sb, mode, out_dtype, C=None, rows=None, what=""):
         D = D[rows]
     if C is not None:
         S = S + np.abs(C if rows is None else C[rows])
-    assert_within_bound(D, Dref, S, out_dtype == torch.bfloat16, what)
+    tol = 1e-5 * S + 2.0 ** -12 * block_max_term(A, B, fa, fb, sa, sb, mode, rows)
+    if out_dtype == torch.bfloat16:
+        tol = tol + 2.0 ** -8 * np.abs(Dref)
+    bad = ~(np.abs(D - Dref) <= tol)
+    if bad.any():
+        i = tuple(np.argwhere(bad)[0])
+        raise AssertionError("%s: %d of %d outside the bound; first %s: got %r ref %r tol %r"
+                             % (what, bad.sum(), bad.size, i, D[i], Dref[i], tol[i]))
     return D, Dref
 
 
@@ -102,3 +145,21 @@ def test_block_scaled_8192x7168x7168_sampled():
     B, sb = quant(wl.normal((7168, 7168), wl.SEED_B), dmu.E4M3, (128, 128))
     rows = np.array(sorted(set(sample_rows(8192, 8).tolist()) | set(out_rows[:4].tolist())), np.int64)
     check(A, B, 0, 0, sa, sb, dmu.SCALE_BLOCK, torch.bfloat16, rows=rows, what="block 8192")
+
+
+@pytest.mark.parametrize("K", [256, 1024, 4096, 16384, 65536])
+def test_accuracy_vs_k_e4m3(K):
+    # M = N = 256, N(0,1) sources quantized per tensor to E4M3, FP32 output;
+    # error against FP64 of the FP8 values ("from the sums") and of the FP32
+    # sources ("total"), as the vidyal.ai page measures it in Step 5
+    Af = wl.normal((256, K), wl.SEED_A)
+    Bf = wl.normal((256, K), wl.SEED_B)
+    A, sa = quant(Af, dmu.E4M3)
+    B, sb = quant(Bf, dmu.E4M3)
+    D, Dref = check(A, B, 0, 0, sa, sb, dmu.SCALE_TENSOR, torch.float32, what="K=%d" % K)
+    total_ref = Af.astype(np.float64) @ Bf.astype(np.float64).T
+    print("E4M3 K=%d rel-RMS sums %.3e total %.3e" % (K, oracle.rel_rms(D, Dref),
+                                                      oracle.rel_rms(D, total_ref)))
+    # the 14-bit in-instruction sums put the FP8 "sums" error near 1.5e-5,
+    # far below the 3.7e-2 that rounding the inputs to E4M3 costs
+    assert oracle.rel_rms(D, Dref) < 1e-4

@@ -86,6 +86,46 @@ def test_accumulator_keeps_fp32_precision(kind):
     assert e == 23
 
 
+def inner_sum_gap(kind, fmt=0):
+    """Largest g such that two products 2^hi and 2^(hi-g) placed in ONE
+    instruction (C = 0) come out exact."""
+    m, n, k = SHAPES[kind]
+    fp8 = kind in (dmu.PROBE_FP8_16X16X128, dmu.PROBE_FP8_32X32X64)
+    best = -1
+    for g in range(0, 30):
+        hi = min(16, g)
+        lo = g - hi
+        if fp8 and lo > 9:
+            break
+        p = hi // 2
+        Af = np.zeros((m, k), np.float32)
+        Bf = np.zeros((n, k), np.float32)
+        Af[:, 0], Bf[:, 0] = 2.0 ** p, 2.0 ** (hi - p)
+        Af[:, 1], Bf[:, 1] = 2.0 ** -lo, 1.0
+        if fp8:
+            A, B = oracle.encode_fp8(Af, fmt), oracle.encode_fp8(Bf, fmt)
+        else:
+            A, B = oracle.encode_bf16(Af), oracle.encode_bf16(Bf)
+        D = run_probe(kind, A, B, np.zeros((m, n), np.float32), fmt, fmt)
+        if np.all(D == 2.0 ** hi + 2.0 ** -lo):
+            best = g
+        else:
+            break
+    return best
+
+
+@pytest.mark.parametrize("kind", list(SHAPES))
+def test_fp8_mfma_inner_sum_keeps_14_bits(kind):
+    # The products inside one FP8 instruction are summed keeping ~14 bits
+    # below the largest (the behaviour the vidyal.ai page reports for Ada's
+    # FP8 instruction, Step 5); BF16 instructions keep FP32's 24 bits.  The
+    # FP8 parity tolerance is derived from this.
+    g = inner_sum_gap(kind)
+    print("inner-sum probe kind %d: two products exact up to a gap of %d binades" % (kind, g))
+    fp8 = kind in (dmu.PROBE_FP8_16X16X128, dmu.PROBE_FP8_32X32X64)
+    assert g == (13 if fp8 else 23)
+
+
 @pytest.mark.parametrize("mode,size", [(0, 16), (1, 4)])
 @pytest.mark.parametrize("oob_from", [64, 40, 0])
 def test_direct_to_lds_copy(mode, size, oob_from):
