@@ -9,7 +9,9 @@ B stored N x K, BF16 output, inputs N(0,1) rounded to BF16, in TFLOP/s.  A
 synchronisations, each launch also bracketed by HIP events on the stream it
 runs on.  The other workloads (B row-major, FP8 per-tensor E4M3/E5M2, the
 block-scaled 8192x7168x7168 GEMM and its quantizers, the LLM-shaped sweep,
-256^3) are timed the same way in the same process and reported under "legs".
+256^3) are timed the same way in the same process and reported under "legs",
+with "mfma_ceiling": the sustained matrix-unit rate with no memory traffic,
+for N(0,1) and for constant operands.
 
 Operands are resident in HBM before timing starts.  The 4096^3 legs rotate
 over several operand copies whose total exceeds the 256 MB Infinity Cache, so
@@ -178,6 +180,38 @@ class Bench:
                 "pct_hbm_peak": round(100 * bytes_ / ms / 1e6 / PEAK_HBM_GBS, 1),
                 "algorithmic_MB": round(bytes_ / 1e6, 2), "wall_ms": round(t["wall_ms"], 5)}
 
+    def mfma_ceiling_leg(self, steps, warmup):
+        """Sustained MFMA rate with no memory traffic (dmu_probe_mfma_rate): the
+        ceiling the GEMM K loops can reach, for N(0,1) operands and for constant
+        ones (the power drawn depends on the operand bits)."""
+        torch, dmu = self.torch, self.dmu
+        res = {}
+        grid = 1024
+        for name, kind, iters, peak in (("bf16", dmu.PROBE_BF16_32X32X16, 2048, PEAK_BF16_TFLOPS),
+                                        ("fp8_e4m3", dmu.PROBE_FP8_32X32X64, 1024,
+                                         PEAK_FP8_TFLOPS)):
+            fb = 16 if name == "bf16" else 32
+            n = 8 * 64 * fb
+            if name == "bf16":
+                rnd = self.normal_bf16((n // 2,), 1).view(torch.uint8)
+                ones = torch.full((n // 2,), 1.0, dtype=torch.bfloat16, device=self.dev)
+                ones = ones.view(torch.uint8)
+            else:
+                q = torch.empty((n,), dtype=torch.uint8, device=self.dev)
+                sc = torch.empty(1, dtype=torch.float32, device=self.dev)
+                dmu.quantize_fp8(self.normal_f32((1, n), 1), q.view(1, n), sc, dmu.E4M3)
+                rnd, ones = q, torch.full((n,), 0x38, dtype=torch.uint8, device=self.dev)
+            out = torch.empty(grid * 256, dtype=torch.float32, device=self.dev)
+            flop = 2.0 * grid * 4 * 16 * iters * (32 * 32 * (16 if name == "bf16" else 64))
+            for dist, src in (("normal", rnd), ("ones", ones)):
+                t = time_launches(torch, lambda i: dmu.probe_mfma_rate(kind, src, iters, grid, out),
+                                  steps, warmup)
+                tf = flop / t["event_mean_ms"] / 1e9
+                res["%s_%s" % (name, dist)] = {"TFLOP_per_s": round(tf, 1),
+                                               "pct_peak": round(100 * tf / peak, 1),
+                                               "ms": round(t["event_mean_ms"], 4)}
+        return res
+
     @staticmethod
     def report(t, flop, bytes_, peak, copies):
         ms = t["event_mean_ms"]
@@ -312,6 +346,10 @@ def main():
         legs["bf16_256_f32out"] = b.gemm_bf16_leg(256, 256, 256, dmu.B_ROW_MAJOR, S, W,
                                                   out_f32=True, seed_dist="uniform")
         log("256^3: %s" % legs["bf16_256_f32out"])
+
+    if want("mfma_ceiling"):
+        legs["mfma_ceiling"] = b.mfma_ceiling_leg(S4, W4)
+        log("mfma ceiling (no memory traffic): %s" % legs["mfma_ceiling"])
 
     cpu = None
     if not args.no_cpu_baseline:

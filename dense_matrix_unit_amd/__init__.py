@@ -49,6 +49,7 @@ SYMBOLS = {
     "dmu_version": (_I, []),
     "dmu_probe_mfma": (_I, [_I, _I, _I, _P, _P, _P, _P, _P]),
     "dmu_probe_lds_load": (_I, [_P, _P, _I, _I, _P]),
+    "dmu_probe_mfma_rate": (_I, [_I, _P, _I, _I, _P, _P]),
 }
 
 _lib = None
@@ -217,3 +218,18 @@ def probe_lds_load(src, dst, mode: int, oob_from: int = 64, stream=None):
                                            oob_from, _stream(stream))
     _check("dmu_probe_lds_load", rc)
     return dst
+
+
+def probe_mfma_rate(kind: int, src, iters: int, grid: int, out, stream=None):
+    """Sustained MFMA loop on fragments read from `src` (see include/dmu_probe.h).
+    `src` needs 8 KiB (BF16 kind) or 16 KiB (FP8 kind); `out` grid*256 floats."""
+    torch = _torch()
+    need = 8 * 64 * (16 if kind == PROBE_BF16_32X32X16 else 32)
+    if src.numel() * src.element_size() < need or not src.is_contiguous():
+        raise ValueError("src must be contiguous and hold %d bytes" % need)
+    if out.numel() < grid * 256 or out.dtype != torch.float32 or not out.is_contiguous():
+        raise ValueError("out must be contiguous float32 with grid*256 elements")
+    rc = load_library().dmu_probe_mfma_rate(kind, _dev_ptr(src, "src"), iters, grid,
+                                            _dev_ptr(out, "out"), _stream(stream))
+    _check("dmu_probe_mfma_rate", rc)
+    return out

@@ -47,6 +47,8 @@ namespace dmu {
 namespace {
 
 constexpr int kThreads = 256;
+// K slices between the L2 prefetch of a slice and its use (0 = no prefetch).
+constexpr int kPrefetch = 3;
 
 // LDS position of logical 16-byte chunk c in row r for RB-byte rows.
 template <int RB>
@@ -59,6 +61,17 @@ __device__ __forceinline__ int swz(int r) {
 template <int N>
 constexpr int waitcnt_vm_lgkm0() {
   return (N & 0xF) | ((N >> 4) << 14) | (0x7 << 4);
+}
+
+// Workgroup barrier for the K loop.  The caller has already waited for its
+// own copies and LDS reads with an explicit s_waitcnt; __syncthreads() would
+// add a release fence, i.e. a wait for every outstanding vector memory
+// operation, including the L2 prefetch that is meant to stay in flight.  The
+// empty asm statements keep the compiler from moving memory accesses across.
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 // Workgroup -> output tile.  Workgroups are dispatched to the 8 XCDs round
@@ -125,7 +138,7 @@ __device__ __forceinline__ void store4(const GemmArgs& p, int64_t row, int64_t c
   }
 }
 
-template <int KIND, int FA, int FB, bool BROW, int BM, int BN, int RB, int S, int kGroupM>
+template <int KIND, int FA, int FB, bool BROW, int BM, int BN, int RB, int S, int kGroupM, int PD>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_kernel(
     GemmArgs p) {
   constexpr int ESZ = KIND == kBF16 ? 2 : 1;
@@ -145,7 +158,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                 "row-major B staging");
   static_assert(KIND != kFP8Block || (BM == kThreads && RB == 128 && WN <= 128), "block scales");
   static_assert(S >= 2 && NL * (S - 2) < 64, "vmcnt range");
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[S * STAGE];
+  static_assert(PD == 0 || (S == 2 && !BROW && BM == 256 && BN == 256 && kGroupM == 4 && PD >= 2),
+                "L2 prefetch layout");
+  constexpr int PF_BYTES = PD > 0 ? 4 * 256 : 0;  // one 256-byte landing area per wave
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[S * STAGE + PF_BYTES];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int swave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, kept scalar
@@ -196,6 +212,37 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
       voffB[it] = row < rowsB ? (uint32_t)row * ldbB + c : kOOB;
     }
   }
+
+  // ---- L2 prefetch of slice kt + PD.  With two LDS stages only one slice of
+  // copies is in flight, so a copy that misses to HBM stalls the K loop.  A
+  // 4-byte copy per 64-byte half line, into a scratch LDS area, brings the
+  // slice into this XCD's L2 a few slices early; the real copy then hits.
+  // The workgroups one XCD runs together form a kGroupM x 8 block of tiles
+  // (tile_coords), so each A panel is shared by 8 of them and each B panel
+  // by kGroupM: each workgroup fetches 1/8 of its A rows (wave 0) and
+  // 1/kGroupM of its B rows (waves 1 and 2), so every line is fetched once.
+  __amdgpu_buffer_rsrc_t rP = rA;
+  uint32_t voffP = kOOB, cP = 0;
+  if constexpr (PD > 0) {
+    const int half = lane & 1;
+    cP = (uint32_t)half * 64;
+    if (swave == 0) {
+      const int row = (tn & 7) * (BM / 8) + (lane >> 1);
+      voffP = row < rowsA ? (uint32_t)row * ldaB + cP : kOOB;
+    } else if (swave <= 2) {
+      rP = rB;
+      const int row = (tm & (kGroupM - 1)) * (BN / kGroupM) + (swave - 1) * 32 + (lane >> 1);
+      voffP = row < rowsB ? (uint32_t)row * ldbB + cP : kOOB;
+    }
+  }
+  auto issue_pf = [&](int kt) __attribute__((always_inline)) {
+    if constexpr (PD > 0) {
+      const bool active = kt < nkt;
+      const uint32_t koff = active ? (uint32_t)kt * RB : 0u;
+      const uint32_t v = active && koff + cP < (uint32_t)kbytes ? voffP : kOOB;
+      buffer_load_lds4(rP, smem + S * STAGE + swave * 256, v, koff);
+    }
+  };
 
   // ---- per-block scales of A (one float per row per K slice)
   const int nkb = (int)(p.K / 128);
@@ -294,11 +341,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   // ---- prologue: slices 0 .. S-2 in flight, wait for slice 0
 #pragma unroll
   for (int t = 0; t < S - 1; ++t) issue_loads(t, t, t < nkt);
+  // slices 1 .. PD-1 are prefetched here; the loop prefetches kt + PD
+#pragma unroll
+  for (int t = 1; t < PD; ++t) issue_pf(t);
+  constexpr int NPF = PD > 0 ? 1 : 0;  // prefetches per slice per thread
   if constexpr (BROW) {
     __builtin_amdgcn_s_waitcnt(0);
     store_brow(0);
   } else {
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<NL * (S - 2)>());
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<NL * (S - 2) + (PD > 1 ? PD - 1 : 0)>());
   }
   __syncthreads();
 
@@ -322,6 +373,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
       for (int j = 0; j < TN; ++j)
 #pragma unroll
         for (int h = 0; h < CPL; ++h) fb[buf][j][h] = lds16(sB, wn * WN + j * 32 + rl, c + h);
+    };
+    // Fragment read k (0 <= k < NR) of step s, in the order the step's MFMAs
+    // first need them: A fragment 0, B fragments 0 .. TN-1, A fragments
+    // 1 .. TM-1 (each CPL 16-byte chunks).  Spreading these reads between the
+    // previous step's MFMAs keeps only a few LDS reads outstanding, so the
+    // next step's first MFMAs never wait on a burst of reads.
+    constexpr int NR = (TM + TN) * CPL;
+    auto read_one = [&](int st, int s, int buf, int k) __attribute__((always_inline)) {
+      const uint8_t* sA = smem + st * STAGE;
+      const uint8_t* sB = sA + A_BYTES;
+      const int c = (2 * s + hl) * CPL;
+      const int slot = k / CPL, h = k % CPL;
+      if (slot == 0)
+        fa[buf][0][h] = lds16(sA, wm * WM + rl, c + h);
+      else if (slot <= TN)
+        fb[buf][slot - 1][h] = lds16(sB, wn * WN + (slot - 1) * 32 + rl, c + h);
+      else
+        fa[buf][slot - TN][h] = lds16(sA, wm * WM + (slot - TN) * 32 + rl, c + h);
     };
     // The B fragment is the instruction's first operand, so each accumulator
     // holds a transposed 32x32 sub-tile (see the epilogue).
@@ -347,7 +416,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     constexpr int PRE = (NSTEP - 1) * TM * TN + (kSplitLast ? TM / 2 : TM) * TN;
     constexpr int R = PRE / NLD < 2 ? PRE / NLD : 2;
     static_assert(R >= 1, "every copy is issued before the slice barrier");
-    load_step(0, 0, 0);
+#pragma unroll
+    for (int k = 0; k < NR; ++k) read_one(0, 0, 0, k);
     int st = 0;
     for (int kt = 0; kt < nkt; ++kt) {
       const int ld_st = st == 0 ? S - 1 : st - 1;  // stage of slice kt+S-1
@@ -356,38 +426,53 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 #pragma unroll
       for (int s = 0; s < NSTEP; ++s) {
         const int buf = s & 1;
-        __builtin_amdgcn_sched_barrier(0);
-        if (s + 1 < NSTEP) load_step(st, s + 1, buf ^ 1);
-        __builtin_amdgcn_sched_barrier(0);
         const int iend = (s + 1 < NSTEP || !kSplitLast) ? TM : TM / 2;
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
           if (i >= iend) continue;
 #pragma unroll
           for (int j = 0; j < TN; ++j) {
             mfma_one(buf, i, j);
-            const int g = (s * TM + i) * TN + j;
-            if (g % R == R - 1 && g / R < NLD) {
-              __builtin_amdgcn_sched_barrier(0);
-              issue_one(kt + S - 1, ld_st, act, g / R);
-              __builtin_amdgcn_sched_barrier(0);
+            const int gl = i * TN + j;  // MFMA index within the step
+            const int g = s * TM * TN + gl;
+            __builtin_amdgcn_sched_barrier(0);
+            if (s + 1 < NSTEP) {
+#pragma unroll
+              for (int k = gl * NR / (TM * TN); k < (gl + 1) * NR / (TM * TN); ++k)
+                read_one(st, s + 1, buf ^ 1, k);
             }
+            if (g % R == R - 1 && g / R < NLD) {
+              issue_one(kt + S - 1, ld_st, act, g / R);
+              if (g / R == NLD - 1) issue_pf(kt + PD);  // after this slice's copies
+            }
+            __builtin_amdgcn_sched_barrier(0);
           }
         }
       }
       __builtin_amdgcn_sched_barrier(0);
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<NL * (S - 2)>());
+      // slice kt+1 has landed; only the prefetch issued in this slice may
+      // still be in flight (vector memory operations complete in order)
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<NL * (S - 2) + NPF>());
       store_brow(ld_st);  // row-major B: registers of slice kt+1 -> LDS (S == 2)
-      __syncthreads();
+      stage_barrier();
       __builtin_amdgcn_sched_barrier(0);
-      // next slice's first reads (zeros after the last slice)
-      load_step(nx_st, 0, 0);
       if constexpr (kSplitLast) {
-        __builtin_amdgcn_sched_barrier(0);
+        // next slice's first fragments, interleaved with the rest of this slice
+        constexpr int NM = (TM - TM / 2) * TN;
 #pragma unroll
         for (int i = TM / 2; i < TM; ++i)
 #pragma unroll
-          for (int j = 0; j < TN; ++j) mfma_one((NSTEP - 1) & 1, i, j);  // rest of this slice
+          for (int j = 0; j < TN; ++j) {
+            const int gl = (i - TM / 2) * TN + j;
+#pragma unroll
+            for (int k = gl * NR / NM; k < (gl + 1) * NR / NM; ++k) read_one(nx_st, 0, 0, k);
+            __builtin_amdgcn_sched_barrier(0);
+            mfma_one((NSTEP - 1) & 1, i, j);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+      } else {
+        load_step(nx_st, 0, 0);  // next slice's first reads (zeros after the last slice)
       }
       st = nx_st;
     }
@@ -486,10 +571,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   }
 }
 
-template <int KIND, int FA, int FB, bool BROW, int BM, int BN, int RB, int S, int G>
+template <int KIND, int FA, int FB, bool BROW, int BM, int BN, int RB, int S, int G, int PD = 0>
 hipError_t launch(const GemmArgs& a, hipStream_t s) {
   const int64_t tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_kernel<KIND, FA, FB, BROW, BM, BN, RB, S, G>), dim3((unsigned)tiles),
+  hipLaunchKernelGGL((gemm_kernel<KIND, FA, FB, BROW, BM, BN, RB, S, G, PD>), dim3((unsigned)tiles),
                      dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
@@ -498,14 +583,14 @@ hipError_t launch(const GemmArgs& a, hipStream_t s) {
 
 hipError_t launch_gemm_bf16(const GemmArgs& a, int b_col_major, hipStream_t s) {
   if (b_col_major && skinny_applies(a)) return launch_gemm_bf16_skinny(a, s);
-  if (b_col_major) return launch<kBF16, 0, 0, false, 256, 256, 128, 2, 4>(a, s);
+  if (b_col_major) return launch<kBF16, 0, 0, false, 256, 256, 128, 2, 4, kPrefetch>(a, s);
   return launch<kBF16, 0, 0, true, 256, 256, 128, 2, 4>(a, s);
 }
 
 template <int FA, int FB>
 static hipError_t launch_fp8_fmt(const GemmArgs& a, int block_scaled, hipStream_t s) {
   if (block_scaled) return launch<kFP8Block, FA, FB, false, 256, 128, 128, 3, 4>(a, s);
-  return launch<kFP8Tensor, FA, FB, false, 256, 256, 128, 2, 4>(a, s);
+  return launch<kFP8Tensor, FA, FB, false, 256, 256, 128, 2, 4, kPrefetch>(a, s);
 }
 
 hipError_t launch_gemm_fp8(const GemmArgs& a, int fmt_a, int fmt_b, int block_scaled,

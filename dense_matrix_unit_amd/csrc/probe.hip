@@ -106,6 +106,63 @@ __global__ void probe_lds_kernel(const uint8_t* src, uint8_t* dst, int mode, int
   for (int i = l; i < 2048 / 4; i += 64) ((uint32_t*)dst)[i] = ((uint32_t*)lds)[i];
 }
 
+// Sustained matrix-unit rate with operands that change from one instruction
+// to the next, and no memory traffic in the loop.  Each wave loads four A and
+// four B fragments from `src` (fragment f of lane l at src + (f*64 + l)*FB,
+// FB = 16 bytes for BF16, 32 for FP8), then runs `iters` rounds of the 4 x 4
+// block of 32x32 MFMAs the GEMM kernel's wave tile issues per K step, into 16
+// independent accumulators (256 registers, one wave per SIMD).  Lane l of
+// wave w then writes the sum of its 256 accumulator values to
+// out[w * 64 + l], which keeps every instruction live.
+template <int KIND>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void probe_rate_kernel(
+    const uint8_t* src, int iters, float* out) {
+  const int l = threadIdx.x & 63;
+  constexpr int FB = KIND == 1 ? 16 : 32;
+  i32x8_t a[4], b[4];
+#pragma unroll
+  for (int f = 0; f < 4; ++f) {
+    const i32x4_t* pa = (const i32x4_t*)(src + (f * 64 + l) * FB);
+    const i32x4_t* pb = (const i32x4_t*)(src + ((4 + f) * 64 + l) * FB);
+    const i32x4_t a0 = pa[0], b0 = pb[0];
+    const i32x4_t a1 = FB == 32 ? pa[1] : i32x4_t{0, 0, 0, 0};
+    const i32x4_t b1 = FB == 32 ? pb[1] : i32x4_t{0, 0, 0, 0};
+    a[f] = i32x8_t{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+    b[f] = i32x8_t{b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+  }
+  f32x16_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if constexpr (KIND == 1) {
+          const i32x4_t x = {a[i][0], a[i][1], a[i][2], a[i][3]};
+          const i32x4_t y = {b[j][0], b[j][1], b[j][2], b[j][3]};
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8_t, y), __builtin_bit_cast(bf16x8_t, x), acc[i][j], 0, 0, 0);
+        } else {
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b[j], a[i], acc[i][j], 0, 0,
+                                                                      0, 0, 0, 0);
+        }
+      }
+  }
+  float sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) sum += acc[i][j][v];
+  out[(int64_t)blockIdx.x * 256 + threadIdx.x] = sum;
+}
+
 template <int KIND>
 hipError_t probe_fmt(int fa, int fb, const void* A, const void* B, const float* C, float* D,
                      hipStream_t s) {
@@ -140,6 +197,17 @@ hipError_t launch_probe_mfma(int kind, int fa, int fb, const void* A, const void
 hipError_t launch_probe_lds(const void* src, void* dst, int mode, int oob_from, hipStream_t s) {
   hipLaunchKernelGGL(probe_lds_kernel, dim3(1), dim3(64), 0, s, (const uint8_t*)src,
                      (uint8_t*)dst, mode, oob_from);
+  return hipGetLastError();
+}
+
+hipError_t launch_probe_rate(int kind, const void* src, int iters, int grid, float* out,
+                             hipStream_t s) {
+  if (kind == 1)
+    hipLaunchKernelGGL(probe_rate_kernel<1>, dim3(grid), dim3(256), 0, s, (const uint8_t*)src,
+                       iters, out);
+  else
+    hipLaunchKernelGGL(probe_rate_kernel<3>, dim3(grid), dim3(256), 0, s, (const uint8_t*)src,
+                       iters, out);
   return hipGetLastError();
 }
 

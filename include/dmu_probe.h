@@ -45,6 +45,24 @@ int dmu_probe_mfma(int kind, int fmt_a, int fmt_b, const void* A, const void* B,
  */
 int dmu_probe_lds_load(const void* src, void* dst, int mode, int oob_from, void* stream);
 
+/*
+ * Sustained matrix-unit rate, the ceiling a GEMM's K loop can reach once the
+ * memory pipeline is taken away (Step 2 of the same page reports each kernel
+ * as a share of the peak at the clock it ran).  Launches `grid` workgroups of
+ * 4 waves (one wave per SIMD); each wave runs `iters` rounds of a 4 x 4 block
+ * of 32x32 MFMAs, kind DMU_PROBE_BF16_32X32X16 (32768 FLOP each) or
+ * DMU_PROBE_FP8_32X32X64 (E4M3 x E4M3, 131072 FLOP each), on operand
+ * fragments read once from `src`: 8 fragments of 64 lanes x 16 bytes (BF16,
+ * 8 KiB) or x 32 bytes (FP8, 16 KiB), fragments 0-3 for A and 4-7 for B.  The
+ * values in `src` set the switching activity, hence the power drawn.
+ * Lane l of wave w writes the sum of its 256 accumulator values to
+ * out[w*64 + l] (grid * 256 floats; all-ones BF16 fragments give
+ * 256 * 16 * iters, all-ones E4M3 256 * 64 * iters).
+ * Requires 1 <= iters <= 2^20 and 1 <= grid <= 65536, else
+ * DMU_ERR_INVALID_ARG.  Total work: grid * 4 * 16 * iters instructions.
+ */
+int dmu_probe_mfma_rate(int kind, const void* src, int iters, int grid, float* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -139,3 +139,19 @@ def test_direct_to_lds_copy(mode, size, oob_from):
     assert np.array_equal(d[:v], src[:v])          # lane l's bytes at l*size
     assert np.all(d[v:64 * size] == 0)             # out-of-range lanes write zeros
     assert np.all(d[64 * size:] == 0xA5)           # nothing written past 64*size
+
+
+@pytest.mark.parametrize("kind,k,one", [(dmu.PROBE_BF16_32X32X16, 16, 0x3F80),
+                                        (dmu.PROBE_FP8_32X32X64, 64, 0x38)])
+def test_mfma_rate_probe_counts_every_instruction(kind, k, one):
+    # All-ones fragments: every accumulator element gains k per round, so lane
+    # sums are 256 * k * iters exactly (well inside FP32's exact integers).
+    iters, grid = 37, 3
+    if kind == dmu.PROBE_BF16_32X32X16:
+        src = torch.full((8 * 64 * 8,), one, dtype=torch.int16, device="cuda")
+    else:
+        src = torch.full((8 * 64 * 32,), one, dtype=torch.uint8, device="cuda")
+    out = torch.full((grid * 256,), float("nan"), dtype=torch.float32, device="cuda")
+    dmu.probe_mfma_rate(kind, src, iters, grid, out)
+    torch.cuda.synchronize()
+    assert torch.all(out == 256.0 * k * iters)
