@@ -351,7 +351,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   } else {
     __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<NL * (S - 2) + (PD > 1 ? PD - 1 : 0)>());
   }
-  __syncthreads();
+  if constexpr (BROW) __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<0>());  // store_brow's LDS writes
+  stage_barrier();
 
   if constexpr (KIND == kBF16 || KIND == kFP8Tensor) {
     constexpr int CPL = KIND == kBF16 ? 1 : 2;  // 16-byte chunks per lane per step
@@ -416,8 +417,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     constexpr int PRE = (NSTEP - 1) * TM * TN + (kSplitLast ? TM / 2 : TM) * TN;
     constexpr int R = PRE / NLD < 2 ? PRE / NLD : 2;
     static_assert(R >= 1, "every copy is issued before the slice barrier");
+    // same order as in the loop, so the waits at the loop head stay exact
 #pragma unroll
-    for (int k = 0; k < NR; ++k) read_one(0, 0, 0, k);
+    for (int k = 0; k < NR; ++k) {
+      read_one(0, 0, 0, k);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     int st = 0;
     for (int kt = 0; kt < nkt; ++kt) {
       const int ld_st = st == 0 ? S - 1 : st - 1;  // stage of slice kt+S-1
@@ -454,7 +459,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
       // slice kt+1 has landed; only the prefetch issued in this slice may
       // still be in flight (vector memory operations complete in order)
       __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<NL * (S - 2) + NPF>());
-      store_brow(ld_st);  // row-major B: registers of slice kt+1 -> LDS (S == 2)
+      if constexpr (BROW) {
+        store_brow(ld_st);  // row-major B: registers of slice kt+1 -> LDS (S == 2)
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<0>());  // LDS writes done before the barrier
+      }
       stage_barrier();
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (kSplitLast) {
@@ -487,30 +495,76 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     // the same column of 16 rows) and the row reads bank-conflict free.
     constexpr int ROWW = WN + 4;  // padded band row, in floats
     static_assert(4 * 32 * ROWW * 4 <= S * STAGE, "epilogue bands fit in LDS");
+    static_assert(4 * TM * 32 * WN * 2 <= S * STAGE && (WN * 2) % 16 == 0 && 64 % (WN / 8) == 0,
+                  "BF16 staging fits in LDS");
     static_assert(WN % 4 == 0 && 64 % (WN / 4) == 0, "band read shape");
     float alpha = 1.0f;
     if constexpr (KIND == kFP8Tensor) alpha = p.sa[0] * p.sb[0];
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();  // every wave is done reading the K-slice stages
-    float* band = (float*)smem + swave * 32 * ROWW;
-    constexpr int LPR = WN / 4;       // lanes per band row on the read side
-    constexpr int RPI = 64 / LPR;     // band rows per read instruction
+    if (p.out_bf16 && !p.C) {
+      // BF16 output: round first, then stage all four bands of the wave at
+      // once (4 x 32 rows x 256 B = 32 KB per wave), so the LDS traffic is
+      // halved and no band waits for the previous one.  16-byte unit u of
+      // staged row r sits at u ^ (r % 16): the 8-byte writes of 16 rows at
+      // one column then fall in distinct bank groups.  Each read instruction
+      // covers 4 rows x 256 B and each store writes 16 B (8 columns) per lane.
+      uint8_t* wbase = smem + swave * (TM * 32 * WN * 2);
+      constexpr int RB16 = WN * 2;  // staged row bytes
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
+      for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
+        for (int j = 0; j < TN; ++j)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          f32x4_t x = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
-                       acc[i][j][4 * q + 3]};
-          if constexpr (KIND == kFP8Tensor) x *= alpha;
-          *(f32x4_t*)(band + rl * ROWW + j * 32 + 8 * q + 4 * hl) = x;
+          for (int q = 0; q < 4; ++q) {
+            f32x4_t x = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                         acc[i][j][4 * q + 3]};
+            if constexpr (KIND == kFP8Tensor) x *= alpha;
+            const uint32_t lo = f32_to_bf16_bits(x[0]) | ((uint32_t)f32_to_bf16_bits(x[1]) << 16);
+            const uint32_t hi = f32_to_bf16_bits(x[2]) | ((uint32_t)f32_to_bf16_bits(x[3]) << 16);
+            const int u = j * 4 + q;  // 16-byte unit of the staged row
+            *(uint2*)(wbase + (i * 32 + rl) * RB16 + ((u ^ (rl & 15)) << 4) + hl * 8) =
+                make_uint2(lo, hi);
+          }
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<0>());  // own region only: no barrier
+      constexpr int UPR = RB16 / 16;  // 16-byte units per row
+      constexpr int RPI16 = 64 / UPR; // rows per read instruction
+#pragma unroll
+      for (int it = 0; it < TM * 32 / RPI16; ++it) {
+        const int r = it * RPI16 + lane / UPR, u = lane % UPR;
+        const u32x4_t v = *(const u32x4_t*)(wbase + r * RB16 + ((u ^ (r & 15)) << 4));
+        const int64_t row = m0 + wm * WM + r, col = n0 + wn * WN + u * 8;
+        if (row < p.M && col < p.N) {
+          uint16_t* d = (uint16_t*)p.D + row * p.ldd + col;
+          if (col + 7 < p.N) {
+            *(u32x4_t*)d = v;
+          } else {
+            for (int e = 0; e < 8; ++e)
+              if (col + e < p.N) d[e] = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
+          }
         }
-#pragma unroll
-      for (int it = 0; it < 32 / RPI; ++it) {
-        const int br = it * RPI + lane / LPR, bc = (lane % LPR) * 4;
-        const f32x4_t x = *(const f32x4_t*)(band + br * ROWW + bc);
-        store4(p, m0 + wm * WM + i * 32 + br, n0 + wn * WN + bc, x);
+      }
+    } else {
+      float* band = (float*)smem + swave * 32 * ROWW;
+      constexpr int LPR = WN / 4;       // lanes per band row on the read side
+      constexpr int RPI = 64 / LPR;     // band rows per read instruction
+  #pragma unroll
+      for (int i = 0; i < TM; ++i) {
+  #pragma unroll
+        for (int j = 0; j < TN; ++j)
+  #pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            f32x4_t x = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                         acc[i][j][4 * q + 3]};
+            if constexpr (KIND == kFP8Tensor) x *= alpha;
+            *(f32x4_t*)(band + rl * ROWW + j * 32 + 8 * q + 4 * hl) = x;
+          }
+  #pragma unroll
+        for (int it = 0; it < 32 / RPI; ++it) {
+          const int br = it * RPI + lane / LPR, bc = (lane % LPR) * 4;
+          const f32x4_t x = *(const f32x4_t*)(band + br * ROWW + bc);
+          store4(p, m0 + wm * WM + i * 32 + br, n0 + wn * WN + bc, x);
+        }
       }
     }
   } else {
