@@ -39,7 +39,8 @@ PEAK_FP8_TFLOPS = 5033.2   # 256 CU x 8192 FLOP/clk x 2.4 GHz (published 5.0 PFL
 PEAK_HBM_GBS = 8000.0
 METRIC = "GEMM TFLOP/s and % of MFMA peak, 4096³ BF16 and FP8 E4M3, 1×MI355X"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCES = ["dense_matrix_unit_amd/csrc/gemm.hip", "dense_matrix_unit_amd/csrc/dmu_device.h"]
+KERNEL_SOURCES = ["dense_matrix_unit_amd/csrc/gemm.hip", "dense_matrix_unit_amd/csrc/gemm_common.h",
+                  "dense_matrix_unit_amd/csrc/dmu_device.h"]
 
 
 def log(msg):

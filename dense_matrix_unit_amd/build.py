@@ -18,8 +18,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdmu.so")
-SOURCES = ["dmu_api.cpp", "gemm.hip", "gemm_skinny.hip", "quantize.hip", "probe.hip"]
-HEADERS = ["dmu_device.h", "dmu_internal.h"]
+SOURCES = ["dmu_api.cpp", "gemm.hip", "gemm_block.hip", "gemm_skinny.hip", "quantize.hip",
+           "probe.hip"]
+HEADERS = ["dmu_device.h", "dmu_internal.h", "gemm_common.h"]
 
 
 def hipcc() -> str:

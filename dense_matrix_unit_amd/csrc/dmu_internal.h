@@ -29,6 +29,8 @@ bool skinny_applies(const GemmArgs& a);
 hipError_t launch_gemm_bf16_skinny(const GemmArgs& a, hipStream_t s);
 hipError_t launch_gemm_fp8(const GemmArgs& a, int fmt_a, int fmt_b, int block_scaled,
                            hipStream_t s);
+// Per-block scaled FP8 (A 1 x 128, B 128 x 128 scales; K % 128 == 0).
+hipError_t launch_gemm_fp8_block(const GemmArgs& a, int fmt_a, int fmt_b, hipStream_t s);
 hipError_t launch_quantize_fp8(const float* X, int64_t rows, int64_t cols, int64_t ldx, int fmt,
                                int64_t br, int64_t bc, uint8_t* Q, int64_t ldq, float* scales,
                                hipStream_t s);

@@ -1,96 +1,45 @@
-// Tiled MFMA GEMM for gfx950 (CDNA4): BF16 and scaled FP8 inputs, FP32
-// accumulation, FP32 or BF16 output.
+// Tiled MFMA GEMM for gfx950 (CDNA4): BF16 and per-tensor-scaled FP8 inputs,
+// FP32 accumulation, FP32 or BF16 output.  (Per-block FP8 scales: gemm_block.hip.)
 //
 // What is computed: D = A*B + C with the products accumulated in FP32 -- the
 // operation of a matrix instruction as the page "Tensor Cores: Matrix
 // Instructions, Swizzling and FP8, Measured" (vidyal.ai) defines it in Step 1,
 // applied to whole matrices as in its Step 2 (B may be stored N x K so both
-// operands are K-contiguous).  For FP8 the per-tensor scales are removed in
-// the epilogue, and with per-block scales each 128-wide partial sum is formed
-// from zero and promoted into the FP32 accumulator with its two scales (Step 5
-// of the same page, promotion of partial results into FP32 registers; the
-// "Tensor Cores" chapter of ai-infra-handbooks, "Precision" section, on
-// per-tensor/per-row/per-block FP8 scaling factors).
+// operands are K-contiguous).  For FP8 the two per-tensor scales are applied
+// in the epilogue ("Tensor Cores" chapter of ai-infra-handbooks, "Precision"
+// section, on per-tensor FP8 scaling factors).
 //
 // Structure (three-level tiling: workgroup tile staged in LDS, wave tile held
-// in accumulator registers, one MFMA per sub-tile):
-//  * a 256-thread workgroup (4 waves, one per SIMD) owns a BM x BN tile of D;
-//    each wave owns a (BM/2) x (BN/2) quarter as 32x32 (or 16x16) sub-tiles;
-//  * K advances in slices of RB bytes per row (RB = 64: 32 BF16 or 64 FP8
-//    values; RB = 128 for the staging paths that need it), held in an S-stage
-//    ring of LDS buffers: the copy of slice k+S-1 is issued while slice k is
-//    multiplied, so global-memory latency is covered by S-1 slices of MFMA
-//    work;
+// in accumulator registers, one MFMA per 32x32 sub-tile and K step):
+//  * a 256-thread workgroup (4 waves, one per SIMD) owns a 256 x 256 tile of
+//    D; each wave owns a 128 x 128 quadrant (4 x 4 sub-tiles, 256 AGPRs);
+//  * K advances in 128-byte slices (64 BF16 or 128 FP8 values per row) held
+//    in a 2-stage LDS ring: the copy of slice k+1 is issued while slice k is
+//    multiplied, and an L2 prefetch brings slice k+3 close;
 //  * A and column-major B are copied global -> LDS by buffer loads that write
 //    LDS directly (no VGPR round trip); a row-major B slice goes through VGPRs
 //    and is transposed 8x8 in registers so that LDS always holds K-contiguous
 //    rows;
-//  * LDS rows are RB bytes of 16-byte chunks; chunk c of row r is stored at
-//    position c ^ f(r), with f(r) = (r ^ (r >> 3)) & 7 for 128-byte rows and
-//    ((r >> 1) ^ (r >> 2)) & 3 for 64-byte rows.  A wave's 16-byte fragment
-//    reads (consecutive rows, one chunk column) then touch every bank exactly
-//    once per 8 lanes (32 four-byte banks) and per 16 lanes (64 banks).  The
-//    same XOR is applied when the slice is written, so no padding is needed
-//    (the XOR-swizzle idea of the vidyal.ai page, Step 3, re-derived for these
-//    row widths and 16-byte reads);
-//  * within a slice, the LDS reads of MFMA step s+1 and the next slice's
-//    copies are issued before the MFMAs of step s; half of the last step's
-//    MFMAs run after the slice barrier, behind the next slice's first reads;
+//  * LDS rows are 128 bytes of 16-byte chunks; chunk c of row r is stored at
+//    position c ^ ((r ^ (r >> 3)) & 7).  A wave's 16-byte fragment reads
+//    (consecutive rows, one chunk column) then touch every bank group once per
+//    8 lanes.  The same XOR is applied when the slice is written, so no
+//    padding is needed (the XOR-swizzle idea of the vidyal.ai page, Step 3,
+//    re-derived for this row width and 16-byte reads);
+//  * within a slice, the next step's fragment reads and the next slice's
+//    copies are spread one or two per MFMA; half of the last step's MFMAs run
+//    after the slice barrier, with the next slice's first reads between them;
 //  * out-of-range rows and the K tail are fetched as zeros by giving their
 //    buffer loads an out-of-range offset;
 //  * workgroup ids are remapped so that the tiles one XCD runs together share
 //    A row panels and B column panels in that XCD's L2.
-#include "dmu_device.h"
-#include "dmu_internal.h"
+#include "gemm_common.h"
 
 namespace dmu {
 namespace {
 
-constexpr int kThreads = 256;
 // K slices between the L2 prefetch of a slice and its use (0 = no prefetch).
 constexpr int kPrefetch = 3;
-
-// LDS position of logical 16-byte chunk c in row r for RB-byte rows.
-template <int RB>
-__device__ __forceinline__ int swz(int r) {
-  if constexpr (RB == 128) return (r ^ (r >> 3)) & 7;
-  else return ((r >> 1) ^ (r >> 2)) & 3;
-}
-
-// s_waitcnt immediate for gfx9-family: vmcnt(N) and lgkmcnt(0), expcnt free.
-template <int N>
-constexpr int waitcnt_vm_lgkm0() {
-  return (N & 0xF) | ((N >> 4) << 14) | (0x7 << 4);
-}
-
-// Workgroup barrier for the K loop.  The caller has already waited for its
-// own copies and LDS reads with an explicit s_waitcnt; __syncthreads() would
-// add a release fence, i.e. a wait for every outstanding vector memory
-// operation, including the L2 prefetch that is meant to stay in flight.  The
-// empty asm statements keep the compiler from moving memory accesses across.
-__device__ __forceinline__ void stage_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-// Workgroup -> output tile.  Workgroups are dispatched to the 8 XCDs round
-// robin (id % 8); give each XCD a contiguous run of logical tile ids, and walk
-// logical ids in column-major groups of kGroupM tile rows so that the tiles
-// resident on one XCD share few A and B panels.
-template <int kGroupM>
-__device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tm, int& tn) {
-  const int b = blockIdx.x, T = gridDim.x;
-  const int x = b & 7, j = b >> 3, per = T >> 3, rem = T & 7;
-  const int logical = x * per + (x < rem ? x : rem) + j;
-  const int group = kGroupM * tiles_n;
-  const int g = logical / group;
-  const int first = g * kGroupM;
-  const int gs = min(tiles_m - first, kGroupM);
-  const int r = logical - g * group;
-  tm = first + r % gs;
-  tn = r / gs;
-}
 
 template <int FA, int FB>
 __device__ __forceinline__ f32x16_t mfma_fp8_32x32x64(const i32x8_t& a, const i32x8_t& b,
@@ -100,44 +49,6 @@ __device__ __forceinline__ f32x16_t mfma_fp8_32x32x64(const i32x8_t& a, const i3
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FA, FB, 0, 0, 0, 0);
 }
 
-__device__ __forceinline__ i32x8_t cat(const i32x4_t& lo, const i32x4_t& hi) {
-  return i32x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-}
-
-// D[row][col .. col+3] = x (+ C), masked to the matrix.
-__device__ __forceinline__ void store4(const GemmArgs& p, int64_t row, int64_t col, f32x4_t x) {
-  if (row >= p.M || col >= p.N) return;
-  const bool full = col + 3 < p.N;
-  if (p.C) {
-    const float* c = p.C + row * p.ldc + col;
-    if (full) {
-      x += *(const f32x4_t*)c;
-    } else {
-      for (int r = 0; r < 4; ++r)
-        if (col + r < p.N) x[r] += c[r];
-    }
-  }
-  if (p.out_bf16) {
-    uint16_t* d = (uint16_t*)p.D + row * p.ldd + col;
-    const uint32_t lo = f32_to_bf16_bits(x[0]) | ((uint32_t)f32_to_bf16_bits(x[1]) << 16);
-    const uint32_t hi = f32_to_bf16_bits(x[2]) | ((uint32_t)f32_to_bf16_bits(x[3]) << 16);
-    if (full) {
-      *(uint2*)d = make_uint2(lo, hi);
-    } else {
-      for (int r = 0; r < 4; ++r)
-        if (col + r < p.N) d[r] = f32_to_bf16_bits(x[r]);
-    }
-  } else {
-    float* d = (float*)p.D + row * p.ldd + col;
-    if (full) {
-      *(f32x4_t*)d = x;
-    } else {
-      for (int r = 0; r < 4; ++r)
-        if (col + r < p.N) d[r] = x[r];
-    }
-  }
-}
-
 template <int KIND, int FA, int FB, bool BROW, int BM, int BN, int RB, int S, int kGroupM, int PD>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_kernel(
     GemmArgs p) {
@@ -145,18 +56,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   constexpr int CPR = RB / 16;  // 16-byte chunks per LDS row
   constexpr int WM = BM / 2, WN = BN / 2;
   constexpr int TM = WM / 32, TN = WN / 32;      // 32x32 sub-tiles per wave
-  constexpr int TM16 = WM / 16, TN16 = WN / 16;  // 16x16 sub-tiles (block-scaled FP8)
   constexpr int A_BYTES = BM * RB, B_BYTES = BN * RB;
-  constexpr int SA_BYTES = KIND == kFP8Block ? BM * 4 : 0;
-  constexpr int STAGE = A_BYTES + B_BYTES + SA_BYTES;
+  constexpr int STAGE = A_BYTES + B_BYTES;
   constexpr int NSTEP = KIND == kBF16 ? RB / 32 : RB / 64;  // MFMA K-steps per slice
   constexpr int NLA = BM * CPR / kThreads;                 // A copies per thread per slice
   constexpr int NLB = BROW ? 8 : BN * CPR / kThreads;      // B copies per thread per slice
-  constexpr int NL = NLA + NLB + (KIND == kFP8Block ? 1 : 0);
+  constexpr int NL = NLA + NLB;
   static_assert(BM % 64 == 0 && BN % 64 == 0 && (BM * CPR) % kThreads == 0, "tile");
   static_assert(!BROW || (KIND == kBF16 && BN == 256 && RB == 128 && S == 2),
                 "row-major B staging");
-  static_assert(KIND != kFP8Block || (BM == kThreads && RB == 128 && WN <= 128), "block scales");
+  static_assert(KIND == kBF16 || KIND == kFP8Tensor, "per-block scales live in gemm_block.hip");
   static_assert(S >= 2 && NL * (S - 2) < 64, "vmcnt range");
   static_assert(PD == 0 || (S == 2 && !BROW && BM == 256 && BN == 256 && kGroupM == 4 && PD >= 2),
                 "L2 prefetch layout");
@@ -244,15 +153,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     }
   };
 
-  // ---- per-block scales of A (one float per row per K slice)
-  const int nkb = (int)(p.K / 128);
-  __amdgpu_buffer_rsrc_t rSA;
-  uint32_t voffSA = kOOB;
-  if constexpr (KIND == kFP8Block) {
-    rSA = make_rsrc(p.sa + m0 * nkb, (int64_t)rowsA * nkb * 4);
-    voffSA = tid < rowsA ? (uint32_t)tid * (uint32_t)nkb * 4 : kOOB;
-  }
-
   u32x4_t breg[BROW ? 8 : 1];  // row-major B staging registers
 
   // Copy K slice `kt` into LDS stage `st`.  With active == false every lane
@@ -283,11 +183,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         const uint32_t v = koff + cB[it] < klim ? voffB[it] : kOOB;
         buffer_load_lds16(rB, sB + (it * kThreads + swave * 64) * 16, v, koff);
       }
-    }
-    if constexpr (KIND == kFP8Block) {
-      uint8_t* sSA = sB + B_BYTES;
-      buffer_load_lds4(rSA, sSA + swave * 256, active ? voffSA : kOOB,
-                       active ? (uint32_t)kt * 4 : 0u);
     }
   };
 
@@ -354,7 +249,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   if constexpr (BROW) __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<0>());  // store_brow's LDS writes
   stage_barrier();
 
-  if constexpr (KIND == kBF16 || KIND == kFP8Tensor) {
+  {
     constexpr int CPL = KIND == kBF16 ? 1 : 2;  // 16-byte chunks per lane per step
     f32x16_t acc[TM][TN];
 #pragma unroll
@@ -548,79 +443,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
       float* band = (float*)smem + swave * 32 * ROWW;
       constexpr int LPR = WN / 4;       // lanes per band row on the read side
       constexpr int RPI = 64 / LPR;     // band rows per read instruction
-  #pragma unroll
+#pragma unroll
       for (int i = 0; i < TM; ++i) {
-  #pragma unroll
+#pragma unroll
         for (int j = 0; j < TN; ++j)
-  #pragma unroll
+#pragma unroll
           for (int q = 0; q < 4; ++q) {
             f32x4_t x = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
                          acc[i][j][4 * q + 3]};
             if constexpr (KIND == kFP8Tensor) x *= alpha;
             *(f32x4_t*)(band + rl * ROWW + j * 32 + 8 * q + 4 * hl) = x;
           }
-  #pragma unroll
+#pragma unroll
         for (int it = 0; it < 32 / RPI; ++it) {
           const int br = it * RPI + lane / LPR, bc = (lane % LPR) * 4;
           const f32x4_t x = *(const f32x4_t*)(band + br * ROWW + bc);
           store4(p, m0 + wm * WM + i * 32 + br, n0 + wn * WN + bc, x);
         }
       }
-    }
-  } else {
-    // Per-block scales.  One 16x16x128 MFMA covers the whole 128-wide K block
-    // of a 16x16 sub-tile, so each partial sum is formed from zero and then
-    // promoted into the FP32 accumulator with its two scales.
-    f32x4_t acc[TM16][TN16];
-#pragma unroll
-    for (int i = 0; i < TM16; ++i)
-#pragma unroll
-      for (int j = 0; j < TN16; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    const int r16 = lane & 15, g16 = lane >> 4;
-    // a wave whose columns all lie beyond N has no scale row to read
-    const int64_t ncol0 = n0 + wn * WN;
-    const int nblk = __builtin_amdgcn_readfirstlane((int)(ncol0 >> 7));
-    const bool colvalid = ncol0 < p.N;
-    int st = 0;
-    for (int kt = 0; kt < nkt; ++kt) {
-      const int ld_st = st == 0 ? S - 1 : st - 1;
-      issue_loads(kt + S - 1, ld_st, kt + S - 1 < nkt);
-      const uint8_t* sA = smem + st * STAGE;
-      const uint8_t* sB = sA + A_BYTES;
-      const float* sSA = (const float*)(sB + B_BYTES);
-      const float sbv = colvalid ? p.sb[(int64_t)nblk * nkb + kt] : 0.0f;
-      i32x8_t a[TM16], b[TN16];
-#pragma unroll
-      for (int i = 0; i < TM16; ++i)
-        a[i] = cat(lds16(sA, wm * WM + i * 16 + r16, 2 * g16),
-                   lds16(sA, wm * WM + i * 16 + r16, 2 * g16 + 1));
-#pragma unroll
-      for (int j = 0; j < TN16; ++j)
-        b[j] = cat(lds16(sB, wn * WN + j * 16 + r16, 2 * g16),
-                   lds16(sB, wn * WN + j * 16 + r16, 2 * g16 + 1));
-#pragma unroll
-      for (int i = 0; i < TM16; ++i) {
-        // lane holds row (i*16 + lane%16) of the sub-tile: one A scale per lane
-        const float sc = sSA[wm * WM + i * 16 + r16] * sbv;
-#pragma unroll
-        for (int j = 0; j < TN16; ++j) {
-          const f32x4_t part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-              b[j], a[i], f32x4_t{0.f, 0.f, 0.f, 0.f}, FB, FA, 0, 0, 0, 0);
-#pragma unroll
-          for (int v = 0; v < 4; ++v) acc[i][j][v] = __builtin_fmaf(part[v], sc, acc[i][j][v]);
-        }
-      }
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<NL * (S - 2)>());
-      __syncthreads();
-      st = st == S - 1 ? 0 : st + 1;
-    }
-    // Lane l, register r of a transposed 16x16 accumulator is
-    // D[row = l%16][col = 4*(l/16) + r].
-#pragma unroll
-    for (int i = 0; i < TM16; ++i) {
-      const int64_t row = m0 + wm * WM + i * 16 + r16;
-#pragma unroll
-      for (int j = 0; j < TN16; ++j) store4(p, row, n0 + wn * WN + j * 16 + 4 * g16, acc[i][j]);
     }
   }
 }
@@ -643,7 +483,7 @@ hipError_t launch_gemm_bf16(const GemmArgs& a, int b_col_major, hipStream_t s) {
 
 template <int FA, int FB>
 static hipError_t launch_fp8_fmt(const GemmArgs& a, int block_scaled, hipStream_t s) {
-  if (block_scaled) return launch<kFP8Block, FA, FB, false, 256, 128, 128, 3, 4>(a, s);
+  if (block_scaled) return launch_gemm_fp8_block(a, FA, FB, s);
   return launch<kFP8Tensor, FA, FB, false, 256, 256, 128, 2, 4, kPrefetch>(a, s);
 }
 

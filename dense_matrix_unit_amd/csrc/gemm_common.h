@@ -1,0 +1,91 @@
+// Device helpers shared by the tiled GEMM kernels (gemm.hip, gemm_block.hip).
+#pragma once
+
+#include "dmu_device.h"
+#include "dmu_internal.h"
+
+namespace dmu {
+
+constexpr int kThreads = 256;  // 4 waves, one per SIMD
+
+// LDS position of logical 16-byte chunk c in row r for RB-byte rows.
+template <int RB>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (RB == 128) return (r ^ (r >> 3)) & 7;
+  else return ((r >> 1) ^ (r >> 2)) & 3;
+}
+
+// s_waitcnt immediate for gfx9-family: vmcnt(N) and lgkmcnt(0), expcnt free.
+template <int N>
+constexpr int waitcnt_vm_lgkm0() {
+  return (N & 0xF) | ((N >> 4) << 14) | (0x7 << 4);
+}
+
+// Workgroup barrier for the K loop.  The caller has already waited for its
+// own copies and LDS reads with an explicit s_waitcnt; __syncthreads() would
+// add a release fence, i.e. a wait for every outstanding vector memory
+// operation, including the L2 prefetch that is meant to stay in flight.  The
+// empty asm statements keep the compiler from moving memory accesses across.
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Workgroup -> output tile.  Workgroups are dispatched to the 8 XCDs round
+// robin (id % 8); give each XCD a contiguous run of logical tile ids, and walk
+// logical ids in column-major groups of kGroupM tile rows so that the tiles
+// resident on one XCD share few A and B panels.
+template <int kGroupM>
+__device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tm, int& tn) {
+  const int b = blockIdx.x, T = gridDim.x;
+  const int x = b & 7, j = b >> 3, per = T >> 3, rem = T & 7;
+  const int logical = x * per + (x < rem ? x : rem) + j;
+  const int group = kGroupM * tiles_n;
+  const int g = logical / group;
+  const int first = g * kGroupM;
+  const int gs = min(tiles_m - first, kGroupM);
+  const int r = logical - g * group;
+  tm = first + r % gs;
+  tn = r / gs;
+}
+
+__device__ __forceinline__ i32x8_t cat(const i32x4_t& lo, const i32x4_t& hi) {
+  return i32x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// D[row][col .. col+3] = x (+ C), masked to the matrix.
+__device__ __forceinline__ void store4(const GemmArgs& p, int64_t row, int64_t col, f32x4_t x) {
+  if (row >= p.M || col >= p.N) return;
+  const bool full = col + 3 < p.N;
+  if (p.C) {
+    const float* c = p.C + row * p.ldc + col;
+    if (full) {
+      x += *(const f32x4_t*)c;
+    } else {
+      for (int r = 0; r < 4; ++r)
+        if (col + r < p.N) x[r] += c[r];
+    }
+  }
+  if (p.out_bf16) {
+    uint16_t* d = (uint16_t*)p.D + row * p.ldd + col;
+    const uint32_t lo = f32_to_bf16_bits(x[0]) | ((uint32_t)f32_to_bf16_bits(x[1]) << 16);
+    const uint32_t hi = f32_to_bf16_bits(x[2]) | ((uint32_t)f32_to_bf16_bits(x[3]) << 16);
+    if (full) {
+      *(uint2*)d = make_uint2(lo, hi);
+    } else {
+      for (int r = 0; r < 4; ++r)
+        if (col + r < p.N) d[r] = f32_to_bf16_bits(x[r]);
+    }
+  } else {
+    float* d = (float*)p.D + row * p.ldd + col;
+    if (full) {
+      *(f32x4_t*)d = x;
+    } else {
+      for (int r = 0; r < 4; ++r)
+        if (col + r < p.N) d[r] = x[r];
+    }
+  }
+}
+
+}  // namespace dmu
