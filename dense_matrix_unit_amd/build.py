@@ -37,9 +37,14 @@ COMMON = [
 ]
 
 
+# Per-file code-generation options.  The block-scaled FP8 kernel promotes MFMA
+# results with VALU FMAs, which cannot read AGPRs: its MFMAs must write VGPRs.
+EXTRA = {"gemm_block.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc()] + COMMON + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc()] + COMMON + EXTRA.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     r = subprocess.run(cmd, capture_output=True, text=True)
