@@ -40,6 +40,7 @@ namespace {
 
 // K slices between the L2 prefetch of a slice and its use (0 = no prefetch).
 constexpr int kPrefetch = 3;
+constexpr int kWavesBF16 = 4, kWavesFP8 = 4;  // waves per workgroup (4: one per SIMD)
 
 template <int FA, int FB>
 __device__ __forceinline__ f32x16_t mfma_fp8_32x32x64(const i32x8_t& a, const i32x8_t& b,
@@ -49,32 +50,34 @@ __device__ __forceinline__ f32x16_t mfma_fp8_32x32x64(const i32x8_t& a, const i3
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FA, FB, 0, 0, 0, 0);
 }
 
-template <int KIND, int FA, int FB, bool BROW, int BM, int BN, int RB, int S, int kGroupM, int PD>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_kernel(
-    GemmArgs p) {
+template <int KIND, int FA, int FB, bool BROW, int BM, int BN, int RB, int S, int kGroupM, int PD,
+          int NW, bool KT>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4))) void
+gemm_kernel(GemmArgs p) {
+  constexpr int NT = NW * 64;   // threads; NW waves in a 2 x (NW/2) grid
   constexpr int ESZ = KIND == kBF16 ? 2 : 1;
   constexpr int CPR = RB / 16;  // 16-byte chunks per LDS row
-  constexpr int WM = BM / 2, WN = BN / 2;
+  constexpr int WM = BM / 2, WN = BN / (NW / 2);
   constexpr int TM = WM / 32, TN = WN / 32;      // 32x32 sub-tiles per wave
   constexpr int A_BYTES = BM * RB, B_BYTES = BN * RB;
   constexpr int STAGE = A_BYTES + B_BYTES;
   constexpr int NSTEP = KIND == kBF16 ? RB / 32 : RB / 64;  // MFMA K-steps per slice
-  constexpr int NLA = BM * CPR / kThreads;                 // A copies per thread per slice
-  constexpr int NLB = BROW ? 8 : BN * CPR / kThreads;      // B copies per thread per slice
+  constexpr int NLA = BM * CPR / NT;                 // A copies per thread per slice
+  constexpr int NLB = BROW ? 8 : BN * CPR / NT;      // B copies per thread per slice
   constexpr int NL = NLA + NLB;
-  static_assert(BM % 64 == 0 && BN % 64 == 0 && (BM * CPR) % kThreads == 0, "tile");
-  static_assert(!BROW || (KIND == kBF16 && BN == 256 && RB == 128 && S == 2),
+  static_assert(BM % 64 == 0 && BN % 64 == 0 && (BM * CPR) % NT == 0, "tile");
+  static_assert(!BROW || (KIND == kBF16 && BN == 256 && RB == 128 && S == 2 && NW == 4),
                 "row-major B staging");
   static_assert(KIND == kBF16 || KIND == kFP8Tensor, "per-block scales live in gemm_block.hip");
   static_assert(S >= 2 && NL * (S - 2) < 64, "vmcnt range");
   static_assert(PD == 0 || (S == 2 && !BROW && BM == 256 && BN == 256 && kGroupM == 4 && PD >= 2),
                 "L2 prefetch layout");
-  constexpr int PF_BYTES = PD > 0 ? 4 * 256 : 0;  // one 256-byte landing area per wave
+  constexpr int PF_BYTES = PD > 0 ? NW * 256 : 0;  // one 256-byte landing area per wave
   __shared__ __attribute__((aligned(1024))) uint8_t smem[S * STAGE + PF_BYTES];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int swave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, kept scalar
-  const int wm = swave >> 1, wn = swave & 1;
+  const int wm = swave / (NW / 2), wn = swave % (NW / 2);
   const int rl = lane & 31, hl = lane >> 5;
   const int tiles_m = (int)((p.M + BM - 1) / BM), tiles_n = (int)((p.N + BN - 1) / BN);
   int tm, tn;
@@ -91,7 +94,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   uint32_t voffA[NLA], cA[NLA];
 #pragma unroll
   for (int it = 0; it < NLA; ++it) {
-    const int q = it * kThreads + tid, row = q / CPR;
+    const int q = it * NT + tid, row = q / CPR;
     const uint32_t c = (uint32_t)(((q % CPR) ^ swz<RB>(row)) << 4);
     cA[it] = c;
     voffA[it] = row < rowsA ? (uint32_t)row * ldaB + c : kOOB;
@@ -115,12 +118,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     rB = make_rsrc((const uint8_t*)p.B + n0 * p.ldb * ESZ, (int64_t)(rowsB - 1) * ldbB + kbytes);
 #pragma unroll
     for (int it = 0; it < NLB; ++it) {
-      const int q = it * kThreads + tid, row = q / CPR;
+      const int q = it * NT + tid, row = q / CPR;
       const uint32_t c = (uint32_t)(((q % CPR) ^ swz<RB>(row)) << 4);
       cB[it] = c;
       voffB[it] = row < rowsB ? (uint32_t)row * ldbB + c : kOOB;
     }
   }
+
+  // A resource with no records: every load through it returns zeros.  When
+  // K fills whole slices (!KT), a slice is either entirely in range or
+  // entirely past the end, so the copies pick this resource with one scalar
+  // select per slice instead of testing every lane's offset.
+  const __amdgpu_buffer_rsrc_t rNull = make_rsrc(p.A, 0);
 
   // ---- L2 prefetch of slice kt + PD.  With two LDS stages only one slice of
   // copies is in flight, so a copy that misses to HBM stalls the K loop.  A
@@ -148,8 +157,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     if constexpr (PD > 0) {
       const bool active = kt < nkt;
       const uint32_t koff = active ? (uint32_t)kt * RB : 0u;
-      const uint32_t v = active && koff + cP < (uint32_t)kbytes ? voffP : kOOB;
-      buffer_load_lds4(rP, smem + S * STAGE + swave * 256, v, koff);
+      if constexpr (KT) {
+        const uint32_t v = active && koff + cP < (uint32_t)kbytes ? voffP : kOOB;
+        buffer_load_lds4(rP, smem + S * STAGE + swave * 256, v, koff);
+      } else {
+        buffer_load_lds4(active ? rP : rNull, smem + S * STAGE + swave * 256, voffP, koff);
+      }
     }
   };
 
@@ -168,7 +181,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 #pragma unroll
     for (int it = 0; it < NLA; ++it) {
       const uint32_t v = koff + cA[it] < klim ? voffA[it] : kOOB;
-      buffer_load_lds16(rA, sA + (it * kThreads + swave * 64) * 16, v, koff);
+      buffer_load_lds16(rA, sA + (it * NT + swave * 64) * 16, v, koff);
     }
     if constexpr (BROW) {
       const int k0 = kt * 64 + kb8 * 8;
@@ -181,7 +194,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 #pragma unroll
       for (int it = 0; it < NLB; ++it) {
         const uint32_t v = koff + cB[it] < klim ? voffB[it] : kOOB;
-        buffer_load_lds16(rB, sB + (it * kThreads + swave * 64) * 16, v, koff);
+        buffer_load_lds16(rB, sB + (it * NT + swave * 64) * 16, v, koff);
       }
     }
   };
@@ -195,8 +208,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     const uint32_t koff = active ? (uint32_t)kt * RB : 0u;
     const uint32_t klim = active ? (uint32_t)kbytes : 0u;
     if (idx < NLA) {
-      const uint32_t v = koff + cA[idx] < klim ? voffA[idx] : kOOB;
-      buffer_load_lds16(rA, sA + (idx * kThreads + swave * 64) * 16, v, koff);
+      if constexpr (KT) {
+        const uint32_t v = koff + cA[idx] < klim ? voffA[idx] : kOOB;
+        buffer_load_lds16(rA, sA + (idx * NT + swave * 64) * 16, v, koff);
+      } else {
+        buffer_load_lds16(active ? rA : rNull, sA + (idx * NT + swave * 64) * 16, voffA[idx], koff);
+      }
     } else if constexpr (BROW) {
       const int i = idx - NLA;
       const bool ok = active && colok && kt * 64 + kb8 * 8 < p.K;
@@ -204,8 +221,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
       breg[i] = buffer_load16(rB, ok ? voffB[0] + (uint32_t)(i * p.ldb * 2) : kOOB, soff);
     } else {
       const int it = idx - NLA;
-      const uint32_t v = koff + cB[it] < klim ? voffB[it] : kOOB;
-      buffer_load_lds16(rB, sB + (it * kThreads + swave * 64) * 16, v, koff);
+      if constexpr (KT) {
+        const uint32_t v = koff + cB[it] < klim ? voffB[it] : kOOB;
+        buffer_load_lds16(rB, sB + (it * NT + swave * 64) * 16, v, koff);
+      } else {
+        buffer_load_lds16(active ? rB : rNull, sB + (it * NT + swave * 64) * 16, voffB[it], koff);
+      }
     }
   };
 
@@ -318,8 +339,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
       read_one(0, 0, 0, k);
       __builtin_amdgcn_sched_barrier(0);
     }
-    int st = 0;
-    for (int kt = 0; kt < nkt; ++kt) {
+    // One K slice in stage st.  The loop runs two slices per iteration so that
+    // every stage index, hence every LDS address offset, is a constant.
+    auto slice = [&](int kt, const int st) __attribute__((always_inline)) {
       const int ld_st = st == 0 ? S - 1 : st - 1;  // stage of slice kt+S-1
       const int nx_st = st == S - 1 ? 0 : st + 1;  // stage of slice kt+1
       const bool act = kt + S - 1 < nkt;
@@ -377,8 +399,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
       } else {
         load_step(nx_st, 0, 0);  // next slice's first reads (zeros after the last slice)
       }
-      st = nx_st;
+    };
+    static_assert(S == 2, "two slices per loop iteration");
+    int kt = 0;
+    for (; kt + 1 < nkt; kt += 2) {
+      slice(kt, 0);
+      slice(kt + 1, 1);
     }
+    if (kt < nkt) slice(kt, 0);
 
     // ---- epilogue: scale, add C, round, store.  Lane l, register 4q+r of a
     // transposed 32x32 accumulator is D[row = l%32][col = 8q + 4*(l/32) + r].
@@ -389,8 +417,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     // are padded by 16 bytes, which makes both the band writes (16 lanes at
     // the same column of 16 rows) and the row reads bank-conflict free.
     constexpr int ROWW = WN + 4;  // padded band row, in floats
-    static_assert(4 * 32 * ROWW * 4 <= S * STAGE, "epilogue bands fit in LDS");
-    static_assert(4 * TM * 32 * WN * 2 <= S * STAGE && (WN * 2) % 16 == 0 && 64 % (WN / 8) == 0,
+    static_assert(NW * 32 * ROWW * 4 <= S * STAGE, "epilogue bands fit in LDS");
+    static_assert(NW * TM * 32 * WN * 2 <= S * STAGE && (WN * 2) % 16 == 0 && 64 % (WN / 8) == 0,
                   "BF16 staging fits in LDS");
     static_assert(WN % 4 == 0 && 64 % (WN / 4) == 0, "band read shape");
     float alpha = 1.0f;
@@ -405,7 +433,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
       // one column then fall in distinct bank groups.  Each read instruction
       // covers 4 rows x 256 B and each store writes 16 B (8 columns) per lane.
       uint8_t* wbase = smem + swave * (TM * 32 * WN * 2);
-      constexpr int RB16 = WN * 2;  // staged row bytes
+      constexpr int RB16 = WN * 2;    // staged row bytes
+      constexpr int UPR = RB16 / 16;  // 16-byte units per row
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -418,16 +447,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
             const uint32_t lo = f32_to_bf16_bits(x[0]) | ((uint32_t)f32_to_bf16_bits(x[1]) << 16);
             const uint32_t hi = f32_to_bf16_bits(x[2]) | ((uint32_t)f32_to_bf16_bits(x[3]) << 16);
             const int u = j * 4 + q;  // 16-byte unit of the staged row
-            *(uint2*)(wbase + (i * 32 + rl) * RB16 + ((u ^ (rl & 15)) << 4) + hl * 8) =
+            *(uint2*)(wbase + (i * 32 + rl) * RB16 + ((u ^ (rl & (UPR - 1))) << 4) + hl * 8) =
                 make_uint2(lo, hi);
           }
       __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<0>());  // own region only: no barrier
-      constexpr int UPR = RB16 / 16;  // 16-byte units per row
-      constexpr int RPI16 = 64 / UPR; // rows per read instruction
+      constexpr int RPI16 = 64 / UPR;  // rows per read instruction
 #pragma unroll
       for (int it = 0; it < TM * 32 / RPI16; ++it) {
         const int r = it * RPI16 + lane / UPR, u = lane % UPR;
-        const u32x4_t v = *(const u32x4_t*)(wbase + r * RB16 + ((u ^ (r & 15)) << 4));
+        const u32x4_t v = *(const u32x4_t*)(wbase + r * RB16 + ((u ^ (r & (UPR - 1))) << 4));
         const int64_t row = m0 + wm * WM + r, col = n0 + wn * WN + u * 8;
         if (row < p.M && col < p.N) {
           uint16_t* d = (uint16_t*)p.D + row * p.ldd + col;
@@ -465,11 +493,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   }
 }
 
-template <int KIND, int FA, int FB, bool BROW, int BM, int BN, int RB, int S, int G, int PD = 0>
+template <int KIND, int FA, int FB, bool BROW, int BM, int BN, int RB, int S, int G, int PD = 0,
+          int NW = 4>
 hipError_t launch(const GemmArgs& a, hipStream_t s) {
   const int64_t tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_kernel<KIND, FA, FB, BROW, BM, BN, RB, S, G, PD>), dim3((unsigned)tiles),
-                     dim3(kThreads), 0, s, a);
+  // K tail: the last slice is partial and its lanes are range-checked one by one
+  const bool ktail = (a.K * (KIND == kBF16 ? 2 : 1)) % RB != 0;
+  if (ktail)
+    hipLaunchKernelGGL((gemm_kernel<KIND, FA, FB, BROW, BM, BN, RB, S, G, PD, NW, true>),
+                       dim3((unsigned)tiles), dim3(NW * 64), 0, s, a);
+  else
+    hipLaunchKernelGGL((gemm_kernel<KIND, FA, FB, BROW, BM, BN, RB, S, G, PD, NW, false>),
+                       dim3((unsigned)tiles), dim3(NW * 64), 0, s, a);
   return hipGetLastError();
 }
 
@@ -477,14 +512,14 @@ hipError_t launch(const GemmArgs& a, hipStream_t s) {
 
 hipError_t launch_gemm_bf16(const GemmArgs& a, int b_col_major, hipStream_t s) {
   if (b_col_major && skinny_applies(a)) return launch_gemm_bf16_skinny(a, s);
-  if (b_col_major) return launch<kBF16, 0, 0, false, 256, 256, 128, 2, 4, kPrefetch>(a, s);
+  if (b_col_major) return launch<kBF16, 0, 0, false, 256, 256, 128, 2, 4, kPrefetch, kWavesBF16>(a, s);
   return launch<kBF16, 0, 0, true, 256, 256, 128, 2, 4>(a, s);
 }
 
 template <int FA, int FB>
 static hipError_t launch_fp8_fmt(const GemmArgs& a, int block_scaled, hipStream_t s) {
   if (block_scaled) return launch_gemm_fp8_block(a, FA, FB, s);
-  return launch<kFP8Tensor, FA, FB, false, 256, 256, 128, 2, 4, kPrefetch>(a, s);
+  return launch<kFP8Tensor, FA, FB, false, 256, 256, 128, 2, 4, kPrefetch, kWavesFP8>(a, s);
 }
 
 hipError_t launch_gemm_fp8(const GemmArgs& a, int fmt_a, int fmt_b, int block_scaled,
