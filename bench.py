@@ -144,10 +144,16 @@ class Bench:
             dmu.quantize_fp8(Xb, Qb, sb, fmt)
         return Xa, Xb, Qa, Qb, sa, sb
 
-    def gemm_fp8_leg(self, M, N, K, fmt, steps, warmup, copies=1, block=False):
+    def gemm_fp8_leg(self, M, N, K, fmt, steps, warmup, copies=1, block=False, promoted=False):
+        """promoted: per-tensor operands run through the block-scaled path with
+        every scale equal, i.e. partial sums promoted into FP32 every 128 K."""
         torch, dmu = self.torch, self.dmu
         Xa, Xb, Qa, Qb, sa, sb = self.fp8_operands(M, N, K, fmt, block)
         del Xa, Xb
+        if promoted:
+            sa = sa.reshape(1, 1).expand(M, K // 128).contiguous()
+            sb = sb.reshape(1, 1).expand((N + 127) // 128, K // 128).contiguous()
+            block = True
         Qas, Qbs = self.copies(Qa, copies), self.copies(Qb, copies)
         out = torch.empty((M, N), dtype=torch.bfloat16, device=self.dev)
         mode = dmu.SCALE_BLOCK if block else dmu.SCALE_TENSOR
@@ -322,6 +328,10 @@ def main():
         if want(name):
             legs[name] = b.gemm_fp8_leg(4096, 4096, 4096, fmt, S, W, copies=10)
             log("%s: %s" % (name, legs[name]))
+    if want("fp8_e4m3_4096_promoted"):
+        legs["fp8_e4m3_4096_promoted"] = b.gemm_fp8_leg(4096, 4096, 4096, dmu.E4M3, S, W, copies=10,
+                                                         promoted=True)
+        log("fp8_e4m3_4096 promoted every 128 K: %s" % legs["fp8_e4m3_4096_promoted"])
     if want("quantize_e4m3_4096_tensor"):
         legs["quantize_e4m3_4096_tensor"] = b.quantize_leg(4096, 4096, dmu.E4M3, None, S, W)
         log("quantize 4096^2: %s" % legs["quantize_e4m3_4096_tensor"])

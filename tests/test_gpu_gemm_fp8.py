@@ -163,3 +163,26 @@ def test_accuracy_vs_k_e4m3(K):
     # the 14-bit in-instruction sums put the FP8 "sums" error near 1.5e-5,
     # far below the 3.7e-2 that rounding the inputs to E4M3 costs
     assert oracle.rel_rms(D, Dref) < 1e-4
+
+
+@pytest.mark.parametrize("K", [256, 4096, 65536])
+def test_promotion_every_128_k_vs_fast_accumulation(K):
+    # The vidyal.ai page, Step 5, promotes FP8 partial sums into FP32 every
+    # 64 K because its accumulator keeps ~14 bits.  On gfx950 the MFMA adds its
+    # C operand in full FP32 (test_gpu_probe: accumulator_keeps_fp32_precision);
+    # only the sum of products inside one instruction keeps ~14 bits.  The
+    # block-scaled path with every scale equal is per-tensor FP8 promoted every
+    # 128 K (one 16x16x128 MFMA from zero per block, then an FP32 FMA).  Both
+    # must meet the bound, and promotion must not change the error materially.
+    Af = wl.normal((256, K), wl.SEED_A)
+    Bf = wl.normal((256, K), wl.SEED_B)
+    A, sa = quant(Af, dmu.E4M3)
+    B, sb = quant(Bf, dmu.E4M3)
+    Dfast, Dref = check(A, B, 0, 0, sa, sb, dmu.SCALE_TENSOR, torch.float32, what="fast K=%d" % K)
+    sa_blk = np.full((256, K // 128), sa[0], np.float32)
+    sb_blk = np.full((2, K // 128), sb[0], np.float32)
+    Dprom, Dref2 = check(A, B, 0, 0, sa_blk, sb_blk, dmu.SCALE_BLOCK, torch.float32,
+                         what="promoted K=%d" % K)
+    e_fast, e_prom = oracle.rel_rms(Dfast, Dref), oracle.rel_rms(Dprom, Dref2)
+    print("E4M3 K=%d rel-RMS from the sums: fast %.3e, promoted every 128 K %.3e" % (K, e_fast, e_prom))
+    assert e_prom > e_fast / 4 and e_prom < e_fast * 4
