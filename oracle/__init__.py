@@ -75,6 +75,13 @@ def lib():
         L.orc_gemm_fp8.argtypes = [p, i64, i32, p, i64, i32, p, p, i32, p, i64, i64, i64,
                                    i64, p, i64, p, p]
         L.orc_gemm_fp8.restype = i32
+        L.orc_decode_e8m0.argtypes = [ctypes.c_uint8]
+        L.orc_decode_e8m0.restype = ctypes.c_double
+        L.orc_quantize_mx.argtypes = [p, i64, i64, i64, i32, p, i64, p, i64]
+        L.orc_quantize_mx.restype = i32
+        L.orc_gemm_mx.argtypes = [p, i64, i32, p, i64, i32, p, i64, p, i64, p, i64, i64, i64, i64,
+                                  p, i64, p, p]
+        L.orc_gemm_mx.restype = i32
         _lib = L
     return _lib
 
@@ -179,6 +186,54 @@ def gemm_fp8(A, B, fmt_a: int, fmt_b: int, sa, sb, scale_mode: int, C=None, rows
                             scale_mode, _ptr(C), N, M, N, K, _ptr(r), nr, _ptr(D), _ptr(S))
     if rc != 0:
         raise ValueError("orc_gemm_fp8: bad arguments")
+    return D, S
+
+
+MX_BLOCK = 32
+
+
+def decode_e8m0(codes) -> np.ndarray:
+    """E8M0 scale codes -> 2^(code-127) (code 255: NaN)."""
+    c = np.asarray(codes, dtype=np.uint8)
+    return np.vectorize(lambda v: lib().orc_decode_e8m0(int(v)), otypes=[np.float64])(c)
+
+
+def quantize_mx(X, fmt: int):
+    """MX quantisation with 1 x 32 blocks along each row: returns (Q uint8
+    like X, S uint8 E8M0 codes [rows][cols/32])."""
+    X = np.ascontiguousarray(X, dtype=np.float32)
+    rows, cols = X.shape
+    Q = np.empty((rows, cols), dtype=np.uint8)
+    S = np.empty((rows, cols // MX_BLOCK), dtype=np.uint8)
+    rc = lib().orc_quantize_mx(_ptr(X), rows, cols, cols, fmt, _ptr(Q), cols, _ptr(S),
+                               cols // MX_BLOCK)
+    if rc != 0:
+        raise ValueError("orc_quantize_mx: bad arguments")
+    return Q, S
+
+
+def gemm_mx(A, B, fmt_a: int, fmt_b: int, SA, SB, C=None, rows=None):
+    """FP64 MX product (selected rows) and S = sum of |scaled a * scaled b|.
+    A: [M][K] uint8, B: [N][K] uint8, SA: [M][K/32], SB: [N][K/32] uint8."""
+    A = np.ascontiguousarray(A, dtype=np.uint8)
+    B = np.ascontiguousarray(B, dtype=np.uint8)
+    M, K = A.shape
+    N = B.shape[0]
+    assert B.shape[1] == K and K % MX_BLOCK == 0
+    SA = np.ascontiguousarray(SA, dtype=np.uint8)
+    SB = np.ascontiguousarray(SB, dtype=np.uint8)
+    assert SA.shape == (M, K // MX_BLOCK) and SB.shape == (N, K // MX_BLOCK)
+    if C is not None:
+        C = np.ascontiguousarray(C, dtype=np.float32)
+        assert C.shape == (M, N)
+    r, nr = _rows_arg(rows, M)
+    D = np.empty((nr, N), dtype=np.float64)
+    S = np.empty((nr, N), dtype=np.float64)
+    rc = lib().orc_gemm_mx(_ptr(A), K, fmt_a, _ptr(B), K, fmt_b, _ptr(SA), K // MX_BLOCK,
+                           _ptr(SB), K // MX_BLOCK, _ptr(C), N, M, N, K, _ptr(r), nr, _ptr(D),
+                           _ptr(S))
+    if rc != 0:
+        raise ValueError("orc_gemm_mx: bad arguments")
     return D, S
 
 

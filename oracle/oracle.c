@@ -122,19 +122,18 @@ uint16_t orc_encode_bf16(float x) {
   return (uint16_t)(sign | (w >> 16));
 }
 
-/* FP32 -> FP8 with round to nearest even and saturation: magnitudes at or
- * above the format's largest finite value (Inf included) become +-max. */
-uint8_t orc_encode_fp8(float x, int fmt) {
-  uint32_t u;
-  memcpy(&u, &x, sizeof u);
-  uint8_t sign = (uint8_t)((u >> 24) & 0x80u);
+/* A finite or infinite double -> FP8 with round to nearest even and
+ * saturation: magnitudes at or above the format's largest finite value (Inf
+ * included) become +-max; NaN becomes 0x7F / 0xFF. */
+static uint8_t encode_fp8_d(double x, int fmt) {
+  uint8_t sign = signbit(x) ? 0x80 : 0x00;
   if (isnan(x)) return (uint8_t)(sign | 0x7F);
   const int mbits = fmt == ORC_FMT_E4M3 ? 3 : 2;
   const int bias = fmt == ORC_FMT_E4M3 ? 7 : 15;
   const int emin = 1 - bias;
   const double fmax = fmt == ORC_FMT_E4M3 ? 448.0 : 57344.0;
   const uint8_t maxcode = fmt == ORC_FMT_E4M3 ? 0x7E : 0x7B;
-  double a = fabs((double)x);
+  double a = fabs(x);
   if (a >= fmax) return (uint8_t)(sign | maxcode);
   double v = round_to_grid(a, mbits, emin);
   if (v == 0.0) return sign;
@@ -152,6 +151,10 @@ uint8_t orc_encode_fp8(float x, int fmt) {
   }
   return (uint8_t)(sign | (efield << mbits) | mfield);
 }
+
+/* FP32 -> FP8 with round to nearest even and saturation (see encode_fp8_d;
+ * the FP32 value widens exactly). */
+uint8_t orc_encode_fp8(float x, int fmt) { return encode_fp8_d((double)x, fmt); }
 
 void orc_encode_bf16_array(const float* x, int64_t n, uint16_t* out) {
 #pragma omp parallel for schedule(static)
@@ -321,6 +324,106 @@ int orc_gemm_fp8(const uint8_t* A, int64_t lda, int fmt_a, const uint8_t* B, int
       if (C) out += (double)C[i * ldc + j];
       D[r * N + j] = out;
       if (S) S[r * N + j] = sabs;
+    }
+  }
+  return bad ? -1 : 0;
+}
+
+/* ---------------------------------------------------------------- MX (microscaling) */
+
+/* Microscaling block formats: every group of 32 consecutive elements along a
+ * row shares one scale that is a bare power of two stored as an 8-bit
+ * exponent (E8M0: code c means 2^(c-127), code 255 is NaN), and a block-scaled
+ * product multiplies every element by its group's scale ("How Blackwell's
+ * Tensor Memory Actually Works", section "Quantization became an allocation
+ * problem": D = C + (A x SFA)(B x SFB) with one scale per 16 or 32 elements
+ * along K; the 32-element, E8M0 variant follows the Open Compute
+ * microscaling specification). */
+#define ORC_MX_BLOCK 32
+
+double orc_decode_e8m0(uint8_t c) { return c == 255 ? NAN : ldexp(1.0, (int)c - 127); }
+
+/* Quantise rows x cols FP32 (row-major, cols % 32 == 0) to FP8 with one E8M0
+ * scale per 1 x 32 block.  Scale choice, read from the microscaling
+ * specification: X = 2^(floor(log2 amax) - emax), emax the largest exponent of
+ * the element format (8 for E4M3, 15 for E5M2), the exponent clamped to the
+ * E8M0 range [-127, 127]; elements q = saturating RNE of x / X (exact: X is a
+ * power of two).  Readings where the pages say nothing: an all-zero block
+ * takes the smallest scale 2^-127; a block holding a NaN or an infinity gets
+ * the NaN scale 255 and NaN element codes.  S is row-major [rows][lds],
+ * lds >= cols/32. */
+int orc_quantize_mx(const float* X, int64_t rows, int64_t cols, int64_t ldx, int fmt, uint8_t* Q,
+                    int64_t ldq, uint8_t* S, int64_t lds) {
+  if (rows <= 0 || cols <= 0 || cols % ORC_MX_BLOCK || ldx < cols || ldq < cols) return -1;
+  if (lds < cols / ORC_MX_BLOCK) return -1;
+  if (fmt != ORC_FMT_E4M3 && fmt != ORC_FMT_E5M2) return -1;
+  const int emax = fmt == ORC_FMT_E4M3 ? 8 : 15;
+  const int64_t nb = cols / ORC_MX_BLOCK;
+#pragma omp parallel for collapse(2) schedule(static)
+  for (int64_t r = 0; r < rows; r++) {
+    for (int64_t b = 0; b < nb; b++) {
+      const float* x = X + r * ldx + b * ORC_MX_BLOCK;
+      uint8_t* q = Q + r * ldq + b * ORC_MX_BLOCK;
+      double amax = 0.0;
+      int nonfinite = 0;
+      for (int k = 0; k < ORC_MX_BLOCK; k++) {
+        if (!isfinite(x[k])) nonfinite = 1;
+        else if (fabs((double)x[k]) > amax) amax = fabs((double)x[k]);
+      }
+      if (nonfinite) {
+        S[r * lds + b] = 255;
+        for (int k = 0; k < ORC_MX_BLOCK; k++) q[k] = (uint8_t)(signbit(x[k]) ? 0xFF : 0x7F);
+        continue;
+      }
+      int e;
+      if (amax == 0.0) {
+        e = -127;
+      } else {
+        int e2;
+        frexp(amax, &e2); /* amax = f * 2^e2, f in [0.5, 1): floor(log2 amax) = e2 - 1 */
+        e = e2 - 1 - emax;
+        if (e < -127) e = -127;
+        if (e > 127) e = 127;
+      }
+      S[r * lds + b] = (uint8_t)(e + 127);
+      for (int k = 0; k < ORC_MX_BLOCK; k++) q[k] = encode_fp8_d(ldexp((double)x[k], -e), fmt);
+    }
+  }
+  return 0;
+}
+
+/* Selected rows of the MX product: A is M x K row-major, B stored N x K, both
+ * FP8 codes (fmt_a, fmt_b); SA [M][ldsa] and SB [N][ldsb] hold one E8M0 code
+ * per 32-element group along K.  D = C + sum_k (a_ik * sa_i,k/32) * (b_jk *
+ * sb_j,k/32) in FP64, k ascending; S = sum_k of the magnitudes. */
+int orc_gemm_mx(const uint8_t* A, int64_t lda, int fmt_a, const uint8_t* B, int64_t ldb, int fmt_b,
+                const uint8_t* SA, int64_t ldsa, const uint8_t* SB, int64_t ldsb, const float* C,
+                int64_t ldc, int64_t M, int64_t N, int64_t K, const int64_t* rows, int64_t nrows,
+                double* D, double* S) {
+  if (M <= 0 || N <= 0 || K <= 0 || K % ORC_MX_BLOCK) return -1;
+  if (!rows) nrows = M;
+  double ta[256], tb[256];
+  for (int v = 0; v < 256; v++) {
+    ta[v] = orc_decode_fp8((uint8_t)v, fmt_a);
+    tb[v] = orc_decode_fp8((uint8_t)v, fmt_b);
+  }
+  int bad = 0;
+#pragma omp parallel for schedule(dynamic)
+  for (int64_t r = 0; r < nrows; r++) {
+    int64_t i = rows ? rows[r] : r;
+    if (i < 0 || i >= M) { bad = 1; continue; }
+    for (int64_t j = 0; j < N; j++) {
+      double acc = 0.0, sacc = 0.0;
+      for (int64_t k = 0; k < K; k++) {
+        const int64_t g = k / ORC_MX_BLOCK;
+        double p = (ta[A[i * lda + k]] * orc_decode_e8m0(SA[i * ldsa + g])) *
+                   (tb[B[j * ldb + k]] * orc_decode_e8m0(SB[j * ldsb + g]));
+        acc += p;
+        sacc += fabs(p);
+      }
+      if (C) acc += (double)C[i * ldc + j];
+      D[r * N + j] = acc;
+      if (S) S[r * N + j] = sacc;
     }
   }
   return bad ? -1 : 0;
