@@ -166,6 +166,45 @@ class Bench:
         bytes_ = 1.0 * (M * K + N * K) + 2.0 * M * N + 4.0 * (sa.numel() + sb.numel())
         return self.report(t, flop, bytes_, PEAK_FP8_TFLOPS, copies)
 
+    def gemm_mx_leg(self, M, N, K, fmt, steps, warmup, copies=1):
+        """Microscaled FP8: operands quantized by quantize_mxfp8 (one E8M0
+        scale per row and 32 K), product by gemm_mxfp8."""
+        torch, dmu = self.torch, self.dmu
+        Qa = torch.empty((M, K), dtype=torch.uint8, device=self.dev)
+        Qb = torch.empty((N, K), dtype=torch.uint8, device=self.dev)
+        Sa = torch.empty((M, K // 32), dtype=torch.uint8, device=self.dev)
+        Sb = torch.empty((N, K // 32), dtype=torch.uint8, device=self.dev)
+        dmu.quantize_mxfp8(self.normal_f32((M, K), 1), Qa, Sa, fmt)
+        dmu.quantize_mxfp8(self.normal_f32((N, K), 2), Qb, Sb, fmt)
+        Qas, Qbs = self.copies(Qa, copies), self.copies(Qb, copies)
+        Sas, Sbs = self.copies(Sa, copies), self.copies(Sb, copies)
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=self.dev)
+
+        def launch(i):
+            j = i % copies
+            dmu.gemm_mxfp8(Qas[j], Qbs[j], Sas[j], Sbs[j], out, fmt, fmt)
+
+        t = time_launches(torch, launch, steps, warmup)
+        flop = 2.0 * M * N * K
+        bytes_ = (1.0 + 1.0 / 32) * (M * K + N * K) + 2.0 * M * N
+        return self.report(t, flop, bytes_, PEAK_FP8_TFLOPS, copies)
+
+    def quantize_mx_leg(self, rows, cols, fmt, steps, warmup):
+        torch, dmu = self.torch, self.dmu
+        X = self.normal_f32((rows, cols), 1)
+        Q = torch.empty((rows, cols), dtype=torch.uint8, device=self.dev)
+        S = torch.empty((rows, cols // 32), dtype=torch.uint8, device=self.dev)
+
+        def launch(i):
+            dmu.quantize_mxfp8(X, Q, S, fmt)
+
+        t = time_launches(torch, launch, steps, warmup)
+        bytes_ = (5.0 + 1.0 / 32) * rows * cols
+        ms = t["event_mean_ms"]
+        return {"ms": round(ms, 5), "GB_per_s": round(bytes_ / ms / 1e6, 1),
+                "pct_hbm_peak": round(100 * bytes_ / ms / 1e6 / PEAK_HBM_GBS, 1),
+                "algorithmic_MB": round(bytes_ / 1e6, 2), "wall_ms": round(t["wall_ms"], 5)}
+
     def quantize_leg(self, rows, cols, fmt, block, steps, warmup, outliers=False):
         torch, dmu = self.torch, self.dmu
         if outliers:
@@ -332,6 +371,12 @@ def main():
         legs["fp8_e4m3_4096_promoted"] = b.gemm_fp8_leg(4096, 4096, 4096, dmu.E4M3, S, W, copies=10,
                                                          promoted=True)
         log("fp8_e4m3_4096 promoted every 128 K: %s" % legs["fp8_e4m3_4096_promoted"])
+    if want("mxfp8_e4m3_4096"):
+        legs["mxfp8_e4m3_4096"] = b.gemm_mx_leg(4096, 4096, 4096, dmu.E4M3, S, W, copies=10)
+        log("mxfp8 e4m3 4096: %s" % legs["mxfp8_e4m3_4096"])
+    if want("quantize_mx_e4m3_4096"):
+        legs["quantize_mx_e4m3_4096"] = b.quantize_mx_leg(4096, 4096, dmu.E4M3, S, W)
+        log("quantize mx 4096^2: %s" % legs["quantize_mx_e4m3_4096"])
     if want("quantize_e4m3_4096_tensor"):
         legs["quantize_e4m3_4096_tensor"] = b.quantize_leg(4096, 4096, dmu.E4M3, None, S, W)
         log("quantize 4096^2: %s" % legs["quantize_e4m3_4096_tensor"])

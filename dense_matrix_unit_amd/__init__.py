@@ -35,6 +35,9 @@ PROBE_BF16_16X16X32 = 0
 PROBE_BF16_32X32X16 = 1
 PROBE_FP8_16X16X128 = 2
 PROBE_FP8_32X32X64 = 3
+MX_BLOCK = 32  # values of K per E8M0 scale (DMU_MX_BLOCK)
+PROBE_MX_16X16X128 = 0  # shapes of dmu_probe_mfma_mx
+PROBE_MX_32X32X64 = 1
 
 # (name, restype, argtypes) of every exported C symbol
 _P = ctypes.c_void_p
@@ -45,11 +48,15 @@ SYMBOLS = {
     "gemm_fp8_scaled": (_I, [_P, _I64, _I, _P, _I64, _I, _P, _P, _I, _P, _I64, _P, _I64, _I,
                              _I64, _I64, _I64, _P]),
     "quantize_fp8": (_I, [_P, _I64, _I64, _I64, _I, _I64, _I64, _P, _I64, _P, _P]),
+    "gemm_mxfp8": (_I, [_P, _I64, _I, _P, _I64, _I, _P, _I64, _P, _I64, _P, _I64, _P, _I64, _I,
+                        _I64, _I64, _I64, _P]),
+    "quantize_mxfp8": (_I, [_P, _I64, _I64, _I64, _I, _P, _I64, _P, _I64, _P]),
     "dmu_status_string": (ctypes.c_char_p, [_I]),
     "dmu_version": (_I, []),
     "dmu_probe_mfma": (_I, [_I, _I, _I, _P, _P, _P, _P, _P]),
     "dmu_probe_lds_load": (_I, [_P, _P, _I, _I, _P]),
     "dmu_probe_mfma_rate": (_I, [_I, _P, _I, _I, _P, _P]),
+    "dmu_probe_mfma_mx": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P]),
 }
 
 _lib = None
@@ -205,11 +212,74 @@ def quantize_fp8(X, Q, scales, fmt: int = E4M3, block=None, stream=None):
     return Q, scales
 
 
+def gemm_mxfp8(A, B, scale_a, scale_b, out, fmt_a: int = E4M3, fmt_b: int = E4M3, C=None,
+               stream=None):
+    """out = (A x 2^(scale_a-127)) @ (B x 2^(scale_b-127))^T (+ C), microscaled
+    FP8.  A: [M, K] FP8 codes, B: [N, K] FP8 codes (B stored N x K), K a
+    multiple of 128.  scale_a: uint8 [M, >= K/32] and scale_b: uint8
+    [N, >= K/32] E8M0 codes, one per row and 32 values of K, row strides a
+    multiple of 4 bytes."""
+    torch = _torch()
+    _check_dtype(out, (torch.float32, torch.bfloat16), "out")
+    M, K = A.shape
+    N = B.shape[0]
+    if B.shape[1] != K or tuple(out.shape) != (M, N):
+        raise ValueError("shape mismatch")
+    _check_dtype(scale_a, (torch.uint8,), "scale_a")
+    _check_dtype(scale_b, (torch.uint8,), "scale_b")
+    if scale_a.shape[0] != M or scale_b.shape[0] != N:
+        raise ValueError("scale arrays need one row per row of A / stored row of B")
+    if scale_a.shape[1] < K // MX_BLOCK or scale_b.shape[1] < K // MX_BLOCK:
+        raise ValueError("scale rows need K/32 codes")
+    cptr, ldc = None, 0
+    if C is not None:
+        _check_dtype(C, (torch.float32,), "C")
+        if tuple(C.shape) != (M, N):
+            raise ValueError("C shape")
+        cptr, ldc = _dev_ptr(C, "C"), _ld(C, "C")
+    rc = load_library().gemm_mxfp8(
+        _fp8_ptr(A, "A"), _ld(A, "A"), fmt_a, _fp8_ptr(B, "B"), _ld(B, "B"), fmt_b,
+        _dev_ptr(scale_a, "scale_a"), _ld(scale_a, "scale_a"), _dev_ptr(scale_b, "scale_b"),
+        _ld(scale_b, "scale_b"), cptr, ldc, _dev_ptr(out, "out"), _ld(out, "out"),
+        OUT_F32 if out.dtype == torch.float32 else OUT_BF16, M, N, K, _stream(stream))
+    _check("gemm_mxfp8", rc)
+    return out
+
+
+def quantize_mxfp8(X, Q, S, fmt: int = E4M3, stream=None):
+    """Q, S = MX quantisation of X (float32 [rows, cols], cols % 32 == 0): Q
+    uint8 [rows, cols] FP8 codes, S uint8 [rows, >= cols/32] E8M0 codes."""
+    torch = _torch()
+    _check_dtype(X, (torch.float32,), "X")
+    _check_dtype(S, (torch.uint8,), "S")
+    rows, cols = X.shape
+    if tuple(Q.shape) != (rows, cols):
+        raise ValueError("Q shape")
+    if S.shape[0] != rows or S.shape[1] < cols // MX_BLOCK:
+        raise ValueError("S shape")
+    rc = load_library().quantize_mxfp8(
+        _dev_ptr(X, "X"), rows, cols, _ld(X, "X"), fmt, _fp8_ptr(Q, "Q"), _ld(Q, "Q"),
+        _dev_ptr(S, "S"), _ld(S, "S"), _stream(stream))
+    _check("quantize_mxfp8", rc)
+    return Q, S
+
+
 def probe_mfma(kind: int, A, B, C, D, fmt_a: int = E4M3, fmt_b: int = E4M3, stream=None):
     """Run one matrix instruction (see include/dmu_probe.h)."""
     rc = load_library().dmu_probe_mfma(kind, fmt_a, fmt_b, _dev_ptr(A, "A"), _dev_ptr(B, "B"),
                                        _dev_ptr(C, "C"), _dev_ptr(D, "D"), _stream(stream))
     _check("dmu_probe_mfma", rc)
+    return D
+
+
+def probe_mfma_mx(shape: int, A, B, SA, SB, C, D, fmt_a: int = E4M3, fmt_b: int = E4M3,
+                  opsel: int = 0, stream=None):
+    """Run one scaled (MX) matrix instruction (see include/dmu_probe.h)."""
+    rc = load_library().dmu_probe_mfma_mx(shape, fmt_a, fmt_b, opsel, _dev_ptr(A, "A"),
+                                          _dev_ptr(B, "B"), _dev_ptr(SA, "SA"),
+                                          _dev_ptr(SB, "SB"), _dev_ptr(C, "C"), _dev_ptr(D, "D"),
+                                          _stream(stream))
+    _check("dmu_probe_mfma_mx", rc)
     return D
 
 

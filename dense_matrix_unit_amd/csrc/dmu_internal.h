@@ -17,9 +17,13 @@ struct GemmArgs {
   const float* sa;  // FP8 scales (device)
   const float* sb;
   int out_bf16;  // 1: D is BF16, 0: FP32
+  // microscaling (MX): E8M0 codes, one per row and 32 values of K (device)
+  const uint8_t* xa = nullptr;
+  const uint8_t* xb = nullptr;
+  int64_t ldxa = 0, ldxb = 0;  // bytes per scale row
 };
 
-enum GemmKind { kBF16 = 0, kFP8Tensor = 1, kFP8Block = 2 };
+enum GemmKind { kBF16 = 0, kFP8Tensor = 1, kFP8Block = 2, kMX = 3 };
 
 // Launchers: argument checking is done by the caller; these only pick a
 // kernel configuration and launch it.  They return a hipError_t.
@@ -31,6 +35,11 @@ hipError_t launch_gemm_fp8(const GemmArgs& a, int fmt_a, int fmt_b, int block_sc
                            hipStream_t s);
 // Per-block scaled FP8 (A 1 x 128, B 128 x 128 scales; K % 128 == 0).
 hipError_t launch_gemm_fp8_block(const GemmArgs& a, int fmt_a, int fmt_b, hipStream_t s);
+// MX-scaled FP8 (E8M0 scale per row and 32 K, applied by the matrix unit;
+// K % 128 == 0, scale rows a multiple of 4 bytes).
+hipError_t launch_gemm_mxfp8(const GemmArgs& a, int fmt_a, int fmt_b, hipStream_t s);
+hipError_t launch_quantize_mxfp8(const float* X, int64_t rows, int64_t cols, int64_t ldx, int fmt,
+                                 uint8_t* Q, int64_t ldq, uint8_t* S, int64_t lds, hipStream_t s);
 hipError_t launch_quantize_fp8(const float* X, int64_t rows, int64_t cols, int64_t ldx, int fmt,
                                int64_t br, int64_t bc, uint8_t* Q, int64_t ldq, float* scales,
                                hipStream_t s);
@@ -40,5 +49,8 @@ hipError_t launch_probe_mfma(int kind, int fa, int fb, const void* A, const void
 hipError_t launch_probe_lds(const void* src, void* dst, int mode, int oob_from, hipStream_t s);
 hipError_t launch_probe_rate(int kind, const void* src, int iters, int grid, float* out,
                              hipStream_t s);
+hipError_t launch_probe_mx(int shape, int fa, int fb, int opsel, const void* A, const void* B,
+                           const void* SA, const void* SB, const float* C, float* D,
+                           hipStream_t s);
 
 }  // namespace dmu

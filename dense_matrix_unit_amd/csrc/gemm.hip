@@ -1,5 +1,6 @@
-// Tiled MFMA GEMM for gfx950 (CDNA4): BF16 and per-tensor-scaled FP8 inputs,
-// FP32 accumulation, FP32 or BF16 output.  (Per-block FP8 scales: gemm_block.hip.)
+// Tiled MFMA GEMM for gfx950 (CDNA4): BF16, per-tensor-scaled FP8 and
+// microscaled (MX) FP8 inputs, FP32 accumulation, FP32 or BF16 output.
+// (Per-block FP32 scales of 1 x 128 / 128 x 128 blocks: gemm_block.hip.)
 //
 // What is computed: D = A*B + C with the products accumulated in FP32 -- the
 // operation of a matrix instruction as the page "Tensor Cores: Matrix
@@ -7,7 +8,11 @@
 // applied to whole matrices as in its Step 2 (B may be stored N x K so both
 // operands are K-contiguous).  For FP8 the two per-tensor scales are applied
 // in the epilogue ("Tensor Cores" chapter of ai-infra-handbooks, "Precision"
-// section, on per-tensor FP8 scaling factors).
+// section, on per-tensor FP8 scaling factors).  MX: D = C + (A x SA)(B x SB)
+// with one power-of-two (E8M0) scale per row and 32 values of K, the
+// block-scaled product of "How Blackwell's Tensor Memory Actually Works",
+// section "Quantization became an allocation problem"; gfx950's scaled MFMA
+// applies the two scales itself, so they ride along with the K slices.
 //
 // Structure (three-level tiling: workgroup tile staged in LDS, wave tile held
 // in accumulator registers, one MFMA per 32x32 sub-tile and K step):
@@ -32,7 +37,14 @@
 //  * out-of-range rows and the K tail are fetched as zeros by giving their
 //    buffer loads an out-of-range offset;
 //  * workgroup ids are remapped so that the tiles one XCD runs together share
-//    A row panels and B column panels in that XCD's L2.
+//    A row panels and B column panels in that XCD's L2;
+//  * MX: each stage also holds the slice's scale codes, one 4-byte word (the
+//    4 E8M0 codes of 128 K) per tile row of A and of B, copied like the data.
+//    Word of row r sits at position (r % 32) * 8 + r / 32, so the four rows a
+//    lane multiplies (r = 32 i + lane % 32 within its wave's quadrant) are
+//    one 16-byte read.  A lane supplies the scale of K block lane / 32 of
+//    each 64-wide step: it shifts each word right by 8 * (lane / 32), and
+//    step s selects byte 2 s with the instruction's op_sel.
 #include "gemm_common.h"
 
 namespace dmu {
@@ -60,15 +72,20 @@ gemm_kernel(GemmArgs p) {
   constexpr int WM = BM / 2, WN = BN / (NW / 2);
   constexpr int TM = WM / 32, TN = WN / 32;      // 32x32 sub-tiles per wave
   constexpr int A_BYTES = BM * RB, B_BYTES = BN * RB;
-  constexpr int STAGE = A_BYTES + B_BYTES;
+  constexpr int SC_BYTES = KIND == kMX ? (BM + BN) * 4 : 0;  // MX scale words
+  constexpr int STAGE = A_BYTES + B_BYTES + SC_BYTES;
   constexpr int NSTEP = KIND == kBF16 ? RB / 32 : RB / 64;  // MFMA K-steps per slice
   constexpr int NLA = BM * CPR / NT;                 // A copies per thread per slice
   constexpr int NLB = BROW ? 8 : BN * CPR / NT;      // B copies per thread per slice
-  constexpr int NL = NLA + NLB;
+  constexpr int NLS = KIND == kMX ? 2 : 0;           // MX scale-word copies (A, B)
+  constexpr int NL = NLA + NLB + NLS;
   static_assert(BM % 64 == 0 && BN % 64 == 0 && (BM * CPR) % NT == 0, "tile");
   static_assert(!BROW || (KIND == kBF16 && BN == 256 && RB == 128 && S == 2 && NW == 4),
                 "row-major B staging");
-  static_assert(KIND == kBF16 || KIND == kFP8Tensor, "per-block scales live in gemm_block.hip");
+  static_assert(KIND == kBF16 || KIND == kFP8Tensor || KIND == kMX,
+                "per-block FP32 scales live in gemm_block.hip");
+  static_assert(KIND != kMX || (!KT && !BROW && RB == 128 && NW == 4 && BM == 256 && BN == 256),
+                "MX: whole 128-K slices, one scale word per tile row and thread");
   static_assert(S >= 2 && NL * (S - 2) < 64, "vmcnt range");
   static_assert(PD == 0 || (S == 2 && !BROW && BM == 256 && BN == 256 && kGroupM == 4 && PD >= 2),
                 "L2 prefetch layout");
@@ -130,6 +147,30 @@ gemm_kernel(GemmArgs p) {
   // entirely past the end, so the copies pick this resource with one scalar
   // select per slice instead of testing every lane's offset.
   const __amdgpu_buffer_rsrc_t rNull = make_rsrc(p.A, 0);
+
+  // ---- MX scale words: thread t copies the word of tile row
+  // (t % 8) * 32 + t / 8 to LDS word t (the order the K loop reads)
+  __amdgpu_buffer_rsrc_t rXA = rNull, rXB = rNull;
+  uint32_t voffXA = kOOB, voffXB = kOOB;
+  if constexpr (KIND == kMX) {
+    const int row = (tid & 7) * 32 + (tid >> 3);
+    const int64_t kb = p.K / 32;  // scale bytes per row
+    rXA = make_rsrc(p.xa + m0 * p.ldxa, (int64_t)(rowsA - 1) * p.ldxa + kb);
+    rXB = make_rsrc(p.xb + n0 * p.ldxb, (int64_t)(rowsB - 1) * p.ldxb + kb);
+    voffXA = row < rowsA ? (uint32_t)(row * p.ldxa) : kOOB;
+    voffXB = row < rowsB ? (uint32_t)(row * p.ldxb) : kOOB;
+  }
+  // MX scale-word copy `which` (0: A, 1: B) of slice kt into stage st
+  auto issue_scale = [&](int kt, int st, bool active, int which) __attribute__((always_inline)) {
+    if constexpr (KIND == kMX) {
+      uint8_t* dst = smem + st * STAGE + A_BYTES + B_BYTES + which * BM * 4 + swave * 256;
+      const uint32_t koff = active ? (uint32_t)kt * (RB / 32) : 0u;
+      if (which == 0)
+        buffer_load_lds4(active ? rXA : rNull, dst, voffXA, koff);
+      else
+        buffer_load_lds4(active ? rXB : rNull, dst, voffXB, koff);
+    }
+  };
 
   // ---- L2 prefetch of slice kt + PD.  With two LDS stages only one slice of
   // copies is in flight, so a copy that misses to HBM stalls the K loop.  A
@@ -197,12 +238,18 @@ gemm_kernel(GemmArgs p) {
         buffer_load_lds16(rB, sB + (it * NT + swave * 64) * 16, v, koff);
       }
     }
+#pragma unroll
+    for (int w = 0; w < NLS; ++w) issue_scale(kt, st, active, w);
   };
 
   // Copy number idx (0 <= idx < NLA + NLB) of slice kt into stage st; the
   // same copies issue_loads makes, one at a time, so they can be spread
   // between MFMAs.
   auto issue_one = [&](int kt, int st, bool active, int idx) __attribute__((always_inline)) {
+    if (NLS > 0 && idx >= NLA + NLB) {
+      issue_scale(kt, st, active, idx - NLA - NLB);
+      return;
+    }
     uint8_t* sA = smem + st * STAGE;
     uint8_t* sB = sA + A_BYTES;
     const uint32_t koff = active ? (uint32_t)kt * RB : 0u;
@@ -278,18 +325,50 @@ gemm_kernel(GemmArgs p) {
 #pragma unroll
       for (int j = 0; j < TN; ++j) acc[i][j] = f32x16_t{};
     i32x4_t fa[2][TM][CPL], fb[2][TN][CPL];
+    // 16-byte chunk (along K) that half h of this lane's step-s fragment
+    // holds.  Unscaled products do not depend on which K positions a lane's
+    // bytes stand for, so those read one contiguous run per lane.  The scaled
+    // MFMA does: a lane's two halves are K positions 16 * (lane / 32) and
+    // 32 + 16 * (lane / 32) of the 64-wide step, and lane group g's scale
+    // covers K block g (32 values) of the step.
+    auto chunk = [&](int s, int h) __attribute__((always_inline)) -> int {
+      if constexpr (KIND == kMX) return 4 * s + 2 * h + hl;
+      else return (2 * s + hl) * CPL + h;
+    };
+    // MX: raw scale words per stage (A rows, B rows) and the current slice's
+    // words shifted to this lane's K-run
+    u32x4_t xraw[2][2];
+    uint32_t xa[TM], xb[TN];
+    auto read_scales = [&](int st) __attribute__((always_inline)) {
+      if constexpr (KIND == kMX) {
+        const uint8_t* sc = smem + st * STAGE + A_BYTES + B_BYTES;
+        xraw[st][0] = *(const u32x4_t*)(sc + (rl * 8 + wm * TM) * 4);
+        xraw[st][1] = *(const u32x4_t*)(sc + BM * 4 + (rl * 8 + wn * TN) * 4);
+      }
+    };
+    auto take_scales = [&](int st) __attribute__((always_inline)) {
+      if constexpr (KIND == kMX) {
+        static_assert(TM == 4 && TN == 4, "one 16-byte read of scale words per operand");
+        const uint32_t sh = 8u * (uint32_t)hl;
+#pragma unroll
+        for (int i = 0; i < TM; ++i) xa[i] = xraw[st][0][i] >> sh;
+#pragma unroll
+        for (int j = 0; j < TN; ++j) xb[j] = xraw[st][1][j] >> sh;
+      }
+    };
     auto load_step = [&](int st, int s, int buf) __attribute__((always_inline)) {
       const uint8_t* sA = smem + st * STAGE;
       const uint8_t* sB = sA + A_BYTES;
-      const int c = (2 * s + hl) * CPL;
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int h = 0; h < CPL; ++h) fa[buf][i][h] = lds16(sA, wm * WM + i * 32 + rl, c + h);
+        for (int h = 0; h < CPL; ++h)
+          fa[buf][i][h] = lds16(sA, wm * WM + i * 32 + rl, chunk(s, h));
 #pragma unroll
       for (int j = 0; j < TN; ++j)
 #pragma unroll
-        for (int h = 0; h < CPL; ++h) fb[buf][j][h] = lds16(sB, wn * WN + j * 32 + rl, c + h);
+        for (int h = 0; h < CPL; ++h)
+          fb[buf][j][h] = lds16(sB, wn * WN + j * 32 + rl, chunk(s, h));
     };
     // Fragment read k (0 <= k < NR) of step s, in the order the step's MFMAs
     // first need them: A fragment 0, B fragments 0 .. TN-1, A fragments
@@ -300,14 +379,14 @@ gemm_kernel(GemmArgs p) {
     auto read_one = [&](int st, int s, int buf, int k) __attribute__((always_inline)) {
       const uint8_t* sA = smem + st * STAGE;
       const uint8_t* sB = sA + A_BYTES;
-      const int c = (2 * s + hl) * CPL;
+      const int c = chunk(s, k % CPL);
       const int slot = k / CPL, h = k % CPL;
       if (slot == 0)
-        fa[buf][0][h] = lds16(sA, wm * WM + rl, c + h);
+        fa[buf][0][h] = lds16(sA, wm * WM + rl, c);
       else if (slot <= TN)
-        fb[buf][slot - 1][h] = lds16(sB, wn * WN + (slot - 1) * 32 + rl, c + h);
+        fb[buf][slot - 1][h] = lds16(sB, wn * WN + (slot - 1) * 32 + rl, c);
       else
-        fa[buf][slot - TN][h] = lds16(sA, wm * WM + (slot - TN) * 32 + rl, c + h);
+        fa[buf][slot - TN][h] = lds16(sA, wm * WM + (slot - TN) * 32 + rl, c);
     };
     // The B fragment is the instruction's first operand, so each accumulator
     // holds a transposed 32x32 sub-tile (see the epilogue).
@@ -316,7 +395,18 @@ gemm_kernel(GemmArgs p) {
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
             __builtin_bit_cast(bf16x8_t, fb[buf][j][0]),
             __builtin_bit_cast(bf16x8_t, fa[buf][i][0]), acc[i][j], 0, 0, 0);
-      else
+      else if constexpr (KIND == kMX) {
+        // step s = buf (two steps per slice) uses scale byte 2 s; the first
+        // operand is B's fragment, so its scale is the instruction's first
+        if (buf == 0)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              cat(fb[buf][j][0], fb[buf][j][1]), cat(fa[buf][i][0], fa[buf][i][1]), acc[i][j],
+              FB, FA, 0, (int)xb[j], 0, (int)xa[i]);
+        else
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              cat(fb[buf][j][0], fb[buf][j][1]), cat(fa[buf][i][0], fa[buf][i][1]), acc[i][j],
+              FB, FA, 2, (int)xb[j], 2, (int)xa[i]);
+      } else
         acc[i][j] = mfma_fp8_32x32x64<FB, FA>(cat(fb[buf][j][0], fb[buf][j][1]),
                                               cat(fa[buf][i][0], fa[buf][i][1]), acc[i][j]);
     };
@@ -329,11 +419,12 @@ gemm_kernel(GemmArgs p) {
     // The next slice's copies are spread between this slice's MFMAs (one
     // every R MFMAs, all before the barrier): a burst of copies would stall
     // the wave at issue while the matrix pipe idles.
-    constexpr int NLD = NLA + NLB;
+    constexpr int NLD = NL;  // copies per slice, MX scale words included
     constexpr int PRE = (NSTEP - 1) * TM * TN + (kSplitLast ? TM / 2 : TM) * TN;
     constexpr int R = PRE / NLD < 2 ? PRE / NLD : 2;
     static_assert(R >= 1, "every copy is issued before the slice barrier");
     // same order as in the loop, so the waits at the loop head stay exact
+    read_scales(0);
 #pragma unroll
     for (int k = 0; k < NR; ++k) {
       read_one(0, 0, 0, k);
@@ -345,6 +436,7 @@ gemm_kernel(GemmArgs p) {
       const int ld_st = st == 0 ? S - 1 : st - 1;  // stage of slice kt+S-1
       const int nx_st = st == S - 1 ? 0 : st + 1;  // stage of slice kt+1
       const bool act = kt + S - 1 < nkt;
+      take_scales(st);
 #pragma unroll
       for (int s = 0; s < NSTEP; ++s) {
         const int buf = s & 1;
@@ -382,6 +474,7 @@ gemm_kernel(GemmArgs p) {
       }
       stage_barrier();
       __builtin_amdgcn_sched_barrier(0);
+      read_scales(nx_st);  // next slice's scale words; this slice's stay in xa / xb
       if constexpr (kSplitLast) {
         // next slice's first fragments, interleaved with the rest of this slice
         constexpr int NM = (TM - TM / 2) * TN;
@@ -497,14 +590,17 @@ template <int KIND, int FA, int FB, bool BROW, int BM, int BN, int RB, int S, in
           int NW = 4>
 hipError_t launch(const GemmArgs& a, hipStream_t s) {
   const int64_t tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
-  // K tail: the last slice is partial and its lanes are range-checked one by one
-  const bool ktail = (a.K * (KIND == kBF16 ? 2 : 1)) % RB != 0;
-  if (ktail)
-    hipLaunchKernelGGL((gemm_kernel<KIND, FA, FB, BROW, BM, BN, RB, S, G, PD, NW, true>),
-                       dim3((unsigned)tiles), dim3(NW * 64), 0, s, a);
-  else
-    hipLaunchKernelGGL((gemm_kernel<KIND, FA, FB, BROW, BM, BN, RB, S, G, PD, NW, false>),
-                       dim3((unsigned)tiles), dim3(NW * 64), 0, s, a);
+  // K tail: the last slice is partial and its lanes are range-checked one by
+  // one (MX requires whole slices and has no such variant)
+  if constexpr (KIND != kMX) {
+    if ((a.K * (KIND == kBF16 ? 2 : 1)) % RB != 0) {
+      hipLaunchKernelGGL((gemm_kernel<KIND, FA, FB, BROW, BM, BN, RB, S, G, PD, NW, true>),
+                         dim3((unsigned)tiles), dim3(NW * 64), 0, s, a);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((gemm_kernel<KIND, FA, FB, BROW, BM, BN, RB, S, G, PD, NW, false>),
+                     dim3((unsigned)tiles), dim3(NW * 64), 0, s, a);
   return hipGetLastError();
 }
 
@@ -528,6 +624,15 @@ hipError_t launch_gemm_fp8(const GemmArgs& a, int fmt_a, int fmt_b, int block_sc
   if (fmt_a == 0 && fmt_b == 1) return launch_fp8_fmt<0, 1>(a, block_scaled, s);
   if (fmt_a == 1 && fmt_b == 0) return launch_fp8_fmt<1, 0>(a, block_scaled, s);
   return launch_fp8_fmt<1, 1>(a, block_scaled, s);
+}
+
+hipError_t launch_gemm_mxfp8(const GemmArgs& a, int fmt_a, int fmt_b, hipStream_t s) {
+#define DMU_MX(FA, FB) launch<kMX, FA, FB, false, 256, 256, 128, 2, 4, kPrefetch, kWavesFP8>(a, s)
+  if (fmt_a == 0 && fmt_b == 0) return DMU_MX(0, 0);
+  if (fmt_a == 0 && fmt_b == 1) return DMU_MX(0, 1);
+  if (fmt_a == 1 && fmt_b == 0) return DMU_MX(1, 0);
+  return DMU_MX(1, 1);
+#undef DMU_MX
 }
 
 }  // namespace dmu

@@ -13,6 +13,12 @@
 //  * 32x32xK MFMA (K = 16 bf16 or 64 fp8): lane l supplies row l%32 of A and
 //    column l%32 of B, holding the K-run [g*K/2, (g+1)*K/2) with g = l/32;
 //    result register v of lane l is D[8*(v/4) + 4*(l/32) + v%4][l%32].
+// Without scales a product is the same under any permutation of K shared by
+// A and B, so these probes pin rows, columns and result registers but not
+// which K positions a lane's bytes stand for.  The scaled (MX) probe does:
+// there a lane's 32 FP8 bytes are two 16-byte halves, half h holding K
+// positions [h*K/2 + 16*g, h*K/2 + 16*g + 16), and lane group b supplies the
+// scale of the 32-wide K block b.
 #include "dmu_device.h"
 #include "dmu_internal.h"
 
@@ -83,6 +89,55 @@ __global__ void probe_mfma_kernel(const void* Av, const void* Bv, const float* C
     const f32x16_t d =
         __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FA, FB, 0, 0, 0, 0);
     for (int v = 0; v < 16; ++v) D[(8 * (v / 4) + 4 * (l / 32) + v % 4) * 32 + l % 32] = d[v];
+  }
+}
+
+// One scaled matrix instruction (microscaling, MX): D = (A x SA)(B x SB) + C
+// with one E8M0 scale (2^(code-127)) per row and 32-element K block, the
+// block-scaled product of the page "How Blackwell's Tensor Memory Actually
+// Works", section "Quantization became an allocation problem".  Layout (with
+// g = l / rows, rows = 16 or 32): lane l holds row l % rows; byte o of its
+// data half h (0, 1) is K position h*K/2 + 16*g + o; it supplies the scale of
+// K block g -- SA[l%16][l/16] for 16x16x128, SA[l%32][l/32] for 32x32x64 --
+// in byte OPSEL of its 32-bit scale register, the other three bytes holding
+// decoys (code ^ 4, a factor 16 away) so a wrong byte choice shows in D.
+template <int SHAPE, int FA, int FB, int OPSEL>
+__global__ void probe_mx_kernel(const uint8_t* A, const uint8_t* B, const uint8_t* SA,
+                                const uint8_t* SB, const float* C, float* D) {
+  const int l = threadIdx.x;
+  constexpr int R = SHAPE == 0 ? 16 : 32;   // rows per K group
+  constexpr int K = SHAPE == 0 ? 128 : 64;  // instruction K
+  const int row = l % R, g = l / R;
+  i32x8_t a, b;
+  for (int w = 0; w < 8; ++w) {
+    uint32_t x = 0, y = 0;
+    for (int q = 0; q < 4; ++q) {
+      const int o = 4 * w + q;  // byte of the lane's 32
+      const int kp = (o / 16) * (K / 2) + 16 * g + o % 16;
+      x |= (uint32_t)A[row * K + kp] << (8 * q);
+      y |= (uint32_t)B[row * K + kp] << (8 * q);
+    }
+    a[w] = (int)x;
+    b[w] = (int)y;
+  }
+  auto word = [&](uint8_t code) {
+    uint32_t v = 0;
+    for (int q = 0; q < 4; ++q) v |= (uint32_t)(q == OPSEL ? code : (uint8_t)(code ^ 4)) << (8 * q);
+    return (int)v;
+  };
+  const int sa = word(SA[row * (K / 32) + g]), sb = word(SB[row * (K / 32) + g]);
+  if constexpr (SHAPE == 0) {
+    f32x4_t c;
+    for (int v = 0; v < 4; ++v) c[v] = C[(4 * g + v) * 16 + row];
+    const f32x4_t d =
+        __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, FA, FB, OPSEL, sa, OPSEL, sb);
+    for (int v = 0; v < 4; ++v) D[(4 * g + v) * 16 + row] = d[v];
+  } else {
+    f32x16_t c;
+    for (int v = 0; v < 16; ++v) c[v] = C[(8 * (v / 4) + 4 * g + v % 4) * 32 + row];
+    const f32x16_t d =
+        __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FA, FB, OPSEL, sa, OPSEL, sb);
+    for (int v = 0; v < 16; ++v) D[(8 * (v / 4) + 4 * g + v % 4) * 32 + row] = d[v];
   }
 }
 
@@ -176,6 +231,32 @@ hipError_t probe_fmt(int fa, int fb, const void* A, const void* B, const float* 
   return hipGetLastError();
 }
 
+template <int SHAPE, int FA, int FB>
+hipError_t probe_mx_opsel(int opsel, const uint8_t* A, const uint8_t* B, const uint8_t* SA,
+                          const uint8_t* SB, const float* C, float* D, hipStream_t s) {
+#define DMU_PROBE_MX(O)                                                                      \
+  hipLaunchKernelGGL((probe_mx_kernel<SHAPE, FA, FB, O>), dim3(1), dim3(64), 0, s, A, B, SA, \
+                     SB, C, D)
+  switch (opsel) {
+    case 0: DMU_PROBE_MX(0); break;
+    case 1: DMU_PROBE_MX(1); break;
+    case 2: DMU_PROBE_MX(2); break;
+    default: DMU_PROBE_MX(3); break;
+  }
+#undef DMU_PROBE_MX
+  return hipGetLastError();
+}
+
+template <int SHAPE>
+hipError_t probe_mx_fmt(int fa, int fb, int opsel, const uint8_t* A, const uint8_t* B,
+                        const uint8_t* SA, const uint8_t* SB, const float* C, float* D,
+                        hipStream_t s) {
+  if (fa == 0 && fb == 0) return probe_mx_opsel<SHAPE, 0, 0>(opsel, A, B, SA, SB, C, D, s);
+  if (fa == 0 && fb == 1) return probe_mx_opsel<SHAPE, 0, 1>(opsel, A, B, SA, SB, C, D, s);
+  if (fa == 1 && fb == 0) return probe_mx_opsel<SHAPE, 1, 0>(opsel, A, B, SA, SB, C, D, s);
+  return probe_mx_opsel<SHAPE, 1, 1>(opsel, A, B, SA, SB, C, D, s);
+}
+
 }  // namespace
 
 hipError_t launch_probe_mfma(int kind, int fa, int fb, const void* A, const void* B,
@@ -209,6 +290,15 @@ hipError_t launch_probe_rate(int kind, const void* src, int iters, int grid, flo
     hipLaunchKernelGGL(probe_rate_kernel<3>, dim3(grid), dim3(256), 0, s, (const uint8_t*)src,
                        iters, out);
   return hipGetLastError();
+}
+
+hipError_t launch_probe_mx(int shape, int fa, int fb, int opsel, const void* A, const void* B,
+                           const void* SA, const void* SB, const float* C, float* D,
+                           hipStream_t s) {
+  const uint8_t *a = (const uint8_t*)A, *b = (const uint8_t*)B;
+  const uint8_t *sa = (const uint8_t*)SA, *sb = (const uint8_t*)SB;
+  if (shape == 0) return probe_mx_fmt<0>(fa, fb, opsel, a, b, sa, sb, C, D, s);
+  return probe_mx_fmt<1>(fa, fb, opsel, a, b, sa, sb, C, D, s);
 }
 
 }  // namespace dmu

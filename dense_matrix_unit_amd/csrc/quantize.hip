@@ -16,6 +16,17 @@
 //  * 1 x 128 blocks: 32 lanes per block (16 bytes per lane), half-wave max.
 //  * 128 x 128 blocks: one 256-thread workgroup per block keeps its 64 values
 //    per thread in registers between the amax and the encode (one HBM read).
+//  * MX (1 x 32 blocks, E8M0 scales; "How Blackwell's Tensor Memory Actually
+//    Works", section "Quantization became an allocation problem", with the
+//    Open Compute microscaling choice of scale): 8 lanes per block.  The
+//    scale is X = 2^(floor(log2 amax) - emax), emax = 8 (E4M3) or 15 (E5M2),
+//    the largest power of two that keeps amax / X below 2^(emax+1); its code
+//    is the biased exponent of amax minus emax, clamped at 0.  Elements are
+//    the saturating RNE codes of x * 2^(127 - code), an exact FP32 product
+//    (the multiplier is a normal power of two, and a product that leaves the
+//    normal range is far below half the smallest FP8 step).  A block holding
+//    NaN or Inf gets code 255 (NaN) and NaN element codes of the elements'
+//    signs.
 #include "dmu_device.h"
 #include "dmu_internal.h"
 
@@ -246,6 +257,49 @@ __global__ __launch_bounds__(256) void quant_128x128(const float* X, int64_t nbc
   if (t == 0) scales[blockIdx.x] = scale_from_amax<FMT>(amax);
 }
 
+// ---- MX: 1 x 32 blocks, E8M0 scale codes ---------------------------------
+// 8 lanes own one block (4 values each); a 256-thread workgroup covers 32
+// blocks per round and does kRounds rounds, loads of all rounds issued first.
+template <int FMT>
+__global__ __launch_bounds__(256) void quant_mx(const float* X, int64_t rows, int64_t nb,
+                                                int64_t ldx, uint8_t* Q, int64_t ldq, uint8_t* S,
+                                                int64_t lds) {
+  constexpr uint32_t kEmax = FMT == 0 ? 8u : 15u;
+  const int sub = threadIdx.x & 7;
+  const int64_t nblk = rows * nb;
+  f32x4_t v[kRounds];
+  int64_t blk[kRounds], r[kRounds], cb[kRounds];
+#pragma unroll
+  for (int u = 0; u < kRounds; ++u) {
+    blk[u] = ((int64_t)blockIdx.x * kRounds + u) * 32 + (threadIdx.x >> 3);
+    v[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    r[u] = blk[u] / nb;
+    cb[u] = blk[u] - r[u] * nb;
+    if (blk[u] < nblk) v[u] = *(const f32x4_t*)(X + r[u] * ldx + cb[u] * 32 + 4 * sub);
+  }
+#pragma unroll
+  for (int u = 0; u < kRounds; ++u) {
+    uint32_t m = amax4(v[u]);
+#pragma unroll
+    for (int o = 4; o > 0; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o, 64));
+    if (blk[u] < nblk) {
+      uint32_t code, q;
+      if (m >= 0x7F800000u) {  // Inf or NaN in the block
+        code = 255u;
+        q = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) q |= ((__float_as_uint(v[u][e]) >> 24 & 0x80u) | 0x7Fu) << (8 * e);
+      } else {
+        const uint32_t eb = m >> 23;  // biased exponent of amax (0: zero or subnormal)
+        code = eb > kEmax ? eb - kEmax : 0u;
+        q = encode4<FMT>(v[u], __uint_as_float((254u - code) << 23));
+      }
+      *(uint32_t*)(Q + r[u] * ldq + cb[u] * 32 + 4 * sub) = q;
+      if (sub == 0) S[r[u] * lds + cb[u]] = (uint8_t)code;
+    }
+  }
+}
+
 template <int FMT>
 hipError_t launch_fmt(const float* X, int64_t rows, int64_t cols, int64_t ldx, int64_t br,
                       int64_t bc, uint8_t* Q, int64_t ldq, float* scales, hipStream_t s) {
@@ -276,6 +330,17 @@ hipError_t launch_fmt(const float* X, int64_t rows, int64_t cols, int64_t ldx, i
 }
 
 }  // namespace
+
+hipError_t launch_quantize_mxfp8(const float* X, int64_t rows, int64_t cols, int64_t ldx, int fmt,
+                                 uint8_t* Q, int64_t ldq, uint8_t* S, int64_t lds, hipStream_t s) {
+  const int64_t nb = cols / 32, nblk = rows * nb;
+  const dim3 grid((unsigned)((nblk + 32 * kRounds - 1) / (32 * kRounds)));
+  if (fmt == 0)
+    hipLaunchKernelGGL(quant_mx<0>, grid, dim3(256), 0, s, X, rows, nb, ldx, Q, ldq, S, lds);
+  else
+    hipLaunchKernelGGL(quant_mx<1>, grid, dim3(256), 0, s, X, rows, nb, ldx, Q, ldq, S, lds);
+  return hipGetLastError();
+}
 
 hipError_t launch_quantize_fp8(const float* X, int64_t rows, int64_t cols, int64_t ldx, int fmt,
                                int64_t br, int64_t bc, uint8_t* Q, int64_t ldq, float* scales,

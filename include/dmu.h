@@ -137,6 +137,62 @@ int quantize_fp8(const float* X, int64_t rows, int64_t cols, int64_t ldx, int fm
                  int64_t block_rows, int64_t block_cols, uint8_t* Q, int64_t ldq, float* scales,
                  void* stream);
 
+/*
+ * Microscaling (MX) FP8: block-scaled operands with one power-of-two scale per
+ * row and 32 consecutive values of K, the product D = C + (A x SFA)(B x SFB)
+ * of "How Blackwell's Tensor Memory Actually Works", section "Quantization
+ * became an allocation problem" (block-scaled MMA, one scale per 32 values,
+ * E8M0 scales).  An E8M0 code c is the value 2^(c - 127); c = 255 is NaN.
+ */
+#define DMU_MX_BLOCK 32
+
+/*
+ * gemm_mxfp8: D = sum_k (a_ik * 2^(sa_i,k/32 - 127)) * (b_jk * 2^(sb_j,k/32 - 127))
+ * (+ C), FP8 inputs, FP32 accumulation; the matrix unit applies the scales.
+ *
+ *   A       : M x K FP8 codes (fmt_a), row-major, lda.
+ *   B       : K x N operand stored N x K (column-major B), FP8 codes (fmt_b), ldb.
+ *   scale_a : M x (K/32) E8M0 codes, row-major with ld_sa bytes per row.
+ *   scale_b : N x (K/32) E8M0 codes (one per stored row of B and 32 K), ld_sb.
+ *   C, D    : as for gemm_bf16.
+ *   M, N >= 1; K >= 128 and K % 128 == 0; ld_sa, ld_sb >= K/32 and multiples
+ *   of 4; scale pointers 4-byte aligned.
+ * Each 64-wide run of K is one matrix instruction whose inner sum is formed at
+ * the instruction's own precision (about 14 bits below its largest term, as
+ * for per-tensor FP8) and added into the FP32 accumulator.  A NaN code makes
+ * every output that uses it NaN.  Scaled products below FP32 range flush to
+ * zero; a 32-wide group whose scaled sum exceeds FP32 range makes the output
+ * non-finite (Inf of unspecified sign, or NaN), whatever the exact sum.
+ * Errors: DMU_ERR_INVALID_ARG as for gemm_fp8_scaled, plus K % 128 != 0, a
+ * null scale array, a short or misaligned scale row stride.
+ */
+int gemm_mxfp8(const uint8_t* A, int64_t lda, int fmt_a, const uint8_t* B, int64_t ldb,
+               int fmt_b, const uint8_t* scale_a, int64_t ld_sa, const uint8_t* scale_b,
+               int64_t ld_sb, const float* C, int64_t ldc, void* D, int64_t ldd, int d_dtype,
+               int64_t M, int64_t N, int64_t K, void* stream);
+
+/*
+ * quantize_mxfp8: FP32 -> FP8 with one E8M0 scale per 1 x 32 block.
+ *
+ *   X      : rows x cols FP32, row-major, ldx; cols % 32 == 0.
+ *   fmt    : DMU_FP8_E4M3 (emax = 8) or DMU_FP8_E5M2 (emax = 15), the exponent
+ *            of the format's largest power of two.
+ *   Q      : rows x cols FP8 codes, row-major, ldq.
+ *   S      : rows x (cols/32) E8M0 codes, row-major, lds bytes per row.
+ * For each block: amax = max |x|; the scale is X = 2^(floor(log2 amax) - emax)
+ * with the exponent clamped to [-127, 127] (the Open Compute microscaling
+ * choice: the block's largest value lands in [2^emax, 2^(emax+1))), stored as
+ * code floor(log2 amax) - emax + 127; every element is the saturating
+ * round-to-nearest-even FP8 code of x / X (so x ~ decode(q) * X, what
+ * gemm_mxfp8 takes).  An all-zero block gets code 0; a block holding NaN or
+ * Inf gets code 255 and every element the NaN code of its own sign.  The
+ * result is bit-exact and independent of launch configuration.
+ * Errors: DMU_ERR_INVALID_ARG for null pointers, cols % 32 != 0, short or
+ * misaligned leading dimensions, an unknown format.
+ */
+int quantize_mxfp8(const float* X, int64_t rows, int64_t cols, int64_t ldx, int fmt, uint8_t* Q,
+                   int64_t ldq, uint8_t* S, int64_t lds, void* stream);
+
 /* Human-readable text for a status code (static storage, never NULL). */
 const char* dmu_status_string(int status);
 

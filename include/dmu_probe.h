@@ -63,6 +63,26 @@ int dmu_probe_lds_load(const void* src, void* dst, int mode, int oob_from, void*
  */
 int dmu_probe_mfma_rate(int kind, const void* src, int iters, int grid, float* out, void* stream);
 
+#define DMU_PROBE_MX_16X16X128 0 /* v_mfma_scale_f32_16x16x128_f8f6f4 */
+#define DMU_PROBE_MX_32X32X64 1  /* v_mfma_scale_f32_32x32x64_f8f6f4 */
+
+/*
+ * Run ONE scaled matrix instruction on a single wave: the microscaling (MX)
+ * product D = (A x SA)(B x SB) + C of the page "How Blackwell's Tensor Memory
+ * Actually Works", section "Quantization became an allocation problem", with
+ * one E8M0 scale (value 2^(code-127)) per row and 32-element run of K.
+ * Shape DMU_PROBE_MX_16X16X128 (m = n = 16, k = 128) or DMU_PROBE_MX_32X32X64
+ * (m = n = 32, k = 64).  A [m][k] and B [n][k] (B stored N x K) are FP8 codes
+ * in fmt_a / fmt_b (0 = E4M3, 1 = E5M2), SA [m][k/32] and SB [n][k/32] are
+ * E8M0 codes, C and D [m][n] row-major FP32.  Each lane puts the scale of the
+ * row and K-run its fragment holds in byte `opsel` (0..3) of its scale
+ * register and decoy codes (code ^ 4) in the other bytes, so a wrong layout or
+ * byte selection shows up as a wrong D.  Returns DMU_OK or
+ * DMU_ERR_INVALID_ARG / DMU_ERR_HIP.
+ */
+int dmu_probe_mfma_mx(int shape, int fmt_a, int fmt_b, int opsel, const void* A, const void* B,
+                      const void* SA, const void* SB, const float* C, float* D, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

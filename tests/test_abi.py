@@ -106,3 +106,40 @@ def test_python_binding_rejects_cpu_tensors():
     A = torch.zeros(64, 64, dtype=torch.bfloat16)
     with pytest.raises(TypeError):
         dmu.gemm_bf16(A, A, torch.zeros(64, 64))
+
+
+def call_mx(**kw):
+    a = dict(A=FAKE, lda=256, fa=0, B=FAKE, ldb=256, fb=0, sa=FAKE, ldsa=8, sb=FAKE, ldsb=8,
+             C=None, ldc=0, D=FAKE, ldd=64, d_dtype=1, M=64, N=64, K=256, stream=None)
+    a.update(kw)
+    return dmu.load_library().gemm_mxfp8(*a.values())
+
+
+@pytest.mark.parametrize("kw", [
+    dict(A=None), dict(B=None), dict(sa=None), dict(sb=None), dict(D=None), dict(fa=2),
+    dict(fb=-1), dict(K=96), dict(K=160, lda=160, ldb=160), dict(K=0), dict(lda=240),
+    dict(ldsa=4), dict(ldsb=6), dict(ldsa=10), dict(sa=FAKE + 2), dict(sb=FAKE + 1),
+    dict(A=FAKE + 8), dict(M=0), dict(N=0), dict(d_dtype=3), dict(ldd=60),
+])
+def test_gemm_mxfp8_rejects(kw):
+    assert call_mx(**kw) == dmu.DMU_ERR_INVALID_ARG
+
+
+def test_gemm_mxfp8_unsupported_huge_scale_ld():
+    assert call_mx(ldsa=1 << 24) == dmu.DMU_ERR_UNSUPPORTED
+
+
+def call_qmx(**kw):
+    a = dict(X=FAKE, rows=64, cols=256, ldx=256, fmt=0, Q=FAKE, ldq=256, S=FAKE, lds=8,
+             stream=None)
+    a.update(kw)
+    return dmu.load_library().quantize_mxfp8(*a.values())
+
+
+@pytest.mark.parametrize("kw", [
+    dict(X=None), dict(Q=None), dict(S=None), dict(rows=0), dict(cols=0), dict(cols=48, ldx=48,
+    ldq=64), dict(cols=16, ldx=16, ldq=16), dict(fmt=2), dict(ldx=250), dict(ldq=240),
+    dict(ldq=264), dict(lds=7), dict(X=FAKE + 4), dict(Q=FAKE + 8),
+])
+def test_quantize_mxfp8_rejects(kw):
+    assert call_qmx(**kw) == dmu.DMU_ERR_INVALID_ARG

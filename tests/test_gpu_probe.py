@@ -155,3 +155,127 @@ def test_mfma_rate_probe_counts_every_instruction(kind, k, one):
     dmu.probe_mfma_rate(kind, src, iters, grid, out)
     torch.cuda.synchronize()
     assert torch.all(out == 256.0 * k * iters)
+
+
+MX_SHAPES = {dmu.PROBE_MX_16X16X128: (16, 16, 128), dmu.PROBE_MX_32X32X64: (32, 32, 64)}
+
+
+def run_mx(shape, A, B, SA, SB, C, fa=0, fb=0, opsel=0):
+    m, n, _ = MX_SHAPES[shape]
+    D = torch.full((m, n), float("nan"), dtype=torch.float32, device="cuda")
+    dmu.probe_mfma_mx(shape, dev(A), dev(B), dev(SA), dev(SB), dev(C), D, fa, fb, opsel)
+    torch.cuda.synchronize()
+    return D.cpu().numpy().astype(np.float64)
+
+
+def cancelling_codes(m, n, groups, seed, lo=120, hi=134):
+    """SA[i][g] = a_i + u_g and SB[j][g] = b_j - u_g: every product feeding
+    D[i][j] carries the same power of two, so the instruction's sum of small
+    integers stays exact, while a lane that took another row's scale, or a
+    decoy byte, changes D.  A mix-up of K blocks shared by A and B cancels
+    here; test_mfma_mx_k_positions pins those."""
+    rng = np.random.default_rng(seed)
+    u = rng.integers(-3, 4, size=groups)
+    a = rng.integers(lo, hi, size=m)
+    b = rng.integers(lo, hi, size=n)
+    SA = (a[:, None] + u[None, :]).astype(np.uint8)
+    SB = (b[:, None] - u[None, :]).astype(np.uint8)
+    return SA, SB
+
+
+@pytest.mark.parametrize("shape", [dmu.PROBE_MX_16X16X128, dmu.PROBE_MX_32X32X64])
+@pytest.mark.parametrize("fa,fb", [(0, 0), (1, 0), (0, 1), (1, 1)])
+@pytest.mark.parametrize("opsel", [0, 1, 2, 3])
+def test_mfma_mx_layout_exact(shape, fa, fb, opsel):
+    m, n, k = MX_SHAPES[shape]
+    A = oracle.encode_fp8(wl.small_ints((m, k), 31) * 0.5, fa)
+    B = oracle.encode_fp8(wl.small_ints((n, k), 32), fb)
+    SA, SB = cancelling_codes(m, n, k // 32, 33 + opsel)
+    C = wl.small_ints((m, n), 34, -50, 50)
+    D = run_mx(shape, A, B, SA, SB, C, fa, fb, opsel)
+    ref, _ = oracle.gemm_mx(A, B, fa, fb, SA, SB, C=C)
+    assert np.array_equal(D, ref)
+
+
+@pytest.mark.parametrize("shape", [dmu.PROBE_MX_16X16X128, dmu.PROBE_MX_32X32X64])
+def test_mfma_mx_k_positions(shape):
+    # one product 1 x 1 at K position k, block scales 2^g on A and 2^(4g) on
+    # B: D = 2^(5 * (k // 32)) exactly when the unit scales K position k with
+    # the codes of its own 32-wide block, which pins where each of a lane's
+    # bytes sits along K (unscaled instructions cannot show it)
+    m, n, k = MX_SHAPES[shape]
+    SA = np.tile((127 + np.arange(k // 32)).astype(np.uint8), (m, 1))
+    SB = np.tile((127 + 4 * np.arange(k // 32)).astype(np.uint8), (n, 1))
+    C = np.zeros((m, n), np.float32)
+    for kk in range(k):
+        Af = np.zeros((m, k), np.float32)
+        Bf = np.zeros((n, k), np.float32)
+        Af[:, kk] = 1.0
+        Bf[:, kk] = 1.0
+        A, B = oracle.encode_fp8(Af, 0), oracle.encode_fp8(Bf, 0)
+        D = run_mx(shape, A, B, SA, SB, C)
+        ref, _ = oracle.gemm_mx(A, B, 0, 0, SA, SB)
+        assert np.all(ref == 2.0 ** (5 * (kk // 32)))
+        assert np.array_equal(D, ref), "K position %d" % kk
+
+
+@pytest.mark.parametrize("shape", [dmu.PROBE_MX_16X16X128, dmu.PROBE_MX_32X32X64])
+def test_mfma_mx_extreme_codes_cancel(shape):
+    # 2^-127 on one side and 2^127 on the other (rows and columns of the same
+    # parity): exact if the instruction combines the two exponents before it
+    # scales the product.  Outputs whose products carry 2^-254 come out zero;
+    # those carrying 2^254 overflow in each 32-wide K group on its own, so the
+    # result is non-finite but its sign need not be the exact sum's.
+    m, n, k = MX_SHAPES[shape]
+    A = oracle.encode_fp8(wl.small_ints((m, k), 41), 0)
+    B = oracle.encode_fp8(wl.small_ints((n, k), 42), 0)
+    SA = np.zeros((m, k // 32), np.uint8)
+    SB = np.full((n, k // 32), 254, np.uint8)
+    SA[1::2] = 254
+    SB[1::2] = 0
+    C = np.zeros((m, n), np.float32)
+    D = run_mx(shape, A, B, SA, SB, C)
+    ref, _ = oracle.gemm_mx(A, B, 0, 0, SA, SB)
+    ri, cj = np.arange(m)[:, None] % 2, np.arange(n)[None, :] % 2
+    same = ri == cj
+    assert np.array_equal(D[same], ref[same])
+    assert np.all(D[(ri == 0) & (cj == 1)] == 0.0)
+    huge = (ri == 1) & (cj == 0) & (ref != 0)
+    assert not np.isfinite(D[huge]).any()
+
+
+@pytest.mark.parametrize("shape", [dmu.PROBE_MX_16X16X128, dmu.PROBE_MX_32X32X64])
+@pytest.mark.parametrize("seed", [1, 2])
+def test_mfma_mx_random_within_instruction_precision(shape, seed):
+    # unrelated scale codes: products of different magnitudes meet inside one
+    # instruction, whose inner sum keeps 14 bits below its largest term
+    # (inner-sum probe above); the FP8 GEMM bound for one instruction chunk
+    m, n, k = MX_SHAPES[shape]
+    rng = np.random.default_rng(seed)
+    A = oracle.encode_fp8(wl.normal((m, k), seed), 0)
+    B = oracle.encode_fp8(wl.normal((n, k), seed + 5), 1)
+    SA = rng.integers(118, 137, size=(m, k // 32)).astype(np.uint8)
+    SB = rng.integers(118, 137, size=(n, k // 32)).astype(np.uint8)
+    C = wl.normal((m, n), seed + 9)
+    D = run_mx(shape, A, B, SA, SB, C, 0, 1)
+    ref, S = oracle.gemm_mx(A, B, 0, 1, SA, SB, C=C)
+    a = oracle.decode_fp8(A, 0) * np.repeat(oracle.decode_e8m0(SA), 32, axis=1)
+    b = oracle.decode_fp8(B, 1) * np.repeat(oracle.decode_e8m0(SB), 32, axis=1)
+    max_term = np.abs(a[:, None, :] * b[None, :, :]).max(axis=2)
+    bound = 1e-5 * (S + np.abs(C)) + 2.0 ** -12 * max_term
+    assert np.all(np.abs(D - ref) <= bound)
+
+
+def test_mfma_mx_nan_scale_code():
+    # E8M0 code 255 is NaN: every output that uses that scale is NaN
+    m, n, k = MX_SHAPES[dmu.PROBE_MX_32X32X64]
+    A = oracle.encode_fp8(wl.small_ints((m, k), 51), 0)
+    B = oracle.encode_fp8(wl.small_ints((n, k), 52), 0)
+    SA = np.full((m, 2), 127, np.uint8)
+    SB = np.full((n, 2), 127, np.uint8)
+    SA[3, 1] = 255
+    C = np.zeros((m, n), np.float32)
+    D = run_mx(dmu.PROBE_MX_32X32X64, A, B, SA, SB, C)
+    ref, _ = oracle.gemm_mx(A, B, 0, 0, SA, SB)
+    assert np.all(np.isnan(ref[3])) and np.all(np.isnan(D[3]))
+    assert np.array_equal(np.delete(D, 3, axis=0), np.delete(ref, 3, axis=0))
