@@ -235,6 +235,8 @@ class Bench:
         grid = 1024
         for name, kind, iters, peak in (("bf16", dmu.PROBE_BF16_32X32X16, 2048, PEAK_BF16_TFLOPS),
                                         ("fp8_e4m3", dmu.PROBE_FP8_32X32X64, 1024,
+                                         PEAK_FP8_TFLOPS),
+                                        ("mxfp8_e4m3", dmu.PROBE_MXFP8_32X32X64, 1024,
                                          PEAK_FP8_TFLOPS)):
             fb = 16 if name == "bf16" else 32
             n = 8 * 64 * fb

@@ -35,6 +35,7 @@ PROBE_BF16_16X16X32 = 0
 PROBE_BF16_32X32X16 = 1
 PROBE_FP8_16X16X128 = 2
 PROBE_FP8_32X32X64 = 3
+PROBE_MXFP8_32X32X64 = 4  # rate probe only: scaled form, unit E8M0 scales
 MX_BLOCK = 32  # values of K per E8M0 scale (DMU_MX_BLOCK)
 PROBE_MX_16X16X128 = 0  # shapes of dmu_probe_mfma_mx
 PROBE_MX_32X32X64 = 1

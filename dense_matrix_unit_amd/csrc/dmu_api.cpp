@@ -177,7 +177,9 @@ int dmu_probe_lds_load(const void* src, void* dst, int mode, int oob_from, void*
 }
 
 int dmu_probe_mfma_rate(int kind, const void* src, int iters, int grid, float* out, void* stream) {
-  if (!src || !out || (kind != DMU_PROBE_BF16_32X32X16 && kind != DMU_PROBE_FP8_32X32X64))
+  if (!src || !out ||
+      (kind != DMU_PROBE_BF16_32X32X16 && kind != DMU_PROBE_FP8_32X32X64 &&
+       kind != DMU_PROBE_MXFP8_32X32X64))
     return DMU_ERR_INVALID_ARG;
   if (iters < 1 || iters > (1 << 20) || grid < 1 || grid > 65536) return DMU_ERR_INVALID_ARG;
   if (!aligned(src, 16) || !aligned(out, 4)) return DMU_ERR_INVALID_ARG;

@@ -23,7 +23,8 @@ struct GemmArgs {
   int64_t ldxa = 0, ldxb = 0;  // bytes per scale row
 };
 
-enum GemmKind { kBF16 = 0, kFP8Tensor = 1, kFP8Block = 2, kMX = 3 };
+// kMX / kMX4: MX scales fetched one / four K slices at a time
+enum GemmKind { kBF16 = 0, kFP8Tensor = 1, kFP8Block = 2, kMX = 3, kMX4 = 4 };
 
 // Launchers: argument checking is done by the caller; these only pick a
 // kernel configuration and launch it.  They return a hipError_t.

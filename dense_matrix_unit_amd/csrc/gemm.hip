@@ -38,13 +38,14 @@
 //    buffer loads an out-of-range offset;
 //  * workgroup ids are remapped so that the tiles one XCD runs together share
 //    A row panels and B column panels in that XCD's L2;
-//  * MX: each stage also holds the slice's scale codes, one 4-byte word (the
-//    4 E8M0 codes of 128 K) per tile row of A and of B, copied like the data.
-//    Word of row r sits at position (r % 32) * 8 + r / 32, so the four rows a
-//    lane multiplies (r = 32 i + lane % 32 within its wave's quadrant) are
-//    one 16-byte read.  A lane supplies the scale of K block lane / 32 of
-//    each 64-wide step: it shifts each word right by 8 * (lane / 32), and
-//    step s selects byte 2 s with the instruction's op_sel.
+//  * MX: a slice's scale codes are one 4-byte word (the 4 E8M0 codes of 128
+//    K) per tile row of A and of B.  They sit in a two-buffer LDS ring beside
+//    the stages, fetched for 4 slices at a time (16 bytes per row) when the
+//    scale rows allow it.  After each slice barrier a lane reads the next
+//    slice's words of its 4 A and 4 B rows; it supplies the scale of K block
+//    lane / 32 of each 64-wide step, so it shifts each word right by
+//    8 * (lane / 32), and step s selects byte 2 s with the instruction's
+//    op_sel.
 #include "gemm_common.h"
 
 namespace dmu {
@@ -72,25 +73,35 @@ gemm_kernel(GemmArgs p) {
   constexpr int WM = BM / 2, WN = BN / (NW / 2);
   constexpr int TM = WM / 32, TN = WN / 32;      // 32x32 sub-tiles per wave
   constexpr int A_BYTES = BM * RB, B_BYTES = BN * RB;
-  constexpr int SC_BYTES = KIND == kMX ? (BM + BN) * 4 : 0;  // MX scale words
-  constexpr int STAGE = A_BYTES + B_BYTES + SC_BYTES;
+  constexpr int STAGE = A_BYTES + B_BYTES;
+  // MX: scale words are fetched XG slices at a time (4 * XG bytes per tile
+  // row) into a two-buffer ring of their own after the stages
+  constexpr bool MX = KIND == kMX || KIND == kMX4;
+  constexpr int XG = KIND == kMX4 ? 4 : 1;
+  constexpr int XROW = 4 * XG;                  // ring bytes per tile row
+  constexpr int XBUF = (BM + BN) * XROW;        // one ring buffer (A rows, then B rows)
+  constexpr int XOFF = S * STAGE;               // ring offset in LDS
+  constexpr int XR = MX ? 2 * XBUF : 0;
   constexpr int NSTEP = KIND == kBF16 ? RB / 32 : RB / 64;  // MFMA K-steps per slice
   constexpr int NLA = BM * CPR / NT;                 // A copies per thread per slice
   constexpr int NLB = BROW ? 8 : BN * CPR / NT;      // B copies per thread per slice
-  constexpr int NLS = KIND == kMX ? 2 : 0;           // MX scale-word copies (A, B)
+  constexpr int NLS = MX ? 2 : 0;                    // MX scale-group copies (A, B)
   constexpr int NL = NLA + NLB + NLS;
   static_assert(BM % 64 == 0 && BN % 64 == 0 && (BM * CPR) % NT == 0, "tile");
   static_assert(!BROW || (KIND == kBF16 && BN == 256 && RB == 128 && S == 2 && NW == 4),
                 "row-major B staging");
-  static_assert(KIND == kBF16 || KIND == kFP8Tensor || KIND == kMX,
+  static_assert(KIND == kBF16 || KIND == kFP8Tensor || MX,
                 "per-block FP32 scales live in gemm_block.hip");
-  static_assert(KIND != kMX || (!KT && !BROW && RB == 128 && NW == 4 && BM == 256 && BN == 256),
-                "MX: whole 128-K slices, one scale word per tile row and thread");
+  static_assert(!MX || (!KT && !BROW && RB == 128 && NW == 4 && BM == 256 && BN == 256 && S == 2),
+                "MX: whole 128-K slices, one scale row per thread and operand");
   static_assert(S >= 2 && NL * (S - 2) < 64, "vmcnt range");
   static_assert(PD == 0 || (S == 2 && !BROW && BM == 256 && BN == 256 && kGroupM == 4 && PD >= 2),
                 "L2 prefetch layout");
-  constexpr int PF_BYTES = PD > 0 ? NW * 256 : 0;  // one 256-byte landing area per wave
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[S * STAGE + PF_BYTES];
+  // one landing area per wave for the L2 prefetch's 4-byte copies, and for
+  // MX scale copies that have nothing to fetch (64 lanes x 4 * XG bytes)
+  constexpr int PF_WAVE = MX ? 64 * XROW : 256;
+  constexpr int PF_BYTES = PD > 0 || MX ? NW * PF_WAVE : 0;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[S * STAGE + XR + PF_BYTES];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int swave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, kept scalar
@@ -148,27 +159,36 @@ gemm_kernel(GemmArgs p) {
   // select per slice instead of testing every lane's offset.
   const __amdgpu_buffer_rsrc_t rNull = make_rsrc(p.A, 0);
 
-  // ---- MX scale words: thread t copies the word of tile row
-  // (t % 8) * 32 + t / 8 to LDS word t (the order the K loop reads)
+  // ---- MX scale words.  Group G holds slices XG*G .. XG*G+XG-1: the 4*XG
+  // codes of each tile row, for A rows then B rows, in ring buffer G % 2.
+  // Thread t copies row t of A and of B (4*XG bytes each; rows past the
+  // matrix read zeros).  A row's codes for one slice are a single word, so
+  // each copy instruction touches 64 rows, i.e. 64 cache lines: fetching XG
+  // slices at once divides those line requests by XG.
   __amdgpu_buffer_rsrc_t rXA = rNull, rXB = rNull;
   uint32_t voffXA = kOOB, voffXB = kOOB;
-  if constexpr (KIND == kMX) {
-    const int row = (tid & 7) * 32 + (tid >> 3);
+  const int ngroups = nkt / XG;
+  if constexpr (MX) {
     const int64_t kb = p.K / 32;  // scale bytes per row
     rXA = make_rsrc(p.xa + m0 * p.ldxa, (int64_t)(rowsA - 1) * p.ldxa + kb);
     rXB = make_rsrc(p.xb + n0 * p.ldxb, (int64_t)(rowsB - 1) * p.ldxb + kb);
-    voffXA = row < rowsA ? (uint32_t)(row * p.ldxa) : kOOB;
-    voffXB = row < rowsB ? (uint32_t)(row * p.ldxb) : kOOB;
+    voffXA = tid < rowsA ? (uint32_t)(tid * p.ldxa) : kOOB;
+    voffXB = tid < rowsB ? (uint32_t)(tid * p.ldxb) : kOOB;
   }
-  // MX scale-word copy `which` (0: A, 1: B) of slice kt into stage st
-  auto issue_scale = [&](int kt, int st, bool active, int which) __attribute__((always_inline)) {
-    if constexpr (KIND == kMX) {
-      uint8_t* dst = smem + st * STAGE + A_BYTES + B_BYTES + which * BM * 4 + swave * 256;
-      const uint32_t koff = active ? (uint32_t)kt * (RB / 32) : 0u;
-      if (which == 0)
-        buffer_load_lds4(active ? rXA : rNull, dst, voffXA, koff);
-      else
-        buffer_load_lds4(active ? rXB : rNull, dst, voffXB, koff);
+  // copy `which` (0: A, 1: B) of scale group G.  A copy with nothing to
+  // fetch (no group G, or `on` false) still issues, through the null
+  // resource into the wave's landing area: one instruction stream for every
+  // slice, with no branch between the MFMAs.
+  auto issue_xgroup = [&](int G, int which, bool on) __attribute__((always_inline)) {
+    if constexpr (MX) {
+      const bool act = on && G < ngroups;
+      uint8_t* dst = act ? smem + XOFF + (G & 1) * XBUF + which * BM * XROW + swave * 64 * XROW
+                         : smem + S * STAGE + XR + swave * PF_WAVE;
+      const uint32_t koff = act ? (uint32_t)G * XROW : 0u;
+      const __amdgpu_buffer_rsrc_t r = act ? (which == 0 ? rXA : rXB) : rNull;
+      const uint32_t v = which == 0 ? voffXA : voffXB;
+      if constexpr (XG == 4) buffer_load_lds16(r, dst, v, koff);
+      else buffer_load_lds4(r, dst, v, koff);
     }
   };
 
@@ -200,9 +220,9 @@ gemm_kernel(GemmArgs p) {
       const uint32_t koff = active ? (uint32_t)kt * RB : 0u;
       if constexpr (KT) {
         const uint32_t v = active && koff + cP < (uint32_t)kbytes ? voffP : kOOB;
-        buffer_load_lds4(rP, smem + S * STAGE + swave * 256, v, koff);
+        buffer_load_lds4(rP, smem + S * STAGE + XR + swave * PF_WAVE, v, koff);
       } else {
-        buffer_load_lds4(active ? rP : rNull, smem + S * STAGE + swave * 256, voffP, koff);
+        buffer_load_lds4(active ? rP : rNull, smem + S * STAGE + XR + swave * PF_WAVE, voffP, koff);
       }
     }
   };
@@ -238,8 +258,6 @@ gemm_kernel(GemmArgs p) {
         buffer_load_lds16(rB, sB + (it * NT + swave * 64) * 16, v, koff);
       }
     }
-#pragma unroll
-    for (int w = 0; w < NLS; ++w) issue_scale(kt, st, active, w);
   };
 
   // Copy number idx (0 <= idx < NLA + NLB) of slice kt into stage st; the
@@ -247,7 +265,13 @@ gemm_kernel(GemmArgs p) {
   // between MFMAs.
   auto issue_one = [&](int kt, int st, bool active, int idx) __attribute__((always_inline)) {
     if (NLS > 0 && idx >= NLA + NLB) {
-      issue_scale(kt, st, active, idx - NLA - NLB);
+      // MX: kt is the slice being copied, one ahead of the slice being
+      // multiplied (cur).  In the first slice of group G, the copy of group
+      // G + 1: it lands by this slice's closing wait, and its buffer last
+      // held group G - 1, whose reads all completed before the barrier that
+      // closed the previous slice.
+      const int cur = kt - (S - 1);
+      issue_xgroup(cur / XG + 1, idx - NLA - NLB, cur % XG == 0);
       return;
     }
     uint8_t* sA = smem + st * STAGE;
@@ -304,6 +328,8 @@ gemm_kernel(GemmArgs p) {
   // ---- prologue: slices 0 .. S-2 in flight, wait for slice 0
 #pragma unroll
   for (int t = 0; t < S - 1; ++t) issue_loads(t, t, t < nkt);
+#pragma unroll
+  for (int w = 0; w < NLS; ++w) issue_xgroup(0, w, true);  // MX scale group 0
   // slices 1 .. PD-1 are prefetched here; the loop prefetches kt + PD
 #pragma unroll
   for (int t = 1; t < PD; ++t) issue_pf(t);
@@ -332,28 +358,29 @@ gemm_kernel(GemmArgs p) {
     // 32 + 16 * (lane / 32) of the 64-wide step, and lane group g's scale
     // covers K block g (32 values) of the step.
     auto chunk = [&](int s, int h) __attribute__((always_inline)) -> int {
-      if constexpr (KIND == kMX) return 4 * s + 2 * h + hl;
+      if constexpr (MX) return 4 * s + 2 * h + hl;
       else return (2 * s + hl) * CPL + h;
     };
-    // MX: raw scale words per stage (A rows, B rows) and the current slice's
-    // words shifted to this lane's K-run
-    u32x4_t xraw[2][2];
-    uint32_t xa[TM], xb[TN];
-    auto read_scales = [&](int st) __attribute__((always_inline)) {
-      if constexpr (KIND == kMX) {
-        const uint8_t* sc = smem + st * STAGE + A_BYTES + B_BYTES;
-        xraw[st][0] = *(const u32x4_t*)(sc + (rl * 8 + wm * TM) * 4);
-        xraw[st][1] = *(const u32x4_t*)(sc + BM * 4 + (rl * 8 + wn * TN) * 4);
+    // MX: the next slice's scale words as read from the ring, and the
+    // current slice's shifted to this lane's K block
+    uint32_t xraw[TM + TN], xa[TM], xb[TN];
+    auto read_scales = [&](int kt) __attribute__((always_inline)) {
+      if constexpr (MX) {
+        const uint8_t* x = smem + XOFF + ((kt / XG) & 1) * XBUF + 4 * (kt % XG);
+#pragma unroll
+        for (int i = 0; i < TM; ++i) xraw[i] = *(const uint32_t*)(x + (wm * WM + i * 32 + rl) * XROW);
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          xraw[TM + j] = *(const uint32_t*)(x + (BM + wn * WN + j * 32 + rl) * XROW);
       }
     };
-    auto take_scales = [&](int st) __attribute__((always_inline)) {
-      if constexpr (KIND == kMX) {
-        static_assert(TM == 4 && TN == 4, "one 16-byte read of scale words per operand");
+    auto take_scales = [&]() __attribute__((always_inline)) {
+      if constexpr (MX) {
         const uint32_t sh = 8u * (uint32_t)hl;
 #pragma unroll
-        for (int i = 0; i < TM; ++i) xa[i] = xraw[st][0][i] >> sh;
+        for (int i = 0; i < TM; ++i) xa[i] = xraw[i] >> sh;
 #pragma unroll
-        for (int j = 0; j < TN; ++j) xb[j] = xraw[st][1][j] >> sh;
+        for (int j = 0; j < TN; ++j) xb[j] = xraw[TM + j] >> sh;
       }
     };
     auto load_step = [&](int st, int s, int buf) __attribute__((always_inline)) {
@@ -395,7 +422,7 @@ gemm_kernel(GemmArgs p) {
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
             __builtin_bit_cast(bf16x8_t, fb[buf][j][0]),
             __builtin_bit_cast(bf16x8_t, fa[buf][i][0]), acc[i][j], 0, 0, 0);
-      else if constexpr (KIND == kMX) {
+      else if constexpr (MX) {
         // step s = buf (two steps per slice) uses scale byte 2 s; the first
         // operand is B's fragment, so its scale is the instruction's first
         if (buf == 0)
@@ -419,7 +446,10 @@ gemm_kernel(GemmArgs p) {
     // The next slice's copies are spread between this slice's MFMAs (one
     // every R MFMAs, all before the barrier): a burst of copies would stall
     // the wave at issue while the matrix pipe idles.
-    constexpr int NLD = NL;  // copies per slice, MX scale words included
+    // MX scale copies ride along with the first data copies, so the data
+    // copies keep their slots and the last of them stays as far from the
+    // slice's closing wait as without scales
+    constexpr int NLD = NLA + NLB;  // data copies per slice
     constexpr int PRE = (NSTEP - 1) * TM * TN + (kSplitLast ? TM / 2 : TM) * TN;
     constexpr int R = PRE / NLD < 2 ? PRE / NLD : 2;
     static_assert(R >= 1, "every copy is issued before the slice barrier");
@@ -436,7 +466,7 @@ gemm_kernel(GemmArgs p) {
       const int ld_st = st == 0 ? S - 1 : st - 1;  // stage of slice kt+S-1
       const int nx_st = st == S - 1 ? 0 : st + 1;  // stage of slice kt+1
       const bool act = kt + S - 1 < nkt;
-      take_scales(st);
+      take_scales();
 #pragma unroll
       for (int s = 0; s < NSTEP; ++s) {
         const int buf = s & 1;
@@ -457,6 +487,7 @@ gemm_kernel(GemmArgs p) {
                 read_one(st, s + 1, buf ^ 1, k);
             }
             if (g % R == R - 1 && g / R < NLD) {
+              if (g / R < NLS) issue_one(kt + S - 1, ld_st, act, NLD + g / R);
               issue_one(kt + S - 1, ld_st, act, g / R);
               if (g / R == NLD - 1) issue_pf(kt + PD);  // after this slice's copies
             }
@@ -474,7 +505,7 @@ gemm_kernel(GemmArgs p) {
       }
       stage_barrier();
       __builtin_amdgcn_sched_barrier(0);
-      read_scales(nx_st);  // next slice's scale words; this slice's stay in xa / xb
+      read_scales(kt + 1);  // next slice's scale words; this slice's stay in xa / xb
       if constexpr (kSplitLast) {
         // next slice's first fragments, interleaved with the rest of this slice
         constexpr int NM = (TM - TM / 2) * TN;
@@ -592,7 +623,7 @@ hipError_t launch(const GemmArgs& a, hipStream_t s) {
   const int64_t tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
   // K tail: the last slice is partial and its lanes are range-checked one by
   // one (MX requires whole slices and has no such variant)
-  if constexpr (KIND != kMX) {
+  if constexpr (KIND != kMX && KIND != kMX4) {
     if ((a.K * (KIND == kBF16 ? 2 : 1)) % RB != 0) {
       hipLaunchKernelGGL((gemm_kernel<KIND, FA, FB, BROW, BM, BN, RB, S, G, PD, NW, true>),
                          dim3((unsigned)tiles), dim3(NW * 64), 0, s, a);
@@ -626,13 +657,23 @@ hipError_t launch_gemm_fp8(const GemmArgs& a, int fmt_a, int fmt_b, int block_sc
   return launch_fp8_fmt<1, 1>(a, block_scaled, s);
 }
 
-hipError_t launch_gemm_mxfp8(const GemmArgs& a, int fmt_a, int fmt_b, hipStream_t s) {
-#define DMU_MX(FA, FB) launch<kMX, FA, FB, false, 256, 256, 128, 2, 4, kPrefetch, kWavesFP8>(a, s)
+template <int KIND>
+static hipError_t launch_mx_kind(const GemmArgs& a, int fmt_a, int fmt_b, hipStream_t s) {
+#define DMU_MX(FA, FB) launch<KIND, FA, FB, false, 256, 256, 128, 2, 4, kPrefetch, kWavesFP8>(a, s)
   if (fmt_a == 0 && fmt_b == 0) return DMU_MX(0, 0);
   if (fmt_a == 0 && fmt_b == 1) return DMU_MX(0, 1);
   if (fmt_a == 1 && fmt_b == 0) return DMU_MX(1, 0);
   return DMU_MX(1, 1);
 #undef DMU_MX
+}
+
+hipError_t launch_gemm_mxfp8(const GemmArgs& a, int fmt_a, int fmt_b, hipStream_t s) {
+  // scale groups of 4 slices (16 bytes per row) when they are whole and
+  // 16-byte aligned, else one slice (4 bytes) at a time
+  const bool g4 = a.K % 512 == 0 && a.ldxa % 16 == 0 && a.ldxb % 16 == 0 &&
+                  (uintptr_t)a.xa % 16 == 0 && (uintptr_t)a.xb % 16 == 0;
+  if (g4) return launch_mx_kind<kMX4>(a, fmt_a, fmt_b, s);
+  return launch_mx_kind<kMX>(a, fmt_a, fmt_b, s);
 }
 
 }  // namespace dmu

@@ -171,9 +171,9 @@ __global__ void probe_lds_kernel(const uint8_t* src, uint8_t* dst, int mode, int
 // out[w * 64 + l], which keeps every instruction live.
 template <int KIND>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void probe_rate_kernel(
-    const uint8_t* src, int iters, float* out) {
+    const uint8_t* src, int iters, float* out, int scale_word) {
   const int l = threadIdx.x & 63;
-  constexpr int FB = KIND == 1 ? 16 : 32;
+  constexpr int FB = KIND == 1 ? 16 : 32;  // fragment bytes per lane
   i32x8_t a[4], b[4];
 #pragma unroll
   for (int f = 0; f < 4; ++f) {
@@ -202,6 +202,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
           const i32x4_t y = {b[j][0], b[j][1], b[j][2], b[j][3]};
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
               __builtin_bit_cast(bf16x8_t, y), __builtin_bit_cast(bf16x8_t, x), acc[i][j], 0, 0, 0);
+        } else if constexpr (KIND == 4) {  // scaled form, E8M0 codes in registers
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              b[j], a[i], acc[i][j], 0, 0, 0, scale_word, 0, scale_word);
         } else {
           acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b[j], a[i], acc[i][j], 0, 0,
                                                                       0, 0, 0, 0);
@@ -285,10 +288,13 @@ hipError_t launch_probe_rate(int kind, const void* src, int iters, int grid, flo
                              hipStream_t s) {
   if (kind == 1)
     hipLaunchKernelGGL(probe_rate_kernel<1>, dim3(grid), dim3(256), 0, s, (const uint8_t*)src,
-                       iters, out);
+                       iters, out, 0);
+  else if (kind == 4)
+    hipLaunchKernelGGL(probe_rate_kernel<4>, dim3(grid), dim3(256), 0, s, (const uint8_t*)src,
+                       iters, out, 0x7F7F7F7F);
   else
     hipLaunchKernelGGL(probe_rate_kernel<3>, dim3(grid), dim3(256), 0, s, (const uint8_t*)src,
-                       iters, out);
+                       iters, out, 0);
   return hipGetLastError();
 }
 

@@ -18,7 +18,8 @@
 //    per thread in registers between the amax and the encode (one HBM read).
 //  * MX (1 x 32 blocks, E8M0 scales; "How Blackwell's Tensor Memory Actually
 //    Works", section "Quantization became an allocation problem", with the
-//    Open Compute microscaling choice of scale): 8 lanes per block.  The
+//    Open Compute microscaling choice of scale): 8 lanes per block, rows
+//    walked by the grid's y dimension.  The
 //    scale is X = 2^(floor(log2 amax) - emax), emax = 8 (E4M3) or 15 (E5M2),
 //    the largest power of two that keeps amax / X below 2^(emax+1); its code
 //    is the biased exponent of amax minus emax, clamped at 0.  Elements are
@@ -258,44 +259,49 @@ __global__ __launch_bounds__(256) void quant_128x128(const float* X, int64_t nbc
 }
 
 // ---- MX: 1 x 32 blocks, E8M0 scale codes ---------------------------------
-// 8 lanes own one block (4 values each); a 256-thread workgroup covers 32
-// blocks per round and does kRounds rounds, loads of all rounds issued first.
+// Workgroup (x, y) walks rows y, y + gridDim.y, ...; in each it covers
+// kRounds chunks of 1024 columns starting at x * 1024 * kRounds, thread t
+// taking columns 4t .. 4t+3 of every chunk, so 8 consecutive lanes own one
+// block and no division is needed.  Loads of all rounds are issued first; X
+// is read once, with nontemporal loads.
 template <int FMT>
-__global__ __launch_bounds__(256) void quant_mx(const float* X, int64_t rows, int64_t nb,
+__global__ __launch_bounds__(256) void quant_mx(const float* X, int64_t rows, int64_t cols,
                                                 int64_t ldx, uint8_t* Q, int64_t ldq, uint8_t* S,
                                                 int64_t lds) {
   constexpr uint32_t kEmax = FMT == 0 ? 8u : 15u;
   const int sub = threadIdx.x & 7;
-  const int64_t nblk = rows * nb;
-  f32x4_t v[kRounds];
-  int64_t blk[kRounds], r[kRounds], cb[kRounds];
+  const int64_t c0 = (int64_t)blockIdx.x * (1024 * kRounds) + 4 * threadIdx.x;
+  for (int64_t r = blockIdx.y; r < rows; r += gridDim.y) {
+    const float* xr = X + r * ldx;
+    f32x4_t v[kRounds];
 #pragma unroll
-  for (int u = 0; u < kRounds; ++u) {
-    blk[u] = ((int64_t)blockIdx.x * kRounds + u) * 32 + (threadIdx.x >> 3);
-    v[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    r[u] = blk[u] / nb;
-    cb[u] = blk[u] - r[u] * nb;
-    if (blk[u] < nblk) v[u] = *(const f32x4_t*)(X + r[u] * ldx + cb[u] * 32 + 4 * sub);
-  }
+    for (int u = 0; u < kRounds; ++u) {
+      const int64_t c = c0 + u * 1024;
+      v[u] = c < cols ? __builtin_nontemporal_load((const f32x4_t*)(xr + c))
+                      : f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
 #pragma unroll
-  for (int u = 0; u < kRounds; ++u) {
-    uint32_t m = amax4(v[u]);
+    for (int u = 0; u < kRounds; ++u) {
+      const int64_t c = c0 + u * 1024;
+      uint32_t m = amax4(v[u]);
 #pragma unroll
-    for (int o = 4; o > 0; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o, 64));
-    if (blk[u] < nblk) {
-      uint32_t code, q;
-      if (m >= 0x7F800000u) {  // Inf or NaN in the block
-        code = 255u;
-        q = 0;
+      for (int o = 4; o > 0; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o, 64));
+      if (c < cols) {  // cols % 32 == 0: a block is entirely in or out
+        uint32_t code, q;
+        if (m >= 0x7F800000u) {  // Inf or NaN in the block
+          code = 255u;
+          q = 0;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) q |= ((__float_as_uint(v[u][e]) >> 24 & 0x80u) | 0x7Fu) << (8 * e);
-      } else {
-        const uint32_t eb = m >> 23;  // biased exponent of amax (0: zero or subnormal)
-        code = eb > kEmax ? eb - kEmax : 0u;
-        q = encode4<FMT>(v[u], __uint_as_float((254u - code) << 23));
+          for (int e = 0; e < 4; ++e)
+            q |= ((__float_as_uint(v[u][e]) >> 24 & 0x80u) | 0x7Fu) << (8 * e);
+        } else {
+          const uint32_t eb = m >> 23;  // biased exponent of amax (0: zero or subnormal)
+          code = eb > kEmax ? eb - kEmax : 0u;
+          q = encode4<FMT>(v[u], __uint_as_float((254u - code) << 23));
+        }
+        *(uint32_t*)(Q + r * ldq + c) = q;
+        if (sub == 0) S[r * lds + c / 32] = (uint8_t)code;
       }
-      *(uint32_t*)(Q + r[u] * ldq + cb[u] * 32 + 4 * sub) = q;
-      if (sub == 0) S[r[u] * lds + cb[u]] = (uint8_t)code;
     }
   }
 }
@@ -333,12 +339,12 @@ hipError_t launch_fmt(const float* X, int64_t rows, int64_t cols, int64_t ldx, i
 
 hipError_t launch_quantize_mxfp8(const float* X, int64_t rows, int64_t cols, int64_t ldx, int fmt,
                                  uint8_t* Q, int64_t ldq, uint8_t* S, int64_t lds, hipStream_t s) {
-  const int64_t nb = cols / 32, nblk = rows * nb;
-  const dim3 grid((unsigned)((nblk + 32 * kRounds - 1) / (32 * kRounds)));
+  const dim3 grid((unsigned)((cols + 1024 * kRounds - 1) / (1024 * kRounds)),
+                  (unsigned)(rows < 65535 ? rows : 65535));
   if (fmt == 0)
-    hipLaunchKernelGGL(quant_mx<0>, grid, dim3(256), 0, s, X, rows, nb, ldx, Q, ldq, S, lds);
+    hipLaunchKernelGGL(quant_mx<0>, grid, dim3(256), 0, s, X, rows, cols, ldx, Q, ldq, S, lds);
   else
-    hipLaunchKernelGGL(quant_mx<1>, grid, dim3(256), 0, s, X, rows, nb, ldx, Q, ldq, S, lds);
+    hipLaunchKernelGGL(quant_mx<1>, grid, dim3(256), 0, s, X, rows, cols, ldx, Q, ldq, S, lds);
   return hipGetLastError();
 }
 

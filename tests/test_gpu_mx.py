@@ -222,3 +222,40 @@ def test_gemm_mx_4096_sampled(fmt):
     B, SB = oracle.quantize_mx(wl.normal((4096, 4096), wl.SEED_B), fmt)
     check(A, B, fmt, fmt, SA, SB, torch.bfloat16, rows=sample_rows(4096),
           what="4096^3 MX fmt %d" % fmt)
+
+
+def run_mx_strided(A, B, fa, fb, SA, SB, ld_extra, offset):
+    """gemm_mxfp8 with scale rows of K/32 + ld_extra bytes, the arrays starting
+    `offset` bytes into their allocation (BF16 out)."""
+    M, N = A.shape[0], B.shape[0]
+    nkb = SA.shape[1]
+
+    def place(S):
+        ld = nkb + ld_extra
+        buf = torch.zeros(S.shape[0] * ld + offset, dtype=torch.uint8, device="cuda")
+        v = buf[offset:].view(S.shape[0], ld)[:, :nkb]
+        v.copy_(torch.from_numpy(np.ascontiguousarray(S)))
+        return v
+    out = empty_padded(M, N, torch.bfloat16)
+    dmu.gemm_mxfp8(padded(A, 16), padded(B, 16), place(SA), place(SB), out, fa, fb)
+    torch.cuda.synchronize()
+    return out_to_f64(out)
+
+
+@pytest.mark.parametrize("K", [512, 1536, 2560])
+@pytest.mark.parametrize("ld_extra,offset", [(0, 0), (4, 0), (16, 4)])
+def test_gemm_mx_scale_fetch_paths(K, ld_extra, offset):
+    # K % 512 == 0 with 16-byte scale rows fetches scale codes 4 slices at a
+    # time (1, 3, 5 groups: both ring buffers, odd and even group counts);
+    # a 4-byte row stride or start falls back to one slice at a time
+    M, N = 384, 272
+    rng = np.random.default_rng(K + ld_extra)
+    A = oracle.encode_fp8(wl.normal((M, K), 1), 0)
+    B = oracle.encode_fp8(wl.normal((N, K), 2), 1)
+    SA = rng.integers(116, 139, size=(M, K // 32)).astype(np.uint8)
+    SB = rng.integers(116, 139, size=(N, K // 32)).astype(np.uint8)
+    D = run_mx_strided(A, B, 0, 1, SA, SB, ld_extra, offset)
+    Dref, S = oracle.gemm_mx(A, B, 0, 1, SA, SB)
+    tol = 1e-5 * S + 2.0 ** -12 * run_max_term(A, B, 0, 1, SA, SB) + 2.0 ** -8 * np.abs(Dref)
+    bad = ~(np.abs(D - Dref) <= tol)
+    assert not bad.any(), "%d outside the bound, first at %s" % (bad.sum(), np.argwhere(bad)[0])

@@ -142,7 +142,8 @@ def test_direct_to_lds_copy(mode, size, oob_from):
 
 
 @pytest.mark.parametrize("kind,k,one", [(dmu.PROBE_BF16_32X32X16, 16, 0x3F80),
-                                        (dmu.PROBE_FP8_32X32X64, 64, 0x38)])
+                                        (dmu.PROBE_FP8_32X32X64, 64, 0x38),
+                                        (dmu.PROBE_MXFP8_32X32X64, 64, 0x38)])
 def test_mfma_rate_probe_counts_every_instruction(kind, k, one):
     # All-ones fragments: every accumulator element gains k per round, so lane
     # sums are 256 * k * iters exactly (well inside FP32's exact integers).
