@@ -28,6 +28,7 @@ _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 
 E4M3 = 0
 E5M2 = 1
+E2M1 = 4  # FP4 element format of MXFP4; codes packed two per byte in MX arrays
 B_ROW_MAJOR = 0
 B_COL_MAJOR = 1
 SCALE_TENSOR = 0
@@ -75,6 +76,8 @@ def lib():
         L.orc_gemm_fp8.argtypes = [p, i64, i32, p, i64, i32, p, p, i32, p, i64, i64, i64,
                                    i64, p, i64, p, p]
         L.orc_gemm_fp8.restype = i32
+        L.orc_encode_fp4_array.argtypes = [p, i64, p]
+        L.orc_decode_fp4_array.argtypes = [p, i64, p]
         L.orc_decode_e8m0.argtypes = [ctypes.c_uint8]
         L.orc_decode_e8m0.restype = ctypes.c_double
         L.orc_quantize_mx.argtypes = [p, i64, i64, i64, i32, p, i64, p, i64]
@@ -120,6 +123,45 @@ def encode_fp8(x, fmt: int) -> np.ndarray:
     out = np.empty(x.shape, dtype=np.uint8)
     lib().orc_encode_fp8_array(_ptr(x), x.size, fmt, _ptr(out))
     return out
+
+
+def decode_fp4(v) -> np.ndarray:
+    """E2M1 codes (one per array element, low 4 bits) -> exact values."""
+    v = np.ascontiguousarray(v, dtype=np.uint8)
+    out = np.empty(v.shape, dtype=np.float64)
+    lib().orc_decode_fp4_array(_ptr(v), v.size, _ptr(out))
+    return out
+
+
+def encode_fp4(x) -> np.ndarray:
+    """FP32 -> E2M1 codes, one per array element (not packed)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(x.shape, dtype=np.uint8)
+    lib().orc_encode_fp4_array(_ptr(x), x.size, _ptr(out))
+    return out
+
+
+def pack_fp4(codes) -> np.ndarray:
+    """[rows][cols] E2M1 codes -> [rows][cols/2] bytes, element 2i in the low
+    nibble of byte i and element 2i+1 in the high nibble."""
+    c = np.ascontiguousarray(codes, dtype=np.uint8) & 15
+    return (c[..., 0::2] | (c[..., 1::2] << 4)).astype(np.uint8)
+
+
+def unpack_fp4(packed) -> np.ndarray:
+    """Inverse of pack_fp4."""
+    p = np.ascontiguousarray(packed, dtype=np.uint8)
+    out = np.empty(p.shape[:-1] + (2 * p.shape[-1],), dtype=np.uint8)
+    out[..., 0::2] = p & 15
+    out[..., 1::2] = p >> 4
+    return out
+
+
+def decode_elems(A, fmt: int) -> np.ndarray:
+    """Exact values of an MX element array: FP8 codes, or packed E2M1."""
+    if fmt == E2M1:
+        return decode_fp4(unpack_fp4(A))
+    return decode_fp8(A, fmt)
 
 
 def quantize_fp8(X, fmt: int, block_rows: int | None = None, block_cols: int | None = None):
@@ -199,13 +241,15 @@ def decode_e8m0(codes) -> np.ndarray:
 
 
 def quantize_mx(X, fmt: int):
-    """MX quantisation with 1 x 32 blocks along each row: returns (Q uint8
-    like X, S uint8 E8M0 codes [rows][cols/32])."""
+    """MX quantisation with 1 x 32 blocks along each row: returns (Q, S uint8
+    E8M0 codes [rows][cols/32]).  Q is uint8 like X for FP8, or [rows][cols/2]
+    packed E2M1 for fmt E2M1."""
     X = np.ascontiguousarray(X, dtype=np.float32)
     rows, cols = X.shape
-    Q = np.empty((rows, cols), dtype=np.uint8)
+    qc = cols // 2 if fmt == E2M1 else cols
+    Q = np.empty((rows, qc), dtype=np.uint8)
     S = np.empty((rows, cols // MX_BLOCK), dtype=np.uint8)
-    rc = lib().orc_quantize_mx(_ptr(X), rows, cols, cols, fmt, _ptr(Q), cols, _ptr(S),
+    rc = lib().orc_quantize_mx(_ptr(X), rows, cols, cols, fmt, _ptr(Q), qc, _ptr(S),
                                cols // MX_BLOCK)
     if rc != 0:
         raise ValueError("orc_quantize_mx: bad arguments")
@@ -214,12 +258,14 @@ def quantize_mx(X, fmt: int):
 
 def gemm_mx(A, B, fmt_a: int, fmt_b: int, SA, SB, C=None, rows=None):
     """FP64 MX product (selected rows) and S = sum of |scaled a * scaled b|.
-    A: [M][K] uint8, B: [N][K] uint8, SA: [M][K/32], SB: [N][K/32] uint8."""
+    A: [M][K] and B: [N][K] uint8 FP8 codes, or [M][K/2] / [N][K/2] packed
+    E2M1 for that operand's format; SA: [M][K/32], SB: [N][K/32] uint8."""
     A = np.ascontiguousarray(A, dtype=np.uint8)
     B = np.ascontiguousarray(B, dtype=np.uint8)
-    M, K = A.shape
+    M = A.shape[0]
+    K = A.shape[1] * (2 if fmt_a == E2M1 else 1)
     N = B.shape[0]
-    assert B.shape[1] == K and K % MX_BLOCK == 0
+    assert B.shape[1] * (2 if fmt_b == E2M1 else 1) == K and K % MX_BLOCK == 0
     SA = np.ascontiguousarray(SA, dtype=np.uint8)
     SB = np.ascontiguousarray(SB, dtype=np.uint8)
     assert SA.shape == (M, K // MX_BLOCK) and SB.shape == (N, K // MX_BLOCK)
@@ -229,7 +275,8 @@ def gemm_mx(A, B, fmt_a: int, fmt_b: int, SA, SB, C=None, rows=None):
     r, nr = _rows_arg(rows, M)
     D = np.empty((nr, N), dtype=np.float64)
     S = np.empty((nr, N), dtype=np.float64)
-    rc = lib().orc_gemm_mx(_ptr(A), K, fmt_a, _ptr(B), K, fmt_b, _ptr(SA), K // MX_BLOCK,
+    rc = lib().orc_gemm_mx(_ptr(A), A.shape[1], fmt_a, _ptr(B), B.shape[1], fmt_b, _ptr(SA),
+                           K // MX_BLOCK,
                            _ptr(SB), K // MX_BLOCK, _ptr(C), N, M, N, K, _ptr(r), nr, _ptr(D),
                            _ptr(S))
     if rc != 0:

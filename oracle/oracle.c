@@ -40,6 +40,7 @@
 
 #define ORC_FMT_E4M3 0
 #define ORC_FMT_E5M2 1
+#define ORC_FMT_E2M1 4 /* FP4 element format of MXFP4, two per byte */
 #define ORC_B_ROW_MAJOR 0 /* B(k,j) at B[k*ldb + j] */
 #define ORC_B_COL_MAJOR 1 /* B(k,j) at B[j*ldb + k], i.e. B stored N x K */
 #define ORC_SCALE_TENSOR 0
@@ -84,6 +85,17 @@ void orc_decode_bf16_array(const uint16_t* h, int64_t n, double* out) {
 
 void orc_decode_fp8_array(const uint8_t* v, int64_t n, int fmt, double* out) {
   for (int64_t i = 0; i < n; i++) out[i] = orc_decode_fp8(v[i], fmt);
+}
+
+/* E2M1 (FP4 of the microscaling formats): sign, 2 exponent bits with bias 1,
+ * 1 mantissa bit, no Inf or NaN.  Exponent field 0 is subnormal (m * 2^-1),
+ * so the magnitudes are 0, 0.5, 1, 1.5, 2, 3, 4, 6.  The low 4 bits of `v`
+ * are the code. */
+double orc_decode_fp4(uint8_t v) {
+  double sign = (v & 8) ? -1.0 : 1.0;
+  int e = (v >> 1) & 3, m = v & 1;
+  if (e == 0) return sign * 0.5 * m;
+  return sign * ldexp(2.0 + m, e - 2); /* (1 + m/2) * 2^(e-1) */
 }
 
 /* ---------------------------------------------------------------- encoders */
@@ -152,6 +164,27 @@ static uint8_t encode_fp8_d(double x, int fmt) {
   return (uint8_t)(sign | (efield << mbits) | mfield);
 }
 
+/* A finite or infinite double -> E2M1 with round to nearest even and
+ * saturation at +-6 (the format has no Inf); -0 keeps its sign.  NaN input
+ * has no code: it gives the signed zero, and the MX quantizer marks its block
+ * with the NaN scale instead. */
+static uint8_t encode_fp4_d(double x) {
+  uint8_t sign = signbit(x) ? 0x8 : 0x0;
+  if (isnan(x)) return sign;
+  double a = fabs(x);
+  if (a >= 6.0) return (uint8_t)(sign | 0x7);
+  double v = round_to_grid(a, 1, 0);
+  if (v == 0.0) return sign;
+  if (v < 1.0) return (uint8_t)(sign | 0x1); /* the subnormal 0.5 */
+  int e2;
+  frexp(v, &e2);
+  int E = e2 - 1; /* v in [2^E, 2^(E+1)), E in 0..2 */
+  int mfield = (int)(v / ldexp(1.0, E - 1)) - 2;
+  return (uint8_t)(sign | ((E + 1) << 1) | mfield);
+}
+
+uint8_t orc_encode_fp4(float x) { return encode_fp4_d((double)x); }
+
 /* FP32 -> FP8 with round to nearest even and saturation (see encode_fp8_d;
  * the FP32 value widens exactly). */
 uint8_t orc_encode_fp8(float x, int fmt) { return encode_fp8_d((double)x, fmt); }
@@ -164,6 +197,15 @@ void orc_encode_bf16_array(const float* x, int64_t n, uint16_t* out) {
 void orc_encode_fp8_array(const float* x, int64_t n, int fmt, uint8_t* out) {
 #pragma omp parallel for schedule(static)
   for (int64_t i = 0; i < n; i++) out[i] = orc_encode_fp8(x[i], fmt);
+}
+
+/* One E2M1 code per output byte (unpacked), for tests. */
+void orc_encode_fp4_array(const float* x, int64_t n, uint8_t* out) {
+  for (int64_t i = 0; i < n; i++) out[i] = orc_encode_fp4(x[i]);
+}
+
+void orc_decode_fp4_array(const uint8_t* v, int64_t n, double* out) {
+  for (int64_t i = 0; i < n; i++) out[i] = orc_decode_fp4(v[i]);
 }
 
 /* ---------------------------------------------------------------- quantize */
@@ -343,27 +385,32 @@ int orc_gemm_fp8(const uint8_t* A, int64_t lda, int fmt_a, const uint8_t* B, int
 
 double orc_decode_e8m0(uint8_t c) { return c == 255 ? NAN : ldexp(1.0, (int)c - 127); }
 
-/* Quantise rows x cols FP32 (row-major, cols % 32 == 0) to FP8 with one E8M0
- * scale per 1 x 32 block.  Scale choice, read from the microscaling
- * specification: X = 2^(floor(log2 amax) - emax), emax the largest exponent of
- * the element format (8 for E4M3, 15 for E5M2), the exponent clamped to the
- * E8M0 range [-127, 127]; elements q = saturating RNE of x / X (exact: X is a
- * power of two).  Readings where the pages say nothing: an all-zero block
- * takes the smallest scale 2^-127; a block holding a NaN or an infinity gets
- * the NaN scale 255 and NaN element codes.  S is row-major [rows][lds],
- * lds >= cols/32. */
+/* Quantise rows x cols FP32 (row-major, cols % 32 == 0) to FP8 or FP4 (E2M1)
+ * with one E8M0 scale per 1 x 32 block.  Scale choice, read from the
+ * microscaling specification: X = 2^(floor(log2 amax) - emax), emax the
+ * largest exponent of the element format (8 for E4M3, 15 for E5M2, 2 for
+ * E2M1), the exponent clamped to the E8M0 range [-127, 127]; elements q =
+ * saturating RNE of x / X (exact: X is a power of two).  Readings where the
+ * pages say nothing: an all-zero block takes the smallest scale 2^-127; a
+ * block holding a NaN or an infinity gets the NaN scale 255 and NaN element
+ * codes (FP8) or signed zeros (FP4, which has no NaN).  Q has ldq bytes per
+ * row: one code per byte (FP8), or two (FP4: element k in the low nibble of
+ * byte k/2 when k is even, the high nibble when odd).  S is row-major
+ * [rows][lds], lds >= cols/32. */
 int orc_quantize_mx(const float* X, int64_t rows, int64_t cols, int64_t ldx, int fmt, uint8_t* Q,
                     int64_t ldq, uint8_t* S, int64_t lds) {
-  if (rows <= 0 || cols <= 0 || cols % ORC_MX_BLOCK || ldx < cols || ldq < cols) return -1;
-  if (lds < cols / ORC_MX_BLOCK) return -1;
-  if (fmt != ORC_FMT_E4M3 && fmt != ORC_FMT_E5M2) return -1;
-  const int emax = fmt == ORC_FMT_E4M3 ? 8 : 15;
+  const int fp4 = fmt == ORC_FMT_E2M1;
+  if (rows <= 0 || cols <= 0 || cols % ORC_MX_BLOCK || ldx < cols) return -1;
+  if (ldq < (fp4 ? cols / 2 : cols) || lds < cols / ORC_MX_BLOCK) return -1;
+  if (fmt != ORC_FMT_E4M3 && fmt != ORC_FMT_E5M2 && !fp4) return -1;
+  const int emax = fmt == ORC_FMT_E4M3 ? 8 : fmt == ORC_FMT_E5M2 ? 15 : 2;
   const int64_t nb = cols / ORC_MX_BLOCK;
 #pragma omp parallel for collapse(2) schedule(static)
   for (int64_t r = 0; r < rows; r++) {
     for (int64_t b = 0; b < nb; b++) {
       const float* x = X + r * ldx + b * ORC_MX_BLOCK;
-      uint8_t* q = Q + r * ldq + b * ORC_MX_BLOCK;
+      uint8_t* q = Q + r * ldq + b * (fp4 ? ORC_MX_BLOCK / 2 : ORC_MX_BLOCK);
+      uint8_t c[ORC_MX_BLOCK];
       double amax = 0.0;
       int nonfinite = 0;
       for (int k = 0; k < ORC_MX_BLOCK; k++) {
@@ -372,9 +419,10 @@ int orc_quantize_mx(const float* X, int64_t rows, int64_t cols, int64_t ldx, int
       }
       if (nonfinite) {
         S[r * lds + b] = 255;
-        for (int k = 0; k < ORC_MX_BLOCK; k++) q[k] = (uint8_t)(signbit(x[k]) ? 0xFF : 0x7F);
-        continue;
-      }
+        for (int k = 0; k < ORC_MX_BLOCK; k++)
+          c[k] = fp4 ? (uint8_t)(signbit(x[k]) ? 0x8 : 0x0)
+                     : (uint8_t)(signbit(x[k]) ? 0xFF : 0x7F);
+      } else {
       int e;
       if (amax == 0.0) {
         e = -127;
@@ -386,15 +434,30 @@ int orc_quantize_mx(const float* X, int64_t rows, int64_t cols, int64_t ldx, int
         if (e > 127) e = 127;
       }
       S[r * lds + b] = (uint8_t)(e + 127);
-      for (int k = 0; k < ORC_MX_BLOCK; k++) q[k] = encode_fp8_d(ldexp((double)x[k], -e), fmt);
+      for (int k = 0; k < ORC_MX_BLOCK; k++) {
+        const double y = ldexp((double)x[k], -e);
+        c[k] = fp4 ? encode_fp4_d(y) : encode_fp8_d(y, fmt);
+      }
+      }
+      if (fp4)
+        for (int k = 0; k < ORC_MX_BLOCK; k += 2) q[k / 2] = (uint8_t)(c[k] | (c[k + 1] << 4));
+      else
+        for (int k = 0; k < ORC_MX_BLOCK; k++) q[k] = c[k];
     }
   }
   return 0;
 }
 
-/* Selected rows of the MX product: A is M x K row-major, B stored N x K, both
- * FP8 codes (fmt_a, fmt_b); SA [M][ldsa] and SB [N][ldsb] hold one E8M0 code
- * per 32-element group along K.  D = C + sum_k (a_ik * sa_i,k/32) * (b_jk *
+/* Element k of a row of codes: a byte (FP8) or a nibble (FP4, packed as in
+ * orc_quantize_mx). */
+static int code_at(const uint8_t* row, int64_t k, int fmt) {
+  if (fmt == ORC_FMT_E2M1) return (row[k >> 1] >> ((k & 1) * 4)) & 15;
+  return row[k];
+}
+
+/* Selected rows of the MX product: A is M x K row-major, B stored N x K, FP8
+ * or FP4 codes (fmt_a, fmt_b; lda, ldb in bytes); SA [M][ldsa] and SB [N][ldsb]
+ * hold one E8M0 code per 32-element group along K.  D = C + sum_k (a_ik * sa_i,k/32) * (b_jk *
  * sb_j,k/32) in FP64, k ascending; S = sum_k of the magnitudes. */
 int orc_gemm_mx(const uint8_t* A, int64_t lda, int fmt_a, const uint8_t* B, int64_t ldb, int fmt_b,
                 const uint8_t* SA, int64_t ldsa, const uint8_t* SB, int64_t ldsb, const float* C,
@@ -402,10 +465,13 @@ int orc_gemm_mx(const uint8_t* A, int64_t lda, int fmt_a, const uint8_t* B, int6
                 double* D, double* S) {
   if (M <= 0 || N <= 0 || K <= 0 || K % ORC_MX_BLOCK) return -1;
   if (!rows) nrows = M;
+  const int ok = (fmt_a == ORC_FMT_E4M3 || fmt_a == ORC_FMT_E5M2 || fmt_a == ORC_FMT_E2M1) &&
+                 (fmt_b == ORC_FMT_E4M3 || fmt_b == ORC_FMT_E5M2 || fmt_b == ORC_FMT_E2M1);
+  if (!ok) return -1;
   double ta[256], tb[256];
   for (int v = 0; v < 256; v++) {
-    ta[v] = orc_decode_fp8((uint8_t)v, fmt_a);
-    tb[v] = orc_decode_fp8((uint8_t)v, fmt_b);
+    ta[v] = fmt_a == ORC_FMT_E2M1 ? orc_decode_fp4((uint8_t)v) : orc_decode_fp8((uint8_t)v, fmt_a);
+    tb[v] = fmt_b == ORC_FMT_E2M1 ? orc_decode_fp4((uint8_t)v) : orc_decode_fp8((uint8_t)v, fmt_b);
   }
   int bad = 0;
 #pragma omp parallel for schedule(dynamic)
@@ -416,8 +482,8 @@ int orc_gemm_mx(const uint8_t* A, int64_t lda, int fmt_a, const uint8_t* B, int6
       double acc = 0.0, sacc = 0.0;
       for (int64_t k = 0; k < K; k++) {
         const int64_t g = k / ORC_MX_BLOCK;
-        double p = (ta[A[i * lda + k]] * orc_decode_e8m0(SA[i * ldsa + g])) *
-                   (tb[B[j * ldb + k]] * orc_decode_e8m0(SB[j * ldsb + g]));
+        double p = (ta[code_at(A + i * lda, k, fmt_a)] * orc_decode_e8m0(SA[i * ldsa + g])) *
+                   (tb[code_at(B + j * ldb, k, fmt_b)] * orc_decode_e8m0(SB[j * ldsb + g]));
         acc += p;
         sacc += fabs(p);
       }

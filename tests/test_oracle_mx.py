@@ -149,3 +149,133 @@ def test_gemm_mx_scale_code_step_doubles_one_block():
     block = a[2, 32:64] @ b[:, 32:64].T
     assert np.allclose(D1[2] - D0[2], block, rtol=0, atol=1e-12 * np.abs(block).max())
     assert np.array_equal(np.delete(D1, 2, axis=0), np.delete(D0, 2, axis=0))
+
+
+# ---------------------------------------------------------------- MXFP4 (E2M1)
+
+import json
+import os
+
+GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "fp4_e2m1.json")))
+MAGS = np.array(GOLD["magnitudes"])
+
+
+def test_fp4_decode_matches_the_format_table():
+    v = oracle.decode_fp4(np.arange(16))
+    assert np.array_equal(v[:8], MAGS)
+    assert np.array_equal(v[8:], -MAGS)
+    assert np.signbit(v[8])  # code 8 is -0
+    # the table itself follows from the field split: subnormal m/2, normal (1 + m/2) 2^(e - 1)
+    for c in range(8):
+        e, m = c >> 1, c & 1
+        want = Fraction(m, 2) if e == 0 else (1 + Fraction(m, 2)) * Fraction(2) ** (e - GOLD["bias"])
+        assert Fraction(MAGS[c]) == want
+
+
+def brute_fp4(x):
+    """nearest E2M1 value, ties to the even code, saturating at +-6, -0 kept"""
+    out = np.empty(np.shape(x), np.uint8)
+    for idx, xv in np.ndenumerate(np.asarray(x, np.float64)):
+        s = 8 if np.signbit(xv) else 0
+        a = min(abs(xv), MAGS[-1])
+        d = np.abs(MAGS - a)
+        cands = np.flatnonzero(d == d.min())
+        c = cands[0] if len(cands) == 1 else [k for k in cands if k % 2 == 0][0]
+        out[idx] = s | c
+    return out
+
+
+def test_fp4_encode_is_the_nearest_code():
+    rng = np.random.default_rng(3)
+    x = np.concatenate([rng.uniform(-8, 8, 4000), MAGS, -MAGS, (MAGS[1:] + MAGS[:-1]) / 2,
+                        [0.25, -0.25, 7.0, 1e9, -1e9, np.inf, -np.inf, -0.0, 1e-30]]).astype(np.float32)
+    assert np.array_equal(oracle.encode_fp4(x), brute_fp4(x))
+    # decode o encode is the identity on every code
+    codes = np.arange(16, dtype=np.uint8)
+    assert np.array_equal(oracle.encode_fp4(oracle.decode_fp4(codes).astype(np.float32)), codes)
+
+
+def test_fp4_packing_order():
+    codes = np.array([[1, 2, 3, 4, 15, 8]], np.uint8)
+    p = oracle.pack_fp4(codes)
+    assert p.tolist() == [[0x21, 0x43, 0x8F]]
+    assert np.array_equal(oracle.unpack_fp4(p), codes)
+
+
+def test_quantize_mx_fp4_scale_property_and_nearest_codes():
+    X, _ = wl.normal_with_outlier_rows((48, 256), 17, frac=0.05)
+    X[3, :32] *= np.float32(1e-30)
+    X[6, 64:96] *= np.float32(1e25)
+    Q, S = oracle.quantize_mx(X, oracle.E2M1)
+    assert Q.shape == (48, 128)
+    scale = oracle.decode_e8m0(S)
+    amax = np.abs(mx_blocks(X.astype(np.float64))).max(axis=2)
+    ratio = amax / scale
+    clamped = (S == 0) | (S == 254)
+    assert np.all((ratio[~clamped] >= 4.0) & (ratio[~clamped] < 8.0))
+    y = mx_blocks(X.astype(np.float64)) / scale[:, :, None]
+    assert np.array_equal(oracle.unpack_fp4(Q), brute_fp4(y.ravel()).reshape(X.shape))
+
+
+def test_quantize_mx_fp4_worked_values_and_special_blocks():
+    X = np.zeros((3, 96), np.float32)
+    X[0, :32] = 6.0              # amax 6: X = 1, every element code 7
+    X[0, 32:64] = 1.0            # amax 1: X = 2^-2, elements 4 -> code 6
+    X[0, 64] = -5.0              # amax 5: X = 1, -5 ties between 4 and 6 -> even code: -4
+    X[1, 3] = np.nan             # NaN block: code 255, signed zeros
+    X[1, 4] = -1.0
+    X[2, 40] = np.inf
+    Q, S = oracle.quantize_mx(X, oracle.E2M1)
+    q = oracle.unpack_fp4(Q)
+    assert S[0].tolist() == [127, 125, 127]
+    assert np.all(q[0, :32] == 7) and np.all(q[0, 32:64] == 6) and q[0, 64] == 8 | 6
+    assert S[1, 0] == 255 and np.all(q[1, :32] == np.where(np.signbit(X[1, :32]), 8, 0))
+    assert S[2, 1] == 255 and S[2, 0] == 0 and S[2, 2] == 0
+
+
+def test_quantize_mx_fp4_power_of_two_equivariance():
+    X = wl.normal((8, 128), 23)
+    Q0, S0 = oracle.quantize_mx(X, oracle.E2M1)
+    for t in (-5, 3, 40):
+        Q1, S1 = oracle.quantize_mx((X * np.float32(2.0 ** t)).astype(np.float32), oracle.E2M1)
+        assert np.array_equal(Q1, Q0)
+        assert np.array_equal(S1.astype(int), S0.astype(int) + t)
+
+
+@pytest.mark.parametrize("fa,fb", [(4, 4), (4, 0), (1, 4)])
+def test_gemm_mx_fp4_matches_numpy(fa, fb):
+    rng = np.random.default_rng(31)
+    M, N, K = 24, 40, 192
+
+    def make(rows, seed, fmt):
+        X = wl.normal((rows, K), seed)
+        return oracle.pack_fp4(oracle.encode_fp4(X)) if fmt == oracle.E2M1 else oracle.encode_fp8(X, fmt)
+    A, B = make(M, 1, fa), make(N, 2, fb)
+    SA = rng.integers(112, 142, size=(M, K // 32)).astype(np.uint8)
+    SB = rng.integers(112, 142, size=(N, K // 32)).astype(np.uint8)
+    C = wl.normal((M, N), 3)
+    D, S = oracle.gemm_mx(A, B, fa, fb, SA, SB, C=C)
+    a = oracle.decode_elems(A, fa) * expand(SA)
+    b = oracle.decode_elems(B, fb) * expand(SB)
+    ref = a @ b.T + C.astype(np.float64)
+    assert np.all(np.abs(D - ref) <= 1e-12 * (S + np.abs(C)))
+
+
+def test_gemm_mx_fp4_brute_force_rational():
+    rng = np.random.default_rng(37)
+    M, N, K = 8, 8, 64
+    qa = rng.integers(0, 16, size=(M, K)).astype(np.uint8)
+    qb = rng.integers(0, 16, size=(N, K)).astype(np.uint8)
+    SA = rng.integers(120, 135, size=(M, 2)).astype(np.uint8)
+    SB = rng.integers(120, 135, size=(N, 2)).astype(np.uint8)
+    D, _ = oracle.gemm_mx(oracle.pack_fp4(qa), oracle.pack_fp4(qb), 4, 4, SA, SB)
+    sgn = lambda c: -1 if c & 8 else 1
+    for i in range(M):
+        for j in range(N):
+            acc = Fraction(0)
+            for k in range(K):
+                va = sgn(qa[i, k]) * Fraction(MAGS[qa[i, k] & 7])
+                vb = sgn(qb[j, k]) * Fraction(MAGS[qb[j, k] & 7])
+                acc += (va * Fraction(2) ** (int(SA[i, k // 32]) - 127) *
+                        vb * Fraction(2) ** (int(SB[j, k // 32]) - 127))
+            assert D[i, j] == float(acc)
