@@ -36,6 +36,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6  # 256 CU x 4096 FLOP/clk x 2.4 GHz (published 2.5 PFLOP/s dense)
 PEAK_FP8_TFLOPS = 5033.2   # 256 CU x 8192 FLOP/clk x 2.4 GHz (published 5.0 PFLOP/s dense)
+PEAK_FP4_TFLOPS = 10066.3  # 256 CU x 16384 FLOP/clk x 2.4 GHz (published 10.1 PFLOP/s dense)
 PEAK_HBM_GBS = 8000.0
 METRIC = "GEMM TFLOP/s and % of MFMA peak, 4096³ BF16 and FP8 E4M3, 1×MI355X"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
@@ -189,17 +190,44 @@ class Bench:
         bytes_ = (1.0 + 1.0 / 32) * (M * K + N * K) + 2.0 * M * N
         return self.report(t, flop, bytes_, PEAK_FP8_TFLOPS, copies)
 
+    def gemm_mxfp4_leg(self, M, N, K, steps, warmup, copies=1):
+        """Microscaled FP4: operands quantized by quantize_mxfp4, product by
+        gemm_mxfp4."""
+        torch, dmu = self.torch, self.dmu
+        Qa = torch.empty((M, K // 2), dtype=torch.uint8, device=self.dev)
+        Qb = torch.empty((N, K // 2), dtype=torch.uint8, device=self.dev)
+        Sa = torch.empty((M, K // 32), dtype=torch.uint8, device=self.dev)
+        Sb = torch.empty((N, K // 32), dtype=torch.uint8, device=self.dev)
+        dmu.quantize_mxfp4(self.normal_f32((M, K), 1), Qa, Sa)
+        dmu.quantize_mxfp4(self.normal_f32((N, K), 2), Qb, Sb)
+        Qas, Qbs = self.copies(Qa, copies), self.copies(Qb, copies)
+        Sas, Sbs = self.copies(Sa, copies), self.copies(Sb, copies)
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=self.dev)
+
+        def launch(i):
+            j = i % copies
+            dmu.gemm_mxfp4(Qas[j], Qbs[j], Sas[j], Sbs[j], out)
+
+        t = time_launches(torch, launch, steps, warmup)
+        flop = 2.0 * M * N * K
+        bytes_ = (0.5 + 1.0 / 32) * (M * K + N * K) + 2.0 * M * N
+        return self.report(t, flop, bytes_, PEAK_FP4_TFLOPS, copies)
+
     def quantize_mx_leg(self, rows, cols, fmt, steps, warmup):
         torch, dmu = self.torch, self.dmu
         X = self.normal_f32((rows, cols), 1)
-        Q = torch.empty((rows, cols), dtype=torch.uint8, device=self.dev)
+        fp4 = fmt == dmu.E2M1
+        Q = torch.empty((rows, cols // 2 if fp4 else cols), dtype=torch.uint8, device=self.dev)
         S = torch.empty((rows, cols // 32), dtype=torch.uint8, device=self.dev)
 
         def launch(i):
-            dmu.quantize_mxfp8(X, Q, S, fmt)
+            if fp4:
+                dmu.quantize_mxfp4(X, Q, S)
+            else:
+                dmu.quantize_mxfp8(X, Q, S, fmt)
 
         t = time_launches(torch, launch, steps, warmup)
-        bytes_ = (5.0 + 1.0 / 32) * rows * cols
+        bytes_ = ((4.5 if fp4 else 5.0) + 1.0 / 32) * rows * cols
         ms = t["event_mean_ms"]
         return {"ms": round(ms, 5), "GB_per_s": round(bytes_ / ms / 1e6, 1),
                 "pct_hbm_peak": round(100 * bytes_ / ms / 1e6 / PEAK_HBM_GBS, 1),
@@ -237,7 +265,9 @@ class Bench:
                                         ("fp8_e4m3", dmu.PROBE_FP8_32X32X64, 1024,
                                          PEAK_FP8_TFLOPS),
                                         ("mxfp8_e4m3", dmu.PROBE_MXFP8_32X32X64, 1024,
-                                         PEAK_FP8_TFLOPS)):
+                                         PEAK_FP8_TFLOPS),
+                                        ("mxfp4_e2m1", dmu.PROBE_MXFP4_32X32X64, 2048,
+                                         PEAK_FP4_TFLOPS)):
             fb = 16 if name == "bf16" else 32
             n = 8 * 64 * fb
             if name == "bf16":
@@ -248,7 +278,8 @@ class Bench:
                 q = torch.empty((n,), dtype=torch.uint8, device=self.dev)
                 sc = torch.empty(1, dtype=torch.float32, device=self.dev)
                 dmu.quantize_fp8(self.normal_f32((1, n), 1), q.view(1, n), sc, dmu.E4M3)
-                rnd, ones = q, torch.full((n,), 0x38, dtype=torch.uint8, device=self.dev)
+                one = 0x22 if name == "mxfp4_e2m1" else 0x38  # E2M1 1.0 twice / E4M3 1.0
+                rnd, ones = q, torch.full((n,), one, dtype=torch.uint8, device=self.dev)
             out = torch.empty(grid * 256, dtype=torch.float32, device=self.dev)
             flop = 2.0 * grid * 4 * 16 * iters * (32 * 32 * (16 if name == "bf16" else 64))
             for dist, src in (("normal", rnd), ("ones", ones)):
@@ -376,6 +407,12 @@ def main():
     if want("mxfp8_e4m3_4096"):
         legs["mxfp8_e4m3_4096"] = b.gemm_mx_leg(4096, 4096, 4096, dmu.E4M3, S, W, copies=10)
         log("mxfp8 e4m3 4096: %s" % legs["mxfp8_e4m3_4096"])
+    if want("mxfp4_4096"):
+        legs["mxfp4_4096"] = b.gemm_mxfp4_leg(4096, 4096, 4096, S, W, copies=10)
+        log("mxfp4 4096: %s" % legs["mxfp4_4096"])
+    if want("quantize_mxfp4_4096"):
+        legs["quantize_mxfp4_4096"] = b.quantize_mx_leg(4096, 4096, dmu.E2M1, S, W)
+        log("quantize mxfp4 4096^2: %s" % legs["quantize_mxfp4_4096"])
     if want("quantize_mx_e4m3_4096"):
         legs["quantize_mx_e4m3_4096"] = b.quantize_mx_leg(4096, 4096, dmu.E4M3, S, W)
         log("quantize mx 4096^2: %s" % legs["quantize_mx_e4m3_4096"])

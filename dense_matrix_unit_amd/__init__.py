@@ -36,7 +36,9 @@ PROBE_BF16_32X32X16 = 1
 PROBE_FP8_16X16X128 = 2
 PROBE_FP8_32X32X64 = 3
 PROBE_MXFP8_32X32X64 = 4  # rate probe only: scaled form, unit E8M0 scales
+PROBE_MXFP4_32X32X64 = 5  # rate probe only: E2M1 operands, unit E8M0 scales
 MX_BLOCK = 32  # values of K per E8M0 scale (DMU_MX_BLOCK)
+E2M1 = 4  # FP4 elements of MXFP4 (DMU_FP4_E2M1), packed two per byte
 PROBE_MX_16X16X128 = 0  # shapes of dmu_probe_mfma_mx
 PROBE_MX_32X32X64 = 1
 
@@ -52,6 +54,9 @@ SYMBOLS = {
     "gemm_mxfp8": (_I, [_P, _I64, _I, _P, _I64, _I, _P, _I64, _P, _I64, _P, _I64, _P, _I64, _I,
                         _I64, _I64, _I64, _P]),
     "quantize_mxfp8": (_I, [_P, _I64, _I64, _I64, _I, _P, _I64, _P, _I64, _P]),
+    "gemm_mxfp4": (_I, [_P, _I64, _P, _I64, _P, _I64, _P, _I64, _P, _I64, _P, _I64, _I, _I64,
+                        _I64, _I64, _P]),
+    "quantize_mxfp4": (_I, [_P, _I64, _I64, _I64, _P, _I64, _P, _I64, _P]),
     "dmu_status_string": (ctypes.c_char_p, [_I]),
     "dmu_version": (_I, []),
     "dmu_probe_mfma": (_I, [_I, _I, _I, _P, _P, _P, _P, _P]),
@@ -262,6 +267,65 @@ def quantize_mxfp8(X, Q, S, fmt: int = E4M3, stream=None):
         _dev_ptr(X, "X"), rows, cols, _ld(X, "X"), fmt, _fp8_ptr(Q, "Q"), _ld(Q, "Q"),
         _dev_ptr(S, "S"), _ld(S, "S"), _stream(stream))
     _check("quantize_mxfp8", rc)
+    return Q, S
+
+
+def _packed_ld(t, name):
+    """Leading dimension, in elements, of a packed E2M1 array held as uint8."""
+    return 2 * _ld(t, name)
+
+
+def gemm_mxfp4(A, B, scale_a, scale_b, out, C=None, stream=None):
+    """out = (A x 2^(scale_a-127)) @ (B x 2^(scale_b-127))^T (+ C), microscaled
+    FP4.  A: uint8 [M, K/2] and B: uint8 [N, K/2] packed E2M1 (element 2i in
+    the low nibble of byte i), K a multiple of 512.  scale_a: uint8
+    [M, >= K/32], scale_b: uint8 [N, >= K/32] E8M0 codes, row strides a
+    multiple of 16 bytes."""
+    torch = _torch()
+    _check_dtype(out, (torch.float32, torch.bfloat16), "out")
+    _check_dtype(A, (torch.uint8,), "A")
+    _check_dtype(B, (torch.uint8,), "B")
+    M, K = A.shape[0], 2 * A.shape[1]
+    N = B.shape[0]
+    if 2 * B.shape[1] != K or tuple(out.shape) != (M, N):
+        raise ValueError("shape mismatch")
+    _check_dtype(scale_a, (torch.uint8,), "scale_a")
+    _check_dtype(scale_b, (torch.uint8,), "scale_b")
+    if scale_a.shape[0] != M or scale_b.shape[0] != N:
+        raise ValueError("scale arrays need one row per row of A / stored row of B")
+    if scale_a.shape[1] < K // MX_BLOCK or scale_b.shape[1] < K // MX_BLOCK:
+        raise ValueError("scale rows need K/32 codes")
+    cptr, ldc = None, 0
+    if C is not None:
+        _check_dtype(C, (torch.float32,), "C")
+        if tuple(C.shape) != (M, N):
+            raise ValueError("C shape")
+        cptr, ldc = _dev_ptr(C, "C"), _ld(C, "C")
+    rc = load_library().gemm_mxfp4(
+        _dev_ptr(A, "A"), _packed_ld(A, "A"), _dev_ptr(B, "B"), _packed_ld(B, "B"),
+        _dev_ptr(scale_a, "scale_a"), _ld(scale_a, "scale_a"), _dev_ptr(scale_b, "scale_b"),
+        _ld(scale_b, "scale_b"), cptr, ldc, _dev_ptr(out, "out"), _ld(out, "out"),
+        OUT_F32 if out.dtype == torch.float32 else OUT_BF16, M, N, K, _stream(stream))
+    _check("gemm_mxfp4", rc)
+    return out
+
+
+def quantize_mxfp4(X, Q, S, stream=None):
+    """Q, S = MXFP4 quantisation of X (float32 [rows, cols], cols % 32 == 0): Q
+    uint8 [rows, cols/2] packed E2M1, S uint8 [rows, >= cols/32] E8M0 codes."""
+    torch = _torch()
+    _check_dtype(X, (torch.float32,), "X")
+    _check_dtype(Q, (torch.uint8,), "Q")
+    _check_dtype(S, (torch.uint8,), "S")
+    rows, cols = X.shape
+    if tuple(Q.shape) != (rows, cols // 2):
+        raise ValueError("Q shape")
+    if S.shape[0] != rows or S.shape[1] < cols // MX_BLOCK:
+        raise ValueError("S shape")
+    rc = load_library().quantize_mxfp4(
+        _dev_ptr(X, "X"), rows, cols, _ld(X, "X"), _dev_ptr(Q, "Q"), _packed_ld(Q, "Q"),
+        _dev_ptr(S, "S"), _ld(S, "S"), _stream(stream))
+    _check("quantize_mxfp4", rc)
     return Q, S
 
 

@@ -143,6 +143,46 @@ int quantize_mxfp8(const float* X, int64_t rows, int64_t cols, int64_t ldx, int 
       dmu::launch_quantize_mxfp8(X, rows, cols, ldx, fmt, Q, ldq, S, lds, (hipStream_t)stream));
 }
 
+int gemm_mxfp4(const uint8_t* A, int64_t lda, const uint8_t* B, int64_t ldb,
+               const uint8_t* scale_a, int64_t ld_sa, const uint8_t* scale_b, int64_t ld_sb,
+               const float* C, int64_t ldc, void* D, int64_t ldd, int d_dtype, int64_t M,
+               int64_t N, int64_t K, void* stream) {
+  int rc = check_out(C, ldc, D, ldd, d_dtype, M, N);
+  if (rc) return rc;
+  if (!A || !B || !scale_a || !scale_b) return DMU_ERR_INVALID_ARG;
+  if (K < 512 || K > INT32_MAX || K % 512) return DMU_ERR_INVALID_ARG;
+  if (lda < K || ldb < K || lda % 32 || ldb % 32) return DMU_ERR_INVALID_ARG;
+  if (ld_sa < K / DMU_MX_BLOCK || ld_sb < K / DMU_MX_BLOCK || ld_sa % 16 || ld_sb % 16)
+    return DMU_ERR_INVALID_ARG;
+  if (!aligned(A, 16) || !aligned(B, 16) || !aligned(scale_a, 16) || !aligned(scale_b, 16))
+    return DMU_ERR_INVALID_ARG;
+  if (kTileRows * (lda / 2) >= kMaxTileBytes || kTileRows * (ldb / 2) >= kMaxTileBytes ||
+      kTileRows * ld_sa >= kMaxTileBytes || kTileRows * ld_sb >= kMaxTileBytes)
+    return DMU_ERR_UNSUPPORTED;
+  // the kernel addresses packed rows in bytes
+  dmu::GemmArgs a{A, B, C, D, lda / 2, ldb / 2, ldc, ldd, M, N, K, nullptr, nullptr,
+                  d_dtype == DMU_OUT_BF16};
+  a.xa = scale_a;
+  a.xb = scale_b;
+  a.ldxa = ld_sa;
+  a.ldxb = ld_sb;
+  (void)hipGetLastError();
+  return finish(dmu::launch_gemm_mxfp4(a, (hipStream_t)stream));
+}
+
+int quantize_mxfp4(const float* X, int64_t rows, int64_t cols, int64_t ldx, uint8_t* Q,
+                   int64_t ldq, uint8_t* S, int64_t lds, void* stream) {
+  if (!X || !Q || !S || rows < 1 || cols < DMU_MX_BLOCK || cols % DMU_MX_BLOCK)
+    return DMU_ERR_INVALID_ARG;
+  if (ldx < cols || ldq < cols || lds < cols / DMU_MX_BLOCK || ldx % 4 || ldq % 32)
+    return DMU_ERR_INVALID_ARG;
+  if (!aligned(X, 16) || !aligned(Q, 16)) return DMU_ERR_INVALID_ARG;
+  if (rows * (cols / DMU_MX_BLOCK) > INT32_MAX) return DMU_ERR_UNSUPPORTED;
+  (void)hipGetLastError();
+  return finish(
+      dmu::launch_quantize_mxfp4(X, rows, cols, ldx, Q, ldq / 2, S, lds, (hipStream_t)stream));
+}
+
 const char* dmu_status_string(int status) {
   switch (status) {
     case DMU_OK:
@@ -179,7 +219,7 @@ int dmu_probe_lds_load(const void* src, void* dst, int mode, int oob_from, void*
 int dmu_probe_mfma_rate(int kind, const void* src, int iters, int grid, float* out, void* stream) {
   if (!src || !out ||
       (kind != DMU_PROBE_BF16_32X32X16 && kind != DMU_PROBE_FP8_32X32X64 &&
-       kind != DMU_PROBE_MXFP8_32X32X64))
+       kind != DMU_PROBE_MXFP8_32X32X64 && kind != DMU_PROBE_MXFP4_32X32X64))
     return DMU_ERR_INVALID_ARG;
   if (iters < 1 || iters > (1 << 20) || grid < 1 || grid > 65536) return DMU_ERR_INVALID_ARG;
   if (!aligned(src, 16) || !aligned(out, 4)) return DMU_ERR_INVALID_ARG;
@@ -190,8 +230,9 @@ int dmu_probe_mfma_rate(int kind, const void* src, int iters, int grid, float* o
 int dmu_probe_mfma_mx(int shape, int fmt_a, int fmt_b, int opsel, const void* A, const void* B,
                       const void* SA, const void* SB, const float* C, float* D, void* stream) {
   if (!A || !B || !SA || !SB || !C || !D || shape < 0 || shape > 1) return DMU_ERR_INVALID_ARG;
-  if (fmt_a < 0 || fmt_a > 1 || fmt_b < 0 || fmt_b > 1 || opsel < 0 || opsel > 3)
-    return DMU_ERR_INVALID_ARG;
+  auto fmt_ok = [](int f) { return f == 0 || f == 1 || f == 4; };
+  if (!fmt_ok(fmt_a) || !fmt_ok(fmt_b) || opsel < 0 || opsel > 3) return DMU_ERR_INVALID_ARG;
+  if ((fmt_a == 1 && fmt_b == 4) || (fmt_a == 4 && fmt_b == 1)) return DMU_ERR_UNSUPPORTED;
   (void)hipGetLastError();
   return finish(
       dmu::launch_probe_mx(shape, fmt_a, fmt_b, opsel, A, B, SA, SB, C, D, (hipStream_t)stream));

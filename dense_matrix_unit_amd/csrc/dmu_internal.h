@@ -23,8 +23,9 @@ struct GemmArgs {
   int64_t ldxa = 0, ldxb = 0;  // bytes per scale row
 };
 
-// kMX / kMX4: MX scales fetched one / four K slices at a time
-enum GemmKind { kBF16 = 0, kFP8Tensor = 1, kFP8Block = 2, kMX = 3, kMX4 = 4 };
+// kMX / kMX4: MXFP8, scales fetched one / four K slices at a time;
+// kMXF4: MXFP4 (E2M1 x E2M1, row strides in bytes), scales two slices at a time
+enum GemmKind { kBF16 = 0, kFP8Tensor = 1, kFP8Block = 2, kMX = 3, kMX4 = 4, kMXF4 = 5 };
 
 // Launchers: argument checking is done by the caller; these only pick a
 // kernel configuration and launch it.  They return a hipError_t.
@@ -39,6 +40,12 @@ hipError_t launch_gemm_fp8_block(const GemmArgs& a, int fmt_a, int fmt_b, hipStr
 // MX-scaled FP8 (E8M0 scale per row and 32 K, applied by the matrix unit;
 // K % 128 == 0, scale rows a multiple of 4 bytes).
 hipError_t launch_gemm_mxfp8(const GemmArgs& a, int fmt_a, int fmt_b, hipStream_t s);
+// MXFP4: A, B packed E2M1 (lda, ldb in bytes in GemmArgs), K % 512 == 0,
+// scale rows 16-byte aligned with strides a multiple of 16 bytes.
+hipError_t launch_gemm_mxfp4(const GemmArgs& a, hipStream_t s);
+hipError_t launch_quantize_mxfp4(const float* X, int64_t rows, int64_t cols, int64_t ldx,
+                                 uint8_t* Q, int64_t ldq_bytes, uint8_t* S, int64_t lds,
+                                 hipStream_t s);
 hipError_t launch_quantize_mxfp8(const float* X, int64_t rows, int64_t cols, int64_t ldx, int fmt,
                                  uint8_t* Q, int64_t ldq, uint8_t* S, int64_t lds, hipStream_t s);
 hipError_t launch_quantize_fp8(const float* X, int64_t rows, int64_t cols, int64_t ldx, int fmt,

@@ -68,6 +68,7 @@ template <int KIND, int FA, int FB, bool BROW, int BM, int BN, int RB, int S, in
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4))) void
 gemm_kernel(GemmArgs p) {
   constexpr int NT = NW * 64;   // threads; NW waves in a 2 x (NW/2) grid
+  constexpr bool F4 = KIND == kMXF4;  // E2M1 operands: 32 bytes of a row per K step of 64
   constexpr int ESZ = KIND == kBF16 ? 2 : 1;
   constexpr int CPR = RB / 16;  // 16-byte chunks per LDS row
   constexpr int WM = BM / 2, WN = BN / (NW / 2);
@@ -76,13 +77,14 @@ gemm_kernel(GemmArgs p) {
   constexpr int STAGE = A_BYTES + B_BYTES;
   // MX: scale words are fetched XG slices at a time (4 * XG bytes per tile
   // row) into a two-buffer ring of their own after the stages
-  constexpr bool MX = KIND == kMX || KIND == kMX4;
-  constexpr int XG = KIND == kMX4 ? 4 : 1;
-  constexpr int XROW = 4 * XG;                  // ring bytes per tile row
+  constexpr bool MX = KIND == kMX || KIND == kMX4 || KIND == kMXF4;
+  constexpr int XG = KIND == kMX4 ? 4 : F4 ? 2 : 1;
+  constexpr int WPS = F4 ? 2 : 1;               // scale words per row and slice
+  constexpr int XROW = 4 * WPS * XG;            // ring bytes per tile row
   constexpr int XBUF = (BM + BN) * XROW;        // one ring buffer (A rows, then B rows)
   constexpr int XOFF = S * STAGE;               // ring offset in LDS
   constexpr int XR = MX ? 2 * XBUF : 0;
-  constexpr int NSTEP = KIND == kBF16 ? RB / 32 : RB / 64;  // MFMA K-steps per slice
+  constexpr int NSTEP = KIND == kBF16 || F4 ? RB / 32 : RB / 64;  // MFMA K-steps per slice
   constexpr int NLA = BM * CPR / NT;                 // A copies per thread per slice
   constexpr int NLB = BROW ? 8 : BN * CPR / NT;      // B copies per thread per slice
   constexpr int NLS = MX ? 2 : 0;                    // MX scale-group copies (A, B)
@@ -111,7 +113,7 @@ gemm_kernel(GemmArgs p) {
   int tm, tn;
   tile_coords<kGroupM>(tiles_m, tiles_n, tm, tn);
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
-  const int64_t kbytes = p.K * ESZ;
+  const int64_t kbytes = F4 ? p.K / 2 : p.K * ESZ;
   const int nkt = (int)((kbytes + RB - 1) / RB);
 
   // ---- A: global -> LDS descriptors (rows beyond M read as zeros)
@@ -187,7 +189,8 @@ gemm_kernel(GemmArgs p) {
       const uint32_t koff = act ? (uint32_t)G * XROW : 0u;
       const __amdgpu_buffer_rsrc_t r = act ? (which == 0 ? rXA : rXB) : rNull;
       const uint32_t v = which == 0 ? voffXA : voffXB;
-      if constexpr (XG == 4) buffer_load_lds16(r, dst, v, koff);
+      static_assert(XROW == 16 || XROW == 4, "scale copy width");
+      if constexpr (XROW == 16) buffer_load_lds16(r, dst, v, koff);
       else buffer_load_lds4(r, dst, v, koff);
     }
   };
@@ -344,7 +347,7 @@ gemm_kernel(GemmArgs p) {
   stage_barrier();
 
   {
-    constexpr int CPL = KIND == kBF16 ? 1 : 2;  // 16-byte chunks per lane per step
+    constexpr int CPL = KIND == kBF16 || F4 ? 1 : 2;  // 16-byte chunks per lane per step
     f32x16_t acc[TM][TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i)
@@ -358,29 +361,38 @@ gemm_kernel(GemmArgs p) {
     // 32 + 16 * (lane / 32) of the 64-wide step, and lane group g's scale
     // covers K block g (32 values) of the step.
     auto chunk = [&](int s, int h) __attribute__((always_inline)) -> int {
-      if constexpr (MX) return 4 * s + 2 * h + hl;
+      if constexpr (MX && !F4) return 4 * s + 2 * h + hl;
       else return (2 * s + hl) * CPL + h;
     };
     // MX: the next slice's scale words as read from the ring, and the
-    // current slice's shifted to this lane's K block
-    uint32_t xraw[TM + TN], xa[TM], xb[TN];
+    // current slice's shifted to this lane's K block (WPS words per row)
+    uint32_t xraw[TM + TN][WPS], xa[WPS][TM], xb[WPS][TN];
     auto read_scales = [&](int kt) __attribute__((always_inline)) {
       if constexpr (MX) {
-        const uint8_t* x = smem + XOFF + ((kt / XG) & 1) * XBUF + 4 * (kt % XG);
+        const uint8_t* x = smem + XOFF + ((kt / XG) & 1) * XBUF + 4 * WPS * (kt % XG);
 #pragma unroll
-        for (int i = 0; i < TM; ++i) xraw[i] = *(const uint32_t*)(x + (wm * WM + i * 32 + rl) * XROW);
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          xraw[TM + j] = *(const uint32_t*)(x + (BM + wn * WN + j * 32 + rl) * XROW);
+        for (int r = 0; r < TM + TN; ++r) {
+          const int row = r < TM ? wm * WM + r * 32 + rl : BM + wn * WN + (r - TM) * 32 + rl;
+          if constexpr (WPS == 2) {
+            const uint2 w = *(const uint2*)(x + row * XROW);
+            xraw[r][0] = w.x;
+            xraw[r][1] = w.y;
+          } else {
+            xraw[r][0] = *(const uint32_t*)(x + row * XROW);
+          }
+        }
       }
     };
     auto take_scales = [&]() __attribute__((always_inline)) {
       if constexpr (MX) {
         const uint32_t sh = 8u * (uint32_t)hl;
 #pragma unroll
-        for (int i = 0; i < TM; ++i) xa[i] = xraw[i] >> sh;
+        for (int w = 0; w < WPS; ++w) {
 #pragma unroll
-        for (int j = 0; j < TN; ++j) xb[j] = xraw[TM + j] >> sh;
+          for (int i = 0; i < TM; ++i) xa[w][i] = xraw[i][w] >> sh;
+#pragma unroll
+          for (int j = 0; j < TN; ++j) xb[w][j] = xraw[TM + j][w] >> sh;
+        }
       }
     };
     auto load_step = [&](int st, int s, int buf) __attribute__((always_inline)) {
@@ -417,22 +429,29 @@ gemm_kernel(GemmArgs p) {
     };
     // The B fragment is the instruction's first operand, so each accumulator
     // holds a transposed 32x32 sub-tile (see the epilogue).
-    auto mfma_one = [&](int buf, int i, int j) __attribute__((always_inline)) {
+    auto mfma_one = [&](int s, int i, int j) __attribute__((always_inline)) {
+      const int buf = s & 1;
       if constexpr (KIND == kBF16)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
             __builtin_bit_cast(bf16x8_t, fb[buf][j][0]),
             __builtin_bit_cast(bf16x8_t, fa[buf][i][0]), acc[i][j], 0, 0, 0);
       else if constexpr (MX) {
-        // step s = buf (two steps per slice) uses scale byte 2 s; the first
-        // operand is B's fragment, so its scale is the instruction's first
-        if (buf == 0)
+        // step s covers K blocks 2 s and 2 s + 1 of the slice: scale word
+        // s / 2, byte 2 (s % 2) (+ the lane group, already shifted in).  The
+        // first operand is B's fragment, so its scale is the instruction's
+        // first.  E2M1 fragments are 16 bytes, in the low half of the
+        // operand registers.
+        const int w = F4 ? s / 2 : 0;
+        const i32x4_t z = {0, 0, 0, 0};
+        const i32x8_t ob = F4 ? cat(fb[buf][j][0], z) : cat(fb[buf][j][0], fb[buf][j][CPL - 1]);
+        const i32x8_t oa = F4 ? cat(fa[buf][i][0], z) : cat(fa[buf][i][0], fa[buf][i][CPL - 1]);
+        constexpr int CF = F4 ? 4 : FB, CA = F4 ? 4 : FA;  // cbsz / blgp format codes
+        if ((F4 ? s % 2 : s) == 0)
           acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-              cat(fb[buf][j][0], fb[buf][j][1]), cat(fa[buf][i][0], fa[buf][i][1]), acc[i][j],
-              FB, FA, 0, (int)xb[j], 0, (int)xa[i]);
+              ob, oa, acc[i][j], CF, CA, 0, (int)xb[w][j], 0, (int)xa[w][i]);
         else
           acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-              cat(fb[buf][j][0], fb[buf][j][1]), cat(fa[buf][i][0], fa[buf][i][1]), acc[i][j],
-              FB, FA, 2, (int)xb[j], 2, (int)xa[i]);
+              ob, oa, acc[i][j], CF, CA, 2, (int)xb[w][j], 2, (int)xa[w][i]);
       } else
         acc[i][j] = mfma_fp8_32x32x64<FB, FA>(cat(fb[buf][j][0], fb[buf][j][1]),
                                               cat(fa[buf][i][0], fa[buf][i][1]), acc[i][j]);
@@ -477,7 +496,7 @@ gemm_kernel(GemmArgs p) {
           if (i >= iend) continue;
 #pragma unroll
           for (int j = 0; j < TN; ++j) {
-            mfma_one(buf, i, j);
+            mfma_one(s, i, j);
             const int gl = i * TN + j;  // MFMA index within the step
             const int g = s * TM * TN + gl;
             __builtin_amdgcn_sched_barrier(0);
@@ -517,7 +536,7 @@ gemm_kernel(GemmArgs p) {
 #pragma unroll
             for (int k = gl * NR / NM; k < (gl + 1) * NR / NM; ++k) read_one(nx_st, 0, 0, k);
             __builtin_amdgcn_sched_barrier(0);
-            mfma_one((NSTEP - 1) & 1, i, j);
+            mfma_one(NSTEP - 1, i, j);
             __builtin_amdgcn_sched_barrier(0);
           }
       } else {
@@ -623,7 +642,7 @@ hipError_t launch(const GemmArgs& a, hipStream_t s) {
   const int64_t tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
   // K tail: the last slice is partial and its lanes are range-checked one by
   // one (MX requires whole slices and has no such variant)
-  if constexpr (KIND != kMX && KIND != kMX4) {
+  if constexpr (KIND != kMX && KIND != kMX4 && KIND != kMXF4) {
     if ((a.K * (KIND == kBF16 ? 2 : 1)) % RB != 0) {
       hipLaunchKernelGGL((gemm_kernel<KIND, FA, FB, BROW, BM, BN, RB, S, G, PD, NW, true>),
                          dim3((unsigned)tiles), dim3(NW * 64), 0, s, a);
@@ -665,6 +684,10 @@ static hipError_t launch_mx_kind(const GemmArgs& a, int fmt_a, int fmt_b, hipStr
   if (fmt_a == 1 && fmt_b == 0) return DMU_MX(1, 0);
   return DMU_MX(1, 1);
 #undef DMU_MX
+}
+
+hipError_t launch_gemm_mxfp4(const GemmArgs& a, hipStream_t s) {
+  return launch<kMXF4, 4, 4, false, 256, 256, 128, 2, 4, kPrefetch, kWavesFP8>(a, s);
 }
 
 hipError_t launch_gemm_mxfp8(const GemmArgs& a, int fmt_a, int fmt_b, hipStream_t s) {

@@ -101,6 +101,28 @@ __global__ void probe_mfma_kernel(const void* Av, const void* Bv, const float* C
 // K block g -- SA[l%16][l/16] for 16x16x128, SA[l%32][l/32] for 32x32x64 --
 // in byte OPSEL of its 32-bit scale register, the other three bytes holding
 // decoys (code ^ 4, a factor 16 away) so a wrong byte choice shows in D.
+// Byte o (0..31) of the operand registers of lane group g, for one row of
+// an operand of instruction width K: FP8 (one value per byte) as described
+// above; FP4 (format 4, E2M1 two per byte, 16 bytes per lane) as byte o of
+// the row's packed bytes [16 g, 16 g + 16).
+template <int FMT, int K>
+__device__ __forceinline__ int mx_src_byte(int g, int o) {
+  if constexpr (FMT == 4) return 16 * g + o;
+  else return (o / 16) * (K / 2) + 16 * g + o % 16;
+}
+
+template <int FMT, int K>
+__device__ __forceinline__ i32x8_t mx_fragment(const uint8_t* rowp, int g) {
+  constexpr int NB = FMT == 4 ? 16 : 32;  // bytes per lane
+  i32x8_t v = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int w = 0; w < NB / 4; ++w) {
+    uint32_t x = 0;
+    for (int q = 0; q < 4; ++q) x |= (uint32_t)rowp[mx_src_byte<FMT, K>(g, 4 * w + q)] << (8 * q);
+    v[w] = (int)x;
+  }
+  return v;
+}
+
 template <int SHAPE, int FA, int FB, int OPSEL>
 __global__ void probe_mx_kernel(const uint8_t* A, const uint8_t* B, const uint8_t* SA,
                                 const uint8_t* SB, const float* C, float* D) {
@@ -108,18 +130,9 @@ __global__ void probe_mx_kernel(const uint8_t* A, const uint8_t* B, const uint8_
   constexpr int R = SHAPE == 0 ? 16 : 32;   // rows per K group
   constexpr int K = SHAPE == 0 ? 128 : 64;  // instruction K
   const int row = l % R, g = l / R;
-  i32x8_t a, b;
-  for (int w = 0; w < 8; ++w) {
-    uint32_t x = 0, y = 0;
-    for (int q = 0; q < 4; ++q) {
-      const int o = 4 * w + q;  // byte of the lane's 32
-      const int kp = (o / 16) * (K / 2) + 16 * g + o % 16;
-      x |= (uint32_t)A[row * K + kp] << (8 * q);
-      y |= (uint32_t)B[row * K + kp] << (8 * q);
-    }
-    a[w] = (int)x;
-    b[w] = (int)y;
-  }
+  constexpr int RBA = FA == 4 ? K / 2 : K, RBB = FB == 4 ? K / 2 : K;  // bytes per row
+  const i32x8_t a = mx_fragment<FA, K>(A + row * RBA, g);
+  const i32x8_t b = mx_fragment<FB, K>(B + row * RBB, g);
   auto word = [&](uint8_t code) {
     uint32_t v = 0;
     for (int q = 0; q < 4; ++q) v |= (uint32_t)(q == OPSEL ? code : (uint8_t)(code ^ 4)) << (8 * q);
@@ -205,6 +218,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         } else if constexpr (KIND == 4) {  // scaled form, E8M0 codes in registers
           acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
               b[j], a[i], acc[i][j], 0, 0, 0, scale_word, 0, scale_word);
+        } else if constexpr (KIND == 5) {  // FP4 (E2M1) operands: low 16 bytes of each fragment
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              b[j], a[i], acc[i][j], 4, 4, 0, scale_word, 0, scale_word);
         } else {
           acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b[j], a[i], acc[i][j], 0, 0,
                                                                       0, 0, 0, 0);
@@ -257,7 +273,10 @@ hipError_t probe_mx_fmt(int fa, int fb, int opsel, const uint8_t* A, const uint8
   if (fa == 0 && fb == 0) return probe_mx_opsel<SHAPE, 0, 0>(opsel, A, B, SA, SB, C, D, s);
   if (fa == 0 && fb == 1) return probe_mx_opsel<SHAPE, 0, 1>(opsel, A, B, SA, SB, C, D, s);
   if (fa == 1 && fb == 0) return probe_mx_opsel<SHAPE, 1, 0>(opsel, A, B, SA, SB, C, D, s);
-  return probe_mx_opsel<SHAPE, 1, 1>(opsel, A, B, SA, SB, C, D, s);
+  if (fa == 1 && fb == 1) return probe_mx_opsel<SHAPE, 1, 1>(opsel, A, B, SA, SB, C, D, s);
+  if (fa == 4 && fb == 4) return probe_mx_opsel<SHAPE, 4, 4>(opsel, A, B, SA, SB, C, D, s);
+  if (fa == 4 && fb == 0) return probe_mx_opsel<SHAPE, 4, 0>(opsel, A, B, SA, SB, C, D, s);
+  return probe_mx_opsel<SHAPE, 0, 4>(opsel, A, B, SA, SB, C, D, s);
 }
 
 }  // namespace
@@ -291,6 +310,9 @@ hipError_t launch_probe_rate(int kind, const void* src, int iters, int grid, flo
                        iters, out, 0);
   else if (kind == 4)
     hipLaunchKernelGGL(probe_rate_kernel<4>, dim3(grid), dim3(256), 0, s, (const uint8_t*)src,
+                       iters, out, 0x7F7F7F7F);
+  else if (kind == 5)
+    hipLaunchKernelGGL(probe_rate_kernel<5>, dim3(grid), dim3(256), 0, s, (const uint8_t*)src,
                        iters, out, 0x7F7F7F7F);
   else
     hipLaunchKernelGGL(probe_rate_kernel<3>, dim3(grid), dim3(256), 0, s, (const uint8_t*)src,

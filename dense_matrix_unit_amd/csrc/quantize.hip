@@ -27,7 +27,9 @@
 //    (the multiplier is a normal power of two, and a product that leaves the
 //    normal range is far below half the smallest FP8 step).  A block holding
 //    NaN or Inf gets code 255 (NaN) and NaN element codes of the elements'
-//    signs.
+//    signs.  MXFP4 (E2M1, emax = 2) packs the four codes of a lane into 16
+//    bits, element 2i in the low nibble; a NaN/Inf block's elements are
+//    signed zeros (E2M1 has no NaN).
 #include "dmu_device.h"
 #include "dmu_internal.h"
 
@@ -78,6 +80,19 @@ __device__ __forceinline__ uint32_t encode_fp8(float y) {
 }
 
 __device__ __forceinline__ uint32_t abs_bits(float x) { return __float_as_uint(x) & 0x7FFFFFFFu; }
+
+// FP32 -> E2M1 (FP4: magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6), round to nearest
+// with ties to the even code, saturating at 6, sign kept.  The magnitude code
+// counts the rounding boundaries |y| has passed: a boundary between codes
+// c and c + 1 is their midpoint, which itself rounds up exactly when c + 1 is
+// even (>=) and down when c + 1 is odd (>).
+__device__ __forceinline__ uint32_t encode_fp4(float y) {
+  const float a = fabsf(y);
+  const uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+                     (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
+                     (uint32_t)(a > 5.0f);
+  return c | ((__float_as_uint(y) >> 28) & 8u);
+}
 
 __device__ __forceinline__ uint32_t wave_max(uint32_t v) {
 #pragma unroll
@@ -268,7 +283,7 @@ template <int FMT>
 __global__ __launch_bounds__(256) void quant_mx(const float* X, int64_t rows, int64_t cols,
                                                 int64_t ldx, uint8_t* Q, int64_t ldq, uint8_t* S,
                                                 int64_t lds) {
-  constexpr uint32_t kEmax = FMT == 0 ? 8u : 15u;
+  constexpr uint32_t kEmax = FMT == 0 ? 8u : FMT == 1 ? 15u : 2u;
   const int sub = threadIdx.x & 7;
   const int64_t c0 = (int64_t)blockIdx.x * (1024 * kRounds) + 4 * threadIdx.x;
   for (int64_t r = blockIdx.y; r < rows; r += gridDim.y) {
@@ -292,14 +307,26 @@ __global__ __launch_bounds__(256) void quant_mx(const float* X, int64_t rows, in
           code = 255u;
           q = 0;
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            q |= ((__float_as_uint(v[u][e]) >> 24 & 0x80u) | 0x7Fu) << (8 * e);
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t sgn = __float_as_uint(v[u][e]) >> 24 & 0x80u;
+            q |= FMT == 4 ? (sgn >> 4) << (4 * e) : (sgn | 0x7Fu) << (8 * e);
+          }
         } else {
           const uint32_t eb = m >> 23;  // biased exponent of amax (0: zero or subnormal)
           code = eb > kEmax ? eb - kEmax : 0u;
-          q = encode4<FMT>(v[u], __uint_as_float((254u - code) << 23));
+          const float mult = __uint_as_float((254u - code) << 23);
+          if constexpr (FMT == 4) {
+            q = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) q |= encode_fp4(v[u][e] * mult) << (4 * e);
+          } else {
+            q = encode4<FMT>(v[u], mult);
+          }
         }
-        *(uint32_t*)(Q + r * ldq + c) = q;
+        if constexpr (FMT == 4)
+          *(uint16_t*)(Q + r * ldq + c / 2) = (uint16_t)q;
+        else
+          *(uint32_t*)(Q + r * ldq + c) = q;
         if (sub == 0) S[r * lds + c / 32] = (uint8_t)code;
       }
     }
@@ -345,6 +372,16 @@ hipError_t launch_quantize_mxfp8(const float* X, int64_t rows, int64_t cols, int
     hipLaunchKernelGGL(quant_mx<0>, grid, dim3(256), 0, s, X, rows, cols, ldx, Q, ldq, S, lds);
   else
     hipLaunchKernelGGL(quant_mx<1>, grid, dim3(256), 0, s, X, rows, cols, ldx, Q, ldq, S, lds);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_mxfp4(const float* X, int64_t rows, int64_t cols, int64_t ldx,
+                                 uint8_t* Q, int64_t ldq_bytes, uint8_t* S, int64_t lds,
+                                 hipStream_t s) {
+  const dim3 grid((unsigned)((cols + 1024 * kRounds - 1) / (1024 * kRounds)),
+                  (unsigned)(rows < 65535 ? rows : 65535));
+  hipLaunchKernelGGL(quant_mx<4>, grid, dim3(256), 0, s, X, rows, cols, ldx, Q, ldq_bytes, S,
+                     lds);
   return hipGetLastError();
 }
 

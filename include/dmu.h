@@ -193,6 +193,48 @@ int gemm_mxfp8(const uint8_t* A, int64_t lda, int fmt_a, const uint8_t* B, int64
 int quantize_mxfp8(const float* X, int64_t rows, int64_t cols, int64_t ldx, int fmt, uint8_t* Q,
                    int64_t ldq, uint8_t* S, int64_t lds, void* stream);
 
+/*
+ * MXFP4: the same microscaled product with E2M1 elements (FP4: sign, 2
+ * exponent bits with bias 1, 1 mantissa bit; magnitudes 0, 0.5, 1, 1.5, 2, 3,
+ * 4, 6; no Inf or NaN), the MXFP4 format [TM]'s section names beside MXFP8.
+ * Elements are packed two per byte, element 2i in the low nibble of byte i of
+ * the row.  Leading dimensions of packed arrays count elements (bytes x 2).
+ */
+#define DMU_FP4_E2M1 4
+
+/*
+ * gemm_mxfp4: D = sum_k (a_ik * 2^(sa_i,k/32 - 127)) * (b_jk * 2^(sb_j,k/32 - 127))
+ * (+ C), E2M1 x E2M1 inputs, FP32 accumulation; the matrix unit applies the
+ * scales.
+ *
+ *   A       : M x K E2M1 packed, row-major, lda elements (lda % 32 == 0).
+ *   B       : K x N operand stored N x K, E2M1 packed, ldb elements (% 32 == 0).
+ *   scale_a : M x (K/32) E8M0 codes, ld_sa bytes per row; scale_b : N x (K/32).
+ *   C, D    : as for gemm_bf16.
+ *   M, N >= 1; K >= 512 and K % 512 == 0; ld_sa, ld_sb >= K/32 and multiples
+ *   of 16; A, B, scale_a, scale_b 16-byte aligned.
+ * Accumulation and special values behave as for gemm_mxfp8.
+ * Errors: DMU_ERR_INVALID_ARG for null pointers, sizes, strides or alignment
+ * outside the above, an unknown output type.
+ */
+int gemm_mxfp4(const uint8_t* A, int64_t lda, const uint8_t* B, int64_t ldb,
+               const uint8_t* scale_a, int64_t ld_sa, const uint8_t* scale_b, int64_t ld_sb,
+               const float* C, int64_t ldc, void* D, int64_t ldd, int d_dtype, int64_t M,
+               int64_t N, int64_t K, void* stream);
+
+/*
+ * quantize_mxfp4: FP32 -> E2M1 with one E8M0 scale per 1 x 32 block, as
+ * quantize_mxfp8 with emax = 2 (the scale puts each block's largest value in
+ * [4, 8)): q = saturating round-to-nearest-even E2M1 of x / X, ties to the even
+ * code.  Q is rows x cols packed (ldq elements, a multiple of 32); S as for
+ * quantize_mxfp8.  A block holding NaN or Inf gets code 255 and signed-zero
+ * elements.  Bit-exact and independent of launch configuration.
+ * Errors: DMU_ERR_INVALID_ARG for null pointers, cols % 32 != 0, short or
+ * misaligned leading dimensions.
+ */
+int quantize_mxfp4(const float* X, int64_t rows, int64_t cols, int64_t ldx, uint8_t* Q,
+                   int64_t ldq, uint8_t* S, int64_t lds, void* stream);
+
 /* Human-readable text for a status code (static storage, never NULL). */
 const char* dmu_status_string(int status);
 

@@ -26,6 +26,9 @@ extern "C" {
 /* dmu_probe_mfma_rate only: v_mfma_scale_f32_32x32x64_f8f6f4 with E8M0 scale
  * codes 127 (x1) held in registers, the form the MX GEMM issues */
 #define DMU_PROBE_MXFP8_32X32X64 4
+/* dmu_probe_mfma_rate only: the same instruction on E2M1 (FP4) operands, 32
+ * values in the low 16 bytes of each lane's fragment, unit E8M0 scales */
+#define DMU_PROBE_MXFP4_32X32X64 5
 
 /*
  * Run ONE matrix instruction of `kind` on a single wave: D = A * B + C with
@@ -55,13 +58,15 @@ int dmu_probe_lds_load(const void* src, void* dst, int mode, int oob_from, void*
  * 4 waves (one wave per SIMD); each wave runs `iters` rounds of a 4 x 4 block
  * of 32x32 MFMAs, kind DMU_PROBE_BF16_32X32X16 (32768 FLOP each),
  * DMU_PROBE_FP8_32X32X64 (E4M3 x E4M3, 131072 FLOP each) or
- * DMU_PROBE_MXFP8_32X32X64 (the same with unit E8M0 scales), on operand
+ * DMU_PROBE_MXFP8_32X32X64 (the same with unit E8M0 scales) or
+ * DMU_PROBE_MXFP4_32X32X64 (E2M1 x E2M1, 131072 FLOP each), on operand
  * fragments read once from `src`: 8 fragments of 64 lanes x 16 bytes (BF16,
  * 8 KiB) or x 32 bytes (FP8, 16 KiB), fragments 0-3 for A and 4-7 for B.  The
  * values in `src` set the switching activity, hence the power drawn.
  * Lane l of wave w writes the sum of its 256 accumulator values to
  * out[w*64 + l] (grid * 256 floats; all-ones BF16 fragments give
- * 256 * 16 * iters, all-ones E4M3 256 * 64 * iters, with or without scales).
+ * 256 * 16 * iters, all-ones E4M3 256 * 64 * iters, with or without scales;
+ * E2M1 bytes 0x22 (two ones) the same).
  * Requires 1 <= iters <= 2^20 and 1 <= grid <= 65536, else
  * DMU_ERR_INVALID_ARG.  Total work: grid * 4 * 16 * iters instructions.
  */

@@ -143,3 +143,33 @@ def call_qmx(**kw):
 ])
 def test_quantize_mxfp8_rejects(kw):
     assert call_qmx(**kw) == dmu.DMU_ERR_INVALID_ARG
+
+
+def call_mx4(**kw):
+    a = dict(A=FAKE, lda=512, B=FAKE, ldb=512, sa=FAKE, ldsa=16, sb=FAKE, ldsb=16, C=None, ldc=0,
+             D=FAKE, ldd=64, d_dtype=1, M=64, N=64, K=512, stream=None)
+    a.update(kw)
+    return dmu.load_library().gemm_mxfp4(*a.values())
+
+
+@pytest.mark.parametrize("kw", [
+    dict(A=None), dict(B=None), dict(sa=None), dict(sb=None), dict(D=None), dict(K=256),
+    dict(K=768, lda=768, ldb=768), dict(lda=496), dict(lda=528), dict(ldsa=8), dict(ldsb=20),
+    dict(sa=FAKE + 4), dict(sb=FAKE + 8), dict(A=FAKE + 8), dict(M=0), dict(d_dtype=2),
+])
+def test_gemm_mxfp4_rejects(kw):
+    assert call_mx4(**kw) == dmu.DMU_ERR_INVALID_ARG
+
+
+def call_qmx4(**kw):
+    a = dict(X=FAKE, rows=64, cols=256, ldx=256, Q=FAKE, ldq=256, S=FAKE, lds=8, stream=None)
+    a.update(kw)
+    return dmu.load_library().quantize_mxfp4(*a.values())
+
+
+@pytest.mark.parametrize("kw", [
+    dict(X=None), dict(Q=None), dict(S=None), dict(rows=0), dict(cols=48, ldx=48, ldq=64),
+    dict(ldq=272), dict(ldq=224), dict(lds=7), dict(X=FAKE + 4), dict(Q=FAKE + 8),
+])
+def test_quantize_mxfp4_rejects(kw):
+    assert call_qmx4(**kw) == dmu.DMU_ERR_INVALID_ARG

@@ -82,8 +82,8 @@ def run_mx(A, B, fa, fb, SA, SB, out_dtype, C=None):
 
 def run_max_term(A, B, fa, fb, SA, SB, rows=None):
     """sum over 64-wide K runs of max_k |a_ik b_jk| with the MX scales"""
-    a = oracle.decode_fp8(A, fa) * np.repeat(oracle.decode_e8m0(SA), 32, axis=1)
-    b = oracle.decode_fp8(B, fb) * np.repeat(oracle.decode_e8m0(SB), 32, axis=1)
+    a = oracle.decode_elems(A, fa) * np.repeat(oracle.decode_e8m0(SA), 32, axis=1)
+    b = oracle.decode_elems(B, fb) * np.repeat(oracle.decode_e8m0(SB), 32, axis=1)
     if rows is not None:
         a = a[rows]
     M, K = a.shape
@@ -259,3 +259,130 @@ def test_gemm_mx_scale_fetch_paths(K, ld_extra, offset):
     tol = 1e-5 * S + 2.0 ** -12 * run_max_term(A, B, 0, 1, SA, SB) + 2.0 ** -8 * np.abs(Dref)
     bad = ~(np.abs(D - Dref) <= tol)
     assert not bad.any(), "%d outside the bound, first at %s" % (bad.sum(), np.argwhere(bad)[0])
+
+
+# ---------------------------------------------------------------- MXFP4 (E2M1)
+
+def gpu_quantize4(X):
+    rows, cols = X.shape
+    Q = empty_padded(rows, cols // 2, torch.uint8, 16)
+    S = empty_padded(rows, cols // 32, torch.uint8, 16)
+    Q.fill_(0xAA)
+    S.fill_(0xAA)
+    dmu.quantize_mxfp4(padded(X, 8), Q, S)
+    torch.cuda.synchronize()
+    return Q.cpu().numpy(), S.cpu().numpy()
+
+
+@pytest.mark.parametrize("shape", [(64, 512), (37, 96), (1, 32), (300, 4128)])
+def test_quantize_mxfp4_bit_exact(shape):
+    X, _ = wl.normal_with_outlier_rows(shape, 9, frac=0.05)
+    X = special_blocks(X)
+    if X.shape[1] >= 64 and X.shape[0] > 4:
+        X[4, 32:64] = np.float32([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 5.5] * 4)  # E2M1 ties
+    Q, S = gpu_quantize4(X)
+    Qr, Sr = oracle.quantize_mx(X, oracle.E2M1)
+    assert np.array_equal(S, Sr)
+    assert np.array_equal(Q, Qr)
+
+
+def test_quantize_mxfp4_4096_bit_exact():
+    X, _ = wl.normal_with_outlier_rows((4096, 4096), wl.SEED_A)
+    Q, S = gpu_quantize4(X)
+    Qr, Sr = oracle.quantize_mx(X, oracle.E2M1)
+    assert np.array_equal(S, Sr)
+    assert np.array_equal(Q, Qr)
+
+
+def run_mx4(A, B, SA, SB, out_dtype, C=None):
+    M, N = A.shape[0], B.shape[0]
+    out = empty_padded(M, N, out_dtype)
+    dmu.gemm_mxfp4(padded(A, 16), padded(B, 16), padded(SA, 16), padded(SB, 16), out,
+                   C=None if C is None else padded(C, 4))
+    torch.cuda.synchronize()
+    return out_to_f64(out)
+
+
+def fp4(X):
+    return oracle.pack_fp4(oracle.encode_fp4(X))
+
+
+def check4(A, B, SA, SB, out_dtype, C=None, rows=None, what=""):
+    D = run_mx4(A, B, SA, SB, out_dtype, C)
+    Dref, S = oracle.gemm_mx(A, B, 4, 4, SA, SB, C=C, rows=rows)
+    if rows is not None:
+        D = D[rows]
+    if C is not None:
+        S = S + np.abs(C if rows is None else C[rows])
+    tol = 1e-5 * S + 2.0 ** -12 * run_max_term(A, B, 4, 4, SA, SB, rows)
+    if out_dtype == torch.bfloat16:
+        tol = tol + 2.0 ** -8 * np.abs(Dref)
+    bad = ~(np.abs(D - Dref) <= tol)
+    if bad.any():
+        i = tuple(np.argwhere(bad)[0])
+        raise AssertionError("%s: %d of %d outside the bound; first %s: got %r ref %r tol %r"
+                             % (what, bad.sum(), bad.size, i, D[i], Dref[i], tol[i]))
+    return D, Dref
+
+
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_gemm_mxfp4_integer_exact(out_dtype):
+    M, N, K = 272, 288, 1024
+    A = fp4(wl.small_ints((M, K), 1) * 0.5)
+    B = fp4(wl.small_ints((N, K), 2) * 0.5)
+    SA, SB = cancelling_codes(M, N, K // 32, 5)
+    C = wl.small_ints((M, N), 4, -1000, 1000)
+    D = run_mx4(A, B, SA, SB, out_dtype, C)
+    Dref, _ = oracle.gemm_mx(A, B, 4, 4, SA, SB, C=C)
+    assert np.array_equal(D, round_out(Dref, out_dtype == torch.bfloat16))
+
+
+@pytest.mark.parametrize("shape", [(320, 264, 512), (1, 16, 512), (513, 600, 1536), (256, 256, 2560)])
+def test_gemm_mxfp4_random_codes(shape):
+    M, N, K = shape
+    rng = np.random.default_rng(13)
+    A = fp4(wl.normal((M, K), 1) * 3)
+    B = fp4(wl.normal((N, K), 2) * 3)
+    SA = rng.integers(116, 139, size=(M, K // 32)).astype(np.uint8)
+    SB = rng.integers(116, 139, size=(N, K // 32)).astype(np.uint8)
+    C = wl.normal((M, N), 3) if M == 320 else None
+    out = torch.float32 if M == 320 else torch.bfloat16
+    check4(A, B, SA, SB, out, C=C, what=str(shape))
+
+
+def test_gemm_mxfp4_gpu_quantized_pipeline():
+    M, N, K = 384, 320, 1024
+    Xa, _ = wl.normal_with_outlier_rows((M, K), 5, frac=0.03)
+    Xb = wl.normal((N, K), 6)
+    Qa, Sa = gpu_quantize4(Xa)
+    Qb, Sb = gpu_quantize4(Xb)
+    Qa_r, Sa_r = oracle.quantize_mx(Xa, oracle.E2M1)
+    Qb_r, Sb_r = oracle.quantize_mx(Xb, oracle.E2M1)
+    assert np.array_equal(Qa, Qa_r) and np.array_equal(Sa, Sa_r)
+    assert np.array_equal(Qb, Qb_r) and np.array_equal(Sb, Sb_r)
+    D, Dref = check4(Qa_r, Qb_r, Sa_r, Sb_r, torch.float32, what="fp4 pipeline")
+    total = Xa.astype(np.float64) @ Xb.astype(np.float64).T
+    print("MXFP4: rel-RMS from the sums %.3e, total %.3e"
+          % (oracle.rel_rms(D, Dref), oracle.rel_rms(D, total)))
+
+
+def test_gemm_mxfp4_nan_scale():
+    M, N, K = 300, 260, 512
+    A = fp4(wl.small_ints((M, K), 31) * 0.5)
+    B = fp4(wl.small_ints((N, K), 32) * 0.5)
+    SA = np.full((M, K // 32), 127, np.uint8)
+    SB = np.full((N, K // 32), 126, np.uint8)
+    SA[17, 9] = 255
+    SB[259, 3] = 255
+    D = run_mx4(A, B, SA, SB, torch.float32)
+    Dref, _ = oracle.gemm_mx(A, B, 4, 4, SA, SB)
+    assert np.array_equal(np.isnan(D), np.isnan(Dref))
+    assert np.isnan(D[17]).all() and np.isnan(D[:, 259]).all()
+    ok = ~np.isnan(Dref)
+    assert np.array_equal(D[ok], Dref[ok])
+
+
+def test_gemm_mxfp4_4096_sampled():
+    A, SA = oracle.quantize_mx(wl.normal((4096, 4096), wl.SEED_A), oracle.E2M1)
+    B, SB = oracle.quantize_mx(wl.normal((4096, 4096), wl.SEED_B), oracle.E2M1)
+    check4(A, B, SA, SB, torch.bfloat16, rows=sample_rows(4096), what="4096^3 MXFP4")

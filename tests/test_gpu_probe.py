@@ -143,7 +143,8 @@ def test_direct_to_lds_copy(mode, size, oob_from):
 
 @pytest.mark.parametrize("kind,k,one", [(dmu.PROBE_BF16_32X32X16, 16, 0x3F80),
                                         (dmu.PROBE_FP8_32X32X64, 64, 0x38),
-                                        (dmu.PROBE_MXFP8_32X32X64, 64, 0x38)])
+                                        (dmu.PROBE_MXFP8_32X32X64, 64, 0x38),
+                                        (dmu.PROBE_MXFP4_32X32X64, 64, 0x22)])
 def test_mfma_rate_probe_counts_every_instruction(kind, k, one):
     # All-ones fragments: every accumulator element gains k per round, so lane
     # sums are 256 * k * iters exactly (well inside FP32's exact integers).
@@ -198,12 +199,21 @@ def test_mfma_mx_layout_exact(shape, fa, fb, opsel):
     assert np.array_equal(D, ref)
 
 
+def mx_encode(X, fmt):
+    """FP32 -> MX element array: FP8 codes, or packed E2M1 (format 4)."""
+    if fmt == oracle.E2M1:
+        return oracle.pack_fp4(oracle.encode_fp4(X))
+    return oracle.encode_fp8(X, fmt)
+
+
+@pytest.mark.parametrize("fmt", [0, 4])
 @pytest.mark.parametrize("shape", [dmu.PROBE_MX_16X16X128, dmu.PROBE_MX_32X32X64])
-def test_mfma_mx_k_positions(shape):
+def test_mfma_mx_k_positions(shape, fmt):
     # one product 1 x 1 at K position k, block scales 2^g on A and 2^(4g) on
     # B: D = 2^(5 * (k // 32)) exactly when the unit scales K position k with
     # the codes of its own 32-wide block, which pins where each of a lane's
-    # bytes sits along K (unscaled instructions cannot show it)
+    # bytes (FP8) or nibbles (FP4) sits along K (unscaled instructions cannot
+    # show it)
     m, n, k = MX_SHAPES[shape]
     SA = np.tile((127 + np.arange(k // 32)).astype(np.uint8), (m, 1))
     SB = np.tile((127 + 4 * np.arange(k // 32)).astype(np.uint8), (n, 1))
@@ -213,11 +223,44 @@ def test_mfma_mx_k_positions(shape):
         Bf = np.zeros((n, k), np.float32)
         Af[:, kk] = 1.0
         Bf[:, kk] = 1.0
-        A, B = oracle.encode_fp8(Af, 0), oracle.encode_fp8(Bf, 0)
-        D = run_mx(shape, A, B, SA, SB, C)
-        ref, _ = oracle.gemm_mx(A, B, 0, 0, SA, SB)
+        A, B = mx_encode(Af, fmt), mx_encode(Bf, fmt)
+        D = run_mx(shape, A, B, SA, SB, C, fmt, fmt)
+        ref, _ = oracle.gemm_mx(A, B, fmt, fmt, SA, SB)
         assert np.all(ref == 2.0 ** (5 * (kk // 32)))
         assert np.array_equal(D, ref), "K position %d" % kk
+
+
+@pytest.mark.parametrize("fa,fb", [(4, 4), (4, 0), (0, 4)])
+@pytest.mark.parametrize("shape", [dmu.PROBE_MX_16X16X128, dmu.PROBE_MX_32X32X64])
+def test_mfma_mx_fp4_exact(shape, fa, fb):
+    # E2M1 (and E2M1 x E4M3) operands with values in {0, +-0.5, ..., +-2} and
+    # cancelling block codes: every sum is exact
+    m, n, k = MX_SHAPES[shape]
+    A = mx_encode(wl.small_ints((m, k), 61) * 0.5, fa)
+    B = mx_encode(wl.small_ints((n, k), 62) * 0.5, fb)
+    SA, SB = cancelling_codes(m, n, k // 32, 63)
+    C = wl.small_ints((m, n), 64, -50, 50)
+    D = run_mx(shape, A, B, SA, SB, C, fa, fb, 1)
+    ref, _ = oracle.gemm_mx(A, B, fa, fb, SA, SB, C=C)
+    assert np.array_equal(D, ref)
+
+
+@pytest.mark.parametrize("shape", [dmu.PROBE_MX_16X16X128, dmu.PROBE_MX_32X32X64])
+def test_mfma_mx_fp4_random_within_instruction_precision(shape):
+    m, n, k = MX_SHAPES[shape]
+    rng = np.random.default_rng(71)
+    A = mx_encode(wl.normal((m, k), 72) * 3, 4)
+    B = mx_encode(wl.normal((n, k), 73) * 3, 4)
+    SA = rng.integers(118, 137, size=(m, k // 32)).astype(np.uint8)
+    SB = rng.integers(118, 137, size=(n, k // 32)).astype(np.uint8)
+    C = wl.normal((m, n), 74)
+    D = run_mx(shape, A, B, SA, SB, C, 4, 4)
+    ref, S = oracle.gemm_mx(A, B, 4, 4, SA, SB, C=C)
+    a = oracle.decode_elems(A, 4) * np.repeat(oracle.decode_e8m0(SA), 32, axis=1)
+    b = oracle.decode_elems(B, 4) * np.repeat(oracle.decode_e8m0(SB), 32, axis=1)
+    max_term = np.abs(a[:, None, :] * b[None, :, :]).max(axis=2)
+    bound = 1e-5 * (S + np.abs(C)) + 2.0 ** -12 * max_term
+    assert np.all(np.abs(D - ref) <= bound)
 
 
 @pytest.mark.parametrize("shape", [dmu.PROBE_MX_16X16X128, dmu.PROBE_MX_32X32X64])
