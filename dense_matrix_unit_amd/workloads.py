@@ -14,6 +14,10 @@ Recipes (value distributions follow the pages' experiments):
     a few large rows, the case fine-grained FP8 scaling is for).
   * ``small_ints``: integers in [lo, hi], exact in BF16 and FP8, so that a
     product computed in any order is exact.
+  * ``expert_rows``: how many of ``total`` routed rows each of G experts gets
+    in one step: a multinomial draw with probabilities proportional to
+    exp(spread * z), z ~ N(0, 1) per expert (uneven load; some experts may
+    get none).
 Seeds: A = 1, B = 2 (the seeds of the handbook chapter's WMMA harness),
 outlier rows = 3.
 """
@@ -57,6 +61,14 @@ def small_ints(shape, seed: int, lo: int = -4, hi: int = 4) -> np.ndarray:
     return _rng(seed).integers(lo, hi + 1, size=shape).astype(np.float32)
 
 
+def expert_rows(G: int, total: int, seed: int, spread: float = 0.5) -> np.ndarray:
+    rng = _rng(seed)
+    w = np.exp(spread * rng.standard_normal(G))
+    return rng.multinomial(total, w / w.sum()).astype(np.int64)
+
+
+SEED_ROUTING = 4
+
 # The workloads: (name, M, N, K) with their input recipe.  B is stored N x K
 # ("column-major B") unless a row-major variant is named.
 WORKLOADS = {
@@ -67,6 +79,8 @@ WORKLOADS = {
                                      out="bf16"),
     "llm_28672x8192": dict(Ms=(16, 128, 1024, 8192), N=28672, K=8192, dist="normal",
                            out="bf16"),
+    "moe_bf16_32x16384x4096x7168": dict(G=32, total_rows=16384, N=4096, K=7168, dist="normal",
+                                        routing="expert_rows(spread 0.5, seed 4)", out="bf16"),
     "acc_sweep_256": dict(M=256, N=256, Ks=(256, 1024, 4096, 16384, 65536), dist="normal",
                           out="f32"),
 }

@@ -76,6 +76,9 @@ def lib():
         L.orc_gemm_fp8.argtypes = [p, i64, i32, p, i64, i32, p, p, i32, p, i64, i64, i64,
                                    i64, p, i64, p, p]
         L.orc_gemm_fp8.restype = i32
+        L.orc_gemm_grouped_bf16.argtypes = [p, i64, p, i64, i64, p, i64, i64, i64, p, i64, p,
+                                            p]
+        L.orc_gemm_grouped_bf16.restype = i32
         L.orc_encode_fp4_array.argtypes = [p, i64, p]
         L.orc_decode_fp4_array.argtypes = [p, i64, p]
         L.orc_decode_e8m0.argtypes = [ctypes.c_uint8]
@@ -281,6 +284,32 @@ def gemm_mx(A, B, fmt_a: int, fmt_b: int, SA, SB, C=None, rows=None):
                            _ptr(S))
     if rc != 0:
         raise ValueError("orc_gemm_mx: bad arguments")
+    return D, S
+
+
+def gemm_grouped_bf16(A, B, offsets, rows=None):
+    """FP64 grouped product (mixture of experts): rows offsets[g] ..
+    offsets[g+1]-1 of A ([M][K] BF16 codes) use expert g's weight B[g]
+    ([G][N][K] BF16 codes, stored N x K).  Returns (D, S) for the selected rows
+    (default: rows offsets[0] .. offsets[G]-1), one row of D per row."""
+    A = np.ascontiguousarray(A, dtype=np.uint16)
+    B = np.ascontiguousarray(B, dtype=np.uint16)
+    off = np.ascontiguousarray(offsets, dtype=np.int64)
+    G, N, K = B.shape
+    assert off.shape == (G + 1,) and A.shape[1] == K and off[-1] <= A.shape[0]
+    if rows is None:
+        r, nr = None, int(off[-1] - off[0])
+    else:
+        r = np.ascontiguousarray(rows, dtype=np.int64)
+        nr = r.size
+    D = np.empty((nr, N), dtype=np.float64)
+    S = np.empty((nr, N), dtype=np.float64)
+    if nr == 0:
+        return D, S
+    rc = lib().orc_gemm_grouped_bf16(_ptr(A), K, _ptr(B), K, N * K, _ptr(off), G, N, K, _ptr(r),
+                                     nr, _ptr(D), _ptr(S))
+    if rc != 0:
+        raise ValueError("orc_gemm_grouped_bf16: bad arguments")
     return D, S
 
 

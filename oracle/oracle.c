@@ -494,3 +494,49 @@ int orc_gemm_mx(const uint8_t* A, int64_t lda, int fmt_a, const uint8_t* B, int6
   }
   return bad ? -1 : 0;
 }
+
+/* ---------------------------------------------------------------- grouped (MoE) */
+
+/* Grouped product of a mixture-of-experts layer ("How Blackwell's Tensor
+ * Memory Actually Works", section "What this does to serving economics", the
+ * third consequence: each expert multiplies the rows routing sent it, so every
+ * expert's GEMM has its own M, which changes from step to step).  Rows
+ * off[g] .. off[g+1]-1 of A (row-major BF16, lda) belong to expert g, whose
+ * weight is the N x K BF16 matrix stored N x K (ldb) at B + g * stride_b;
+ * D[r][j] = sum_k A[r][k] * B_g[j][k] in FP64, k ascending; S the same sum of
+ * magnitudes.  off holds G + 1 non-decreasing entries, off[0] >= 0.  `rows`
+ * (nrows entries) selects which rows of A / D to compute, else all rows
+ * off[0] .. off[G]-1 (nrows is then ignored); a selected row outside every
+ * group is an error. */
+int orc_gemm_grouped_bf16(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
+                          int64_t stride_b, const int64_t* off, int64_t G, int64_t N, int64_t K,
+                          const int64_t* rows, int64_t nrows, double* D, double* S) {
+  if (G <= 0 || N <= 0 || K <= 0 || off[0] < 0) return -1;
+  for (int64_t g = 0; g < G; g++)
+    if (off[g + 1] < off[g]) return -1;
+  if (!rows) nrows = off[G] - off[0];
+  double* tab = (double*)malloc(65536 * sizeof(double));
+  if (!tab) return -2;
+  for (int h = 0; h < 65536; h++) tab[h] = orc_decode_bf16((uint16_t)h);
+  int bad = 0;
+#pragma omp parallel for schedule(dynamic)
+  for (int64_t q = 0; q < nrows; q++) {
+    const int64_t r = rows ? rows[q] : off[0] + q;
+    int64_t g = 0;
+    while (g < G && !(off[g] <= r && r < off[g + 1])) g++;
+    if (g == G) { bad = 1; continue; }
+    const uint16_t* Bg = B + g * stride_b;
+    for (int64_t j = 0; j < N; j++) {
+      double acc = 0.0, sacc = 0.0;
+      for (int64_t k = 0; k < K; k++) {
+        double p = tab[A[r * lda + k]] * tab[Bg[j * ldb + k]];
+        acc += p;
+        sacc += fabs(p);
+      }
+      D[q * N + j] = acc;
+      if (S) S[q * N + j] = sacc;
+    }
+  }
+  free(tab);
+  return bad ? -1 : 0;
+}
