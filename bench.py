@@ -167,6 +167,31 @@ class Bench:
         bytes_ = 1.0 * (M * K + N * K) + 2.0 * M * N + 4.0 * (sa.numel() + sb.numel())
         return self.report(t, flop, bytes_, PEAK_FP8_TFLOPS, copies)
 
+    def grouped_leg(self, steps, warmup):
+        """Mixture-of-experts grouped BF16 product: 32 experts, 16384 routed
+        rows split by expert_rows (seed 4), N = 4096, K = 7168; the row offsets
+        are a device array, as routing leaves them."""
+        torch, dmu = self.torch, self.dmu
+        w = self.wl.WORKLOADS["moe_bf16_32x16384x4096x7168"]
+        G, N, K, T = w["G"], w["N"], w["K"], w["total_rows"]
+        counts = self.wl.expert_rows(G, T, self.wl.SEED_ROUTING)
+        offs = torch.zeros(G + 1, dtype=torch.int64, device=self.dev)
+        offs[1:] = torch.cumsum(torch.from_numpy(counts).to(self.dev), 0)
+        A = self.normal_bf16((T, K), 1)
+        B = self.normal_bf16((G * N, K), 2).view(G, N, K)
+        out = torch.empty((T, N), dtype=torch.bfloat16, device=self.dev)
+
+        def launch(i):
+            dmu.gemm_grouped_bf16(A, B, offs, out)
+
+        t = time_launches(torch, launch, steps, warmup)
+        flop = 2.0 * T * N * K
+        bytes_ = 2.0 * (T * K + G * N * K + T * N)
+        r = self.report(t, flop, bytes_, PEAK_BF16_TFLOPS, 1)
+        r["experts"] = G
+        r["rows_per_expert_min_max"] = [int(counts.min()), int(counts.max())]
+        return r
+
     def gemm_mx_leg(self, M, N, K, fmt, steps, warmup, copies=1):
         """Microscaled FP8: operands quantized by quantize_mxfp8 (one E8M0
         scale per row and 32 K), product by gemm_mxfp8."""
@@ -407,6 +432,9 @@ def main():
     if want("mxfp8_e4m3_4096"):
         legs["mxfp8_e4m3_4096"] = b.gemm_mx_leg(4096, 4096, 4096, dmu.E4M3, S, W, copies=10)
         log("mxfp8 e4m3 4096: %s" % legs["mxfp8_e4m3_4096"])
+    if want("moe_bf16_32x16384x4096x7168"):
+        legs["moe_bf16_32x16384x4096x7168"] = b.grouped_leg(S4, W4)
+        log("moe grouped: %s" % legs["moe_bf16_32x16384x4096x7168"])
     if want("mxfp4_4096"):
         legs["mxfp4_4096"] = b.gemm_mxfp4_leg(4096, 4096, 4096, S, W, copies=10)
         log("mxfp4 4096: %s" % legs["mxfp4_4096"])

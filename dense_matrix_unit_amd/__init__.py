@@ -51,6 +51,8 @@ SYMBOLS = {
     "gemm_fp8_scaled": (_I, [_P, _I64, _I, _P, _I64, _I, _P, _P, _I, _P, _I64, _P, _I64, _I,
                              _I64, _I64, _I64, _P]),
     "quantize_fp8": (_I, [_P, _I64, _I64, _I64, _I, _I64, _I64, _P, _I64, _P, _P]),
+    "gemm_grouped_bf16": (_I, [_P, _I64, _P, _I64, _I64, _P, _I64, _P, _I64, _I, _I64, _I64,
+                               _I64, _P]),
     "gemm_mxfp8": (_I, [_P, _I64, _I, _P, _I64, _I, _P, _I64, _P, _I64, _P, _I64, _P, _I64, _I,
                         _I64, _I64, _I64, _P]),
     "quantize_mxfp8": (_I, [_P, _I64, _I64, _I64, _I, _P, _I64, _P, _I64, _P]),
@@ -155,6 +157,34 @@ def gemm_bf16(A, B, out, b_layout: int = B_COL_MAJOR, C=None, stream=None):
         _dev_ptr(out, "out"), _ld(out, "out"),
         OUT_F32 if out.dtype == torch.float32 else OUT_BF16, M, N, K, _stream(stream))
     _check("gemm_bf16", rc)
+    return out
+
+
+def gemm_grouped_bf16(A, B, offsets, out, stream=None):
+    """Mixture-of-experts grouped product: out[r] = A[r] @ B[g].T for rows r in
+    [offsets[g], offsets[g+1]).  A: [max_m, K] BF16; B: [G, N, K] BF16 (each
+    expert's weight stored N x K); offsets: int64 GPU tensor [G+1] (read on the
+    device); out: [max_m, N] float32 or bfloat16 (rows outside every expert's
+    range are left as they are)."""
+    torch = _torch()
+    bf = (torch.bfloat16, torch.int16, torch.uint16)
+    _check_dtype(A, bf, "A")
+    _check_dtype(B, bf, "B")
+    _check_dtype(offsets, (torch.int64,), "offsets")
+    _check_dtype(out, (torch.float32, torch.bfloat16), "out")
+    if B.dim() != 3 or B.stride(2) != 1 or B.stride(1) < B.shape[2]:
+        raise ValueError("B must be [G, N, K] with unit K stride")
+    G, N, K = B.shape
+    max_m = A.shape[0]
+    if A.shape[1] != K or tuple(out.shape) != (max_m, N):
+        raise ValueError("shape mismatch")
+    if offsets.numel() != G + 1 or not offsets.is_contiguous():
+        raise ValueError("offsets needs G + 1 contiguous entries")
+    rc = load_library().gemm_grouped_bf16(
+        _dev_ptr(A, "A"), _ld(A, "A"), _dev_ptr(B, "B"), B.stride(1), B.stride(0),
+        _dev_ptr(offsets, "offsets"), G, _dev_ptr(out, "out"), _ld(out, "out"),
+        OUT_F32 if out.dtype == torch.float32 else OUT_BF16, max_m, N, K, _stream(stream))
+    _check("gemm_grouped_bf16", rc)
     return out
 
 

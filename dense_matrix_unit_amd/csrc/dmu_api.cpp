@@ -55,6 +55,29 @@ int gemm_bf16(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, in
   return finish(dmu::launch_gemm_bf16(a, b_layout == DMU_B_COL_MAJOR, (hipStream_t)stream));
 }
 
+int gemm_grouped_bf16(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
+                      int64_t stride_b, const int64_t* offsets, int64_t groups, void* D,
+                      int64_t ldd, int d_dtype, int64_t max_m, int64_t N, int64_t K,
+                      void* stream) {
+  int rc = check_out(nullptr, 0, D, ldd, d_dtype, max_m, N);
+  if (rc) return rc;
+  if (!A || !B || !offsets || groups < 1 || groups > 65536) return DMU_ERR_INVALID_ARG;
+  if (K < 8 || K % 8 || K > INT32_MAX) return DMU_ERR_INVALID_ARG;
+  if (lda < K || ldb < K || (lda * 2) % 16 || (ldb * 2) % 16) return DMU_ERR_INVALID_ARG;
+  if (stride_b < N * ldb || (stride_b * 2) % 16) return DMU_ERR_INVALID_ARG;
+  if (!aligned(A, 16) || !aligned(B, 16) || !aligned(offsets, 8)) return DMU_ERR_INVALID_ARG;
+  if (kTileRows * lda * 2 >= kMaxTileBytes || kTileRows * ldb * 2 >= kMaxTileBytes)
+    return DMU_ERR_UNSUPPORTED;
+  dmu::GemmArgs a{A, B, nullptr, D, lda, ldb, 0, ldd, max_m, N, K, nullptr, nullptr,
+                  d_dtype == DMU_OUT_BF16};
+  a.goff = offsets;
+  a.G = groups;
+  a.gstride = stride_b;
+  a.Mmax = max_m;
+  (void)hipGetLastError();
+  return finish(dmu::launch_gemm_grouped_bf16(a, (hipStream_t)stream));
+}
+
 int gemm_fp8_scaled(const uint8_t* A, int64_t lda, int fmt_a, const uint8_t* B, int64_t ldb,
                     int fmt_b, const float* scale_a, const float* scale_b, int scale_mode,
                     const float* C, int64_t ldc, void* D, int64_t ldd, int d_dtype, int64_t M,

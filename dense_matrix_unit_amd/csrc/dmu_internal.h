@@ -21,15 +21,23 @@ struct GemmArgs {
   const uint8_t* xa = nullptr;
   const uint8_t* xb = nullptr;
   int64_t ldxa = 0, ldxb = 0;  // bytes per scale row
+  // grouped (mixture of experts): rows goff[g] .. goff[g+1]-1 of A and D use
+  // the weight at B + g * gstride (elements); every offset is clamped to
+  // [0, Mmax], the rows A and D hold
+  const int64_t* goff = nullptr;
+  int64_t G = 0, gstride = 0, Mmax = 0;
 };
 
 // kMX / kMX4: MXFP8, scales fetched one / four K slices at a time;
 // kMXF4: MXFP4 (E2M1 x E2M1, row strides in bytes), scales two slices at a time
-enum GemmKind { kBF16 = 0, kFP8Tensor = 1, kFP8Block = 2, kMX = 3, kMX4 = 4, kMXF4 = 5 };
+// kBF16G: BF16 grouped over experts (B stored N x K per expert)
+enum GemmKind { kBF16 = 0, kFP8Tensor = 1, kFP8Block = 2, kMX = 3, kMX4 = 4, kMXF4 = 5,
+                kBF16G = 6 };
 
 // Launchers: argument checking is done by the caller; these only pick a
 // kernel configuration and launch it.  They return a hipError_t.
 hipError_t launch_gemm_bf16(const GemmArgs& a, int b_col_major, hipStream_t s);
+hipError_t launch_gemm_grouped_bf16(const GemmArgs& a, hipStream_t s);
 // Skinny-M BF16 path (M <= 128, B stored N x K): HBM-bound streaming of B.
 bool skinny_applies(const GemmArgs& a);
 hipError_t launch_gemm_bf16_skinny(const GemmArgs& a, hipStream_t s);

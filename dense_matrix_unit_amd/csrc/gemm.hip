@@ -69,7 +69,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
 gemm_kernel(GemmArgs p) {
   constexpr int NT = NW * 64;   // threads; NW waves in a 2 x (NW/2) grid
   constexpr bool F4 = KIND == kMXF4;  // E2M1 operands: 32 bytes of a row per K step of 64
-  constexpr int ESZ = KIND == kBF16 ? 2 : 1;
+  constexpr bool GRP = KIND == kBF16G;                // grouped over experts
+  constexpr bool BF = KIND == kBF16 || GRP;            // BF16 operands
+  constexpr int ESZ = BF ? 2 : 1;
   constexpr int CPR = RB / 16;  // 16-byte chunks per LDS row
   constexpr int WM = BM / 2, WN = BN / (NW / 2);
   constexpr int TM = WM / 32, TN = WN / 32;      // 32x32 sub-tiles per wave
@@ -84,7 +86,7 @@ gemm_kernel(GemmArgs p) {
   constexpr int XBUF = (BM + BN) * XROW;        // one ring buffer (A rows, then B rows)
   constexpr int XOFF = S * STAGE;               // ring offset in LDS
   constexpr int XR = MX ? 2 * XBUF : 0;
-  constexpr int NSTEP = KIND == kBF16 || F4 ? RB / 32 : RB / 64;  // MFMA K-steps per slice
+  constexpr int NSTEP = BF || F4 ? RB / 32 : RB / 64;  // MFMA K-steps per slice
   constexpr int NLA = BM * CPR / NT;                 // A copies per thread per slice
   constexpr int NLB = BROW ? 8 : BN * CPR / NT;      // B copies per thread per slice
   constexpr int NLS = MX ? 2 : 0;                    // MX scale-group copies (A, B)
@@ -92,7 +94,7 @@ gemm_kernel(GemmArgs p) {
   static_assert(BM % 64 == 0 && BN % 64 == 0 && (BM * CPR) % NT == 0, "tile");
   static_assert(!BROW || (KIND == kBF16 && BN == 256 && RB == 128 && S == 2 && NW == 4),
                 "row-major B staging");
-  static_assert(KIND == kBF16 || KIND == kFP8Tensor || MX,
+  static_assert(BF || KIND == kFP8Tensor || MX,
                 "per-block FP32 scales live in gemm_block.hip");
   static_assert(!MX || (!KT && !BROW && RB == 128 && NW == 4 && BM == 256 && BN == 256 && S == 2),
                 "MX: whole 128-K slices, one scale row per thread and operand");
@@ -109,10 +111,34 @@ gemm_kernel(GemmArgs p) {
   const int swave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, kept scalar
   const int wm = swave / (NW / 2), wn = swave % (NW / 2);
   const int rl = lane & 31, hl = lane >> 5;
-  const int tiles_m = (int)((p.M + BM - 1) / BM), tiles_n = (int)((p.N + BN - 1) / BN);
+  // grouped: an upper bound of the experts' m-tile count, sum ceil(M_g / BM)
+  const int tiles_m = GRP ? (int)((p.Mmax + BM - 1) / BM + p.G) : (int)((p.M + BM - 1) / BM);
+  const int tiles_n = (int)((p.N + BN - 1) / BN);
   int tm, tn;
   tile_coords<kGroupM>(tiles_m, tiles_n, tm, tn);
-  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+  int64_t m0 = (int64_t)tm * BM;
+  if constexpr (GRP) {
+    // m-tile tm is tile t of expert g: walk the experts' tile counts (row
+    // offsets written by routing on the device, read with scalar loads).
+    // Offsets are clamped to [0, Mmax] and made non-decreasing, so no
+    // workgroup touches rows outside A and D whatever they hold.
+    int64_t lo = min(max(p.goff[0], (int64_t)0), p.Mmax);
+    int t = tm, g = 0;
+    for (; g < p.G; ++g) {
+      const int64_t hi = min(max(p.goff[g + 1], lo), p.Mmax);
+      const int nt = (int)((hi - lo + BM - 1) / BM);
+      if (t < nt) {
+        m0 = lo + (int64_t)t * BM;
+        p.M = hi;  // the expert's last row bounds this tile's loads and stores
+        break;
+      }
+      t -= nt;
+      lo = hi;
+    }
+    if (g == p.G) return;  // past the last expert's tiles: the whole workgroup exits
+    p.B = (const uint16_t*)p.B + g * p.gstride;
+  }
+  const int64_t n0 = (int64_t)tn * BN;
   const int64_t kbytes = F4 ? p.K / 2 : p.K * ESZ;
   const int nkt = (int)((kbytes + RB - 1) / RB);
 
@@ -347,7 +373,7 @@ gemm_kernel(GemmArgs p) {
   stage_barrier();
 
   {
-    constexpr int CPL = KIND == kBF16 || F4 ? 1 : 2;  // 16-byte chunks per lane per step
+    constexpr int CPL = BF || F4 ? 1 : 2;  // 16-byte chunks per lane per step
     f32x16_t acc[TM][TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i)
@@ -431,7 +457,7 @@ gemm_kernel(GemmArgs p) {
     // holds a transposed 32x32 sub-tile (see the epilogue).
     auto mfma_one = [&](int s, int i, int j) __attribute__((always_inline)) {
       const int buf = s & 1;
-      if constexpr (KIND == kBF16)
+      if constexpr (BF)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
             __builtin_bit_cast(bf16x8_t, fb[buf][j][0]),
             __builtin_bit_cast(bf16x8_t, fa[buf][i][0]), acc[i][j], 0, 0, 0);
@@ -639,11 +665,12 @@ gemm_kernel(GemmArgs p) {
 template <int KIND, int FA, int FB, bool BROW, int BM, int BN, int RB, int S, int G, int PD = 0,
           int NW = 4>
 hipError_t launch(const GemmArgs& a, hipStream_t s) {
-  const int64_t tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
+  const int64_t tiles_m = KIND == kBF16G ? (a.Mmax + BM - 1) / BM + a.G : (a.M + BM - 1) / BM;
+  const int64_t tiles = tiles_m * ((a.N + BN - 1) / BN);
   // K tail: the last slice is partial and its lanes are range-checked one by
   // one (MX requires whole slices and has no such variant)
   if constexpr (KIND != kMX && KIND != kMX4 && KIND != kMXF4) {
-    if ((a.K * (KIND == kBF16 ? 2 : 1)) % RB != 0) {
+    if ((a.K * (KIND == kBF16 || KIND == kBF16G ? 2 : 1)) % RB != 0) {
       hipLaunchKernelGGL((gemm_kernel<KIND, FA, FB, BROW, BM, BN, RB, S, G, PD, NW, true>),
                          dim3((unsigned)tiles), dim3(NW * 64), 0, s, a);
       return hipGetLastError();
@@ -655,6 +682,10 @@ hipError_t launch(const GemmArgs& a, hipStream_t s) {
 }
 
 }  // namespace
+
+hipError_t launch_gemm_grouped_bf16(const GemmArgs& a, hipStream_t s) {
+  return launch<kBF16G, 0, 0, false, 256, 256, 128, 2, 4, kPrefetch, kWavesBF16>(a, s);
+}
 
 hipError_t launch_gemm_bf16(const GemmArgs& a, int b_col_major, hipStream_t s) {
   if (b_col_major && skinny_applies(a)) return launch_gemm_bf16_skinny(a, s);

@@ -83,6 +83,37 @@ int gemm_bf16(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, in
               int64_t N, int64_t K, void* stream);
 
 /*
+ * gemm_grouped_bf16: one launch for the experts of a mixture-of-experts layer,
+ * each with its own number of rows ("How Blackwell's Tensor Memory Actually
+ * Works", section "What this does to serving economics": each expert's M is
+ * set by routing and changes from step to step).
+ *
+ *   A       : max_m x K BF16, row-major, lda; rows offsets[g] .. offsets[g+1]-1
+ *             are the rows routed to expert g.
+ *   B       : the experts' weights, each N x K BF16 stored N x K ("col-major"),
+ *             leading dimension ldb; expert g's weight starts at B + g * stride_b
+ *             (elements; stride_b >= N * ldb).
+ *   offsets : DEVICE array of groups + 1 int64 row offsets, as routing writes
+ *             them, read by the kernel (no host synchronisation).  Expected
+ *             non-decreasing with offsets[0] >= 0 and offsets[groups] <= max_m;
+ *             the kernel clamps every entry to [0, max_m] and to at least the
+ *             entry before it, so no value makes it touch rows outside A or D.
+ *   D       : max_m x N output, FP32 or BF16 (d_dtype), ldd.  D[r] = A[r] * B_g^T
+ *             for r in expert g's range; rows outside every range are not
+ *             written.
+ *   groups in 1..65536; max_m >= 1 bounds the launch (max_m / 256 + groups
+ *   row tiles); N >= 1; K >= 8, K % 8 == 0.
+ * Accumulation and rounding are those of gemm_bf16.
+ * Errors: DMU_ERR_INVALID_ARG for null pointers, sizes, strides or alignment
+ * (A, B, D 16-byte aligned, offsets 8-byte aligned, stride_b * 2 a multiple
+ * of 16).
+ */
+int gemm_grouped_bf16(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
+                      int64_t stride_b, const int64_t* offsets, int64_t groups, void* D,
+                      int64_t ldd, int d_dtype, int64_t max_m, int64_t N, int64_t K,
+                      void* stream);
+
+/*
  * gemm_fp8_scaled: D = dequantised(A) * dequantised(B) (+ C) with FP8 inputs
  * and FP32 accumulation.
  *

@@ -173,3 +173,19 @@ def call_qmx4(**kw):
 ])
 def test_quantize_mxfp4_rejects(kw):
     assert call_qmx4(**kw) == dmu.DMU_ERR_INVALID_ARG
+
+
+def call_grouped(**kw):
+    a = dict(A=FAKE, lda=64, B=FAKE, ldb=64, stride_b=64 * 64, off=FAKE, G=4, D=FAKE, ldd=64,
+             d_dtype=1, max_m=256, N=64, K=64, stream=None)
+    a.update(kw)
+    return dmu.load_library().gemm_grouped_bf16(*a.values())
+
+
+@pytest.mark.parametrize("kw", [
+    dict(A=None), dict(B=None), dict(off=None), dict(D=None), dict(G=0), dict(G=70000),
+    dict(K=12), dict(lda=60), dict(ldb=60), dict(stride_b=64 * 63), dict(stride_b=64 * 64 + 4),
+    dict(off=FAKE + 4), dict(A=FAKE + 2), dict(max_m=0), dict(N=0), dict(d_dtype=7),
+])
+def test_gemm_grouped_rejects(kw):
+    assert call_grouped(**kw) == dmu.DMU_ERR_INVALID_ARG
