@@ -79,6 +79,8 @@ def lib():
         L.orc_gemm_grouped_bf16.argtypes = [p, i64, p, i64, i64, p, i64, i64, i64, p, i64, p,
                                             p]
         L.orc_gemm_grouped_bf16.restype = i32
+        L.orc_epilogue.argtypes = [p, i64, i64, ctypes.c_double, p, i32, p]
+        L.orc_epilogue.restype = i32
         L.orc_encode_fp4_array.argtypes = [p, i64, p]
         L.orc_decode_fp4_array.argtypes = [p, i64, p]
         L.orc_decode_e8m0.argtypes = [ctypes.c_uint8]
@@ -311,6 +313,24 @@ def gemm_grouped_bf16(A, B, offsets, rows=None):
     if rc != 0:
         raise ValueError("orc_gemm_grouped_bf16: bad arguments")
     return D, S
+
+
+ACT_NONE, ACT_RELU, ACT_GELU, ACT_SILU = 0, 1, 2, 3
+
+
+def epilogue(D, alpha: float = 1.0, bias=None, act: int = ACT_NONE) -> np.ndarray:
+    """Y = act(alpha * D + bias) in FP64 for FP64 products D [rows][N]; bias
+    float32 [N] or None."""
+    D = np.ascontiguousarray(D, dtype=np.float64)
+    rows, N = D.shape
+    if bias is not None:
+        bias = np.ascontiguousarray(bias, dtype=np.float32)
+        assert bias.shape == (N,)
+    Y = np.empty_like(D)
+    rc = lib().orc_epilogue(_ptr(D), rows, N, float(alpha), _ptr(bias), act, _ptr(Y))
+    if rc != 0:
+        raise ValueError("orc_epilogue: bad arguments")
+    return Y
 
 
 # ------------------------------------------------------------------ metrics

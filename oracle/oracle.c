@@ -540,3 +540,28 @@ int orc_gemm_grouped_bf16(const uint16_t* A, int64_t lda, const uint16_t* B, int
   free(tab);
   return bad ? -1 : 0;
 }
+
+/* ---------------------------------------------------------------- fused epilogue */
+
+/* The epilogue applied to the accumulator while it is still at hand ("How
+ * Blackwell's Tensor Memory Actually Works", section "The cost of getting the
+ * answer back": scale it, add a bias, apply an activation, cast down):
+ * Y[i][j] = act(alpha * D[i][j] + bias[j]) in FP64 for a rows x N block of
+ * FP64 products (bias may be NULL).  act: 0 none; 1 ReLU, x > 0 ? x : 0 (so
+ * NaN gives 0); 2 GELU, x * Phi(x) with Phi the standard normal distribution
+ * function 0.5 * (1 + erf(x / sqrt 2)); 3 SiLU, x / (1 + exp(-x)).  The cast
+ * is left to the caller. */
+int orc_epilogue(const double* D, int64_t rows, int64_t N, double alpha, const float* bias,
+                 int act, double* Y) {
+  if (rows < 0 || N <= 0 || act < 0 || act > 3) return -1;
+  for (int64_t i = 0; i < rows; i++) {
+    for (int64_t j = 0; j < N; j++) {
+      double x = alpha * D[i * N + j] + (bias ? (double)bias[j] : 0.0);
+      if (act == 1) x = x > 0.0 ? x : 0.0;
+      else if (act == 2) x = x * 0.5 * (1.0 + erf(x / sqrt(2.0)));
+      else if (act == 3) x = x / (1.0 + exp(-x));
+      Y[i * N + j] = x;
+    }
+  }
+  return 0;
+}
