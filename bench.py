@@ -167,6 +167,38 @@ class Bench:
         bytes_ = 1.0 * (M * K + N * K) + 2.0 * M * N + 4.0 * (sa.numel() + sb.numel())
         return self.report(t, flop, bytes_, PEAK_FP8_TFLOPS, copies)
 
+    def fused_leg(self, kind, steps, warmup, copies):
+        """4096^3 with the fused epilogue: "bf16_gelu" (BF16 in, + bias, GELU,
+        BF16 out) or "fp8_relu_fp8out" (per-tensor E4M3 in, + bias, ReLU, E4M3
+        out with a static scale)."""
+        torch, dmu = self.torch, self.dmu
+        M = N = K = 4096
+        bias = self.normal_f32((N,), 3)
+        if kind == "bf16_gelu":
+            As = self.copies(self.normal_bf16((M, K), 1), copies)
+            Bs = self.copies(self.normal_bf16((N, K), 2), copies)
+            out = torch.empty((M, N), dtype=torch.bfloat16, device=self.dev)
+
+            def launch(i):
+                dmu.gemm_bf16_fused(As[i % copies], Bs[i % copies], out, dmu.B_COL_MAJOR, bias,
+                                    dmu.ACT_GELU)
+            peak, ab = PEAK_BF16_TFLOPS, 2.0
+        else:
+            Xa, Xb, Qa, Qb, sa, sb = self.fp8_operands(M, N, K, dmu.E4M3)
+            del Xa, Xb
+            Qas, Qbs = self.copies(Qa, copies), self.copies(Qb, copies)
+            out = torch.empty((M, N), dtype=torch.uint8, device=self.dev)
+            ds = torch.full((1,), 0.25, dtype=torch.float32, device=self.dev)
+
+            def launch(i):
+                dmu.gemm_fp8_fused(Qas[i % copies], Qbs[i % copies], sa, sb, out, dmu.E4M3,
+                                   dmu.E4M3, bias, dmu.ACT_RELU, dmu.E4M3, ds)
+            peak, ab = PEAK_FP8_TFLOPS, 1.0
+        t = time_launches(torch, launch, steps, warmup)
+        flop = 2.0 * M * N * K
+        bytes_ = ab * (M * K + N * K) + (2.0 if kind == "bf16_gelu" else 1.0) * M * N + 4.0 * N
+        return self.report(t, flop, bytes_, peak, copies)
+
     def grouped_leg(self, steps, warmup):
         """Mixture-of-experts grouped BF16 product: 32 experts, 16384 routed
         rows split by expert_rows (seed 4), N = 4096, K = 7168; the row offsets
@@ -432,6 +464,12 @@ def main():
     if want("mxfp8_e4m3_4096"):
         legs["mxfp8_e4m3_4096"] = b.gemm_mx_leg(4096, 4096, 4096, dmu.E4M3, S, W, copies=10)
         log("mxfp8 e4m3 4096: %s" % legs["mxfp8_e4m3_4096"])
+    if want("bf16_4096_bias_gelu"):
+        legs["bf16_4096_bias_gelu"] = b.fused_leg("bf16_gelu", S, W, 6)
+        log("bf16 4096 + bias + GELU: %s" % legs["bf16_4096_bias_gelu"])
+    if want("fp8_e4m3_4096_bias_relu_fp8out"):
+        legs["fp8_e4m3_4096_bias_relu_fp8out"] = b.fused_leg("fp8_relu_fp8out", S, W, 10)
+        log("fp8 4096 + bias + ReLU -> E4M3: %s" % legs["fp8_e4m3_4096_bias_relu_fp8out"])
     if want("moe_bf16_32x16384x4096x7168"):
         legs["moe_bf16_32x16384x4096x7168"] = b.grouped_leg(S4, W4)
         log("moe grouped: %s" % legs["moe_bf16_32x16384x4096x7168"])

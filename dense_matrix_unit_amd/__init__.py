@@ -37,6 +37,9 @@ PROBE_FP8_16X16X128 = 2
 PROBE_FP8_32X32X64 = 3
 PROBE_MXFP8_32X32X64 = 4  # rate probe only: scaled form, unit E8M0 scales
 PROBE_MXFP4_32X32X64 = 5  # rate probe only: E2M1 operands, unit E8M0 scales
+OUT_FP8_E4M3 = 2  # fused entry points: FP8 output with a dequantisation scale
+OUT_FP8_E5M2 = 3
+ACT_NONE, ACT_RELU, ACT_GELU, ACT_SILU = 0, 1, 2, 3
 MX_BLOCK = 32  # values of K per E8M0 scale (DMU_MX_BLOCK)
 E2M1 = 4  # FP4 elements of MXFP4 (DMU_FP4_E2M1), packed two per byte
 PROBE_MX_16X16X128 = 0  # shapes of dmu_probe_mfma_mx
@@ -51,6 +54,10 @@ SYMBOLS = {
     "gemm_fp8_scaled": (_I, [_P, _I64, _I, _P, _I64, _I, _P, _P, _I, _P, _I64, _P, _I64, _I,
                              _I64, _I64, _I64, _P]),
     "quantize_fp8": (_I, [_P, _I64, _I64, _I64, _I, _I64, _I64, _P, _I64, _P, _P]),
+    "gemm_bf16_fused": (_I, [_P, _I64, _P, _I64, _I, _P, _I, _P, _I64, _I, _P, _I64, _I64, _I64,
+                             _P]),
+    "gemm_fp8_fused": (_I, [_P, _I64, _I, _P, _I64, _I, _P, _P, _P, _I, _P, _I64, _I, _P, _I64,
+                            _I64, _I64, _P]),
     "gemm_grouped_bf16": (_I, [_P, _I64, _P, _I64, _I64, _P, _I64, _P, _I64, _I, _I64, _I64,
                                _I64, _P]),
     "gemm_mxfp8": (_I, [_P, _I64, _I, _P, _I64, _I, _P, _I64, _P, _I64, _P, _I64, _P, _I64, _I,
@@ -64,6 +71,7 @@ SYMBOLS = {
     "dmu_probe_mfma": (_I, [_I, _I, _I, _P, _P, _P, _P, _P]),
     "dmu_probe_lds_load": (_I, [_P, _P, _I, _I, _P]),
     "dmu_probe_mfma_rate": (_I, [_I, _P, _I, _I, _P, _P]),
+    "dmu_probe_cvt_fp8": (_I, [_P, _I64, _I, _I, _P, _P]),
     "dmu_probe_mfma_mx": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P]),
 }
 
@@ -157,6 +165,69 @@ def gemm_bf16(A, B, out, b_layout: int = B_COL_MAJOR, C=None, stream=None):
         _dev_ptr(out, "out"), _ld(out, "out"),
         OUT_F32 if out.dtype == torch.float32 else OUT_BF16, M, N, K, _stream(stream))
     _check("gemm_bf16", rc)
+    return out
+
+
+def _fused_out(out, out_fmt, out_scale, bias, N):
+    """(d_dtype, d_scale pointer, bias pointer) of a fused call."""
+    torch = _torch()
+    if out.dtype == torch.uint8:
+        if out_fmt not in (E4M3, E5M2) or out_scale is None:
+            raise ValueError("FP8 output needs out_fmt (E4M3/E5M2) and out_scale")
+        _check_dtype(out_scale, (torch.float32,), "out_scale")
+        dt = OUT_FP8_E4M3 if out_fmt == E4M3 else OUT_FP8_E5M2
+        sp = _dev_ptr(out_scale, "out_scale")
+    else:
+        _check_dtype(out, (torch.float32, torch.bfloat16), "out")
+        dt = OUT_F32 if out.dtype == torch.float32 else OUT_BF16
+        sp = None
+    bp = None
+    if bias is not None:
+        _check_dtype(bias, (torch.float32,), "bias")
+        if bias.numel() != N or not bias.is_contiguous():
+            raise ValueError("bias needs N contiguous floats")
+        bp = _dev_ptr(bias, "bias")
+    return dt, sp, bp
+
+
+def gemm_bf16_fused(A, B, out, b_layout: int = B_COL_MAJOR, bias=None, act: int = ACT_NONE,
+                    out_fmt=None, out_scale=None, stream=None):
+    """out = cast(act(A @ B + bias)).  A, B as gemm_bf16; bias float32 [N] or
+    None; out float32, bfloat16, or uint8 FP8 codes (out_fmt E4M3/E5M2 with
+    out_scale, a one-float GPU tensor: out ~ decode(q) * out_scale)."""
+    torch = _torch()
+    bf = (torch.bfloat16, torch.int16, torch.uint16)
+    _check_dtype(A, bf, "A")
+    _check_dtype(B, bf, "B")
+    M, K = A.shape
+    N = B.shape[1] if b_layout == B_ROW_MAJOR else B.shape[0]
+    if tuple(out.shape) != (M, N):
+        raise ValueError("out shape")
+    dt, sp, bp = _fused_out(out, out_fmt, out_scale, bias, N)
+    rc = load_library().gemm_bf16_fused(
+        _dev_ptr(A, "A"), _ld(A, "A"), _dev_ptr(B, "B"), _ld(B, "B"), b_layout, bp, act,
+        _dev_ptr(out, "out"), _ld(out, "out"), dt, sp, M, N, K, _stream(stream))
+    _check("gemm_bf16_fused", rc)
+    return out
+
+
+def gemm_fp8_fused(A, B, scale_a, scale_b, out, fmt_a: int = E4M3, fmt_b: int = E4M3,
+                   bias=None, act: int = ACT_NONE, out_fmt=None, out_scale=None, stream=None):
+    """out = cast(act(scale_a * scale_b * (A @ B^T) + bias)), per-tensor FP8
+    inputs as gemm_fp8_scaled; out as gemm_bf16_fused."""
+    torch = _torch()
+    M, K = A.shape
+    N = B.shape[0]
+    if B.shape[1] != K or tuple(out.shape) != (M, N):
+        raise ValueError("shape mismatch")
+    _check_dtype(scale_a, (torch.float32,), "scale_a")
+    _check_dtype(scale_b, (torch.float32,), "scale_b")
+    dt, sp, bp = _fused_out(out, out_fmt, out_scale, bias, N)
+    rc = load_library().gemm_fp8_fused(
+        _fp8_ptr(A, "A"), _ld(A, "A"), fmt_a, _fp8_ptr(B, "B"), _ld(B, "B"), fmt_b,
+        _dev_ptr(scale_a, "scale_a"), _dev_ptr(scale_b, "scale_b"), bp, act,
+        _dev_ptr(out, "out"), _ld(out, "out"), dt, sp, M, N, K, _stream(stream))
+    _check("gemm_fp8_fused", rc)
     return out
 
 
@@ -376,6 +447,20 @@ def probe_mfma_mx(shape: int, A, B, SA, SB, C, D, fmt_a: int = E4M3, fmt_b: int 
                                           _stream(stream))
     _check("dmu_probe_mfma_mx", rc)
     return D
+
+
+def probe_cvt_fp8(x, q, fmt: int = E4M3, clamp: int = 1, stream=None):
+    """Hardware FP32 -> FP8 conversion of x (float32, even length) into q
+    (uint8, same length); see include/dmu_probe.h."""
+    torch = _torch()
+    _check_dtype(x, (torch.float32,), "x")
+    _check_dtype(q, (torch.uint8,), "q")
+    if x.numel() != q.numel() or not (x.is_contiguous() and q.is_contiguous()):
+        raise ValueError("x and q: contiguous, same length")
+    rc = load_library().dmu_probe_cvt_fp8(_dev_ptr(x, "x"), x.numel(), fmt, clamp,
+                                          _dev_ptr(q, "q"), _stream(stream))
+    _check("dmu_probe_cvt_fp8", rc)
+    return q
 
 
 def probe_lds_load(src, dst, mode: int, oob_from: int = 64, stream=None):

@@ -206,6 +206,75 @@ int quantize_mxfp4(const float* X, int64_t rows, int64_t cols, int64_t ldx, uint
       dmu::launch_quantize_mxfp4(X, rows, cols, ldx, Q, ldq / 2, S, lds, (hipStream_t)stream));
 }
 
+namespace {
+
+// Output checks of the fused entry points (FP8 output allowed) and the
+// epilogue fields of the launch arguments.
+int fused_out(const void* D, int64_t ldd, int d_dtype, const float* d_scale, const float* bias,
+              int act, int64_t M, int64_t N, dmu::GemmArgs& a) {
+  if (!D || M < 1 || N < 1 || M > INT32_MAX || N > INT32_MAX) return DMU_ERR_INVALID_ARG;
+  if (act < DMU_ACT_NONE || act > DMU_ACT_SILU) return DMU_ERR_INVALID_ARG;
+  const bool fp8 = d_dtype == DMU_OUT_FP8_E4M3 || d_dtype == DMU_OUT_FP8_E5M2;
+  if (d_dtype != DMU_OUT_F32 && d_dtype != DMU_OUT_BF16 && !fp8) return DMU_ERR_INVALID_ARG;
+  const int64_t osz = d_dtype == DMU_OUT_F32 ? 4 : d_dtype == DMU_OUT_BF16 ? 2 : 1;
+  if (ldd < N || !aligned(D, 16) || (ldd * osz) % 16) return DMU_ERR_INVALID_ARG;
+  if (fp8 && (!d_scale || !aligned(d_scale, 4))) return DMU_ERR_INVALID_ARG;
+  if (bias && !aligned(bias, 4)) return DMU_ERR_INVALID_ARG;
+  a.out_bf16 = d_dtype == DMU_OUT_BF16;
+  a.out_fp8 = d_dtype == DMU_OUT_FP8_E4M3 ? 0 : d_dtype == DMU_OUT_FP8_E5M2 ? 1 : -1;
+  a.out_scale = fp8 ? d_scale : nullptr;
+  a.bias = bias;
+  a.act = act;
+  return DMU_OK;
+}
+
+}  // namespace
+
+int gemm_bf16_fused(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
+                    int b_layout, const float* bias, int act, void* D, int64_t ldd,
+                    int d_dtype, const float* d_scale, int64_t M, int64_t N, int64_t K,
+                    void* stream) {
+  dmu::GemmArgs a{A, B, nullptr, D, lda, ldb, 0, ldd, M, N, K, nullptr, nullptr, 0};
+  int rc = fused_out(D, ldd, d_dtype, d_scale, bias, act, M, N, a);
+  if (rc) return rc;
+  if (!A || !B || K < 8 || K % 8 || K > INT32_MAX) return DMU_ERR_INVALID_ARG;
+  if (b_layout != DMU_B_ROW_MAJOR && b_layout != DMU_B_COL_MAJOR) return DMU_ERR_INVALID_ARG;
+  if (lda < K || (lda * 2) % 16 || !aligned(A, 16) || !aligned(B, 16)) return DMU_ERR_INVALID_ARG;
+  if (b_layout == DMU_B_ROW_MAJOR ? ldb < N : ldb < K) return DMU_ERR_INVALID_ARG;
+  if ((ldb * 2) % 16) return DMU_ERR_INVALID_ARG;
+  if (kTileRows * lda * 2 >= kMaxTileBytes) return DMU_ERR_UNSUPPORTED;
+  if (b_layout == DMU_B_COL_MAJOR ? kTileRows * ldb * 2 >= kMaxTileBytes
+                                  : K * ldb * 2 >= kMaxTileBytes)
+    return DMU_ERR_UNSUPPORTED;
+  (void)hipGetLastError();
+  const bool plain = !a.bias && !a.act && a.out_fp8 < 0;  // nothing to fuse: the plain kernels
+  return finish(plain ? dmu::launch_gemm_bf16(a, b_layout == DMU_B_COL_MAJOR, (hipStream_t)stream)
+                      : dmu::launch_gemm_bf16_fused(a, b_layout == DMU_B_COL_MAJOR,
+                                                    (hipStream_t)stream));
+}
+
+int gemm_fp8_fused(const uint8_t* A, int64_t lda, int fmt_a, const uint8_t* B, int64_t ldb,
+                   int fmt_b, const float* scale_a, const float* scale_b, const float* bias,
+                   int act, void* D, int64_t ldd, int d_dtype, const float* d_scale, int64_t M,
+                   int64_t N, int64_t K, void* stream) {
+  dmu::GemmArgs a{A, B, nullptr, D, lda, ldb, 0, ldd, M, N, K, scale_a, scale_b, 0};
+  int rc = fused_out(D, ldd, d_dtype, d_scale, bias, act, M, N, a);
+  if (rc) return rc;
+  if (!A || !B || !scale_a || !scale_b) return DMU_ERR_INVALID_ARG;
+  if (fmt_a != DMU_FP8_E4M3 && fmt_a != DMU_FP8_E5M2) return DMU_ERR_INVALID_ARG;
+  if (fmt_b != DMU_FP8_E4M3 && fmt_b != DMU_FP8_E5M2) return DMU_ERR_INVALID_ARG;
+  if (K < 16 || K > INT32_MAX || K % 16) return DMU_ERR_INVALID_ARG;
+  if (lda < K || ldb < K || lda % 16 || ldb % 16) return DMU_ERR_INVALID_ARG;
+  if (!aligned(A, 16) || !aligned(B, 16) || !aligned(scale_a, 4) || !aligned(scale_b, 4))
+    return DMU_ERR_INVALID_ARG;
+  if (kTileRows * lda >= kMaxTileBytes || kTileRows * ldb >= kMaxTileBytes)
+    return DMU_ERR_UNSUPPORTED;
+  (void)hipGetLastError();
+  const bool plain = !a.bias && !a.act && a.out_fp8 < 0;
+  return finish(plain ? dmu::launch_gemm_fp8(a, fmt_a, fmt_b, 0, (hipStream_t)stream)
+                      : dmu::launch_gemm_fp8_fused(a, fmt_a, fmt_b, (hipStream_t)stream));
+}
+
 const char* dmu_status_string(int status) {
   switch (status) {
     case DMU_OK:
@@ -259,6 +328,14 @@ int dmu_probe_mfma_mx(int shape, int fmt_a, int fmt_b, int opsel, const void* A,
   (void)hipGetLastError();
   return finish(
       dmu::launch_probe_mx(shape, fmt_a, fmt_b, opsel, A, B, SA, SB, C, D, (hipStream_t)stream));
+}
+
+int dmu_probe_cvt_fp8(const float* x, int64_t n, int fmt, int clamp, uint8_t* q, void* stream) {
+  if (!x || !q || n < 2 || n % 2 || n > ((int64_t)1 << 31)) return DMU_ERR_INVALID_ARG;
+  if ((fmt != 0 && fmt != 1) || (clamp != 0 && clamp != 1) || !aligned(x, 8))
+    return DMU_ERR_INVALID_ARG;
+  (void)hipGetLastError();
+  return finish(dmu::launch_probe_cvt(x, n, fmt, clamp, q, (hipStream_t)stream));
 }
 
 }  // extern "C"

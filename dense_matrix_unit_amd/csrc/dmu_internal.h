@@ -26,18 +26,30 @@ struct GemmArgs {
   // [0, Mmax], the rows A and D hold
   const int64_t* goff = nullptr;
   int64_t G = 0, gstride = 0, Mmax = 0;
+  // fused epilogue: y = act(alpha * acc + C + bias[col]); D is FP32, BF16
+  // (out_bf16) or FP8 (out_fp8 = 0 E4M3 / 1 E5M2) coded from y * out_mult[0]
+  const float* bias = nullptr;
+  int act = 0;       // 0 none, 1 ReLU, 2 GELU, 3 SiLU
+  int out_fp8 = -1;  // -1: not FP8
+  const float* out_scale = nullptr;  // FP8 out: D ~ decode(q) * out_scale[0]
 };
 
 // kMX / kMX4: MXFP8, scales fetched one / four K slices at a time;
 // kMXF4: MXFP4 (E2M1 x E2M1, row strides in bytes), scales two slices at a time
-// kBF16G: BF16 grouped over experts (B stored N x K per expert)
+// kBF16G: BF16 grouped over experts (B stored N x K per expert);
+// kBF16F / kFP8TensorF: BF16 / per-tensor FP8 with the fused epilogue (bias,
+// activation, FP8 output), kept out of the plain kernels, whose register
+// allocation its code would change
 enum GemmKind { kBF16 = 0, kFP8Tensor = 1, kFP8Block = 2, kMX = 3, kMX4 = 4, kMXF4 = 5,
-                kBF16G = 6 };
+                kBF16G = 6, kBF16F = 7, kFP8TensorF = 8 };
 
 // Launchers: argument checking is done by the caller; these only pick a
 // kernel configuration and launch it.  They return a hipError_t.
 hipError_t launch_gemm_bf16(const GemmArgs& a, int b_col_major, hipStream_t s);
 hipError_t launch_gemm_grouped_bf16(const GemmArgs& a, hipStream_t s);
+// fused epilogue (a.bias / a.act / a.out_fp8 set)
+hipError_t launch_gemm_bf16_fused(const GemmArgs& a, int b_col_major, hipStream_t s);
+hipError_t launch_gemm_fp8_fused(const GemmArgs& a, int fmt_a, int fmt_b, hipStream_t s);
 // Skinny-M BF16 path (M <= 128, B stored N x K): HBM-bound streaming of B.
 bool skinny_applies(const GemmArgs& a);
 hipError_t launch_gemm_bf16_skinny(const GemmArgs& a, hipStream_t s);
@@ -65,6 +77,8 @@ hipError_t launch_probe_mfma(int kind, int fa, int fb, const void* A, const void
 hipError_t launch_probe_lds(const void* src, void* dst, int mode, int oob_from, hipStream_t s);
 hipError_t launch_probe_rate(int kind, const void* src, int iters, int grid, float* out,
                              hipStream_t s);
+hipError_t launch_probe_cvt(const float* x, int64_t n, int fmt, int clamp, uint8_t* q,
+                            hipStream_t s);
 hipError_t launch_probe_mx(int shape, int fa, int fb, int opsel, const void* A, const void* B,
                            const void* SA, const void* SB, const float* C, float* D,
                            hipStream_t s);

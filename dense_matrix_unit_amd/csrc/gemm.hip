@@ -51,6 +51,11 @@
 namespace dmu {
 namespace {
 
+template <int V>
+struct IntConst {
+  static constexpr int value = V;
+};
+
 // K slices between the L2 prefetch of a slice and its use (0 = no prefetch).
 constexpr int kPrefetch = 3;
 constexpr int kWavesBF16 = 4, kWavesFP8 = 4;  // waves per workgroup (4: one per SIMD)
@@ -70,7 +75,9 @@ gemm_kernel(GemmArgs p) {
   constexpr int NT = NW * 64;   // threads; NW waves in a 2 x (NW/2) grid
   constexpr bool F4 = KIND == kMXF4;  // E2M1 operands: 32 bytes of a row per K step of 64
   constexpr bool GRP = KIND == kBF16G;                // grouped over experts
-  constexpr bool BF = KIND == kBF16 || GRP;            // BF16 operands
+  constexpr bool EPI = KIND == kBF16F || KIND == kFP8TensorF;  // fused epilogue
+  constexpr bool BF = KIND == kBF16 || GRP || KIND == kBF16F;  // BF16 operands
+  constexpr bool F8T = KIND == kFP8Tensor || KIND == kFP8TensorF;  // per-tensor FP8
   constexpr int ESZ = BF ? 2 : 1;
   constexpr int CPR = RB / 16;  // 16-byte chunks per LDS row
   constexpr int WM = BM / 2, WN = BN / (NW / 2);
@@ -92,9 +99,10 @@ gemm_kernel(GemmArgs p) {
   constexpr int NLS = MX ? 2 : 0;                    // MX scale-group copies (A, B)
   constexpr int NL = NLA + NLB + NLS;
   static_assert(BM % 64 == 0 && BN % 64 == 0 && (BM * CPR) % NT == 0, "tile");
-  static_assert(!BROW || (KIND == kBF16 && BN == 256 && RB == 128 && S == 2 && NW == 4),
+  static_assert(!BROW || ((KIND == kBF16 || KIND == kBF16F) && BN == 256 && RB == 128 && S == 2 &&
+                          NW == 4),
                 "row-major B staging");
-  static_assert(BF || KIND == kFP8Tensor || MX,
+  static_assert(BF || F8T || MX,
                 "per-block FP32 scales live in gemm_block.hip");
   static_assert(!MX || (!KT && !BROW && RB == 128 && NW == 4 && BM == 256 && BN == 256 && S == 2),
                 "MX: whole 128-K slices, one scale row per thread and operand");
@@ -116,6 +124,8 @@ gemm_kernel(GemmArgs p) {
   const int tiles_n = (int)((p.N + BN - 1) / BN);
   int tm, tn;
   tile_coords<kGroupM>(tiles_m, tiles_n, tm, tn);
+  tm = __builtin_amdgcn_readfirstlane(tm);
+  tn = __builtin_amdgcn_readfirstlane(tn);
   int64_t m0 = (int64_t)tm * BM;
   if constexpr (GRP) {
     // m-tile tm is tile t of expert g: walk the experts' tile counts (row
@@ -591,10 +601,153 @@ gemm_kernel(GemmArgs p) {
                   "BF16 staging fits in LDS");
     static_assert(WN % 4 == 0 && 64 % (WN / 4) == 0, "band read shape");
     float alpha = 1.0f;
-    if constexpr (KIND == kFP8Tensor) alpha = p.sa[0] * p.sb[0];
+    if constexpr (F8T) alpha = p.sa[0] * p.sb[0];
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();  // every wave is done reading the K-slice stages
-    if (p.out_bf16 && !p.C) {
+    if constexpr (EPI) {
+      // Fused epilogue (the fused entry points take no C): scale, bias,
+      // activation and conversion on the accumulators, one 32-row block row
+      // of the wave at a time.  The block's converted bytes are staged in the
+      // wave's own LDS region (16-byte unit u of staged row r at
+      // u ^ (r % units-per-row), so neither the writes nor the reads collide
+      // in the banks), read back a row segment per lane and stored 16 bytes
+      // at a time.  Lane l, register 4q+r of sub-tile (i, j) is column
+      // j*32 + 8q + 4*(l/32) + r of row i*32 + l%32.
+      //
+      // The lane's bias values are loaded once, before any is used, from
+      // addresses clamped into the vector, so the loads carry no branch.
+      f32x4_t bv[TN][4];
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) bv[j][q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      if (p.bias) {
+        const int64_t cb = n0 + wn * WN + 4 * hl;
+        if (p.N % 4 == 0) {
+          // a group of four columns is wholly inside or wholly outside
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int64_t c = cb + j * 32 + 8 * q;
+              const f32x4_t v = *(const f32x4_t*)(p.bias + min(c, p.N - 4));
+              bv[j][q] = c < p.N ? v : f32x4_t{0.f, 0.f, 0.f, 0.f};
+            }
+        } else {
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                const int64_t c = cb + j * 32 + 8 * q + r;
+                const float v = p.bias[min(c, p.N - 1)];
+                bv[j][q][r] = c < p.N ? v : 0.0f;
+              }
+        }
+      }
+      // One copy of the loop per output type and activation (EB output
+      // bytes, ACT, FMT the FP8 format): a test of the activation per element
+      // would split the code into thousands of branches.  The block-row loop
+      // stays rolled; a switch copies block row i out of the accumulators,
+      // which are never indexed at run time.
+      static_assert(TM == 4, "block-row switch");
+      auto fused = [&](auto ob, auto ac, auto fc) __attribute__((always_inline)) {
+        constexpr int EB = decltype(ob)::value;  // output bytes per element
+        constexpr int ACT = decltype(ac)::value;
+        constexpr int FMT = decltype(fc)::value;
+        constexpr int RBS = WN * EB;             // staged row bytes
+        constexpr int UPS = RBS / 16;            // 16-byte units per staged row
+        constexpr int RPIS = 64 / UPS;           // staged rows per read instruction
+        static_assert(NW * 32 * RBS <= S * STAGE && RBS % 16 == 0 && 64 % UPS == 0,
+                      "block staging fits in LDS");
+        const float m = EB == 1 ? 1.0f / p.out_scale[0] : 1.0f;
+        uint8_t* wb = smem + swave * (32 * RBS);
+#pragma unroll 1
+        for (int i = 0; i < TM; ++i) {
+          f32x16_t cur[TN];
+          switch (i) {
+            case 0:
+#pragma unroll
+              for (int j = 0; j < TN; ++j) cur[j] = acc[0][j];
+              break;
+            case 1:
+#pragma unroll
+              for (int j = 0; j < TN; ++j) cur[j] = acc[1][j];
+              break;
+            case 2:
+#pragma unroll
+              for (int j = 0; j < TN; ++j) cur[j] = acc[2][j];
+              break;
+            default:
+#pragma unroll
+              for (int j = 0; j < TN; ++j) cur[j] = acc[3][j];
+          }
+          uint8_t* row = wb + rl * RBS;
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              f32x4_t x = {cur[j][4 * q], cur[j][4 * q + 1], cur[j][4 * q + 2], cur[j][4 * q + 3]};
+              if constexpr (F8T) x *= alpha;
+              x += bv[j][q];
+              if constexpr (ACT != 0)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) x[r] = activate(x[r], ACT);
+              if constexpr (EB == 4) {
+                const int u = j * 8 + 2 * q + hl;
+                *(f32x4_t*)(row + ((u ^ (rl & (UPS - 1))) << 4)) = x;
+              } else if constexpr (EB == 2) {
+                const uint32_t lo =
+                    f32_to_bf16_bits(x[0]) | ((uint32_t)f32_to_bf16_bits(x[1]) << 16);
+                const uint32_t hi =
+                    f32_to_bf16_bits(x[2]) | ((uint32_t)f32_to_bf16_bits(x[3]) << 16);
+                const int u = j * 4 + q;
+                *(uint2*)(row + ((u ^ (rl & (UPS - 1))) << 4) + hl * 8) = make_uint2(lo, hi);
+              } else {
+                const int u = j * 2 + q / 2;
+                *(uint32_t*)(row + ((u ^ (rl & (UPS - 1))) << 4) + 8 * (q & 1) + 4 * hl) =
+                    cvt4_fp8<FMT>(x * m);
+              }
+            }
+          // own region only: no barrier, and no wait for earlier blocks'
+          // stores; the next block's writes cannot pass these reads, as the
+          // LDS work of one wave stays in order.  All reads go out before the
+          // first store waits for its data.
+          __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<63>());
+          u32x4_t v[32 / RPIS];
+#pragma unroll
+          for (int it = 0; it < 32 / RPIS; ++it) {
+            const int r = it * RPIS + lane / UPS, u = lane % UPS;
+            v[it] = *(const u32x4_t*)(wb + r * RBS + ((u ^ (r & (UPS - 1))) << 4));
+          }
+#pragma unroll
+          for (int it = 0; it < 32 / RPIS; ++it) {
+            const int r = it * RPIS + lane / UPS, u = lane % UPS;
+            const int64_t grow = m0 + wm * WM + i * 32 + r, col = n0 + wn * WN + u * (16 / EB);
+            if (grow < p.M && col < p.N) {
+              uint8_t* d = (uint8_t*)p.D + (grow * p.ldd + col) * EB;
+              if (col + 16 / EB - 1 < p.N) {
+                *(u32x4_t*)d = v[it];
+              } else {
+                for (int e = 0; e < 16; ++e)
+                  if (col + e / EB < p.N) d[e] = (uint8_t)(v[it][e >> 2] >> (8 * (e & 3)));
+              }
+            }
+          }
+        }
+      };
+      auto by_act = [&](auto ob, auto fc) __attribute__((always_inline)) {
+        if (p.act == 1) fused(ob, IntConst<1>{}, fc);
+        else if (p.act == 2) fused(ob, IntConst<2>{}, fc);
+        else if (p.act == 3) fused(ob, IntConst<3>{}, fc);
+        else fused(ob, IntConst<0>{}, fc);
+      };
+      if (p.out_fp8 == 0) by_act(IntConst<1>{}, IntConst<0>{});
+      else if (p.out_fp8 == 1) by_act(IntConst<1>{}, IntConst<1>{});
+      else if (p.out_bf16) by_act(IntConst<2>{}, IntConst<0>{});
+      else by_act(IntConst<4>{}, IntConst<0>{});
+    } else if (p.out_bf16 && !p.C) {
       // BF16 output: round first, then stage all four bands of the wave at
       // once (4 x 32 rows x 256 B = 32 KB per wave), so the LDS traffic is
       // halved and no band waits for the previous one.  16-byte unit u of
@@ -612,7 +765,7 @@ gemm_kernel(GemmArgs p) {
           for (int q = 0; q < 4; ++q) {
             f32x4_t x = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
                          acc[i][j][4 * q + 3]};
-            if constexpr (KIND == kFP8Tensor) x *= alpha;
+            if constexpr (F8T) x *= alpha;
             const uint32_t lo = f32_to_bf16_bits(x[0]) | ((uint32_t)f32_to_bf16_bits(x[1]) << 16);
             const uint32_t hi = f32_to_bf16_bits(x[2]) | ((uint32_t)f32_to_bf16_bits(x[3]) << 16);
             const int u = j * 4 + q;  // 16-byte unit of the staged row
@@ -648,7 +801,7 @@ gemm_kernel(GemmArgs p) {
           for (int q = 0; q < 4; ++q) {
             f32x4_t x = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
                          acc[i][j][4 * q + 3]};
-            if constexpr (KIND == kFP8Tensor) x *= alpha;
+            if constexpr (F8T) x *= alpha;
             *(f32x4_t*)(band + rl * ROWW + j * 32 + 8 * q + 4 * hl) = x;
           }
 #pragma unroll
@@ -670,7 +823,7 @@ hipError_t launch(const GemmArgs& a, hipStream_t s) {
   // K tail: the last slice is partial and its lanes are range-checked one by
   // one (MX requires whole slices and has no such variant)
   if constexpr (KIND != kMX && KIND != kMX4 && KIND != kMXF4) {
-    if ((a.K * (KIND == kBF16 || KIND == kBF16G ? 2 : 1)) % RB != 0) {
+    if ((a.K * (KIND == kBF16 || KIND == kBF16G || KIND == kBF16F ? 2 : 1)) % RB != 0) {
       hipLaunchKernelGGL((gemm_kernel<KIND, FA, FB, BROW, BM, BN, RB, S, G, PD, NW, true>),
                          dim3((unsigned)tiles), dim3(NW * 64), 0, s, a);
       return hipGetLastError();
@@ -682,6 +835,20 @@ hipError_t launch(const GemmArgs& a, hipStream_t s) {
 }
 
 }  // namespace
+
+hipError_t launch_gemm_bf16_fused(const GemmArgs& a, int b_col_major, hipStream_t s) {
+  if (b_col_major) return launch<kBF16F, 0, 0, false, 256, 256, 128, 2, 4, kPrefetch, kWavesBF16>(a, s);
+  return launch<kBF16F, 0, 0, true, 256, 256, 128, 2, 4>(a, s);
+}
+
+hipError_t launch_gemm_fp8_fused(const GemmArgs& a, int fmt_a, int fmt_b, hipStream_t s) {
+#define DMU_F8F(FA, FB) launch<kFP8TensorF, FA, FB, false, 256, 256, 128, 2, 4, kPrefetch, kWavesFP8>(a, s)
+  if (fmt_a == 0 && fmt_b == 0) return DMU_F8F(0, 0);
+  if (fmt_a == 0 && fmt_b == 1) return DMU_F8F(0, 1);
+  if (fmt_a == 1 && fmt_b == 0) return DMU_F8F(1, 0);
+  return DMU_F8F(1, 1);
+#undef DMU_F8F
+}
 
 hipError_t launch_gemm_grouped_bf16(const GemmArgs& a, hipStream_t s) {
   return launch<kBF16G, 0, 0, false, 256, 256, 128, 2, 4, kPrefetch, kWavesBF16>(a, s);

@@ -54,6 +54,62 @@ __device__ __forceinline__ i32x8_t cat(const i32x4_t& lo, const i32x4_t& hi) {
   return i32x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
+// Activations of the fused epilogue, in few instructions: every output
+// element goes through one, and a wave holds 16384 of them per tile.
+// e^y is 2^(y log2 e) on the hardware exp2 (v_exp_f32), 1 / y the hardware
+// reciprocal (v_rcp_f32).
+constexpr float kLog2e = 1.44269504088896341f;
+
+// GELU, x * Phi(x).  For z = |x| / sqrt 2, (1 - erf z) / 2 is taken from the
+// erf approximation of Abramowitz & Stegun, Handbook of Mathematical
+// Functions, formula 7.1.26 (absolute error <= 1.5e-7):
+// 1 - erf z ~ t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) e^(-z^2), t = 1 / (1 + p z).
+// Phi(x) is that half-complement for x < 0 and 1 minus it otherwise, so the
+// negative tail is not a difference of nearly equal numbers.
+__device__ __forceinline__ float gelu(float x) {
+  const float z = fabsf(x) * 0.70710678118654752f;
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, z, 1.0f));
+  const float poly =
+      t * fmaf(t, fmaf(t, fmaf(t, fmaf(t, 1.061405429f, -1.453152027f), 1.421413741f),
+                       -0.284496736f),
+               0.254829592f);
+  const float q = 0.5f * poly * __builtin_amdgcn_exp2f(-z * z * kLog2e);
+  return x * (x < 0.0f ? q : 1.0f - q);
+}
+
+// SiLU, x / (1 + e^-x).
+__device__ __forceinline__ float silu(float x) {
+  return x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-x * kLog2e));
+}
+
+// 1 ReLU (x > 0 ? x : 0), 2 GELU, 3 SiLU, else x.
+__device__ __forceinline__ float activate(float x, int act) {
+  if (act == 1) return x > 0.0f ? x : 0.0f;
+  if (act == 2) return gelu(x);
+  if (act == 3) return silu(x);
+  return x;
+}
+
+// Four FP32 values -> four FP8 codes (byte r = value r), saturating RNE: the
+// hardware conversion (v_cvt_pk_fp8_f32 / v_cvt_pk_bf8_f32) rounds to nearest
+// even but turns values past the largest finite one into NaN / Inf, so they
+// are clamped first (NaN passed through).
+template <int FMT>
+__device__ __forceinline__ uint32_t cvt4_fp8(f32x4_t y) {
+  constexpr float kMax = FMT == 0 ? 448.0f : 57344.0f;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) y[r] = y[r] != y[r] ? y[r] : fminf(fmaxf(y[r], -kMax), kMax);
+  int w;
+  if constexpr (FMT == 0) {
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], w, true);
+  } else {
+    w = __builtin_amdgcn_cvt_pk_bf8_f32(y[0], y[1], 0, false);
+    w = __builtin_amdgcn_cvt_pk_bf8_f32(y[2], y[3], w, true);
+  }
+  return (uint32_t)w;
+}
+
 // D[row][col .. col+3] = x (+ C), masked to the matrix.
 __device__ __forceinline__ void store4(const GemmArgs& p, int64_t row, int64_t col, f32x4_t x) {
   if (row >= p.M || col >= p.N) return;

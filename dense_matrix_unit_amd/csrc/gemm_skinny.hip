@@ -187,7 +187,10 @@ hipError_t launch_mb(const GemmArgs& a, hipStream_t s) {
 
 }  // namespace
 
-bool skinny_applies(const GemmArgs& a) { return a.M <= 128; }
+// the skinny kernel has no fused epilogue (bias, activation, FP8 output)
+bool skinny_applies(const GemmArgs& a) {
+  return a.M <= 128 && !a.bias && !a.act && a.out_fp8 < 0;
+}
 
 hipError_t launch_gemm_bf16_skinny(const GemmArgs& a, hipStream_t s) {
   if (a.M <= 16) return launch_mb<16, 3>(a, s);

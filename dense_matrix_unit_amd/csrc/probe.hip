@@ -154,6 +154,28 @@ __global__ void probe_mx_kernel(const uint8_t* A, const uint8_t* B, const uint8_
   }
 }
 
+// FP32 -> FP8 with the hardware conversion, two values per instruction:
+// v_cvt_pk_fp8_f32 (E4M3) / v_cvt_pk_bf8_f32 (E5M2), applied to x as it is
+// (CLAMP == 0) or to x clamped to the format's largest finite magnitude with
+// NaN passed through (CLAMP == 1; the instruction takes no clamp modifier on
+// gfx950).  Thread t converts x[2t], x[2t+1] into q[2t], q[2t+1].
+template <int FMT, int CLAMP>
+__global__ void probe_cvt_kernel(const float* x, int64_t npairs, uint8_t* q) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= npairs) return;
+  float a = x[2 * t], b = x[2 * t + 1];
+  if constexpr (CLAMP) {
+    constexpr float kMax = FMT == 0 ? 448.0f : 57344.0f;
+    a = a != a ? a : fminf(fmaxf(a, -kMax), kMax);
+    b = b != b ? b : fminf(fmaxf(b, -kMax), kMax);
+  }
+  int r;
+  if constexpr (FMT == 0) r = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  else r = __builtin_amdgcn_cvt_pk_bf8_f32(a, b, 0, false);
+  q[2 * t] = (uint8_t)(r & 0xFF);
+  q[2 * t + 1] = (uint8_t)((r >> 8) & 0xFF);
+}
+
 // One wave copies 64 x 16 bytes (mode 0) or 64 x 4 bytes (mode 1) from src to
 // LDS with buffer loads that write LDS directly, then dumps 2 KiB of LDS to
 // dst.  Lanes >= oob_from get an out-of-range offset (they must write zeros).
@@ -327,6 +349,19 @@ hipError_t launch_probe_mx(int shape, int fa, int fb, int opsel, const void* A, 
   const uint8_t *sa = (const uint8_t*)SA, *sb = (const uint8_t*)SB;
   if (shape == 0) return probe_mx_fmt<0>(fa, fb, opsel, a, b, sa, sb, C, D, s);
   return probe_mx_fmt<1>(fa, fb, opsel, a, b, sa, sb, C, D, s);
+}
+
+hipError_t launch_probe_cvt(const float* x, int64_t n, int fmt, int clamp, uint8_t* q,
+                            hipStream_t s) {
+  const int64_t np = n / 2;
+  const dim3 grid((unsigned)((np + 255) / 256));
+#define DMU_CVT(F, C) hipLaunchKernelGGL((probe_cvt_kernel<F, C>), grid, dim3(256), 0, s, x, np, q)
+  if (fmt == 0 && !clamp) DMU_CVT(0, 0);
+  else if (fmt == 0) DMU_CVT(0, 1);
+  else if (!clamp) DMU_CVT(1, 0);
+  else DMU_CVT(1, 1);
+#undef DMU_CVT
+  return hipGetLastError();
 }
 
 }  // namespace dmu

@@ -36,49 +36,6 @@
 namespace dmu {
 namespace {
 
-template <int FMT>
-struct Fp8Fmt;
-template <>
-struct Fp8Fmt<0> {  // E4M3 (OCP FN)
-  static constexpr int kMant = 3, kBias = 7;
-  static constexpr uint32_t kMaxBits = 0x43E00000u;  // 448.0f
-  static constexpr uint32_t kMaxCode = 0x7E;
-  static constexpr float kMax = 448.0f;
-};
-template <>
-struct Fp8Fmt<1> {  // E5M2
-  static constexpr int kMant = 2, kBias = 15;
-  static constexpr uint32_t kMaxBits = 0x47600000u;  // 57344.0f
-  static constexpr uint32_t kMaxCode = 0x7B;
-  static constexpr float kMax = 57344.0f;
-};
-
-// Saturating round-to-nearest-even FP32 -> FP8 on the bit pattern.
-template <int FMT>
-__device__ __forceinline__ uint32_t encode_fp8(float y) {
-  using F = Fp8Fmt<FMT>;
-  const uint32_t u = __float_as_uint(y);
-  const uint32_t sign = (u >> 24) & 0x80u;
-  const uint32_t a = u & 0x7FFFFFFFu;
-  if (a > 0x7F800000u) return sign | 0x7Fu;         // NaN
-  if (a >= F::kMaxBits) return sign | F::kMaxCode;  // saturate (Inf included)
-  constexpr uint32_t kMinNormal = (uint32_t)(127 + 1 - F::kBias) << 23;
-  constexpr int kDrop = 23 - F::kMant;
-  if (a >= kMinNormal) {
-    // keep kMant fraction bits, round half to even, re-bias the exponent
-    const uint32_t r = (a + ((1u << (kDrop - 1)) - 1u) + ((a >> kDrop) & 1u)) >> kDrop;
-    return sign | (r - ((uint32_t)(127 - F::kBias) << F::kMant));
-  }
-  if (a < 0x00800000u) return sign;  // zero or FP32 subnormal: far below half an FP8 step
-  // FP8 subnormal: count multiples of 2^(1 - bias - mant), round half to even
-  const int e = (int)(a >> 23);
-  const uint32_t sig = (a & 0x007FFFFFu) | 0x00800000u;
-  const int shift = 150 + 1 - F::kBias - F::kMant - e;
-  if (shift > 24) return sign;
-  const uint32_t n = (sig + (1u << (shift - 1)) - 1u + ((sig >> shift) & 1u)) >> shift;
-  return sign | n;
-}
-
 __device__ __forceinline__ uint32_t abs_bits(float x) { return __float_as_uint(x) & 0x7FFFFFFFu; }
 
 // FP32 -> E2M1 (FP4: magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6), round to nearest

@@ -48,6 +48,13 @@ extern "C" {
 /* Output element type of D. */
 #define DMU_OUT_F32 0  /* IEEE binary32 */
 #define DMU_OUT_BF16 1 /* bfloat16, rounded to nearest even from the FP32 result */
+#define DMU_OUT_FP8_E4M3 2 /* fused entry points only: FP8 with a dequantisation scale */
+#define DMU_OUT_FP8_E5M2 3
+/* Activation of the fused epilogue. */
+#define DMU_ACT_NONE 0
+#define DMU_ACT_RELU 1 /* x > 0 ? x : 0 */
+#define DMU_ACT_GELU 2 /* x * Phi(x) = x * (1 + erf(x / sqrt 2)) / 2 */
+#define DMU_ACT_SILU 3 /* x / (1 + exp(-x)) */
 
 /* Storage of the K x N operand B. */
 #define DMU_B_ROW_MAJOR 0 /* B(k, n) at B[k * ldb + n] */
@@ -265,6 +272,47 @@ int gemm_mxfp4(const uint8_t* A, int64_t lda, const uint8_t* B, int64_t ldb,
  */
 int quantize_mxfp4(const float* X, int64_t rows, int64_t cols, int64_t ldx, uint8_t* Q,
                    int64_t ldq, uint8_t* S, int64_t lds, void* stream);
+
+/*
+ * Fused epilogue: the accumulator is turned into the layer's output while it
+ * is still in registers -- scaled, biased, activated and cast down ("How
+ * Blackwell's Tensor Memory Actually Works", section "The cost of getting the
+ * answer back") -- instead of a second pass over D in HBM:
+ *
+ *   y[i][j] = act(alpha * acc[i][j] + bias[j])
+ *
+ * with acc the FP32 sum of the products, alpha = 1 (BF16) or
+ * scale_a[0] * scale_b[0] (per-tensor FP8), bias an optional FP32 vector of N
+ * (NULL: none) and act a DMU_ACT_* value evaluated in FP32 on the hardware
+ * exp2 and reciprocal: SiLU directly, GELU with Phi from the erf
+ * approximation of Abramowitz & Stegun formula 7.1.26 (absolute error at
+ * most 1.5e-7, so GELU within 7.5e-8 |x| of x Phi(x)).  D receives y as FP32, as BF16 (RNE), or as
+ * FP8 (DMU_OUT_FP8_*): q = saturating round-to-nearest-even of fl32(y * m),
+ * m = fl32(1 / d_scale[0]) -- the quantize_fp8 convention (computed with the
+ * hardware conversion after clamping to +-max, bit-exact with that encoder), so that
+ * y ~ decode(q) * d_scale[0] and D can feed gemm_fp8_scaled directly.
+ * d_scale is a device pointer to one float, required for FP8 output and
+ * ignored otherwise.  FP8 output rows are ldd bytes apart (ldd % 16 == 0).
+ * bias and d_scale are device pointers aligned to 4 bytes, read only; the
+ * caller keeps ownership of every buffer.  An act or d_dtype outside the
+ * values above, a missing d_scale for FP8 output, or a misaligned pointer
+ * returns DMU_ERR_INVALID_ARG before anything is launched; the remaining
+ * checks are those of the plain entry point.  With no bias, no activation
+ * and no FP8 output the plain kernels run.
+ */
+
+/* gemm_bf16_fused: gemm_bf16 (no C addend) with the fused epilogue. */
+int gemm_bf16_fused(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
+                    int b_layout, const float* bias, int act, void* D, int64_t ldd,
+                    int d_dtype, const float* d_scale, int64_t M, int64_t N, int64_t K,
+                    void* stream);
+
+/* gemm_fp8_fused: per-tensor gemm_fp8_scaled (no C addend) with the fused
+ * epilogue. */
+int gemm_fp8_fused(const uint8_t* A, int64_t lda, int fmt_a, const uint8_t* B, int64_t ldb,
+                   int fmt_b, const float* scale_a, const float* scale_b, const float* bias,
+                   int act, void* D, int64_t ldd, int d_dtype, const float* d_scale, int64_t M,
+                   int64_t N, int64_t K, void* stream);
 
 /* Human-readable text for a status code (static storage, never NULL). */
 const char* dmu_status_string(int status);

@@ -92,6 +92,17 @@ int dmu_probe_mfma_rate(int kind, const void* src, int iters, int grid, float* o
 int dmu_probe_mfma_mx(int shape, int fmt_a, int fmt_b, int opsel, const void* A, const void* B,
                       const void* SA, const void* SB, const float* C, float* D, void* stream);
 
+/*
+ * Convert n FP32 values (n even, n <= 2^31) to FP8 codes with gfx950's
+ * conversion instruction (v_cvt_pk_fp8_f32 for fmt 0 = E4M3,
+ * v_cvt_pk_bf8_f32 for fmt 1 = E5M2), two values per instruction, on x as
+ * given (clamp = 0) or on x clamped to +-the format's largest finite value
+ * with NaN passed through (clamp = 1).  x and q
+ * are device arrays of n floats / n bytes.  Exists so the tests can pin the
+ * conversion's rounding, saturation and special values against the oracle.
+ */
+int dmu_probe_cvt_fp8(const float* x, int64_t n, int fmt, int clamp, uint8_t* q, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -189,3 +189,34 @@ def call_grouped(**kw):
 ])
 def test_gemm_grouped_rejects(kw):
     assert call_grouped(**kw) == dmu.DMU_ERR_INVALID_ARG
+
+
+def call_bf16_fused(**kw):
+    a = dict(A=FAKE, lda=64, B=FAKE, ldb=64, b_layout=1, bias=None, act=0, D=FAKE, ldd=64,
+             d_dtype=2, d_scale=FAKE, M=64, N=64, K=64, stream=None)
+    a.update(kw)
+    return dmu.load_library().gemm_bf16_fused(*a.values())
+
+
+@pytest.mark.parametrize("kw", [
+    dict(A=None), dict(D=None), dict(act=4), dict(act=-1), dict(d_dtype=4), dict(d_scale=None),
+    dict(d_scale=FAKE + 2), dict(bias=FAKE + 1), dict(ldd=56, N=56, d_dtype=2), dict(K=12),
+    dict(b_layout=3), dict(M=0),
+])
+def test_gemm_bf16_fused_rejects(kw):
+    assert call_bf16_fused(**kw) == dmu.DMU_ERR_INVALID_ARG
+
+
+def call_fp8_fused(**kw):
+    a = dict(A=FAKE, lda=128, fa=0, B=FAKE, ldb=128, fb=0, sa=FAKE, sb=FAKE, bias=None, act=2,
+             D=FAKE, ldd=64, d_dtype=1, d_scale=None, M=64, N=64, K=128, stream=None)
+    a.update(kw)
+    return dmu.load_library().gemm_fp8_fused(*a.values())
+
+
+@pytest.mark.parametrize("kw", [
+    dict(sa=None), dict(sb=None), dict(fa=4), dict(K=8), dict(d_dtype=3), dict(act=9),
+    dict(lda=120), dict(D=FAKE + 4),
+])
+def test_gemm_fp8_fused_rejects(kw):
+    assert call_fp8_fused(**kw) == dmu.DMU_ERR_INVALID_ARG

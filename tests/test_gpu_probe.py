@@ -323,3 +323,49 @@ def test_mfma_mx_nan_scale_code():
     ref, _ = oracle.gemm_mx(A, B, 0, 0, SA, SB)
     assert np.all(np.isnan(ref[3])) and np.all(np.isnan(D[3]))
     assert np.array_equal(np.delete(D, 3, axis=0), np.delete(ref, 3, axis=0))
+
+
+def cvt_points(fmt):
+    """FP32 values that decide an FP8 encoder: every finite code value, every
+    midpoint between neighbours and one FP32 step either side of it, signed
+    zeros, FP32 subnormals, values past the largest finite, infinities, NaN,
+    and random values over the whole range."""
+    rng = np.random.default_rng(fmt)
+    vals = oracle.decode_fp8(np.arange(256, dtype=np.uint8), fmt)
+    fin = np.sort(np.unique(np.abs(vals[np.isfinite(vals)])))
+    mids = ((fin[1:] + fin[:-1]) / 2).astype(np.float32)
+    up = np.nextafter(mids, np.float32(np.inf))
+    dn = np.nextafter(mids, np.float32(0))
+    special = np.float32([0.0, -0.0, 1e-45, -1e-45, 1e-38, np.inf, -np.inf, np.nan, 1e30, -1e30,
+                          fin[-1] * 1.01, -fin[-1] * 1.2, fin[-1] * 2])
+    x = np.concatenate([special, fin, -fin, mids, -mids, up, -up, dn, -dn,
+                        (rng.standard_normal(100000) * fin[-1] / 4),
+                        np.exp(rng.uniform(-40, 12, 100000)) * rng.choice([-1, 1], 100000)])
+    x = x.astype(np.float32)
+    return x if x.size % 2 == 0 else np.append(x, np.float32(0))
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_hardware_fp8_conversion(fmt):
+    # gfx950's v_cvt_pk_{fp8,bf8}_f32 rounds to nearest even but does not
+    # saturate: past the largest finite value E4M3 gives NaN and E5M2 gives
+    # Inf.  Clamped to +-max first (NaN passed through) it is exactly the
+    # saturating encoder of the oracle -- what the fused epilogue relies on.
+    x = cvt_points(fmt)
+    want = oracle.encode_fp8(x, fmt)
+    xt = dev(x)
+    out = {}
+    for clamp in (0, 1):
+        q = torch.empty(x.size, dtype=torch.uint8, device="cuda")
+        dmu.probe_cvt_fp8(xt, q, fmt, clamp)
+        torch.cuda.synchronize()
+        out[clamp] = q.cpu().numpy()
+    nan = np.isnan(x)
+    assert np.array_equal(out[1][~nan], want[~nan])
+    assert np.all(np.isnan(oracle.decode_fp8(out[1][nan], fmt)))
+    fmax = 448.0 if fmt == 0 else 57344.0
+    big = np.abs(x.astype(np.float64)) > fmax * (1 + 2.0 ** -(4 if fmt == 0 else 3))
+    raw = oracle.decode_fp8(out[0][big], fmt)
+    assert np.all(np.isnan(raw)) if fmt == 0 else np.all(np.isinf(raw))
+    inrange = ~nan & (np.abs(x) <= fmax)
+    assert np.array_equal(out[0][inrange], want[inrange])
