@@ -80,6 +80,8 @@ def lib():
                                             p]
         L.orc_gemm_grouped_bf16.restype = i32
         L.orc_epilogue.argtypes = [p, i64, i64, ctypes.c_double, p, i32, p]
+        L.orc_attention_bf16.argtypes = [p, p, p, i64, i64, i64, i64, ctypes.c_double, i32, p,
+                                         p, p]
         L.orc_epilogue.restype = i32
         L.orc_encode_fp4_array.argtypes = [p, i64, p]
         L.orc_decode_fp4_array.argtypes = [p, i64, p]
@@ -331,6 +333,30 @@ def epilogue(D, alpha: float = 1.0, bias=None, act: int = ACT_NONE) -> np.ndarra
     if rc != 0:
         raise ValueError("orc_epilogue: bad arguments")
     return Y
+
+
+# ------------------------------------------------------------------ attention chain
+
+def attention_bf16(Q, K, V, scale: float, causal: bool = False):
+    """Softmax attention per head in FP64 (orc_attention_bf16): Q [BH, Sq, d],
+    K and V [BH, Sk, d] BF16 bit patterns (uint16; 2-D arrays are one head).
+    Returns (O [BH, Sq, d], lse [BH, Sq], Aabs [BH, Sq, d]) in the input's
+    rank, Aabs = sum_j w_j |v_j| / l, the scale of the rounding error of O."""
+    two = np.ndim(Q) == 2
+    Q, K, V = (np.ascontiguousarray(np.asarray(x, dtype=np.uint16)) for x in (Q, K, V))
+    if two:
+        Q, K, V = Q[None], K[None], V[None]
+    BH, Sq, d = Q.shape
+    Sk = K.shape[1]
+    assert K.shape == (BH, Sk, d) and V.shape == (BH, Sk, d)
+    O = np.empty((BH, Sq, d))
+    lse = np.empty((BH, Sq))
+    A = np.empty((BH, Sq, d))
+    rc = lib().orc_attention_bf16(_ptr(Q), _ptr(K), _ptr(V), BH, Sq, Sk, d, float(scale),
+                                  int(bool(causal)), _ptr(O), _ptr(lse), _ptr(A))
+    if rc != 0:
+        raise ValueError("orc_attention_bf16: bad arguments")
+    return (O[0], lse[0], A[0]) if two else (O, lse, A)
 
 
 # ------------------------------------------------------------------ metrics

@@ -565,3 +565,74 @@ int orc_epilogue(const double* D, int64_t rows, int64_t N, double alpha, const f
   }
   return 0;
 }
+
+/* ---------------------------------------------------------------- attention chain */
+
+/* Two products chained through an elementwise step: the scores of the first
+ * feed, after a row-wise softmax, the second.  The "Tensor Cores" chapter
+ * (ai-infra-handbooks), section "mma.sync: the register layout is explicit",
+ * names this as the case FlashAttention needs (one product's output consumed
+ * by the next, elementwise work done on the result in between), and
+ * "Tensor Cores: Matrix Instructions, Swizzling and FP8, Measured"
+ * (vidyal.ai), section "In the real world", cites FlashAttention as the
+ * kernel built that way.  The pages do not restate attention itself; this is
+ * its textbook definition, per head bh and query row i:
+ *
+ *   s_j = scale * sum_k q[i][k] * k[j][k]      for the keys j the row sees
+ *   w_j = exp(s_j - max_j s_j),  l = sum_j w_j
+ *   O[i][n]   = sum_j w_j * v[j][n] / l
+ *   lse[i]    = max_j s_j + log l              (log of sum_j exp(s_j))
+ *   Aabs[i][n] = sum_j w_j * |v[j][n]| / l      (for error bounds)
+ *
+ * Non-causal rows see every key; causal rows see keys j <= i + (Sk - Sq)
+ * (the last query row sees every key), which needs Sq <= Sk.  Q is
+ * [BH][Sq][d], K and V [BH][Sk][d], all BF16 bit patterns, contiguous;
+ * outputs are FP64 [BH][Sq][d] and [BH][Sq]; lse and Aabs may be NULL.
+ * Inputs are decoded exactly and every sum runs in increasing index order. */
+int orc_attention_bf16(const uint16_t* Q, const uint16_t* K, const uint16_t* V, int64_t BH,
+                       int64_t Sq, int64_t Sk, int64_t d, double scale, int causal, double* O,
+                       double* lse, double* Aabs) {
+  if (BH < 1 || Sq < 1 || Sk < 1 || d < 1 || (causal && Sq > Sk)) return -1;
+  int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) collapse(2)
+  for (int64_t bh = 0; bh < BH; bh++) {
+    for (int64_t i = 0; i < Sq; i++) {
+      const uint16_t* q = Q + (bh * Sq + i) * d;
+      const int64_t nk = causal ? i + (Sk - Sq) + 1 : Sk;
+      double* s = (double*)malloc((size_t)nk * sizeof(double));
+      if (!s) {
+#pragma omp atomic write
+        bad = 1;
+        continue;
+      }
+      double m = -INFINITY;
+      for (int64_t j = 0; j < nk; j++) {
+        const uint16_t* kr = K + (bh * Sk + j) * d;
+        double acc = 0.0;
+        for (int64_t k = 0; k < d; k++) acc += orc_decode_bf16(q[k]) * orc_decode_bf16(kr[k]);
+        s[j] = scale * acc;
+        if (s[j] > m) m = s[j];
+      }
+      double l = 0.0;
+      for (int64_t j = 0; j < nk; j++) {
+        s[j] = exp(s[j] - m);
+        l += s[j];
+      }
+      double* o = O + (bh * Sq + i) * d;
+      double* a = Aabs ? Aabs + (bh * Sq + i) * d : NULL;
+      for (int64_t n = 0; n < d; n++) {
+        double acc = 0.0, aa = 0.0;
+        for (int64_t j = 0; j < nk; j++) {
+          const double v = orc_decode_bf16(V[(bh * Sk + j) * d + n]);
+          acc += s[j] * v;
+          aa += s[j] * fabs(v);
+        }
+        o[n] = acc / l;
+        if (a) a[n] = aa / l;
+      }
+      if (lse) lse[bh * Sq + i] = m + log(l);
+      free(s);
+    }
+  }
+  return bad ? -1 : 0;
+}
