@@ -60,6 +60,8 @@ SYMBOLS = {
                             _I64, _I64, _P]),
     "gemm_grouped_bf16": (_I, [_P, _I64, _P, _I64, _I64, _P, _I64, _P, _I64, _I, _I64, _I64,
                                _I64, _P]),
+    "attention_bf16": (_I, [_P, _I64, _I64, _P, _I64, _I64, _P, _I64, _I64, _P, _I64, _I64, _P,
+                            _I64, _I64, _I64, _I64, ctypes.c_float, _I, _P]),
     "gemm_mxfp8": (_I, [_P, _I64, _I, _P, _I64, _I, _P, _I64, _P, _I64, _P, _I64, _P, _I64, _I,
                         _I64, _I64, _I64, _P]),
     "quantize_mxfp8": (_I, [_P, _I64, _I64, _I64, _I, _P, _I64, _P, _I64, _P]),
@@ -257,6 +259,40 @@ def gemm_grouped_bf16(A, B, offsets, out, stream=None):
         OUT_F32 if out.dtype == torch.float32 else OUT_BF16, max_m, N, K, _stream(stream))
     _check("gemm_grouped_bf16", rc)
     return out
+
+
+def attention_bf16(Q, K, V, O, scale: float, causal: bool = False, lse=None, stream=None):
+    """O = softmax(scale * Q K^T) V per head (attention_bf16 in dmu.h).  Q, O:
+    [heads, Sq, d] BF16; K, V: [heads, Sk, d] BF16 (2-D tensors are one head);
+    any row and head strides with a unit d stride.  lse: optional float32
+    [heads, Sq] contiguous tensor for log sum_j exp(s_j)."""
+    torch = _torch()
+    bf = (torch.bfloat16, torch.int16, torch.uint16)
+    for t, n in ((Q, "Q"), (K, "K"), (V, "V"), (O, "O")):
+        _check_dtype(t, bf, n)
+        if t.dim() not in (2, 3) or t.stride(-1) != 1:
+            raise ValueError("%s must be [heads, S, d] or [S, d] with a unit d stride" % n)
+    def hs(t):
+        return t.stride(0) if t.dim() == 3 else 0
+    def h3(t):
+        return t.shape if t.dim() == 3 else (1,) + tuple(t.shape)
+    heads, Sq, d = h3(Q)
+    Sk = h3(K)[1]
+    if tuple(h3(K)) != (heads, Sk, d) or tuple(h3(V)) != (heads, Sk, d) or \
+            tuple(h3(O)) != (heads, Sq, d):
+        raise ValueError("shape mismatch")
+    lp = None
+    if lse is not None:
+        _check_dtype(lse, (torch.float32,), "lse")
+        if lse.numel() != heads * Sq or not lse.is_contiguous():
+            raise ValueError("lse needs heads * Sq contiguous float32 entries")
+        lp = _dev_ptr(lse, "lse")
+    rc = load_library().attention_bf16(
+        _dev_ptr(Q, "Q"), Q.stride(-2), hs(Q), _dev_ptr(K, "K"), K.stride(-2), hs(K),
+        _dev_ptr(V, "V"), V.stride(-2), hs(V), _dev_ptr(O, "O"), O.stride(-2), hs(O), lp,
+        heads, Sq, Sk, d, float(scale), int(bool(causal)), _stream(stream))
+    _check("attention_bf16", rc)
+    return O
 
 
 def _fp8_ptr(t, name):

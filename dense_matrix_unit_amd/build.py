@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdmu.so")
 SOURCES = ["dmu_api.cpp", "gemm.hip", "gemm_block.hip", "gemm_skinny.hip", "quantize.hip",
-           "probe.hip"]
+           "probe.hip", "attention.hip"]
 HEADERS = ["dmu_device.h", "dmu_internal.h", "gemm_common.h"]
 
 
@@ -38,8 +38,11 @@ COMMON = [
 
 
 # Per-file code-generation options.  The block-scaled FP8 kernel promotes MFMA
-# results with VALU FMAs, which cannot read AGPRs: its MFMAs must write VGPRs.
-EXTRA = {"gemm_block.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+# results with VALU FMAs, and the attention kernel rescales its output
+# accumulators; VALU instructions cannot read AGPRs, so their MFMAs must write
+# VGPRs.
+EXTRA = {"gemm_block.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+         "attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def _compile(src: str) -> str:

@@ -1,0 +1,310 @@
+// Attention chain for gfx950: O = softmax(scale * Q K^T) V per head, BF16
+// inputs, FP32 accumulation, BF16 output.  Two products are chained through
+// a row-wise softmax without the scores ever leaving the chip: the chain the
+// "Tensor Cores" chapter (ai-infra-handbooks), section "mma.sync: the register
+// layout is explicit", names as FlashAttention's, where one product's output
+// is worked on in registers and fed to the next.  The softmax is taken online
+// over blocks of 64 keys (running row maximum m and sum l; the partial output
+// is rescaled by exp(m_old - m_new) whenever a row's maximum moves).
+//
+// Layout on the chip, per workgroup of 4 waves and 128 query rows:
+//  * each wave owns 32 query rows; its Q rows sit in registers for the whole
+//    kernel (B operand of the first product);
+//  * both products use the swapped form (K or V^T first), so a lane always
+//    holds one query row: lane l has row l % 32 and, of each 32-wide tile, the
+//    columns 8q + 4(l/32) + r (register 4q + r).  The scores of a 16-key step
+//    are then exactly the B operand the second product needs, so P goes from
+//    the score registers straight into the next MFMA, rounded to BF16;
+//  * a block of 64 keys is staged in LDS: K rows by direct LDS copies, two
+//    128-byte halves per row when d = 128, with the 16-byte chunks
+//    XOR-swizzled by row; V transposed through registers into V^T rows of 64
+//    keys, the keys of each 16-key group ordered so that the 8 a lane half
+//    needs are one 16-byte chunk;
+//  * two stages of K and V^T (64 KB for d = 128), so two workgroups share a
+//    CU and one wave's softmax arithmetic can run beside another's MFMAs;
+//  * the copies of block t+2 go out right after the barrier that ends block
+//    t, one barrier per block.
+#include "dmu_device.h"
+#include "dmu_internal.h"
+#include "gemm_common.h"
+
+namespace dmu {
+namespace {
+
+constexpr int kBM = 128;  // query rows per workgroup (32 per wave)
+constexpr int kBN = 64;   // keys per block
+constexpr int kThreads = 256;
+constexpr float kMinusBig = -1.0e30f;  // running maximum before the first key
+
+// Physical 16-byte chunk of logical chunk c of a 128-byte LDS row r: c ^ aswz(r).
+__device__ __forceinline__ int aswz(int r) { return (r ^ (r >> 3)) & 7; }
+
+// Position of key j (0..63) in a V^T row: within each group of 16 keys the
+// runs of 4 keys go to slots 0, 2, 1, 3.  A lane half h takes keys 4h..4h+3
+// and 8+4h..8+4h+3 of the group in one MFMA step; they become positions
+// 8h..8h+7, i.e. chunk 2*(group) + h.
+__device__ __forceinline__ int vpos(int j) {
+  const int a = (j >> 2) & 3;
+  return (j & ~15) | ((((a & 1) << 1) | (a >> 1)) << 2) | (j & 3);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  return (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void
+attention_kernel(AttnArgs p) {
+  static_assert(D == 64 || D == 128, "head dimension");
+  constexpr int NSTEP = D / 16;              // 16-wide d steps of the first product
+  constexpr int NT = D / 32;                 // 32-column tiles of the output
+  constexpr int KROW = 128;                  // bytes of a K half-row / a V^T row
+  constexpr int K_BYTES = kBN * D * 2;       // one K stage: D/64 halves of 64 x 128 B
+  constexpr int V_BYTES = D * kBN * 2;       // one V^T stage: D rows of 128 B
+  constexpr int KCOPY = K_BYTES / 16 / kThreads;  // 16-byte K copies per thread per block
+  constexpr int CPR = D / 8;                 // 16-byte chunks of a V row
+  constexpr int RPT = kBN * CPR / kThreads;  // V rows per thread (4 or 2)
+  constexpr int OB = 32 * D * 2;             // one wave's staged output rows
+  static_assert(4 * OB <= 2 * K_BYTES + 2 * V_BYTES, "output staging fits");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * K_BYTES + 2 * V_BYTES];
+  uint8_t* const sK = smem;
+  uint8_t* const sV = smem + 2 * K_BYTES;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rl = lane & 31, hl = lane >> 5;
+
+  // Workgroup -> (head, query block).  Dispatch goes round robin over the 8
+  // XCDs; give each XCD a contiguous run of ids, so the query blocks of one
+  // head (which read the same K and V) share an L2.  Causal: the longest
+  // query blocks of a head first.
+  const int nqb = (int)((p.Sq + kBM - 1) / kBM);
+  int logical;
+  {
+    const int b = blockIdx.x, T = gridDim.x;
+    const int x = b & 7, per = T >> 3, rem = T & 7;
+    logical = __builtin_amdgcn_readfirstlane(x * per + (x < rem ? x : rem) + (b >> 3));
+  }
+  const int64_t bh = logical / nqb;
+  int qb = logical - (int)(bh * nqb);
+  if constexpr (CAUSAL) qb = nqb - 1 - qb;
+  const int64_t q0 = (int64_t)qb * kBM;
+  const int64_t i0 = q0 + wave * 32;  // the wave's first query row
+  const int64_t off = p.Sk - p.Sq;    // causal: row i sees keys j <= i + off
+  int64_t kend = p.Sk;
+  if constexpr (CAUSAL) kend = min(p.Sk, q0 + kBM + off);
+  const int nblk = (int)((kend + kBN - 1) / kBN);
+
+  const uint16_t* Qh = p.Q + bh * p.hq;
+  const uint16_t* Kh = p.K + bh * p.hk;
+  const uint16_t* Vh = p.V + bh * p.hv;
+
+  // ---- Q rows of this wave, in registers: lane holds row i0 + l%32, d = 16s + 8h .. +7
+  u32x4_t qf[NSTEP];
+  {
+    const __amdgpu_buffer_rsrc_t rQ = make_rsrc(Qh, ((p.Sq - 1) * p.ldq + D) * 2);
+    const int64_t i = i0 + rl;
+    const uint32_t vo = i < p.Sq ? (uint32_t)(i * p.ldq * 2) + (uint32_t)hl * 16u : kOOB;
+#pragma unroll
+    for (int s = 0; s < NSTEP; ++s) qf[s] = buffer_load16(rQ, vo, (uint32_t)s * 32u);
+  }
+
+  // ---- per-thread parts of the block copies (the block start moves the resource base)
+  // K: copy unit u = it * 256 + tid -> half st = u / 512, row j, slot c of that
+  // half; it fetches logical chunk c ^ aswz(j) of the row's half st.
+  uint32_t kvo[KCOPY];
+#pragma unroll
+  for (int it = 0; it < KCOPY; ++it) {
+    const int u = it * kThreads + tid, st = u >> 9, j = (u >> 3) & 63, c = u & 7;
+    kvo[it] = (uint32_t)j * (uint32_t)(p.ldk * 2) + (uint32_t)st * KROW +
+              (uint32_t)((c ^ aswz(j)) << 4);
+  }
+  // V: thread loads rows j0 .. j0+RPT-1, columns n0 .. n0+7
+  const int vcg = tid % CPR, vj0 = (tid / CPR) * RPT, vn0 = vcg * 8;
+  u32x4_t vr[RPT];
+
+  auto issue_block = [&](int t, int stage) __attribute__((always_inline)) {
+    const int64_t k0 = (int64_t)t * kBN;
+    const int64_t rows = p.Sk - k0;  // >= 1
+    const __amdgpu_buffer_rsrc_t rK = make_rsrc(Kh + k0 * p.ldk, ((rows - 1) * p.ldk + D) * 2);
+#pragma unroll
+    for (int it = 0; it < KCOPY; ++it)
+      buffer_load_lds16(rK, sK + stage * K_BYTES + (it * kThreads + wave * 64) * 16, kvo[it], 0);
+    const __amdgpu_buffer_rsrc_t rV = make_rsrc(Vh + k0 * p.ldv, ((rows - 1) * p.ldv + D) * 2);
+#pragma unroll
+    for (int r = 0; r < RPT; ++r)
+      vr[r] = buffer_load16(rV, (uint32_t)(vj0 + r) * (uint32_t)(p.ldv * 2) + (uint32_t)vn0 * 2u,
+                            0);
+  };
+  // V^T(t) from the registers: column n0 + e of rows j0.. is RPT keys at
+  // positions vpos(j0) .. of V^T row n0 + e
+  auto write_vt = [&](int stage) __attribute__((always_inline)) {
+    uint8_t* base = sV + stage * V_BYTES;
+    const int pos = vpos(vj0);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int n = vn0 + e, w = e >> 1;
+      const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;  // high or low halves
+      uint8_t* dst = base + n * KROW + ((((pos >> 3) ^ aswz(n))) << 4) + (pos & 7) * 2;
+      if constexpr (RPT == 4) {
+        const uint32_t lo = __builtin_amdgcn_perm(vr[1][w], vr[0][w], sel);
+        const uint32_t hi = __builtin_amdgcn_perm(vr[3][w], vr[2][w], sel);
+        *(uint2*)dst = make_uint2(lo, hi);
+      } else {
+        *(uint32_t*)dst = __builtin_amdgcn_perm(vr[1][w], vr[0][w], sel);
+      }
+    }
+  };
+
+  // ---- prologue: block 0 staged, block 1 in flight
+  issue_block(0, 0);
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<0>());
+  write_vt(0);
+  if (nblk > 1) issue_block(1, 1);
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<63>());  // LDS writes done, copies in flight
+  stage_barrier();
+
+  const float c = p.scale * kLog2e;  // exp(scale * x) = exp2(c * x)
+  f32x16_t o[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) o[nt] = f32x16_t{};
+  float m = kMinusBig;  // running row maximum of the raw scores (both lane halves agree)
+  float l = 0.0f;       // this lane's part of the running row sum
+  const int64_t irow = i0 + rl;
+  const int64_t lim_row = CAUSAL ? min(p.Sk - 1, irow + off) : p.Sk - 1;  // last key the row sees
+
+  for (int t = 0; t < nblk; ++t) {
+    const int stage = t & 1;
+    const int64_t k0 = (int64_t)t * kBN;
+    bool visible = true, masked = k0 + kBN > p.Sk;
+    if constexpr (CAUSAL) {
+      visible = k0 <= i0 + 31 + off;
+      masked = masked || k0 + kBN - 1 > i0 + off;
+    }
+    if (visible) {
+      // ---- scores S^T = K Q^T, two 32-key tiles
+      const uint8_t* kb = sK + stage * K_BYTES;
+      f32x16_t sc[2] = {f32x16_t{}, f32x16_t{}};
+#pragma unroll
+      for (int s = 0; s < NSTEP; ++s) {
+        const int dc = 2 * s + hl, half = dc >> 3, cc = dc & 7;
+#pragma unroll
+        for (int jt = 0; jt < 2; ++jt) {
+          const int j = jt * 32 + rl;
+          const u32x4_t kf =
+              *(const u32x4_t*)(kb + half * (kBN * KROW) + j * KROW + ((cc ^ aswz(j)) << 4));
+          sc[jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kf),
+                                                           __builtin_bit_cast(bf16x8_t, qf[s]),
+                                                           sc[jt], 0, 0, 0);
+        }
+      }
+      // ---- keys past the end, or past the row's causal limit
+      if (masked) {
+        const int lim = (int)max(min(lim_row - k0, (int64_t)kBN), (int64_t)-1);
+#pragma unroll
+        for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int j = jt * 32 + (v >> 2) * 8 + hl * 4 + (v & 3);
+            if (j > lim) sc[jt][v] = -__builtin_huge_valf();
+          }
+      }
+      // ---- online softmax: row maximum over both lane halves
+      float mx = sc[0][0];
+#pragma unroll
+      for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sc[jt][v]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mnew = fmaxf(m, mx);
+      const float alpha = __builtin_amdgcn_exp2f((m - mnew) * c);
+      m = mnew;
+      const float mc = mnew * c;
+      uint32_t pk[2][8];
+      float rs = 0.0f;
+#pragma unroll
+      for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+        for (int w = 0; w < 8; ++w) {
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[jt][2 * w], c, -mc));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[jt][2 * w + 1], c, -mc));
+          rs += p0 + p1;
+          pk[jt][w] = pack_bf16(p0, p1);
+        }
+      l = l * alpha + rs;
+      if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) o[nt] *= alpha;
+      }
+      // ---- O^T += V^T P^T, four 16-key steps
+      const uint8_t* vb = sV + stage * V_BYTES;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const int jt = ks >> 1, w0 = (ks & 1) * 4;
+        const u32x4_t pf = {pk[jt][w0], pk[jt][w0 + 1], pk[jt][w0 + 2], pk[jt][w0 + 3]};
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const int n = nt * 32 + rl;
+          const u32x4_t vf = *(const u32x4_t*)(vb + n * KROW + (((2 * ks + hl) ^ aswz(n)) << 4));
+          o[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vf),
+                                                          __builtin_bit_cast(bf16x8_t, pf), o[nt],
+                                                          0, 0, 0);
+        }
+      }
+    }
+    // ---- stage block t+1 (its copies are in), then start block t+2
+    if (t + 1 < nblk) {
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<0>());
+      write_vt(stage ^ 1);
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<63>());
+    }
+    stage_barrier();  // block t's stage is free; block t+1's is complete
+    if (t + 2 < nblk) issue_block(t + 2, stage);
+  }
+
+  // ---- epilogue: O / l, rounded to BF16, staged per wave and stored in row segments
+  l += __shfl_xor(l, 32);
+  const float inv = 1.0f / l;
+  {
+    constexpr int RB = D * 2;       // staged row bytes
+    constexpr int UPR = RB / 16;    // 16-byte units per row
+    constexpr int RPI = 64 / UPR;   // rows per read instruction
+    uint8_t* wb = smem + wave * OB;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4_t x = {o[nt][4 * q] * inv, o[nt][4 * q + 1] * inv, o[nt][4 * q + 2] * inv,
+                           o[nt][4 * q + 3] * inv};
+        const int u = nt * 4 + q;  // columns 8u .. 8u+7; this lane half has 4u*2 + 4h ..
+        *(uint2*)(wb + rl * RB + ((u ^ (rl & (UPR - 1))) << 4) + hl * 8) =
+            make_uint2(pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3]));
+      }
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<63>());  // own region: no barrier
+    uint16_t* Oh = p.O + bh * p.ho;
+#pragma unroll
+    for (int it = 0; it < 32 / RPI; ++it) {
+      const int r = it * RPI + lane / UPR, u = lane % UPR;
+      const u32x4_t v = *(const u32x4_t*)(wb + r * RB + ((u ^ (r & (UPR - 1))) << 4));
+      const int64_t i = i0 + r;
+      if (i < p.Sq) *(u32x4_t*)(Oh + i * p.ldo + u * 8) = v;
+    }
+  }
+  if (p.lse && hl == 0 && irow < p.Sq) p.lse[bh * p.Sq + irow] = m * p.scale + __logf(l);
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch(const AttnArgs& a, hipStream_t s) {
+  const int64_t wgs = (a.Sq + kBM - 1) / kBM * a.BH;
+  hipLaunchKernelGGL((attention_kernel<D, CAUSAL>), dim3((unsigned)wgs), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attention_bf16(const AttnArgs& a, int d, int causal, hipStream_t s) {
+  if (d == 64) return causal ? launch<64, true>(a, s) : launch<64, false>(a, s);
+  return causal ? launch<128, true>(a, s) : launch<128, false>(a, s);
+}
+
+}  // namespace dmu

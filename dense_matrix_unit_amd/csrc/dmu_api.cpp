@@ -2,6 +2,7 @@
 // Semantics and error behaviour of each entry point are documented in
 // include/dmu.h and include/dmu_probe.h.
 #include <hip/hip_runtime.h>
+#include <math.h>
 #include <stdint.h>
 
 #include "../../include/dmu.h"
@@ -76,6 +77,33 @@ int gemm_grouped_bf16(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t
   a.Mmax = max_m;
   (void)hipGetLastError();
   return finish(dmu::launch_gemm_grouped_bf16(a, (hipStream_t)stream));
+}
+
+int attention_bf16(const uint16_t* Q, int64_t ldq, int64_t head_stride_q, const uint16_t* K,
+                   int64_t ldk, int64_t head_stride_k, const uint16_t* V, int64_t ldv,
+                   int64_t head_stride_v, uint16_t* O, int64_t ldo, int64_t head_stride_o,
+                   float* lse, int64_t heads, int64_t Sq, int64_t Sk, int64_t d, float scale,
+                   int causal, void* stream) {
+  if (!Q || !K || !V || !O) return DMU_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return DMU_ERR_INVALID_ARG;
+  if (heads < 1 || Sq < 1 || Sk < 1 || (causal != 0 && causal != 1)) return DMU_ERR_INVALID_ARG;
+  if (causal && Sq > Sk) return DMU_ERR_INVALID_ARG;
+  if (!(scale > 0.0f) || !(scale < INFINITY)) return DMU_ERR_INVALID_ARG;
+  const int64_t ld[4] = {ldq, ldk, ldv, ldo};
+  const int64_t hs[4] = {head_stride_q, head_stride_k, head_stride_v, head_stride_o};
+  for (int t = 0; t < 4; ++t)
+    if (ld[t] < d || (ld[t] * 2) % 16 || hs[t] < 0 || (hs[t] * 2) % 16) return DMU_ERR_INVALID_ARG;
+  if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16) ||
+      (lse && !aligned(lse, 4)))
+    return DMU_ERR_INVALID_ARG;
+  // one head's rows are addressed with 32-bit byte offsets
+  if (Sq * ldq * 2 >= kMaxTileBytes || Sk * ldk * 2 >= kMaxTileBytes ||
+      Sk * ldv * 2 >= kMaxTileBytes || ((Sq + 127) / 128) * heads > INT32_MAX)
+    return DMU_ERR_UNSUPPORTED;
+  dmu::AttnArgs a{Q,     K,     V,     O,  lse, ldq, ldk, ldv, ldo, head_stride_q, head_stride_k,
+                  head_stride_v, head_stride_o, heads, Sq, Sk, scale};
+  (void)hipGetLastError();
+  return finish(dmu::launch_attention_bf16(a, (int)d, causal, (hipStream_t)stream));
 }
 
 int gemm_fp8_scaled(const uint8_t* A, int64_t lda, int fmt_a, const uint8_t* B, int64_t ldb,

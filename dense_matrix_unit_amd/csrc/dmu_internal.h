@@ -34,6 +34,21 @@ struct GemmArgs {
   const float* out_scale = nullptr;  // FP8 out: D ~ decode(q) * out_scale[0]
 };
 
+// Attention chain, per head bh (0 <= bh < BH): O = softmax(scale * Q K^T) V,
+// row i of a causal head seeing keys j <= i + Sk - Sq.  Strides in elements:
+// row strides ld*, head strides h*.  lse (optional) is [BH][Sq] FP32.
+struct AttnArgs {
+  const uint16_t* Q;
+  const uint16_t* K;
+  const uint16_t* V;
+  uint16_t* O;
+  float* lse;
+  int64_t ldq, ldk, ldv, ldo;
+  int64_t hq, hk, hv, ho;
+  int64_t BH, Sq, Sk;
+  float scale;
+};
+
 // kMX / kMX4: MXFP8, scales fetched one / four K slices at a time;
 // kMXF4: MXFP4 (E2M1 x E2M1, row strides in bytes), scales two slices at a time
 // kBF16G: BF16 grouped over experts (B stored N x K per expert);
@@ -47,6 +62,7 @@ enum GemmKind { kBF16 = 0, kFP8Tensor = 1, kFP8Block = 2, kMX = 3, kMX4 = 4, kMX
 // kernel configuration and launch it.  They return a hipError_t.
 hipError_t launch_gemm_bf16(const GemmArgs& a, int b_col_major, hipStream_t s);
 hipError_t launch_gemm_grouped_bf16(const GemmArgs& a, hipStream_t s);
+hipError_t launch_attention_bf16(const AttnArgs& a, int d, int causal, hipStream_t s);
 // fused epilogue (a.bias / a.act / a.out_fp8 set)
 hipError_t launch_gemm_bf16_fused(const GemmArgs& a, int b_col_major, hipStream_t s);
 hipError_t launch_gemm_fp8_fused(const GemmArgs& a, int fmt_a, int fmt_b, hipStream_t s);

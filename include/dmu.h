@@ -314,6 +314,43 @@ int gemm_fp8_fused(const uint8_t* A, int64_t lda, int fmt_a, const uint8_t* B, i
                    int act, void* D, int64_t ldd, int d_dtype, const float* d_scale, int64_t M,
                    int64_t N, int64_t K, void* stream);
 
+/*
+ * attention_bf16: two products chained through a row-wise softmax, the
+ * scores never written to memory -- the chain the "Tensor Cores" chapter
+ * (ai-infra-handbooks), section "mma.sync: the register layout is explicit",
+ * names as FlashAttention's (one product's output worked on in registers and
+ * fed to the next).  For each head bh < heads and query row i < Sq:
+ *
+ *   s_j    = scale * sum_k Q[i][k] K[j][k]            (FP32 accumulation)
+ *   O[i]   = sum_j exp(s_j - max s) V[j] / sum_j exp(s_j - max s)
+ *   lse[i] = log sum_j exp(s_j)
+ *
+ * over the keys j the row sees: all Sk of them, or with causal = 1 the keys
+ * j <= i + (Sk - Sq) (the last query row sees every key; requires Sq <= Sk).
+ * The softmax is taken online over blocks of keys: the weights are computed
+ * in FP32 (hardware exp2), rounded to BF16 for the second product, which
+ * accumulates in FP32; the row sum uses the FP32 weights.  O is rounded to
+ * BF16 once at the end.
+ *
+ *   Q : heads x Sq x d BF16, row i of head bh at Q + bh*head_stride_q + i*ldq
+ *   K, V : heads x Sk x d BF16, likewise (ldk, head_stride_k, ldv, head_stride_v)
+ *   O : heads x Sq x d BF16 output, likewise (ldo, head_stride_o); must not
+ *       overlap Q, K or V
+ *   lse : optional heads x Sq FP32 output (NULL: not written), natural log
+ *   d = 64 or 128; scale > 0 and finite (typically 1 / sqrt(d)).
+ * Scores must stay finite in FP32.  All pointers are device pointers owned by
+ * the caller; Q, K, V, O 16-byte aligned, row and head strides multiples of
+ * 8 elements, row strides >= d.
+ * Errors: DMU_ERR_INVALID_ARG for a null or misaligned pointer, d not 64 or
+ * 128, non-positive sizes, causal with Sq > Sk, a bad stride or scale;
+ * DMU_ERR_UNSUPPORTED when one head spans 2^31 bytes or more.
+ */
+int attention_bf16(const uint16_t* Q, int64_t ldq, int64_t head_stride_q, const uint16_t* K,
+                   int64_t ldk, int64_t head_stride_k, const uint16_t* V, int64_t ldv,
+                   int64_t head_stride_v, uint16_t* O, int64_t ldo, int64_t head_stride_o,
+                   float* lse, int64_t heads, int64_t Sq, int64_t Sk, int64_t d, float scale,
+                   int causal, void* stream);
+
 /* Human-readable text for a status code (static storage, never NULL). */
 const char* dmu_status_string(int status);
 

@@ -220,3 +220,26 @@ def call_fp8_fused(**kw):
 ])
 def test_gemm_fp8_fused_rejects(kw):
     assert call_fp8_fused(**kw) == dmu.DMU_ERR_INVALID_ARG
+
+
+def call_attention(**kw):
+    a = dict(Q=FAKE, ldq=128, hq=128 * 256, K=FAKE, ldk=128, hk=128 * 256, V=FAKE, ldv=128,
+             hv=128 * 256, O=FAKE, ldo=128, ho=128 * 256, lse=None, heads=2, Sq=256, Sk=256,
+             d=128, scale=0.088, causal=0, stream=None)
+    a.update(kw)
+    return dmu.load_library().attention_bf16(*a.values())
+
+
+@pytest.mark.parametrize("kw", [
+    dict(Q=None), dict(K=None), dict(V=None), dict(O=None), dict(d=96), dict(d=256),
+    dict(heads=0), dict(Sq=0), dict(Sk=-1), dict(causal=2), dict(causal=1, Sq=300),
+    dict(scale=0.0), dict(scale=-1.0), dict(scale=float("inf")), dict(scale=float("nan")),
+    dict(ldq=120), dict(ldk=100), dict(ldv=132), dict(ldo=64), dict(hq=-8), dict(hv=12),
+    dict(Q=FAKE + 8), dict(O=FAKE + 2), dict(lse=FAKE + 2),
+])
+def test_attention_rejects(kw):
+    assert call_attention(**kw) == dmu.DMU_ERR_INVALID_ARG
+
+
+def test_attention_rejects_heads_past_32_bit_offsets():
+    assert call_attention(ldq=1 << 16, Sq=1 << 15) == dmu.DMU_ERR_UNSUPPORTED
