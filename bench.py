@@ -199,6 +199,31 @@ class Bench:
         bytes_ = ab * (M * K + N * K) + (2.0 if kind == "bf16_gelu" else 1.0) * M * N + 4.0 * N
         return self.report(t, flop, bytes_, peak, copies)
 
+    def attention_leg(self, causal, steps, warmup):
+        """The attention chain: 32 heads (batch 2 x 16), 4096 queries and keys,
+        d = 128, N(0,1) BF16 Q, K, V, scale 1/sqrt(d), with and without the
+        causal mask.  FLOP: the two products over the keys each row sees,
+        4 d per (row, key) pair."""
+        torch, dmu = self.torch, self.dmu
+        w = self.wl.WORKLOADS["attention_bf16_32x4096x4096x128"]
+        H, S, d = w["heads"], w["S"], w["d"]
+        Q = self.normal_bf16((H * S, d), 1).view(H, S, d)
+        K = self.normal_bf16((H * S, d), 2).view(H, S, d)
+        V = self.normal_bf16((H * S, d), 3).view(H, S, d)
+        O = torch.empty_like(Q)
+        scale = d ** -0.5
+
+        def launch(i):
+            dmu.attention_bf16(Q, K, V, O, scale, causal)
+
+        t = time_launches(torch, launch, steps, warmup)
+        pairs = S * (S + 1) / 2 if causal else S * S
+        flop = 4.0 * d * H * pairs
+        bytes_ = 2.0 * 4 * H * S * d
+        r = self.report(t, flop, bytes_, PEAK_BF16_TFLOPS, 1)
+        r["heads"], r["seq"], r["head_dim"], r["causal"] = H, S, d, bool(causal)
+        return r
+
     def grouped_leg(self, steps, warmup):
         """Mixture-of-experts grouped BF16 product: 32 experts, 16384 routed
         rows split by expert_rows (seed 4), N = 4096, K = 7168; the row offsets
@@ -470,6 +495,15 @@ def main():
     if want("fp8_e4m3_4096_bias_relu_fp8out"):
         legs["fp8_e4m3_4096_bias_relu_fp8out"] = b.fused_leg("fp8_relu_fp8out", S, W, 10)
         log("fp8 4096 + bias + ReLU -> E4M3: %s" % legs["fp8_e4m3_4096_bias_relu_fp8out"])
+    # the attention legs follow half a second of input generation on the host,
+    # during which the idle GPU clocks down: they need a longer warmup
+    SA, WA = max(S // 2, 20), max(W // 2, 20)
+    if want("attention_bf16_32x4096x4096x128"):
+        legs["attention_bf16_32x4096x4096x128"] = b.attention_leg(False, SA, WA)
+        log("attention 32 x 4096 x 4096 x 128: %s" % legs["attention_bf16_32x4096x4096x128"])
+    if want("attention_bf16_32x4096x4096x128_causal"):
+        legs["attention_bf16_32x4096x4096x128_causal"] = b.attention_leg(True, SA, WA)
+        log("attention causal: %s" % legs["attention_bf16_32x4096x4096x128_causal"])
     if want("moe_bf16_32x16384x4096x7168"):
         legs["moe_bf16_32x16384x4096x7168"] = b.grouped_leg(S4, W4)
         log("moe grouped: %s" % legs["moe_bf16_32x16384x4096x7168"])

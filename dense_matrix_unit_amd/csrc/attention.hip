@@ -48,9 +48,18 @@ __device__ __forceinline__ int vpos(int j) {
   return (j & ~15) | ((((a & 1) << 1) | (a >> 1)) << 2) | (j & 3);
 }
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Two FP32 values -> two BF16 (round to nearest even) in one v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-  return (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
+
+// The reference maximum of a row moves only when a block's maximum exceeds
+// it by more than this (in exp2 units): weights then stay below 2^8, and the
+// output is rescaled rarely instead of after nearly every block.
+constexpr float kRescaleSlack = 8.0f;
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void
@@ -164,6 +173,15 @@ attention_kernel(AttnArgs p) {
   __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<63>());  // LDS writes done, copies in flight
   stage_barrier();
 
+  // Fragment reads.  Row 32t + l%32 of a K half-tile or of V^T has
+  // aswz = aswz(l%32) ^ (4t & 7), and the chunk a lane half h reads is
+  // (2s + h) ^ aswz = ((2s ^ 4t) & 7) ^ (h ^ aswz(l%32)): one of four per-lane
+  // offsets (k = 0, 2, 4, 6) plus a constant, which the LDS read takes as its
+  // immediate offset.
+  int foff[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) foff[k] = rl * KROW + (((2 * k) ^ hl ^ aswz(rl)) << 4);
+
   const float c = p.scale * kLog2e;  // exp(scale * x) = exp2(c * x)
   f32x16_t o[NT];
 #pragma unroll
@@ -183,20 +201,25 @@ attention_kernel(AttnArgs p) {
     }
     if (visible) {
       // ---- scores S^T = K Q^T, two 32-key tiles
+      // (fragment reads run two MFMAs ahead of their use: a ring of three)
       const uint8_t* kb = sK + stage * K_BYTES;
+      auto kread = [&](int x) __attribute__((always_inline)) {
+        const int s = x >> 1, jt = x & 1;  // d step, key tile
+        const int half = s >> 2, k = ((2 * s) ^ (4 * jt)) & 7;
+        return *(const u32x4_t*)(kb + foff[k >> 1] + half * (kBN * KROW) + jt * 32 * KROW);
+      };
       f32x16_t sc[2] = {f32x16_t{}, f32x16_t{}};
+      u32x4_t kr[3];
+      kr[0] = kread(0);
+      kr[1] = kread(1);
 #pragma unroll
-      for (int s = 0; s < NSTEP; ++s) {
-        const int dc = 2 * s + hl, half = dc >> 3, cc = dc & 7;
-#pragma unroll
-        for (int jt = 0; jt < 2; ++jt) {
-          const int j = jt * 32 + rl;
-          const u32x4_t kf =
-              *(const u32x4_t*)(kb + half * (kBN * KROW) + j * KROW + ((cc ^ aswz(j)) << 4));
-          sc[jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kf),
-                                                           __builtin_bit_cast(bf16x8_t, qf[s]),
-                                                           sc[jt], 0, 0, 0);
-        }
+      for (int x = 0; x < 2 * NSTEP; ++x) {
+        if (x + 2 < 2 * NSTEP) kr[(x + 2) % 3] = kread(x + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        sc[x & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kr[x % 3]),
+                                                            __builtin_bit_cast(bf16x8_t, qf[x >> 1]),
+                                                            sc[x & 1], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
       // ---- keys past the end, or past the row's causal limit
       if (masked) {
@@ -216,8 +239,9 @@ attention_kernel(AttnArgs p) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sc[jt][v]);
       mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mnew = fmaxf(m, mx);
-      const float alpha = __builtin_amdgcn_exp2f((m - mnew) * c);
+      const bool move = (mx - m) * c > kRescaleSlack;  // false for an all-masked row (-inf)
+      const float mnew = move ? mx : m;
+      const float alpha = move ? __builtin_amdgcn_exp2f((m - mnew) * c) : 1.0f;
       m = mnew;
       const float mc = mnew * c;
       uint32_t pk[2][8];
@@ -232,24 +256,30 @@ attention_kernel(AttnArgs p) {
           pk[jt][w] = pack_bf16(p0, p1);
         }
       l = l * alpha + rs;
-      if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
+      if (__builtin_amdgcn_ballot_w64(move)) {
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) o[nt] *= alpha;
       }
       // ---- O^T += V^T P^T, four 16-key steps
       const uint8_t* vb = sV + stage * V_BYTES;
+      auto vread = [&](int x) __attribute__((always_inline)) {
+        const int ks = x / NT, nt = x % NT;  // key step, output tile
+        const int k = ((2 * ks) ^ (4 * nt)) & 7;
+        return *(const u32x4_t*)(vb + foff[k >> 1] + nt * 32 * KROW);
+      };
+      u32x4_t vq[3];
+      vq[0] = vread(0);
+      vq[1] = vread(1);
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const int jt = ks >> 1, w0 = (ks & 1) * 4;
+      for (int x = 0; x < 4 * NT; ++x) {
+        if (x + 2 < 4 * NT) vq[(x + 2) % 3] = vread(x + 2);
+        const int ks = x / NT, nt = x % NT, jt = ks >> 1, w0 = (ks & 1) * 4;
         const u32x4_t pf = {pk[jt][w0], pk[jt][w0 + 1], pk[jt][w0 + 2], pk[jt][w0 + 3]};
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          const int n = nt * 32 + rl;
-          const u32x4_t vf = *(const u32x4_t*)(vb + n * KROW + (((2 * ks + hl) ^ aswz(n)) << 4));
-          o[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vf),
-                                                          __builtin_bit_cast(bf16x8_t, pf), o[nt],
-                                                          0, 0, 0);
-        }
+        __builtin_amdgcn_sched_barrier(0);
+        o[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vq[x % 3]),
+                                                        __builtin_bit_cast(bf16x8_t, pf), o[nt], 0,
+                                                        0, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     // ---- stage block t+1 (its copies are in), then start block t+2

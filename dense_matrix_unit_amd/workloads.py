@@ -81,6 +81,8 @@ WORKLOADS = {
                            out="bf16"),
     "moe_bf16_32x16384x4096x7168": dict(G=32, total_rows=16384, N=4096, K=7168, dist="normal",
                                         routing="expert_rows(spread 0.5, seed 4)", out="bf16"),
+    "attention_bf16_32x4096x4096x128": dict(heads=32, S=4096, d=128, dist="normal",
+                                            scale="1/sqrt(d)", out="bf16"),
     "acc_sweep_256": dict(M=256, N=256, Ks=(256, 1024, 4096, 16384, 65536), dist="normal",
                           out="f32"),
 }
