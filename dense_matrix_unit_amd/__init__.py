@@ -74,6 +74,7 @@ SYMBOLS = {
     "dmu_probe_lds_load": (_I, [_P, _P, _I, _I, _P]),
     "dmu_probe_mfma_rate": (_I, [_I, _P, _I, _I, _P, _P]),
     "dmu_probe_cvt_fp8": (_I, [_P, _I64, _I, _I, _P, _P]),
+    "dmu_probe_lds_tr16": (_I, [_P, _P, _P, _P]),
     "dmu_probe_mfma_mx": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P]),
 }
 
@@ -497,6 +498,22 @@ def probe_cvt_fp8(x, q, fmt: int = E4M3, clamp: int = 1, stream=None):
                                           _dev_ptr(q, "q"), _stream(stream))
     _check("dmu_probe_cvt_fp8", rc)
     return q
+
+
+def probe_lds_tr16(src, offsets, out, stream=None):
+    """ds_read_b64_tr_b16 probe (include/dmu_probe.h): src 1024 16-bit values
+    (GPU), offsets 64 byte offsets (host sequence), out 256 16-bit values (GPU)."""
+    torch = _torch()
+    _check_dtype(src, (torch.int16, torch.uint16, torch.bfloat16), "src")
+    _check_dtype(out, (torch.int16, torch.uint16, torch.bfloat16), "out")
+    if src.numel() != 1024 or out.numel() != 256 or not (src.is_contiguous() and
+                                                          out.is_contiguous()):
+        raise ValueError("src: 1024 and out: 256 contiguous values")
+    offs = (ctypes.c_uint32 * 64)(*[int(o) for o in offsets])
+    rc = load_library().dmu_probe_lds_tr16(_dev_ptr(src, "src"), ctypes.cast(offs, _P),
+                                           _dev_ptr(out, "out"), _stream(stream))
+    _check("dmu_probe_lds_tr16", rc)
+    return out
 
 
 def probe_lds_load(src, dst, mode: int, oob_from: int = 64, stream=None):

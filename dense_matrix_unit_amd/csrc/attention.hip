@@ -15,12 +15,15 @@
 //    columns 8q + 4(l/32) + r (register 4q + r).  The scores of a 16-key step
 //    are then exactly the B operand the second product needs, so P goes from
 //    the score registers straight into the next MFMA, rounded to BF16;
-//  * a block of 64 keys is staged in LDS: K rows by direct LDS copies, two
-//    128-byte halves per row when d = 128, with the 16-byte chunks
-//    XOR-swizzled by row; V transposed through registers into V^T rows of 64
-//    keys, the keys of each 16-key group ordered so that the 8 a lane half
-//    needs are one 16-byte chunk;
-//  * two stages of K and V^T (64 KB for d = 128), so two workgroups share a
+//  * a block of 64 keys is staged in LDS by direct copies: K rows in two
+//    128-byte halves when d = 128, V rows whole, the 16-byte chunks of both
+//    XOR-swizzled by row so that the fragment reads meet no bank conflict;
+//  * the second product needs V transposed (keys along the lane's operand):
+//    gfx950's transposing LDS read, ds_read_b64_tr_b16, gives each lane four
+//    keys of its column from four rows, so V is never transposed in
+//    registers; two such reads, of keys 4h..4h+3 and 8+4h..8+4h+3 of a 16-key
+//    step, match the order of the weights in the score registers;
+//  * two stages of K and V (64 KB for d = 128), so two workgroups share a
 //    CU and one wave's softmax arithmetic can run beside another's MFMAs;
 //  * the copies of block t+2 go out right after the barrier that ends block
 //    t, one barrier per block.
@@ -39,13 +42,24 @@ constexpr float kMinusBig = -1.0e30f;  // running maximum before the first key
 // Physical 16-byte chunk of logical chunk c of a 128-byte LDS row r: c ^ aswz(r).
 __device__ __forceinline__ int aswz(int r) { return (r ^ (r >> 3)) & 7; }
 
-// Position of key j (0..63) in a V^T row: within each group of 16 keys the
-// runs of 4 keys go to slots 0, 2, 1, 3.  A lane half h takes keys 4h..4h+3
-// and 8+4h..8+4h+3 of the group in one MFMA step; they become positions
-// 8h..8h+7, i.e. chunk 2*(group) + h.
-__device__ __forceinline__ int vpos(int j) {
-  const int a = (j >> 2) & 3;
-  return (j & ~15) | ((((a & 1) << 1) | (a >> 1)) << 2) | (j & 3);
+// Swizzle of the 16-byte chunks of V row j (d * 2 bytes): a transposing read
+// covers 4 consecutive rows and 64 bytes of each per 32 lanes; flipping bits
+// 2-3 of the chunk index with the row puts those 4 x 64 bytes in distinct
+// banks.
+template <int D>
+__device__ __forceinline__ int vswz(int j) {
+  return D == 128 ? (j & 3) << 2 : ((j >> 1) & 1) << 2;
+}
+
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
+
+// gfx950 transposing LDS read: in each group of 16 lanes, lane i names row
+// i / 4, 16-bit elements 4 (i % 4) .. +3 of a row-major 4 x 16 block; lane j
+// receives element j of the 4 rows, in row order.
+__device__ __forceinline__ uint2 read_tr16(const uint8_t* p) {
+  const v4i16_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)p);
+  return __builtin_bit_cast(uint2, r);
 }
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -67,12 +81,13 @@ attention_kernel(AttnArgs p) {
   static_assert(D == 64 || D == 128, "head dimension");
   constexpr int NSTEP = D / 16;              // 16-wide d steps of the first product
   constexpr int NT = D / 32;                 // 32-column tiles of the output
-  constexpr int KROW = 128;                  // bytes of a K half-row / a V^T row
+  constexpr int KROW = 128;                  // bytes of a K half-row
+  constexpr int VROW = D * 2;                // bytes of a V row
   constexpr int K_BYTES = kBN * D * 2;       // one K stage: D/64 halves of 64 x 128 B
-  constexpr int V_BYTES = D * kBN * 2;       // one V^T stage: D rows of 128 B
-  constexpr int KCOPY = K_BYTES / 16 / kThreads;  // 16-byte K copies per thread per block
+  constexpr int V_BYTES = kBN * VROW;        // one V stage: 64 rows
+  constexpr int KCOPY = K_BYTES / 16 / kThreads;  // 16-byte copies per thread per block, K
+  constexpr int VCOPY = V_BYTES / 16 / kThreads;  // and V
   constexpr int CPR = D / 8;                 // 16-byte chunks of a V row
-  constexpr int RPT = kBN * CPR / kThreads;  // V rows per thread (4 or 2)
   constexpr int OB = 32 * D * 2;             // one wave's staged output rows
   static_assert(4 * OB <= 2 * K_BYTES + 2 * V_BYTES, "output staging fits");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * K_BYTES + 2 * V_BYTES];
@@ -128,9 +143,13 @@ attention_kernel(AttnArgs p) {
     kvo[it] = (uint32_t)j * (uint32_t)(p.ldk * 2) + (uint32_t)st * KROW +
               (uint32_t)((c ^ aswz(j)) << 4);
   }
-  // V: thread loads rows j0 .. j0+RPT-1, columns n0 .. n0+7
-  const int vcg = tid % CPR, vj0 = (tid / CPR) * RPT, vn0 = vcg * 8;
-  u32x4_t vr[RPT];
+  // V: copy unit u -> row j = u / CPR, slot c, fetching chunk c ^ vswz(j)
+  uint32_t vvo[VCOPY];
+#pragma unroll
+  for (int it = 0; it < VCOPY; ++it) {
+    const int u = it * kThreads + tid, j = u / CPR, c = u % CPR;
+    vvo[it] = (uint32_t)j * (uint32_t)(p.ldv * 2) + (uint32_t)((c ^ vswz<D>(j)) << 4);
+  }
 
   auto issue_block = [&](int t, int stage) __attribute__((always_inline)) {
     const int64_t k0 = (int64_t)t * kBN;
@@ -141,46 +160,39 @@ attention_kernel(AttnArgs p) {
       buffer_load_lds16(rK, sK + stage * K_BYTES + (it * kThreads + wave * 64) * 16, kvo[it], 0);
     const __amdgpu_buffer_rsrc_t rV = make_rsrc(Vh + k0 * p.ldv, ((rows - 1) * p.ldv + D) * 2);
 #pragma unroll
-    for (int r = 0; r < RPT; ++r)
-      vr[r] = buffer_load16(rV, (uint32_t)(vj0 + r) * (uint32_t)(p.ldv * 2) + (uint32_t)vn0 * 2u,
-                            0);
+    for (int it = 0; it < VCOPY; ++it)
+      buffer_load_lds16(rV, sV + stage * V_BYTES + (it * kThreads + wave * 64) * 16, vvo[it], 0);
   };
-  // V^T(t) from the registers: column n0 + e of rows j0.. is RPT keys at
-  // positions vpos(j0) .. of V^T row n0 + e
-  auto write_vt = [&](int stage) __attribute__((always_inline)) {
-    uint8_t* base = sV + stage * V_BYTES;
-    const int pos = vpos(vj0);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int n = vn0 + e, w = e >> 1;
-      const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;  // high or low halves
-      uint8_t* dst = base + n * KROW + ((((pos >> 3) ^ aswz(n))) << 4) + (pos & 7) * 2;
-      if constexpr (RPT == 4) {
-        const uint32_t lo = __builtin_amdgcn_perm(vr[1][w], vr[0][w], sel);
-        const uint32_t hi = __builtin_amdgcn_perm(vr[3][w], vr[2][w], sel);
-        *(uint2*)dst = make_uint2(lo, hi);
-      } else {
-        *(uint32_t*)dst = __builtin_amdgcn_perm(vr[1][w], vr[0][w], sel);
-      }
-    }
-  };
-
   // ---- prologue: block 0 staged, block 1 in flight
   issue_block(0, 0);
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<0>());
-  write_vt(0);
-  if (nblk > 1) issue_block(1, 1);
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<63>());  // LDS writes done, copies in flight
+  if (nblk > 1) {
+    issue_block(1, 1);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<KCOPY + VCOPY>());  // block 0 (and Q) in
+  } else {
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<0>());
+  }
   stage_barrier();
 
-  // Fragment reads.  Row 32t + l%32 of a K half-tile or of V^T has
-  // aswz = aswz(l%32) ^ (4t & 7), and the chunk a lane half h reads is
-  // (2s + h) ^ aswz = ((2s ^ 4t) & 7) ^ (h ^ aswz(l%32)): one of four per-lane
-  // offsets (k = 0, 2, 4, 6) plus a constant, which the LDS read takes as its
-  // immediate offset.
+  // Fragment reads.  Row 32t + l%32 of a K half-tile has
+  // aswz = aswz(l%32) ^ (4t & 7), and the chunk a lane half h reads at d step
+  // s is (2s + h) ^ aswz = ((2s ^ 4t) & 7) ^ (h ^ aswz(l%32)): one of four
+  // per-lane offsets (k = 0, 2, 4, 6) plus a constant, which the LDS read
+  // takes as its immediate offset.
   int foff[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) foff[k] = rl * KROW + (((2 * k) ^ hl ^ aswz(rl)) << 4);
+  // V operand of output tile nt: lane i of 16-lane group g reads row 4h + i/4
+  // (+ the step's first key, + 8 for the second read), columns
+  // 32 nt + 16 (g % 2) + 4 (i % 4) .. +3; the swizzle depends on the row only
+  // through i / 4, so each tile has one per-lane offset.
+  int voff[NT];
+  {
+    const int g = lane >> 4, i = lane & 15;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+      voff[nt] = (4 * hl + (i >> 2)) * VROW +
+                 (((4 * nt + 2 * (g & 1) + ((i & 3) >> 1)) ^ vswz<D>(i >> 2)) << 4) + ((i & 1) << 3);
+  }
 
   const float c = p.scale * kLog2e;  // exp(scale * x) = exp2(c * x)
   f32x16_t o[NT];
@@ -264,8 +276,9 @@ attention_kernel(AttnArgs p) {
       const uint8_t* vb = sV + stage * V_BYTES;
       auto vread = [&](int x) __attribute__((always_inline)) {
         const int ks = x / NT, nt = x % NT;  // key step, output tile
-        const int k = ((2 * ks) ^ (4 * nt)) & 7;
-        return *(const u32x4_t*)(vb + foff[k >> 1] + nt * 32 * KROW);
+        const uint2 lo = read_tr16(vb + voff[nt] + ks * 16 * VROW);
+        const uint2 hi = read_tr16(vb + voff[nt] + (ks * 16 + 8) * VROW);
+        return u32x4_t{lo.x, lo.y, hi.x, hi.y};
       };
       u32x4_t vq[3];
       vq[0] = vread(0);
@@ -282,12 +295,8 @@ attention_kernel(AttnArgs p) {
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    // ---- stage block t+1 (its copies are in), then start block t+2
-    if (t + 1 < nblk) {
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<0>());
-      write_vt(stage ^ 1);
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<63>());
-    }
+    // ---- block t+1's copies are in; then start block t+2
+    if (t + 1 < nblk) __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<0>());
     stage_barrier();  // block t's stage is free; block t+1's is complete
     if (t + 2 < nblk) issue_block(t + 2, stage);
   }

@@ -358,6 +358,15 @@ int dmu_probe_mfma_mx(int shape, int fmt_a, int fmt_b, int opsel, const void* A,
       dmu::launch_probe_mx(shape, fmt_a, fmt_b, opsel, A, B, SA, SB, C, D, (hipStream_t)stream));
 }
 
+int dmu_probe_lds_tr16(const uint16_t* src, const uint32_t* offsets, uint16_t* out,
+                       void* stream) {
+  if (!src || !offsets || !out || !aligned(src, 2) || !aligned(out, 2)) return DMU_ERR_INVALID_ARG;
+  for (int l = 0; l < 64; ++l)
+    if (offsets[l] % 8 || offsets[l] > 2040) return DMU_ERR_INVALID_ARG;
+  (void)hipGetLastError();
+  return finish(dmu::launch_probe_tr16(src, offsets, out, (hipStream_t)stream));
+}
+
 int dmu_probe_cvt_fp8(const float* x, int64_t n, int fmt, int clamp, uint8_t* q, void* stream) {
   if (!x || !q || n < 2 || n % 2 || n > ((int64_t)1 << 31)) return DMU_ERR_INVALID_ARG;
   if ((fmt != 0 && fmt != 1) || (clamp != 0 && clamp != 1) || !aligned(x, 8))

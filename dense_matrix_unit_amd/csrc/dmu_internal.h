@@ -93,6 +93,8 @@ hipError_t launch_probe_mfma(int kind, int fa, int fb, const void* A, const void
 hipError_t launch_probe_lds(const void* src, void* dst, int mode, int oob_from, hipStream_t s);
 hipError_t launch_probe_rate(int kind, const void* src, int iters, int grid, float* out,
                              hipStream_t s);
+hipError_t launch_probe_tr16(const uint16_t* src, const uint32_t* offsets, uint16_t* out,
+                             hipStream_t s);
 hipError_t launch_probe_cvt(const float* x, int64_t n, int fmt, int clamp, uint8_t* q,
                             hipStream_t s);
 hipError_t launch_probe_mx(int shape, int fa, int fb, int opsel, const void* A, const void* B,

@@ -176,6 +176,25 @@ __global__ void probe_cvt_kernel(const float* x, int64_t npairs, uint8_t* q) {
   q[2 * t + 1] = (uint8_t)((r >> 8) & 0xFF);
 }
 
+// gfx950's transposing LDS read, ds_read_b64_tr_b16: one wave loads 2 KiB
+// of 16-bit values into LDS, then lane l issues the transposing read at byte
+// offset off.v[l] (checked on the host: 8-byte aligned, inside the 2 KiB) and
+// writes the four 16-bit values it receives to out[4l .. 4l+3].
+struct TrOffsets {
+  uint32_t v[64];
+};
+typedef short tr_v4i16 __attribute__((ext_vector_type(4)));
+__global__ void probe_tr16_kernel(const uint16_t* src, TrOffsets off, uint16_t* out) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[1024];
+  const int l = threadIdx.x;
+  for (int i = l; i < 1024; i += 64) lds[i] = src[i];
+  __syncthreads();
+  const uint32_t o = off.v[l] & 2040u;  // in range by construction (host check)
+  const tr_v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) tr_v4i16*)((uint8_t*)lds + o));
+  for (int e = 0; e < 4; ++e) out[4 * l + e] = (uint16_t)r[e];
+}
+
 // One wave copies 64 x 16 bytes (mode 0) or 64 x 4 bytes (mode 1) from src to
 // LDS with buffer loads that write LDS directly, then dumps 2 KiB of LDS to
 // dst.  Lanes >= oob_from get an out-of-range offset (they must write zeros).
@@ -349,6 +368,14 @@ hipError_t launch_probe_mx(int shape, int fa, int fb, int opsel, const void* A, 
   const uint8_t *sa = (const uint8_t*)SA, *sb = (const uint8_t*)SB;
   if (shape == 0) return probe_mx_fmt<0>(fa, fb, opsel, a, b, sa, sb, C, D, s);
   return probe_mx_fmt<1>(fa, fb, opsel, a, b, sa, sb, C, D, s);
+}
+
+hipError_t launch_probe_tr16(const uint16_t* src, const uint32_t* offsets, uint16_t* out,
+                             hipStream_t s) {
+  TrOffsets o;
+  for (int l = 0; l < 64; ++l) o.v[l] = offsets[l];
+  hipLaunchKernelGGL(probe_tr16_kernel, dim3(1), dim3(64), 0, s, src, o, out);
+  return hipGetLastError();
 }
 
 hipError_t launch_probe_cvt(const float* x, int64_t n, int fmt, int clamp, uint8_t* q,

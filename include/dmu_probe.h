@@ -103,6 +103,18 @@ int dmu_probe_mfma_mx(int shape, int fmt_a, int fmt_b, int opsel, const void* A,
  */
 int dmu_probe_cvt_fp8(const float* x, int64_t n, int fmt, int clamp, uint8_t* q, void* stream);
 
+/*
+ * gfx950's transposing LDS read (ds_read_b64_tr_b16) on known data: src is a
+ * device array of 1024 16-bit values, copied into LDS; lane l (of one wave)
+ * reads with the transposing instruction at LDS byte offset offsets[l] and
+ * writes the four 16-bit values it receives to out[4l .. 4l+3] (device, 256
+ * values).  offsets is a HOST array of 64 byte offsets, each a multiple of 8
+ * and at most 2040 (DMU_ERR_INVALID_ARG otherwise).  Exists so the tests can
+ * pin the lane layout the attention kernel's V operand relies on.
+ */
+int dmu_probe_lds_tr16(const uint16_t* src, const uint32_t* offsets, uint16_t* out,
+                       void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -369,3 +369,30 @@ def test_hardware_fp8_conversion(fmt):
     assert np.all(np.isnan(raw)) if fmt == 0 else np.all(np.isinf(raw))
     inrange = ~nan & (np.abs(x) <= fmax)
     assert np.array_equal(out[0][inrange], want[inrange])
+
+
+def run_tr16(offsets):
+    src = torch.arange(1024, dtype=torch.int16, device="cuda")
+    out = torch.full((256,), -1, dtype=torch.int16, device="cuda")
+    dmu.probe_lds_tr16(src, offsets, out)
+    torch.cuda.synchronize()
+    return out.cpu().numpy().astype(np.int64).reshape(64, 4)
+
+
+@pytest.mark.parametrize("row_elems", [32, 64, 128])
+def test_lds_transpose_read_layout(row_elems):
+    # The use the attention kernel makes of ds_read_b64_tr_b16: within each
+    # group of 16 lanes, lane i points at row i // 4, elements 4 (i % 4) ..
+    # 4 (i % 4) + 3 of a row-major block; lane j of the group then receives
+    # element j of rows 0 .. 3, in row order (a 4 x 16 block transposed).
+    # Groups start at different rows and columns to show they are independent.
+    offs, want = [], np.zeros((64, 4), np.int64)
+    for l in range(64):
+        g, i = l // 16, l % 16
+        # (rows start inside the probe's 2 KiB of LDS)
+        row0, col0 = (3 - g) * (4 if row_elems < 128 else 1), 16 * (g % 2)
+        offs.append(((row0 + i // 4) * row_elems + col0 + 4 * (i % 4)) * 2)
+        for e in range(4):
+            want[l, e] = (row0 + e) * row_elems + col0 + i
+    got = run_tr16(offs)
+    assert np.array_equal(got, want), "lane -> element indices:\n%s" % got
