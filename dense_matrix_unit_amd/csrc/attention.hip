@@ -75,6 +75,30 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
 // output is rescaled rarely instead of after nearly every block.
 constexpr float kRescaleSlack = 8.0f;
 
+// The two halves of a query row (lanes l and l ^ 32) side by side, with
+// gfx950's v_permlane32_swap_b32 (lanes 32-63 of the first register trade
+// places with lanes 0-31 of the second): on two copies of x it leaves the
+// first holding lanes 0-31 of x twice and the second lanes 32-63 twice.  It
+// is issued as inline assembly: the compiler's builtin, given the same value
+// twice, folds its two results into one.  The s_nop gives the two wait
+// states a VALU write needs before v_permlane32_swap reads the register.
+__device__ __forceinline__ void halves(float x, float& lo, float& hi) {
+  uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+  lo = __builtin_bit_cast(float, a);
+  hi = __builtin_bit_cast(float, b);
+}
+__device__ __forceinline__ float half_max(float x) {
+  float lo, hi;
+  halves(x, lo, hi);
+  return fmaxf(lo, hi);
+}
+__device__ __forceinline__ float half_sum(float x) {
+  float lo, hi;
+  halves(x, lo, hi);
+  return lo + hi;
+}
+
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 attention_kernel(AttnArgs p) {
@@ -250,7 +274,7 @@ attention_kernel(AttnArgs p) {
       for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
         for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sc[jt][v]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx = half_max(mx);
       const bool move = (mx - m) * c > kRescaleSlack;  // false for an all-masked row (-inf)
       const float mnew = move ? mx : m;
       const float alpha = move ? __builtin_amdgcn_exp2f((m - mnew) * c) : 1.0f;
@@ -302,7 +326,7 @@ attention_kernel(AttnArgs p) {
   }
 
   // ---- epilogue: O / l, rounded to BF16, staged per wave and stored in row segments
-  l += __shfl_xor(l, 32);
+  l = half_sum(l);
   const float inv = 1.0f / l;
   {
     constexpr int RB = D * 2;       // staged row bytes
