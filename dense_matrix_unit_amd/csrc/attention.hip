@@ -4,8 +4,9 @@
 // "Tensor Cores" chapter (ai-infra-handbooks), section "mma.sync: the register
 // layout is explicit", names as FlashAttention's, where one product's output
 // is worked on in registers and fed to the next.  The softmax is taken online
-// over blocks of 64 keys (running row maximum m and sum l; the partial output
-// is rescaled by exp(m_old - m_new) whenever a row's maximum moves).
+// over blocks of 64 keys: a reference maximum m and a running sum l per row,
+// the partial output rescaled by exp(m_old - m_new) when m moves, which it
+// does only when a block's maximum exceeds it by more than 2^8 in weight.
 //
 // Layout on the chip, per workgroup of 4 waves and 128 query rows:
 //  * each wave owns 32 query rows; its Q rows sit in registers for the whole
@@ -339,7 +340,7 @@ attention_kernel(AttnArgs p) {
       for (int q = 0; q < 4; ++q) {
         const f32x4_t x = {o[nt][4 * q] * inv, o[nt][4 * q + 1] * inv, o[nt][4 * q + 2] * inv,
                            o[nt][4 * q + 3] * inv};
-        const int u = nt * 4 + q;  // columns 8u .. 8u+7; this lane half has 4u*2 + 4h ..
+        const int u = nt * 4 + q;  // unit of columns 8u .. 8u+7; this lane half's are 8u + 4h ..
         *(uint2*)(wb + rl * RB + ((u ^ (rl & (UPR - 1))) << 4) + hl * 8) =
             make_uint2(pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3]));
       }
