@@ -77,6 +77,62 @@ def time_launches(torch, launch, steps, warmup):
             "event_median_ms": statistics.median(d)}
 
 
+def sample_clocks(torch, launch, seconds=1.5):
+    """Shader clock and socket power while `launch` runs back to back for about
+    `seconds`: amd-smi (a child process) polled every ~100 ms by a thread.
+    Returns medians over the samples (the clock as the median over the XCDs of
+    each sample), or None when amd-smi is missing or prints nothing usable."""
+    import shutil
+    import subprocess
+    import threading
+
+    smi = shutil.which("amd-smi") or "/opt/rocm/bin/amd-smi"
+    if not os.path.exists(smi):
+        return None
+    samples, stop = [], threading.Event()
+
+    def num(x):
+        v = x.get("value") if isinstance(x, dict) else x
+        return float(v) if isinstance(v, (int, float)) else None
+
+    def poll():
+        while not stop.is_set():
+            try:
+                r = subprocess.run([smi, "metric", "-g", "0", "-c", "-p", "--json"],
+                                   capture_output=True, text=True, timeout=5)
+                d = json.loads(r.stdout)["gpu_data"][0]
+                clks = [num(v.get("clk")) for k, v in d["clock"].items()
+                        if k.startswith("gfx_") and isinstance(v, dict)]
+                clks = [c for c in clks if c]
+                pw = num(d["power"]["socket_power"])
+                if clks and pw:
+                    samples.append((time.perf_counter(), statistics.median(clks), pw))
+            except Exception:  # a sample that fails to parse is skipped
+                pass
+            stop.wait(0.1)
+
+    th = threading.Thread(target=poll, daemon=True)
+    th.start()
+    t0, i = time.perf_counter(), 0
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(100):
+            launch(i)
+            i += 1
+        torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    stop.set()
+    th.join(timeout=10)
+    # only samples taken while the launches ran (not the idle card before them)
+    samples = [(c, w) for ts, c, w in samples if t0 + 0.25 <= ts <= t1]
+    if not samples:
+        return None
+    return {"sclk_mhz_median": statistics.median(c for c, _ in samples),
+            "sclk_mhz_min": min(c for c, _ in samples),
+            "socket_power_w_median": statistics.median(w for _, w in samples),
+            "samples": len(samples), "launches": i,
+            "during": "%.1f s of back-to-back headline launches after the timed region" % seconds}
+
+
 class Bench:
     def __init__(self, args):
         import torch
@@ -472,6 +528,8 @@ def main():
     achieved = flop / (t["event_mean_ms"] * 1e-3) / 1e12
     log("headline: %.1f TFLOP/s wall, %.1f TFLOP/s per kernel (%.1f%% of peak)"
         % (value, achieved, 100 * achieved / PEAK_BF16_TFLOPS))
+    clocks = sample_clocks(torch, launch)
+    log("clocks under the headline kernel: %s" % clocks)
     del As, Bs, out
 
     legs = {}
@@ -576,6 +634,9 @@ def main():
                      "kernel": "gemm_kernel<kBF16, B col-major, 256x256>",
                      "kernel_ms": round(t["event_mean_ms"], 5)},
         "cpu_baseline": cpu,
+        "clocks": clocks,
+        "pct_peak_at_measured_sclk": (round(100 * achieved / (PEAK_BF16_TFLOPS * clocks["sclk_mhz_median"]
+                                                              / 2400.0), 1) if clocks else None),
         "legs": legs,
     }
     print(json.dumps(line), flush=True)
