@@ -194,3 +194,42 @@ def test_plain_entry_unchanged_by_fused_build():
     dmu.gemm_bf16_fused(dev(A), dev(B), fused, dmu.B_COL_MAJOR)
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int16), fused.view(torch.int16))
+
+
+def sample_rows(M, n=10, seed=0):
+    rng = np.random.default_rng(seed)
+    return np.array(sorted(set([0, 1, M - 1]) | set(rng.integers(0, M, n).tolist())), np.int64)
+
+
+def test_fused_4096_bf16_gelu_sampled():
+    # the bench leg bf16_4096_bias_gelu: N(0,1) BF16 operands (seeds 1, 2), B
+    # stored N x K, N(0,1) bias (seed 3), GELU, BF16 out; sampled rows
+    M = N = K = 4096
+    A = bf16(wl.normal((M, K), wl.SEED_A))
+    B = bf16(wl.normal((N, K), wl.SEED_B))
+    bias = wl.normal((N,), 3)
+    D = run_bf16_fused(A, B, dmu.B_COL_MAJOR, "bf16", bias, dmu.ACT_GELU)
+    rows = sample_rows(M)
+    Dref, S = oracle.gemm_bf16(A, B, dmu.B_COL_MAJOR, rows=rows)
+    y = oracle.epilogue(Dref, 1.0, bias, dmu.ACT_GELU)
+    check_y(D[rows], y, tol_of(S, y, bias), True, "4096^3 bias + GELU")
+
+
+def test_fused_4096_fp8_relu_fp8out_sampled():
+    # the bench leg fp8_e4m3_4096_bias_relu_fp8out: per-tensor E4M3 operands,
+    # N(0,1) bias, ReLU, E4M3 out with d_scale 0.25 (many values saturate)
+    M = N = K = 4096
+    A, sa = oracle.quantize_fp8(wl.normal((M, K), wl.SEED_A), dmu.E4M3)
+    B, sb = oracle.quantize_fp8(wl.normal((N, K), wl.SEED_B), dmu.E4M3)
+    bias = wl.normal((N,), 3)
+    out = torch.empty((M, N), dtype=torch.uint8, device="cuda")
+    dmu.gemm_fp8_fused(dev(A), dev(B), dev(sa), dev(sb), out, dmu.E4M3, dmu.E4M3, dev(bias),
+                       dmu.ACT_RELU, dmu.E4M3, dev(np.float32([0.25])))
+    torch.cuda.synchronize()
+    rows = sample_rows(M)
+    Q = out.cpu().numpy()[rows]
+    Dref, S = oracle.gemm_fp8(A, B, 0, 0, sa, sb, oracle.SCALE_TENSOR, rows=rows)
+    y = oracle.epilogue(Dref, 1.0, bias, dmu.ACT_RELU)
+    tol = tol_of(S, y, bias, fp8_in_term(A[rows], B, sa, sb))
+    check_fp8_codes(Q, y, tol, dmu.E4M3, 0.25, "4096^3 bias + ReLU -> E4M3")
+    assert np.any(Q == 0x7E)  # saturated codes occur at this scale
