@@ -81,13 +81,18 @@ def sample_clocks(torch, launch, seconds=1.5):
     """Shader clock and socket power while `launch` runs back to back for about
     `seconds`: amd-smi (a child process) polled every ~100 ms by a thread.
     Returns medians over the samples (the clock as the median over the XCDs of
-    each sample), or None when amd-smi is missing or prints nothing usable."""
+    each sample), or None when amd-smi is missing, prints nothing usable, or
+    the process runs under rocprofv3."""
     import shutil
     import subprocess
     import threading
 
     smi = shutil.which("amd-smi") or "/opt/rocm/bin/amd-smi"
     if not os.path.exists(smi):
+        return None
+    # under a profiler every child process starts with the profiler's library
+    # loaded, and amd-smi's own start-up then fails: no samples there
+    if "rocprof" in os.environ.get("LD_PRELOAD", "") or any(k.startswith("ROCPROF") for k in os.environ):
         return None
     samples, stop = [], threading.Event()
 
