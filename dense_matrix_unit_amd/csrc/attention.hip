@@ -23,11 +23,15 @@
 //    gfx950's transposing LDS read, ds_read_b64_tr_b16, gives each lane four
 //    keys of its column from four rows, so V is never transposed in
 //    registers; two such reads, of keys 4h..4h+3 and 8+4h..8+4h+3 of a 16-key
-//    step, match the order of the weights in the score registers;
+//    step, match the order of the weights in the score registers.  They are
+//    issued as inline assembly with explicit LDS-counter waits, so they do
+//    not wait for the copies of later blocks;
 //  * two stages of K and V (64 KB for d = 128), so two workgroups share a
 //    CU and one wave's softmax arithmetic can run beside another's MFMAs;
 //  * the copies of block t+2 go out right after the barrier that ends block
 //    t, one barrier per block.
+#include <utility>
+
 #include "dmu_device.h"
 #include "dmu_internal.h"
 #include "gemm_common.h"
@@ -52,15 +56,43 @@ __device__ __forceinline__ int vswz(int j) {
   return D == 128 ? (j & 3) << 2 : ((j >> 1) & 1) << 2;
 }
 
-typedef short v4i16_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
+// gfx950 transposing LDS read (ds_read_b64_tr_b16): in each group of 16
+// lanes, lane i names row i / 4, 16-bit elements 4 (i % 4) .. +3 of a
+// row-major 4 x 16 block; lane j receives element j of the 4 rows, in row
+// order.  Issued as inline assembly, at LDS byte address addr + OFF: given
+// the compiler's builtin, the compiler cannot tell which LDS bytes the read
+// touches and makes it wait for every outstanding global -> LDS copy (the
+// next blocks' K and V), which stalls the wave in the middle of each block.
+// The caller waits on the LDS counter itself before using the result.
+template <int OFF>
+__device__ __forceinline__ uint2 read_tr16_at(uint32_t addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset field");
+  uint2 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+  return r;
+}
 
-// gfx950 transposing LDS read: in each group of 16 lanes, lane i names row
-// i / 4, 16-bit elements 4 (i % 4) .. +3 of a row-major 4 x 16 block; lane j
-// receives element j of the 4 rows, in row order.
-__device__ __forceinline__ uint2 read_tr16(const uint8_t* p) {
-  const v4i16_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)p);
-  return __builtin_bit_cast(uint2, r);
+// s_waitcnt for the LDS counter alone: at most N LDS (or scalar-load)
+// operations outstanding.
+template <int N>
+constexpr int waitcnt_lgkm() {
+  static_assert(N >= 0 && N < 16, "lgkmcnt range");
+  return 0xF | (0x7 << 4) | (N << 8) | (0x3 << 14);
+}
+
+// Compile-time loop: f(Idx<0>{}), ..., f(Idx<N-1>{}), so that an index can
+// feed a template argument (an instruction's immediate offset).
+template <int V>
+struct Idx {
+  static constexpr int value = V;
+};
+template <typename F, int... I>
+__device__ __forceinline__ void unroll_seq(F&& f, std::integer_sequence<int, I...>) {
+  (f(Idx<I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void unroll_n(F&& f) {
+  unroll_seq(f, std::make_integer_sequence<int, N>{});
 }
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -210,13 +242,18 @@ attention_kernel(AttnArgs p) {
   // (+ the step's first key, + 8 for the second read), columns
   // 32 nt + 16 (g % 2) + 4 (i % 4) .. +3; the swizzle depends on the row only
   // through i / 4, so each tile has one per-lane offset.
-  int voff[NT];
+  // Kept as LDS byte addresses of V stage 0; stage, key step and half go in
+  // the read's immediate offset.
+  uint32_t vaddr[NT];
   {
+    typedef __attribute__((address_space(3))) uint8_t lds_u8;
+    const uint32_t vbase = (uint32_t)(size_t)(lds_u8*)sV;
     const int g = lane >> 4, i = lane & 15;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
-      voff[nt] = (4 * hl + (i >> 2)) * VROW +
-                 (((4 * nt + 2 * (g & 1) + ((i & 3) >> 1)) ^ vswz<D>(i >> 2)) << 4) + ((i & 1) << 3);
+      vaddr[nt] = vbase + (uint32_t)((4 * hl + (i >> 2)) * VROW +
+                                     (((4 * nt + 2 * (g & 1) + ((i & 3) >> 1)) ^ vswz<D>(i >> 2)) << 4) +
+                                     ((i & 1) << 3));
   }
 
   const float c = p.scale * kLog2e;  // exp(scale * x) = exp2(c * x)
@@ -228,8 +265,9 @@ attention_kernel(AttnArgs p) {
   const int64_t irow = i0 + rl;
   const int64_t lim_row = CAUSAL ? min(p.Sk - 1, irow + off) : p.Sk - 1;  // last key the row sees
 
-  for (int t = 0; t < nblk; ++t) {
-    const int stage = t & 1;
+  // One block; ST (0 or 1) is its stage, a constant, so every LDS offset is.
+  auto blk = [&](int t, auto ST) __attribute__((always_inline)) {
+    constexpr int stage = decltype(ST)::value;
     const int64_t k0 = (int64_t)t * kBN;
     bool visible = true, masked = k0 + kBN > p.Sk;
     if constexpr (CAUSAL) {
@@ -298,32 +336,45 @@ attention_kernel(AttnArgs p) {
         for (int nt = 0; nt < NT; ++nt) o[nt] *= alpha;
       }
       // ---- O^T += V^T P^T, four 16-key steps
-      const uint8_t* vb = sV + stage * V_BYTES;
-      auto vread = [&](int x) __attribute__((always_inline)) {
-        const int ks = x / NT, nt = x % NT;  // key step, output tile
-        const uint2 lo = read_tr16(vb + voff[nt] + ks * 16 * VROW);
-        const uint2 hi = read_tr16(vb + voff[nt] + (ks * 16 + 8) * VROW);
+      // (reads two MFMAs ahead, each fragment two transposing reads; the LDS
+      // counter is drained first, so the waits below count these reads only)
+      auto vread = [&](auto X) __attribute__((always_inline)) {
+        constexpr int x = decltype(X)::value;
+        constexpr int ks = x / NT, nt = x % NT;  // key step, output tile
+        constexpr int off = stage * V_BYTES + ks * 16 * VROW;
+        const uint2 lo = read_tr16_at<off>(vaddr[nt]);
+        const uint2 hi = read_tr16_at<off + 8 * VROW>(vaddr[nt]);
         return u32x4_t{lo.x, lo.y, hi.x, hi.y};
       };
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(waitcnt_lgkm<0>());
+      __builtin_amdgcn_sched_barrier(0);
       u32x4_t vq[3];
-      vq[0] = vread(0);
-      vq[1] = vread(1);
-#pragma unroll
-      for (int x = 0; x < 4 * NT; ++x) {
-        if (x + 2 < 4 * NT) vq[(x + 2) % 3] = vread(x + 2);
-        const int ks = x / NT, nt = x % NT, jt = ks >> 1, w0 = (ks & 1) * 4;
+      vq[0] = vread(Idx<0>{});
+      vq[1] = vread(Idx<1>{});
+      unroll_n<4 * NT>([&](auto X) __attribute__((always_inline)) {
+        constexpr int x = decltype(X)::value;
+        if constexpr (x + 2 < 4 * NT) vq[(x + 2) % 3] = vread(Idx<x + 2>{});
+        constexpr int ahead = x + 2 < 4 * NT ? 2 : x + 1 < 4 * NT ? 1 : 0;  // fragments after x
+        constexpr int ks = x / NT, nt = x % NT, jt = ks >> 1, w0 = (ks & 1) * 4;
         const u32x4_t pf = {pk[jt][w0], pk[jt][w0 + 1], pk[jt][w0 + 2], pk[jt][w0 + 3]};
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(waitcnt_lgkm<2 * ahead>());
         __builtin_amdgcn_sched_barrier(0);
         o[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vq[x % 3]),
                                                         __builtin_bit_cast(bf16x8_t, pf), o[nt], 0,
                                                         0, 0);
         __builtin_amdgcn_sched_barrier(0);
-      }
+      });
     }
     // ---- block t+1's copies are in; then start block t+2
     if (t + 1 < nblk) __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<0>());
     stage_barrier();  // block t's stage is free; block t+1's is complete
     if (t + 2 < nblk) issue_block(t + 2, stage);
+  };
+  for (int t = 0; t < nblk; t += 2) {
+    blk(t, Idx<0>{});
+    if (t + 1 < nblk) blk(t + 1, Idx<1>{});
   }
 
   // ---- epilogue: O / l, rounded to BF16, staged per wave and stored in row segments
