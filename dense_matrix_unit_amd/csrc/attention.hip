@@ -154,6 +154,12 @@ attention_kernel(AttnArgs p) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int rl = lane & 31, hl = lane >> 5;
+  // Two workgroups share a CU, so each SIMD runs one wave of each; when they
+  // run in step, both want the matrix unit, then both the VALU.  Workgroups
+  // in alternate runs of 256 ids (one per CU on this chip, the two that share
+  // a CU in the first dispatch round) run at different wave priority, which
+  // keeps them out of step: 2-4% faster across the measured shapes.
+  if (((blockIdx.x >> 8) & 1) != 0) __builtin_amdgcn_s_setprio(2);
 
   // Workgroup -> (head, query block).  Dispatch goes round robin over the 8
   // XCDs; give each XCD a contiguous run of ids, so the query blocks of one
