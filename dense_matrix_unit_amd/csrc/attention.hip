@@ -28,6 +28,8 @@
 //    not wait for the copies of later blocks;
 //  * two stages of K and V (64 KB for d = 128), so two workgroups share a
 //    CU and one wave's softmax arithmetic can run beside another's MFMAs;
+//    alternate runs of 256 workgroup ids run at a higher wave priority, which
+//    keeps the two on a CU from running in step;
 //  * the copies of block t+2 go out right after the barrier that ends block
 //    t, one barrier per block.
 #include <utility>
