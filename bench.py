@@ -493,7 +493,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(the GEMM shards without communication; see the design notes). "
               "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
