@@ -9,6 +9,7 @@ from __future__ import annotations
 
 import concurrent.futures as cf
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -60,10 +61,81 @@ def _compile(src: str) -> str:
     return obj
 
 
+_VREG = re.compile(r"v\[(\d+):(\d+)\]|v(\d+)$")
+
+
+def _vregs(tok: str) -> set:
+    m = _VREG.match(tok)
+    if not m:
+        return set()
+    if m.group(3) is not None:
+        return {int(m.group(3))}
+    return set(range(int(m.group(1)), int(m.group(2)) + 1))
+
+
+def check_lds_asm_waits(src: str = "attention.hip") -> int:
+    """The attention kernel issues its transposing LDS reads as inline
+    assembly and waits on the LDS counter itself; the compiler does not know
+    their registers fill later.  Scan the generated gfx950 code: between such
+    a read and the s_waitcnt lgkmcnt that covers it (LDS reads complete in
+    order), no instruction may read or write its destination.  Returns the
+    number of reads checked; raises on a violation."""
+    asm = os.path.join(BUILD, os.path.splitext(src)[0] + ".s")
+    cmd = ([hipcc()] + COMMON + EXTRA.get(src, []) +
+           ["-S", "--cuda-device-only", os.path.join(CSRC, src), "-o", asm])
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("assembly listing failed: %s\n%s" % (" ".join(cmd), r.stderr))
+    with open(asm) as f:
+        return scan_lds_asm_waits(f, asm)
+
+
+def scan_lds_asm_waits(lines, name: str = "<listing>") -> int:
+    """The check of check_lds_asm_waits over an assembly listing (an iterable
+    of lines); returns the number of transposing reads checked."""
+    pending, checked = {}, 0
+    for n, line in enumerate(lines):
+        t = line.strip()
+        if line[:1] not in (" ", "\t") or not t or t[0] in ";." or t.endswith(":"):
+            if t.endswith(":") and not t.startswith("."):
+                pending = {}  # a new function
+            continue
+        op = t.split()[0]
+        if op == "s_waitcnt":
+            m = re.search(r"lgkmcnt\((\d+)\)", t)
+            if m:
+                c = int(m.group(1))
+                order = sorted(set(pending.values()))
+                keep = set(order[len(order) - c:]) if c else set()
+                pending = {reg: ln for reg, ln in pending.items() if ln in keep}
+            continue
+        if op.startswith("s_"):
+            continue
+        args = [a.strip().split()[0] if a.strip() else "" for a in t[len(op):].split(",")]
+        touched = set()
+        for a in args[1:]:
+            touched |= _vregs(a)
+        if not op.startswith(("ds_", "buffer_", "global_")) and args:
+            touched |= _vregs(args[0])  # a VALU/MFMA write
+        if touched & set(pending):
+            raise RuntimeError("%s:%d uses a transposing LDS read's registers before its "
+                               "wait: %s" % (name, n + 1, t))
+        if op == "ds_read_b64_tr_b16":
+            checked += 1
+            for reg in _vregs(args[0]):
+                pending[reg] = n
+    if checked == 0:
+        raise RuntimeError("%s: no transposing LDS reads found to check" % name)
+    return checked
+
+
 def build(verbose: bool = True) -> str:
     os.makedirs(BUILD, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
         objs = list(ex.map(_compile, SOURCES))
+        checked = ex.submit(check_lds_asm_waits).result()
+    if verbose:
+        print("checked %d hand-waited LDS reads in the generated code" % checked)
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC"] + objs + ["-o", tmp]
     subprocess.check_call(cmd)
