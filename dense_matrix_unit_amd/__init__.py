@@ -71,6 +71,7 @@ SYMBOLS = {
     "dmu_status_string": (ctypes.c_char_p, [_I]),
     "dmu_version": (_I, []),
     "dmu_probe_mfma": (_I, [_I, _I, _I, _P, _P, _P, _P, _P]),
+    "dmu_probe_mfma_batch": (_I, [_I, _I, _I, _P, _P, _P, _P, _I, _P]),
     "dmu_probe_lds_load": (_I, [_P, _P, _I, _I, _P]),
     "dmu_probe_mfma_rate": (_I, [_I, _P, _I, _I, _P, _P]),
     "dmu_probe_cvt_fp8": (_I, [_P, _I64, _I, _I, _P, _P]),
@@ -472,6 +473,35 @@ def probe_mfma(kind: int, A, B, C, D, fmt_a: int = E4M3, fmt_b: int = E4M3, stre
     rc = load_library().dmu_probe_mfma(kind, fmt_a, fmt_b, _dev_ptr(A, "A"), _dev_ptr(B, "B"),
                                        _dev_ptr(C, "C"), _dev_ptr(D, "D"), _stream(stream))
     _check("dmu_probe_mfma", rc)
+    return D
+
+
+PROBE_SHAPES = {PROBE_BF16_16X16X32: (16, 16, 32), PROBE_BF16_32X32X16: (32, 32, 16),
+                PROBE_FP8_16X16X128: (16, 16, 128), PROBE_FP8_32X32X64: (32, 32, 64)}
+
+
+def probe_mfma_batch(kind: int, A, B, C, D, fmt_a: int = E4M3, fmt_b: int = E4M3, stream=None):
+    """Run count independent matrix instructions of `kind` in one launch (see
+    include/dmu_probe.h): A [count][m][k], B [count][n][k], C and D
+    [count][m][n] FP32, all contiguous on the GPU."""
+    torch = _torch()
+    if kind not in PROBE_SHAPES:
+        raise ValueError("unknown probe kind %r" % kind)
+    m, n, k = PROBE_SHAPES[kind]
+    count = A.shape[0] if A.dim() == 3 else -1
+    for t, shp, name in ((A, (count, m, k), "A"), (B, (count, n, k), "B"),
+                         (C, (count, m, n), "C"), (D, (count, m, n), "D")):
+        if tuple(t.shape) != shp or not t.is_contiguous():
+            raise ValueError("%s must be contiguous with shape %s" % (name, shp))
+    esz = 2 if kind in (PROBE_BF16_16X16X32, PROBE_BF16_32X32X16) else 1
+    if A.element_size() != esz or B.element_size() != esz:
+        raise TypeError("A and B must hold %d-byte elements" % esz)
+    _check_dtype(C, (torch.float32,), "C")
+    _check_dtype(D, (torch.float32,), "D")
+    rc = load_library().dmu_probe_mfma_batch(kind, fmt_a, fmt_b, _dev_ptr(A, "A"),
+                                             _dev_ptr(B, "B"), _dev_ptr(C, "C"),
+                                             _dev_ptr(D, "D"), count, _stream(stream))
+    _check("dmu_probe_mfma_batch", rc)
     return D
 
 

@@ -96,6 +96,15 @@ int attention_bf16(const uint16_t* Q, int64_t ldq, int64_t head_stride_q, const 
   if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16) ||
       (lse && !aligned(lse, 4)))
     return DMU_ERR_INVALID_ARG;
+  // the heads' outputs must be disjoint, or workgroups of different heads
+  // would store to the same O elements: heads one after another
+  // ([heads][Sq][d]-like) or side by side within each row stride
+  // ([Sq][heads][d]-like)
+  if (heads > 1) {
+    const bool stacked = head_stride_o >= (Sq - 1) * ldo + d;
+    const bool side_by_side = head_stride_o >= d && ldo >= (heads - 1) * head_stride_o + d;
+    if (!stacked && !side_by_side) return DMU_ERR_INVALID_ARG;
+  }
   // one head's rows are addressed with 32-bit byte offsets
   if (Sq * ldq * 2 >= kMaxTileBytes || Sk * ldk * 2 >= kMaxTileBytes ||
       Sk * ldv * 2 >= kMaxTileBytes || ((Sq + 127) / 128) * heads > INT32_MAX)
@@ -320,12 +329,21 @@ const char* dmu_status_string(int status) {
 
 int dmu_version(void) { return (1 << 16) | 0; }
 
-int dmu_probe_mfma(int kind, int fmt_a, int fmt_b, const void* A, const void* B,
-                   const float* C, float* D, void* stream) {
+int dmu_probe_mfma_batch(int kind, int fmt_a, int fmt_b, const void* A, const void* B,
+                         const float* C, float* D, int count, void* stream) {
   if (!A || !B || !C || !D || kind < 0 || kind > 3) return DMU_ERR_INVALID_ARG;
   if (fmt_a < 0 || fmt_a > 1 || fmt_b < 0 || fmt_b > 1) return DMU_ERR_INVALID_ARG;
+  if (count < 1 || count > (1 << 20)) return DMU_ERR_INVALID_ARG;
+  if (!aligned(A, 4) || !aligned(B, 4) || !aligned(C, 4) || !aligned(D, 4))
+    return DMU_ERR_INVALID_ARG;
   (void)hipGetLastError();
-  return finish(dmu::launch_probe_mfma(kind, fmt_a, fmt_b, A, B, C, D, (hipStream_t)stream));
+  return finish(
+      dmu::launch_probe_mfma(kind, fmt_a, fmt_b, A, B, C, D, count, (hipStream_t)stream));
+}
+
+int dmu_probe_mfma(int kind, int fmt_a, int fmt_b, const void* A, const void* B,
+                   const float* C, float* D, void* stream) {
+  return dmu_probe_mfma_batch(kind, fmt_a, fmt_b, A, B, C, D, 1, stream);
 }
 
 int dmu_probe_lds_load(const void* src, void* dst, int mode, int oob_from, void* stream) {

@@ -89,7 +89,7 @@ hipError_t launch_quantize_fp8(const float* X, int64_t rows, int64_t cols, int64
                                hipStream_t s);
 
 hipError_t launch_probe_mfma(int kind, int fa, int fb, const void* A, const void* B,
-                             const float* C, float* D, hipStream_t s);
+                             const float* C, float* D, int count, hipStream_t s);
 hipError_t launch_probe_lds(const void* src, void* dst, int mode, int oob_from, hipStream_t s);
 hipError_t launch_probe_rate(int kind, const void* src, int iters, int grid, float* out,
                              hipStream_t s);

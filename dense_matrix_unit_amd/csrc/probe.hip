@@ -26,9 +26,21 @@ namespace dmu {
 namespace {
 
 // A: [M][K] row-major, B: [N][K] row-major (B stored N x K), C/D: [M][N] FP32.
+// Workgroup i (one wave) runs instance i of a batch: its A, B, C and D follow
+// instance i-1's, one instruction's operands each (A and B: 512 BF16 values
+// = 1024 bytes, or 2048 FP8 codes; C and D: 16x16 or 32x32 floats).
 template <int KIND, int FA, int FB>
 __global__ void probe_mfma_kernel(const void* Av, const void* Bv, const float* C, float* D) {
   const int l = threadIdx.x;
+  {
+    constexpr int64_t kOperandBytes = KIND < 2 ? 1024 : 2048;      // one A (or B) instance
+    constexpr int64_t kOut = KIND == 0 || KIND == 2 ? 256 : 1024;  // floats of C (or D)
+    const int64_t i = blockIdx.x;
+    Av = (const uint8_t*)Av + i * kOperandBytes;
+    Bv = (const uint8_t*)Bv + i * kOperandBytes;
+    C += i * kOut;
+    D += i * kOut;
+  }
   if constexpr (KIND == 0) {  // bf16 16x16x32
     const uint16_t* A = (const uint16_t*)Av;
     const uint16_t* B = (const uint16_t*)Bv;
@@ -280,9 +292,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
 template <int KIND>
 hipError_t probe_fmt(int fa, int fb, const void* A, const void* B, const float* C, float* D,
-                     hipStream_t s) {
-#define DMU_PROBE_LAUNCH(FA, FB) \
-  hipLaunchKernelGGL((probe_mfma_kernel<KIND, FA, FB>), dim3(1), dim3(64), 0, s, A, B, C, D)
+                     int count, hipStream_t s) {
+#define DMU_PROBE_LAUNCH(FA, FB)                                                           \
+  hipLaunchKernelGGL((probe_mfma_kernel<KIND, FA, FB>), dim3(count), dim3(64), 0, s, A, B, C, \
+                     D)
   if (fa == 0 && fb == 0) DMU_PROBE_LAUNCH(0, 0);
   else if (fa == 0 && fb == 1) DMU_PROBE_LAUNCH(0, 1);
   else if (fa == 1 && fb == 0) DMU_PROBE_LAUNCH(1, 0);
@@ -323,18 +336,18 @@ hipError_t probe_mx_fmt(int fa, int fb, int opsel, const uint8_t* A, const uint8
 }  // namespace
 
 hipError_t launch_probe_mfma(int kind, int fa, int fb, const void* A, const void* B,
-                             const float* C, float* D, hipStream_t s) {
+                             const float* C, float* D, int count, hipStream_t s) {
   switch (kind) {
     case 0:
-      hipLaunchKernelGGL((probe_mfma_kernel<0, 0, 0>), dim3(1), dim3(64), 0, s, A, B, C, D);
+      hipLaunchKernelGGL((probe_mfma_kernel<0, 0, 0>), dim3(count), dim3(64), 0, s, A, B, C, D);
       return hipGetLastError();
     case 1:
-      hipLaunchKernelGGL((probe_mfma_kernel<1, 0, 0>), dim3(1), dim3(64), 0, s, A, B, C, D);
+      hipLaunchKernelGGL((probe_mfma_kernel<1, 0, 0>), dim3(count), dim3(64), 0, s, A, B, C, D);
       return hipGetLastError();
     case 2:
-      return probe_fmt<2>(fa, fb, A, B, C, D, s);
+      return probe_fmt<2>(fa, fb, A, B, C, D, count, s);
     default:
-      return probe_fmt<3>(fa, fb, A, B, C, D, s);
+      return probe_fmt<3>(fa, fb, A, B, C, D, count, s);
   }
 }
 

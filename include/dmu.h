@@ -335,14 +335,18 @@ int gemm_fp8_fused(const uint8_t* A, int64_t lda, int fmt_a, const uint8_t* B, i
  *   Q : heads x Sq x d BF16, row i of head bh at Q + bh*head_stride_q + i*ldq
  *   K, V : heads x Sk x d BF16, likewise (ldk, head_stride_k, ldv, head_stride_v)
  *   O : heads x Sq x d BF16 output, likewise (ldo, head_stride_o); must not
- *       overlap Q, K or V
+ *       overlap Q, K or V; with heads > 1 the heads' outputs must not
+ *       overlap: head_stride_o >= (Sq - 1) * ldo + d (heads one after
+ *       another) or head_stride_o >= d and ldo >= (heads - 1) * head_stride_o
+ *       + d (heads side by side within each row, [Sq][heads][d] storage)
  *   lse : optional heads x Sq FP32 output (NULL: not written), natural log
  *   d = 64 or 128; scale > 0 and finite (typically 1 / sqrt(d)).
  * Scores must stay finite in FP32.  All pointers are device pointers owned by
  * the caller; Q, K, V, O 16-byte aligned, row and head strides multiples of
  * 8 elements, row strides >= d.
  * Errors: DMU_ERR_INVALID_ARG for a null or misaligned pointer, d not 64 or
- * 128, non-positive sizes, causal with Sq > Sk, a bad stride or scale;
+ * 128, non-positive sizes, causal with Sq > Sk, a bad stride (including an
+ * output head stride that makes heads overlap) or scale;
  * DMU_ERR_UNSUPPORTED when one head spans 2^31 bytes or more.
  */
 int attention_bf16(const uint16_t* Q, int64_t ldq, int64_t head_stride_q, const uint16_t* K,

@@ -43,6 +43,21 @@ int dmu_probe_mfma(int kind, int fmt_a, int fmt_b, const void* A, const void* B,
                    const float* C, float* D, void* stream);
 
 /*
+ * The same for `count` independent instructions in one launch (1 <= count <=
+ * 2^20), one wave each: instance i reads its A and B at element offset
+ * i * m * k and i * n * k (one instruction's operand: 2048 FP8 codes for
+ * kinds 2 and 3, 512 BF16 values for kinds 0 and 1) and its C and D at
+ * element offset i * m * n.  Used to
+ * pin how one FP8 instruction forms its inner sum (which product bits it
+ * keeps, where it rounds) on many random and constructed operand sets; the
+ * vidyal.ai page, Step 5, probes the same property of Ada's FP8 instruction.
+ * The caller sizes A, B, C and D for `count` instances (pointers 4-byte
+ * aligned).  Returns DMU_OK, DMU_ERR_INVALID_ARG or DMU_ERR_HIP.
+ */
+int dmu_probe_mfma_batch(int kind, int fmt_a, int fmt_b, const void* A, const void* B,
+                         const float* C, float* D, int count, void* stream);
+
+/*
  * Copy 64 x 16 bytes (mode 0) or 64 x 4 bytes (mode 1) from src into LDS with
  * one buffer load per lane that writes LDS directly (lane l's bytes are
  * expected at LDS offset l*size), lanes >= oob_from using an out-of-range

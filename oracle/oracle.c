@@ -473,17 +473,25 @@ int orc_gemm_mx(const uint8_t* A, int64_t lda, int fmt_a, const uint8_t* B, int6
     ta[v] = fmt_a == ORC_FMT_E2M1 ? orc_decode_fp4((uint8_t)v) : orc_decode_fp8((uint8_t)v, fmt_a);
     tb[v] = fmt_b == ORC_FMT_E2M1 ? orc_decode_fp4((uint8_t)v) : orc_decode_fp8((uint8_t)v, fmt_b);
   }
+  /* every scale decoded once (exact powers of two, or NaN) */
+  const int64_t ng = K / ORC_MX_BLOCK;
+  double* sB = (double*)malloc((size_t)N * ng * sizeof(double));
+  if (!sB) return -1;
+  for (int64_t j = 0; j < N; j++)
+    for (int64_t g = 0; g < ng; g++) sB[j * ng + g] = orc_decode_e8m0(SB[j * ldsb + g]);
   int bad = 0;
 #pragma omp parallel for schedule(dynamic)
   for (int64_t r = 0; r < nrows; r++) {
     int64_t i = rows ? rows[r] : r;
     if (i < 0 || i >= M) { bad = 1; continue; }
+    double sA[ng > 0 ? ng : 1];
+    for (int64_t g = 0; g < ng; g++) sA[g] = orc_decode_e8m0(SA[i * ldsa + g]);
     for (int64_t j = 0; j < N; j++) {
       double acc = 0.0, sacc = 0.0;
       for (int64_t k = 0; k < K; k++) {
         const int64_t g = k / ORC_MX_BLOCK;
-        double p = (ta[code_at(A + i * lda, k, fmt_a)] * orc_decode_e8m0(SA[i * ldsa + g])) *
-                   (tb[code_at(B + j * ldb, k, fmt_b)] * orc_decode_e8m0(SB[j * ldsb + g]));
+        double p = (ta[code_at(A + i * lda, k, fmt_a)] * sA[g]) *
+                   (tb[code_at(B + j * ldb, k, fmt_b)] * sB[j * ng + g]);
         acc += p;
         sacc += fabs(p);
       }
@@ -492,6 +500,7 @@ int orc_gemm_mx(const uint8_t* A, int64_t lda, int fmt_a, const uint8_t* B, int6
       if (S) S[r * N + j] = sacc;
     }
   }
+  free(sB);
   return bad ? -1 : 0;
 }
 
@@ -606,13 +615,29 @@ int orc_attention_bf16(const uint16_t* Q, const uint16_t* K, const uint16_t* V, 
         continue;
       }
       double m = -INFINITY;
-      for (int64_t j = 0; j < nk; j++) {
+      /* s_j = scale * sum_k q_k k_jk, each sum in increasing k; four keys at a
+       * time, their four sums kept apart */
+      int64_t j = 0;
+      for (; j + 4 <= nk; j += 4) {
+        const uint16_t* k0 = K + (bh * Sk + j) * d;
+        double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
+        for (int64_t k = 0; k < d; k++) {
+          const double qk = orc_decode_bf16(q[k]);
+          a0 += qk * orc_decode_bf16(k0[k]);
+          a1 += qk * orc_decode_bf16(k0[d + k]);
+          a2 += qk * orc_decode_bf16(k0[2 * d + k]);
+          a3 += qk * orc_decode_bf16(k0[3 * d + k]);
+        }
+        s[j] = scale * a0, s[j + 1] = scale * a1, s[j + 2] = scale * a2, s[j + 3] = scale * a3;
+      }
+      for (; j < nk; j++) {
         const uint16_t* kr = K + (bh * Sk + j) * d;
         double acc = 0.0;
         for (int64_t k = 0; k < d; k++) acc += orc_decode_bf16(q[k]) * orc_decode_bf16(kr[k]);
         s[j] = scale * acc;
-        if (s[j] > m) m = s[j];
       }
+      for (j = 0; j < nk; j++)
+        if (s[j] > m) m = s[j];
       double l = 0.0;
       for (int64_t j = 0; j < nk; j++) {
         s[j] = exp(s[j] - m);
@@ -620,17 +645,30 @@ int orc_attention_bf16(const uint16_t* Q, const uint16_t* K, const uint16_t* V, 
       }
       double* o = O + (bh * Sq + i) * d;
       double* a = Aabs ? Aabs + (bh * Sq + i) * d : NULL;
-      for (int64_t n = 0; n < d; n++) {
-        double acc = 0.0, aa = 0.0;
-        for (int64_t j = 0; j < nk; j++) {
-          const double v = orc_decode_bf16(V[(bh * Sk + j) * d + n]);
-          acc += s[j] * v;
-          aa += s[j] * fabs(v);
+      /* o[n] = sum_j s[j] v[j][n] / l, each sum taken in increasing j (the
+       * rows of V are walked in memory order, one accumulator per column) */
+      double* acc = (double*)calloc((size_t)(2 * d), sizeof(double));
+      if (!acc) {
+#pragma omp atomic write
+        bad = 1;
+        free(s);
+        continue;
+      }
+      double* aa = acc + d;
+      for (int64_t j = 0; j < nk; j++) {
+        const uint16_t* vr = V + (bh * Sk + j) * d;
+        for (int64_t n = 0; n < d; n++) {
+          const double v = orc_decode_bf16(vr[n]);
+          acc[n] += s[j] * v;
+          aa[n] += s[j] * fabs(v);
         }
-        o[n] = acc / l;
-        if (a) a[n] = aa / l;
+      }
+      for (int64_t n = 0; n < d; n++) {
+        o[n] = acc[n] / l;
+        if (a) a[n] = aa[n] / l;
       }
       if (lse) lse[bh * Sq + i] = m + log(l);
+      free(acc);
       free(s);
     }
   }

@@ -69,3 +69,24 @@ def round_out(D_ref, bf16_out):
     if bf16_out:
         return oracle.decode_bf16(oracle.encode_bf16(f32))
     return f32.astype(np.float64)
+
+
+def within_fp8_bound(D, Dref, S, bf16_out, loss_of_rows):
+    """Element-wise |D - Dref| <= 1e-5 S (+ 2^-8 |Dref| for BF16 output) + the
+    FP8 instructions' own loss.  The loss (an O(MNK) computation) is only
+    evaluated for rows where the FP32 term alone is exceeded: the verdict is
+    the same as with the loss everywhere, since it only adds to the bound.
+    loss_of_rows(r) gives the loss of the rows r (indices into D).  Returns
+    the mask of elements within the bound, and the full tolerance of those rows."""
+    tol = 1e-5 * S
+    if bf16_out:
+        tol = tol + 2.0 ** -8 * np.abs(Dref)
+    err = np.abs(D - Dref)
+    ok = err <= tol
+    rows = np.flatnonzero(~ok.all(axis=1))
+    if rows.size:
+        tol_rows = tol[rows] + loss_of_rows(rows)
+        ok[rows] = err[rows] <= tol_rows
+        tol = tol.copy()
+        tol[rows] = tol_rows
+    return ok, tol

@@ -236,10 +236,14 @@ def call_attention(**kw):
     dict(scale=0.0), dict(scale=-1.0), dict(scale=float("inf")), dict(scale=float("nan")),
     dict(ldq=120), dict(ldk=100), dict(ldv=132), dict(ldo=64), dict(hq=-8), dict(hv=12),
     dict(Q=FAKE + 8), dict(O=FAKE + 2), dict(lse=FAKE + 2),
+    # heads whose outputs overlap: stride 0, one row short of a whole head,
+    # side by side in a row stride that cannot hold both
+    dict(ho=0), dict(ho=128 * 255), dict(ho=128, ldo=192), dict(ho=64, ldo=256),
 ])
 def test_attention_rejects(kw):
     assert call_attention(**kw) == dmu.DMU_ERR_INVALID_ARG
 
 
 def test_attention_rejects_heads_past_32_bit_offsets():
-    assert call_attention(ldq=1 << 16, Sq=1 << 15) == dmu.DMU_ERR_UNSUPPORTED
+    # Q's rows span 2^31 bytes; the output heads are laid out without overlap
+    assert call_attention(ldq=1 << 16, Sq=1 << 15, ho=1 << 22) == dmu.DMU_ERR_UNSUPPORTED

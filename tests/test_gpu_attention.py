@@ -4,8 +4,11 @@ the register layout is explicit", names as FlashAttention's) against the
 oracle.
 
 Tolerance, from the arithmetic of the kernel.  The weights are rounded to
-BF16 for the second product while the row sum uses the FP32 weights, so O
-moves by at most 2^-9 sum_j w_j |v_j| / l = 2^-9 A (A from the oracle).  The
+BF16 for the second product while the row sum uses the FP32 weights.  BF16
+keeps 8 significant bits (1/8/7 split, "Tensor Cores" chapter, section
+"Precision"), so round-to-nearest moves a weight by up to 2^-8 of itself
+(0.502 becomes 0.50390625), and O by at most 2^-8 sum_j w_j |v_j| / l =
+2^-8 A (A from the oracle).  The
 FP32 scores carry at most scale (d + 4) 2^-23 max_j sum_k |q_k k_jk| of
 error into the exponent, which moves every weight ratio by twice that.  The
 output is rounded to BF16 once (2^-8 |O| with slack), and 2^-16 A covers the
@@ -45,7 +48,7 @@ def check(O, lse, Q, K, V, scale, causal, what):
     d = Q.shape[-1]
     Oref, lref, A = oracle.attention_bf16(Q, K, V, scale, causal)
     e = expo_err(Q, K, scale, d)[..., None]
-    tol = A * (2.0 ** -9 + 2.0 ** -16 + 2 * e) + 2.0 ** -8 * np.abs(Oref) + 1e-30
+    tol = A * (2.0 ** -8 + 2.0 ** -16 + 2 * e) + 2.0 ** -8 * np.abs(Oref) + 1e-30
     bad = ~(np.abs(O - Oref) <= tol)
     if bad.any():
         i = tuple(np.argwhere(bad)[0])
@@ -113,23 +116,18 @@ def test_attention_strided_heads():
 
 
 @pytest.mark.parametrize("causal", [False, True])
-def test_attention_workload_sampled(causal):
-    # the benchmark's shape (32 heads of 4096 x 4096, d = 128), checked on two
-    # heads and three blocks of query rows; rows i0 .. i1-1 of a causal head
-    # see keys below i1, so the oracle gets the matching key prefix
+def test_attention_workload(causal):
+    # the benchmark's shape (32 heads of 4096 x 4096, d = 128) in full: every
+    # output row of every head against the oracle, one head at a time
     H, S, d = 32, 4096, 128
     Q = bf16((H, S, d), 21)
     K = bf16((H, S, d), 22)
     V = bf16((H, S, d), 23)
     scale = 1.0 / np.sqrt(d)
     O, lse = run(Q, K, V, scale, causal)
-    for h in (0, 31):
-        for i0 in (0, 2000, 3968):
-            i1 = i0 + 128
-            kk = i1 if causal else S
-            sl = np.s_[h:h + 1]
-            check(O[sl, i0:i1], lse[sl, i0:i1], Q[sl, i0:i1], K[sl, :kk], V[sl, :kk], scale, causal,
-                  "head %d rows %d" % (h, i0))
+    for h in range(H):
+        sl = np.s_[h:h + 1]
+        check(O[sl], lse[sl], Q[sl], K[sl], V[sl], scale, causal, "head %d" % h)
 
 
 def test_attention_rejects_bad_arguments():

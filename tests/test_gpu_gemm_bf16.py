@@ -95,27 +95,22 @@ def test_strided_operands():
     assert torch.all(out_big[:, N:] == 0)
 
 
-def sample_rows(M, n=12, seed=0):
-    rng = np.random.default_rng(seed)
-    r = set([0, 1, M - 1, M - 2]) | set(rng.integers(0, M, n).tolist())
-    return np.array(sorted(r), np.int64)
-
-
 @pytest.mark.parametrize("layout", LAYOUTS)
-def test_4096_normal_bf16_out_sampled(layout):
-    # 4096^3, N(0,1) inputs in BF16, BF16 output, B row- and column-major
+def test_4096_normal_bf16_out(layout):
+    # 4096^3, N(0,1) inputs in BF16, BF16 output, B row- and column-major:
+    # every one of the 16.8 M outputs against the oracle
     A = bf16(wl.normal((4096, 4096), wl.SEED_A))
     B = make_B(bf16(wl.normal((4096, 4096), wl.SEED_B)), layout)
-    check(A, B, layout, torch.bfloat16, rows=sample_rows(4096), what="4096^3")
+    check(A, B, layout, torch.bfloat16, what="4096^3")
 
 
 @pytest.mark.parametrize("M", [16, 128, 1024, 8192])
-def test_llm_shapes_sampled(M):
+def test_llm_shapes(M):
+    # N = 28672, K = 8192, every output (M = 8192: 235 M outputs)
     N, K = 28672, 8192
     A = bf16(wl.normal((M, K), wl.SEED_A))
     B = bf16(wl.normal((N, K), wl.SEED_B))
-    rows = np.arange(M) if M <= 16 else sample_rows(M, 6)
-    check(A, B, dmu.B_COL_MAJOR, torch.bfloat16, rows=rows, what="M=%d" % M)
+    check(A, B, dmu.B_COL_MAJOR, torch.bfloat16, what="M=%d" % M)
 
 
 @pytest.mark.parametrize("K", [256, 1024, 4096, 16384, 65536])

@@ -2,16 +2,16 @@
 per-block (A: 1 x 128, B: 128 x 128) scales, E4M3 and E5M2.
 
 Tolerance: the FP32-accumulation bound 1e-5 * sum|ab| (+ 2^-8 |D| for BF16
-output) plus a term for the matrix unit's own FP8 arithmetic.  gfx950's FP8
-MFMAs sum the products inside one instruction on a grid tied to the largest
-product (2^p + 2^(p-13) is exact, 2^p + 2^(p-14) is not; pinned by
-test_gpu_probe.py::test_fp8_mfma_inner_sum_keeps_14_bits), the ~14-bit
-behaviour the vidyal.ai page measures for Ada's FP8 instruction in Step 5.
-Each instruction can therefore be off by about 2^-13 of its largest product;
-the test allows 2^-12 x (sum over the instruction's K blocks of the largest
-|a*b| in the block, with its scales): twice the worst case measured on random
-data, and orders of magnitude below what a dropped term or a wrong index
-produces."""
+output) plus what the matrix unit's own FP8 arithmetic discards.  gfx950's FP8
+instructions sum their products in aligned groups of 8 K positions and cut
+each product toward zero to the grid 2^(E - 13) of the group's largest
+exponent-field sum E (pinned instruction by instruction in test_gpu_probe.py,
+the accumulator probe of the vidyal.ai page, Step 5, carried further).  The
+exact amount each product loses is |p| mod 2^(E - 13); oracle.fp8_group_loss
+sums it per output element with the product's scales, and the test allows
+exactly that much on top of the FP32 term -- a bound derived from the pinned
+instruction model, not from errors observed on the kernels.  A dropped term or
+a wrong index moves an output by whole products, thousands of times more."""
 import numpy as np
 import pytest
 import torch
@@ -19,7 +19,7 @@ import torch
 import oracle
 import dense_matrix_unit_amd as dmu
 from dense_matrix_unit_amd import workloads as wl
-from gpu_helpers import dev, empty_padded, out_to_f64, padded, round_out
+from gpu_helpers import dev, empty_padded, out_to_f64, padded, round_out, within_fp8_bound
 
 pytestmark = pytest.mark.gpu
 FMT_PAIRS = [(0, 0), (0, 1), (1, 0), (1, 1)]
@@ -36,28 +36,14 @@ def run_fp8(A, B, fa, fb, sa, sb, mode, out_dtype, C=None):
     return out_to_f64(out)
 
 
-def block_max_term(A, B, fa, fb, sa, sb, mode, rows=None):
-    """sum over K blocks of max_k |a_ik b_jk| (dequantised): 64-wide blocks for
-    the per-tensor kernel's 32x32x64 MFMA, 128-wide for the block-scaled
-    kernel's 16x16x128."""
-    blk = 64 if mode == dmu.SCALE_TENSOR else 128
-    Ad = oracle.decode_fp8(A, fa)
-    if rows is not None:
-        Ad = Ad[rows]
-    Bd = oracle.decode_fp8(B, fb)
-    M, K = Ad.shape
-    N = Bd.shape[0]
-    out = np.zeros((M, N))
-    for b in range(0, K, blk):
-        for r0 in range(0, M, 16):
-            p = np.abs(Ad[r0:r0 + 16, None, b:b + blk] * Bd[None, :, b:b + blk]).max(axis=2)
-            if mode == dmu.SCALE_TENSOR:
-                p = p * (float(np.ravel(sa)[0]) * float(np.ravel(sb)[0]))
-            else:
-                ra = np.arange(M)[r0:r0 + 16] if rows is None else np.asarray(rows)[r0:r0 + 16]
-                p = p * sa[ra, b // 128][:, None] * np.repeat(sb[:, b // 128], 128)[None, :N]
-            out[r0:r0 + 16] += p
-    return out
+def fp8_loss(A, B, fa, fb, sa, sb, mode, rows=None):
+    """What the FP8 instructions discard, per output element, scaled:
+    per-tensor scales multiply every product; block scales the products of
+    their 1 x 128 (A) and 128 x 128 (B) block."""
+    if mode == dmu.SCALE_TENSOR:
+        return oracle.fp8_group_loss(A, B, fa, fb, sa, sb, rows=rows)
+    return oracle.fp8_group_loss(A, B, fa, fb, sa, sb, k_per_scale=128, b_rows_per_scale=128,
+                                 rows=rows)
 
 
 def check(A, B, fa, fb, sa, sb, mode, out_dtype, C=None, rows=None, what=""):
@@ -67,14 +53,13 @@ def check(A, B, fa, fb, sa, sb, mode, out_dtype, C=None, rows=None, what=""):
         D = D[rows]
     if C is not None:
         S = S + np.abs(C if rows is None else C[rows])
-    tol = 1e-5 * S + 2.0 ** -12 * block_max_term(A, B, fa, fb, sa, sb, mode, rows)
-    if out_dtype == torch.bfloat16:
-        tol = tol + 2.0 ** -8 * np.abs(Dref)
-    bad = ~(np.abs(D - Dref) <= tol)
-    if bad.any():
-        i = tuple(np.argwhere(bad)[0])
+    sel = np.arange(A.shape[0]) if rows is None else np.asarray(rows)
+    ok, tol = within_fp8_bound(D, Dref, S, out_dtype == torch.bfloat16,
+                               lambda r: fp8_loss(A, B, fa, fb, sa, sb, mode, sel[r]))
+    if not ok.all():
+        i = tuple(np.argwhere(~ok)[0])
         raise AssertionError("%s: %d of %d outside the bound; first %s: got %r ref %r tol %r"
-                             % (what, bad.sum(), bad.size, i, D[i], Dref[i], tol[i]))
+                             % (what, (~ok).sum(), ok.size, i, D[i], Dref[i], tol[i]))
     return D, Dref
 
 
@@ -125,26 +110,21 @@ def test_block_scaled(fa, fb, shape):
     check(A, B, fa, fb, sa, sb, dmu.SCALE_BLOCK, torch.bfloat16, what=str(shape))
 
 
-def sample_rows(M, n=10, seed=0):
-    rng = np.random.default_rng(seed)
-    return np.array(sorted(set([0, M - 1]) | set(rng.integers(0, M, n).tolist())), np.int64)
-
-
 @pytest.mark.parametrize("fmt", [dmu.E4M3, dmu.E5M2])
-def test_4096_per_tensor_sampled(fmt):
+def test_4096_per_tensor(fmt):
+    # the per-tensor workload in full: every output of 4096^3
     A, sa = quant(wl.normal((4096, 4096), wl.SEED_A), fmt)
     B, sb = quant(wl.normal((4096, 4096), wl.SEED_B), fmt)
-    check(A, B, fmt, fmt, sa, sb, dmu.SCALE_TENSOR, torch.bfloat16, rows=sample_rows(4096),
-          what="4096^3 fmt %d" % fmt)
+    check(A, B, fmt, fmt, sa, sb, dmu.SCALE_TENSOR, torch.bfloat16, what="4096^3 fmt %d" % fmt)
 
 
-def test_block_scaled_8192x7168x7168_sampled():
+def test_block_scaled_8192x7168x7168():
+    # the block-scaled workload in full (82 outlier rows x100 included)
     Xa, out_rows = wl.normal_with_outlier_rows((8192, 7168), wl.SEED_A)
     A, sa = quant(Xa, dmu.E4M3, (1, 128))
     del Xa
     B, sb = quant(wl.normal((7168, 7168), wl.SEED_B), dmu.E4M3, (128, 128))
-    rows = np.array(sorted(set(sample_rows(8192, 8).tolist()) | set(out_rows[:4].tolist())), np.int64)
-    check(A, B, 0, 0, sa, sb, dmu.SCALE_BLOCK, torch.bfloat16, rows=rows, what="block 8192")
+    check(A, B, 0, 0, sa, sb, dmu.SCALE_BLOCK, torch.bfloat16, what="block 8192")
 
 
 @pytest.mark.parametrize("K", [256, 1024, 4096, 16384, 65536])
