@@ -7,7 +7,12 @@ Headline (the JSON line's `value`): gemm_bf16 at M = N = K = 4096, A row-major,
 B stored N x K, BF16 output, inputs N(0,1) rounded to BF16, in TFLOP/s.  A
 "step" is one launch of that GEMM; K steps are timed between two device
 synchronisations, each launch also bracketed by HIP events on the stream it
-runs on.  The other workloads (B row-major, FP8 per-tensor E4M3/E5M2, the
+runs on.  After the timed region the headline kernel (and the FP8 E4M3 4096^3
+kernel, the metric's other half) is timed again with the protocol of the
+vidyal.ai page, Step 2 (protocol_rounds): three rounds of back-to-back
+launches, the median of the last three quarters of each, the rounds'
+agreement, and clocks and power polled during those launches; the roofline
+object's per-kernel rate comes from it.  The other workloads (B row-major, FP8 per-tensor E4M3/E5M2, the
 block-scaled 8192x7168x7168 GEMM and its quantizers, the LLM-shaped sweep,
 256^3) are timed the same way in the same process and reported under "legs",
 with "mfma_ceiling": the sustained matrix-unit rate with no memory traffic,
@@ -77,65 +82,121 @@ def time_launches(torch, launch, steps, warmup):
             "event_median_ms": statistics.median(d)}
 
 
-def sample_clocks(torch, launch, seconds=1.5):
-    """Shader clock and socket power while `launch` runs back to back for about
-    `seconds`: amd-smi (a child process) polled every ~100 ms by a thread.
-    Returns medians over the samples (the clock as the median over the XCDs of
-    each sample), or None when amd-smi is missing, prints nothing usable, or
-    the process runs under rocprofv3."""
-    import shutil
-    import subprocess
-    import threading
+class ClockSampler:
+    """Shader clock and socket power polled every ~100 ms by a thread that
+    runs amd-smi (a child process), for as long as the sampler is open.
+    Samples carry their host time, so they can be matched to the rounds they
+    fell in.  Inactive (no samples) when amd-smi is missing or the process
+    runs under rocprofv3, whose preloaded library keeps amd-smi from
+    starting."""
 
-    smi = shutil.which("amd-smi") or "/opt/rocm/bin/amd-smi"
-    if not os.path.exists(smi):
-        return None
-    # under a profiler every child process starts with the profiler's library
-    # loaded, and amd-smi's own start-up then fails: no samples there
-    if "rocprof" in os.environ.get("LD_PRELOAD", "") or any(k.startswith("ROCPROF") for k in os.environ):
-        return None
-    samples, stop = [], threading.Event()
+    def __init__(self):
+        import shutil
 
-    def num(x):
+        self.smi = shutil.which("amd-smi") or "/opt/rocm/bin/amd-smi"
+        self.active = os.path.exists(self.smi) and not (
+            "rocprof" in os.environ.get("LD_PRELOAD", "") or
+            any(k.startswith("ROCPROF") for k in os.environ))
+        self.samples = []
+        self._stop = None
+        self._th = None
+
+    @staticmethod
+    def _num(x):
         v = x.get("value") if isinstance(x, dict) else x
         return float(v) if isinstance(v, (int, float)) else None
 
-    def poll():
-        while not stop.is_set():
+    def _poll(self):
+        import subprocess
+
+        while not self._stop.is_set():
             try:
-                r = subprocess.run([smi, "metric", "-g", "0", "-c", "-p", "--json"],
+                r = subprocess.run([self.smi, "metric", "-g", "0", "-c", "-p", "--json"],
                                    capture_output=True, text=True, timeout=5)
                 d = json.loads(r.stdout)["gpu_data"][0]
-                clks = [num(v.get("clk")) for k, v in d["clock"].items()
+                clks = [self._num(v.get("clk")) for k, v in d["clock"].items()
                         if k.startswith("gfx_") and isinstance(v, dict)]
                 clks = [c for c in clks if c]
-                pw = num(d["power"]["socket_power"])
+                pw = self._num(d["power"]["socket_power"])
                 if clks and pw:
-                    samples.append((time.perf_counter(), statistics.median(clks), pw))
+                    # the clock is the median over the 8 XCDs of one sample
+                    self.samples.append((time.perf_counter(), statistics.median(clks), pw))
             except Exception:  # a sample that fails to parse is skipped
                 pass
-            stop.wait(0.1)
+            self._stop.wait(0.1)
 
-    th = threading.Thread(target=poll, daemon=True)
-    th.start()
-    t0, i = time.perf_counter(), 0
-    while time.perf_counter() - t0 < seconds:
-        for _ in range(100):
-            launch(i)
-            i += 1
-        torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    stop.set()
-    th.join(timeout=10)
-    # only samples taken while the launches ran (not the idle card before them)
-    samples = [(c, w) for ts, c, w in samples if t0 + 0.25 <= ts <= t1]
-    if not samples:
-        return None
-    return {"sclk_mhz_median": statistics.median(c for c, _ in samples),
-            "sclk_mhz_min": min(c for c, _ in samples),
-            "socket_power_w_median": statistics.median(w for _, w in samples),
-            "samples": len(samples), "launches": i,
-            "during": "%.1f s of back-to-back headline launches after the timed region" % seconds}
+    def __enter__(self):
+        import threading
+
+        if self.active:
+            self._stop = threading.Event()
+            self._th = threading.Thread(target=self._poll, daemon=True)
+            self._th.start()
+        return self
+
+    def __exit__(self, *exc):
+        if self._th is not None:
+            self._stop.set()
+            self._th.join(timeout=10)
+
+    def between(self, t0, t1):
+        return [(c, w) for ts, c, w in self.samples if t0 <= ts <= t1]
+
+
+def protocol_rounds(torch, launch, flop, peak, rounds=3, seconds=1.0, warm_s=0.5):
+    """The timing protocol of the vidyal.ai page, Step 2: a warm-up of
+    `warm_s` seconds of back-to-back launches, then `rounds` rounds of
+    `seconds` each, every launch bracketed by HIP events on its stream; each
+    round keeps the median of the last three quarters of its launches, the
+    rounds must agree within 2%, and clocks and power are polled every
+    ~100 ms while the rounds run.  Throughput and clock come from the same
+    launches."""
+    i = 0
+    with ClockSampler() as smp:
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < warm_s:
+            for _ in range(20):
+                launch(i)
+                i += 1
+            torch.cuda.synchronize()
+        out = []
+        for _ in range(rounds):
+            starts, ends = [], []
+            torch.cuda.synchronize()
+            ts = time.perf_counter()
+            while time.perf_counter() - ts < seconds:
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                launch(i)
+                b.record()
+                starts.append(a)
+                ends.append(b)
+                i += 1
+            torch.cuda.synchronize()
+            te = time.perf_counter()
+            d = [x.elapsed_time(y) for x, y in zip(starts, ends)]
+            med = statistics.median(d[len(d) // 4:])
+            clk = smp.between(ts, te)
+            out.append({"median_ms": round(med, 5), "TFLOP_per_s": round(flop / med / 1e9, 1),
+                        "launches": len(d),
+                        "sclk_mhz_median": statistics.median(c for c, _ in clk) if clk else None,
+                        "socket_power_w_median": (statistics.median(w for _, w in clk)
+                                                  if clk else None),
+                        "clock_samples": len(clk)})
+    meds = [r["median_ms"] for r in out]
+    ms = statistics.median(meds)
+    spread = (max(meds) - min(meds)) / ms
+    clk_all = [r["sclk_mhz_median"] for r in out if r["sclk_mhz_median"]]
+    sclk = statistics.median(clk_all) if clk_all else None
+    tf = flop / ms / 1e9
+    return {"ms": round(ms, 5), "TFLOP_per_s": round(tf, 1), "pct_peak": round(100 * tf / peak, 1),
+            "rounds": out, "spread": round(spread, 4), "rounds_agree_within_2pct": spread <= 0.02,
+            "sclk_mhz_median": sclk,
+            "pct_peak_at_measured_sclk": (round(100 * tf / (peak * sclk / 2400.0), 1)
+                                          if sclk else None),
+            "statistic": "median over %d rounds of each round's median of the last 75%% of "
+                         "per-launch HIP-event durations; %.1f s warm-up, %.1f s rounds, clocks "
+                         "and power polled during the rounds" % (rounds, warm_s, seconds)}
 
 
 class Bench:
@@ -206,9 +267,11 @@ class Bench:
             dmu.quantize_fp8(Xb, Qb, sb, fmt)
         return Xa, Xb, Qa, Qb, sa, sb
 
-    def gemm_fp8_leg(self, M, N, K, fmt, steps, warmup, copies=1, block=False, promoted=False):
+    def gemm_fp8_leg(self, M, N, K, fmt, steps, warmup, copies=1, block=False, promoted=False,
+                     protocol=False):
         """promoted: per-tensor operands run through the block-scaled path with
-        every scale equal, i.e. partial sums promoted into FP32 every 128 K."""
+        every scale equal, i.e. partial sums promoted into FP32 every 128 K.
+        protocol: also time the kernel with protocol_rounds."""
         torch, dmu = self.torch, self.dmu
         Xa, Xb, Qa, Qb, sa, sb = self.fp8_operands(M, N, K, fmt, block)
         del Xa, Xb
@@ -226,7 +289,10 @@ class Bench:
         t = time_launches(torch, launch, steps, warmup)
         flop = 2.0 * M * N * K
         bytes_ = 1.0 * (M * K + N * K) + 2.0 * M * N + 4.0 * (sa.numel() + sb.numel())
-        return self.report(t, flop, bytes_, PEAK_FP8_TFLOPS, copies)
+        r = self.report(t, flop, bytes_, PEAK_FP8_TFLOPS, copies)
+        if protocol:
+            r["protocol"] = protocol_rounds(torch, launch, flop, PEAK_FP8_TFLOPS)
+        return r
 
     def fused_leg(self, kind, steps, warmup, copies):
         """4096^3 with the fused epilogue: "bf16_gelu" (BF16 in, + bias, GELU,
@@ -463,12 +529,24 @@ def cpu_baseline(A_bf16, B_bf16, budget_s=10.0):
         done = min(M, done + 256)
     dt = time.perf_counter() - t0
     return {"value": round(2.0 * done * N * K / dt / 1e12, 5), "unit": "TFLOP/s",
-            "cores": oracle.num_threads(), "kind": "oracle",
+            "cores": oracle.num_threads(), "cpu_model": cpu_model(), "kind": "oracle",
             "sample": "rows 0..%d of the 4096^3 BF16 product (FP64 sums, exact decoding), %.1f s"
                       % (done - 1, dt)}
 
 
-def traffic_for(kernel_key, launch_ms):
+def cpu_model() -> str:
+    """The host CPU's model name (first processor in /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def traffic_for(kernel_key):
     """HBM bytes per launch measured with rocprofv3 counters (profiles/traffic.json),
     valid only while the kernel source is unchanged."""
     try:
@@ -493,9 +571,9 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print("bench.py measures one GPU only: the library has no multi-GPU path "
-              "(the GEMM shards without communication; see the design notes). "
-              "Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: libdmu has no multi-GPU path. The GEMM "
+              "would shard over N without communication, each GPU running this kernel on "
+              "its column shard. Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -530,11 +608,15 @@ def main():
     t = time_launches(torch, launch, S, W)
     flop = 2.0 * 4096 ** 3
     value = flop / (t["wall_ms"] * 1e-3) / 1e12
-    achieved = flop / (t["event_mean_ms"] * 1e-3) / 1e12
-    log("headline: %.1f TFLOP/s wall, %.1f TFLOP/s per kernel (%.1f%% of peak)"
-        % (value, achieved, 100 * achieved / PEAK_BF16_TFLOPS))
-    clocks = sample_clocks(torch, launch)
-    log("clocks under the headline kernel: %s" % clocks)
+    log("headline: %.1f TFLOP/s wall over the %d timed launches (HIP-event mean %.5f ms)"
+        % (value, S, t["event_mean_ms"]))
+    # the per-kernel rate of the roofline: the page's protocol, after the
+    # timed region (which stays exactly S launches)
+    proto = protocol_rounds(torch, launch, flop, PEAK_BF16_TFLOPS)
+    achieved = proto["TFLOP_per_s"]
+    log("headline per kernel: %.1f TFLOP/s (%.1f%% of peak), rounds %s, spread %.2f%%, sclk %s MHz"
+        % (achieved, proto["pct_peak"], [r["median_ms"] for r in proto["rounds"]],
+           100 * proto["spread"], proto["sclk_mhz_median"]))
     del As, Bs, out
 
     legs = {}
@@ -543,7 +625,8 @@ def main():
         log("bf16 4096 B row-major: %s" % legs["bf16_4096_nn"])
     for name, fmt in (("fp8_e4m3_4096", dmu.E4M3), ("fp8_e5m2_4096", dmu.E5M2)):
         if want(name):
-            legs[name] = b.gemm_fp8_leg(4096, 4096, 4096, fmt, S, W, copies=10)
+            legs[name] = b.gemm_fp8_leg(4096, 4096, 4096, fmt, S, W, copies=10,
+                                        protocol=name == "fp8_e4m3_4096")
             log("%s: %s" % (name, legs[name]))
     if want("fp8_e4m3_4096_promoted"):
         legs["fp8_e4m3_4096_promoted"] = b.gemm_fp8_leg(4096, 4096, 4096, dmu.E4M3, S, W, copies=10,
@@ -635,13 +718,11 @@ def main():
         "fp8_e4m3_4096": legs.get("fp8_e4m3_4096"),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic_for("gemm_bf16_4096_tn", t["event_mean_ms"]),
+                     "traffic": traffic_for("gemm_bf16_4096_tn"),
                      "kernel": "gemm_kernel<kBF16, B col-major, 256x256>",
-                     "kernel_ms": round(t["event_mean_ms"], 5)},
+                     "kernel_ms": proto["ms"]},
+        "protocol": proto,
         "cpu_baseline": cpu,
-        "clocks": clocks,
-        "pct_peak_at_measured_sclk": (round(100 * achieved / (PEAK_BF16_TFLOPS * clocks["sclk_mhz_median"]
-                                                              / 2400.0), 1) if clocks else None),
         "legs": legs,
     }
     print(json.dumps(line), flush=True)
