@@ -61,16 +61,20 @@ def _compile(src: str) -> str:
     return obj
 
 
-_VREG = re.compile(r"v\[(\d+):(\d+)\]|v(\d+)$")
+# a vector register operand, with or without modifiers (-v9, |v9|, -|v9|,
+# neg(v9), sext(v9)): v9 or the range v[8:11]
+_VREG = re.compile(r"(?<![\w.])v(?:\[(\d+):(\d+)\]|(\d+))(?!\w)")
 
 
-def _vregs(tok: str) -> set:
-    m = _VREG.match(tok)
-    if not m:
-        return set()
-    if m.group(3) is not None:
-        return {int(m.group(3))}
-    return set(range(int(m.group(1)), int(m.group(2)) + 1))
+def _vregs(text: str) -> set:
+    """Every vector register named in `text` (an operand list)."""
+    regs = set()
+    for m in _VREG.finditer(text):
+        if m.group(3) is not None:
+            regs.add(int(m.group(3)))
+        else:
+            regs.update(range(int(m.group(1)), int(m.group(2)) + 1))
+    return regs
 
 
 def check_lds_asm_waits(src: str = "attention.hip") -> int:
@@ -92,14 +96,26 @@ def check_lds_asm_waits(src: str = "attention.hip") -> int:
 
 def scan_lds_asm_waits(lines, name: str = "<listing>") -> int:
     """The check of check_lds_asm_waits over an assembly listing (an iterable
-    of lines); returns the number of transposing reads checked."""
+    of lines); returns the number of transposing reads checked.  While a read
+    is pending (issued, its s_waitcnt lgkmcnt not yet reached), any
+    instruction naming one of its destination registers in any operand --
+    read, written, stored or used as an address, with or without modifiers --
+    is an error, and so is a basic-block label or a branch: the scan follows
+    the listing in order, so a pending read must not cross control flow."""
     pending, checked = {}, 0
     for n, line in enumerate(lines):
-        t = line.strip()
-        if line[:1] not in (" ", "\t") or not t or t[0] in ";." or t.endswith(":"):
-            if t.endswith(":") and not t.startswith("."):
-                pending = {}  # a new function
+        t = line.split(";")[0].strip()
+        if not t:
             continue
+        if t.endswith(":"):
+            if not t.startswith("."):
+                pending = {}  # a new function
+            elif pending:
+                raise RuntimeError("%s:%d: label %s with hand-waited LDS reads pending"
+                                   % (name, n + 1, t))
+            continue
+        if line[:1] not in (" ", "\t") or t[0] == ".":
+            continue  # directives and other non-instruction lines
         op = t.split()[0]
         if op == "s_waitcnt":
             m = re.search(r"lgkmcnt\((\d+)\)", t)
@@ -109,20 +125,19 @@ def scan_lds_asm_waits(lines, name: str = "<listing>") -> int:
                 keep = set(order[len(order) - c:]) if c else set()
                 pending = {reg: ln for reg, ln in pending.items() if ln in keep}
             continue
+        if pending and op.startswith(("s_branch", "s_cbranch", "s_setpc", "s_swappc")):
+            raise RuntimeError("%s:%d: branch with hand-waited LDS reads pending: %s"
+                               % (name, n + 1, t))
         if op.startswith("s_"):
             continue
-        args = [a.strip().split()[0] if a.strip() else "" for a in t[len(op):].split(",")]
-        touched = set()
-        for a in args[1:]:
-            touched |= _vregs(a)
-        if not op.startswith(("ds_", "buffer_", "global_")) and args:
-            touched |= _vregs(args[0])  # a VALU/MFMA write
-        if touched & set(pending):
+        operands = t[len(op):]
+        if _vregs(operands) & set(pending):
             raise RuntimeError("%s:%d uses a transposing LDS read's registers before its "
                                "wait: %s" % (name, n + 1, t))
         if op == "ds_read_b64_tr_b16":
             checked += 1
-            for reg in _vregs(args[0]):
+            dest = operands.split(",")[0]
+            for reg in _vregs(dest):
                 pending[reg] = n
     if checked == 0:
         raise RuntimeError("%s: no transposing LDS reads found to check" % name)
