@@ -444,6 +444,7 @@ class Bench:
 
     def quantize_leg(self, rows, cols, fmt, block, steps, warmup, outliers=False):
         torch, dmu = self.torch, self.dmu
+        quantize = dmu.quantize_fp8
         if outliers:
             X, _ = self.wl.normal_with_outlier_rows((rows, cols), 1)
             X = torch.from_numpy(X).to(self.dev)
@@ -454,7 +455,7 @@ class Bench:
         s = torch.empty(((rows // br) * (cols // bc),), dtype=torch.float32, device=self.dev)
 
         def launch(i):
-            dmu.quantize_fp8(X, Q, s, fmt, block)
+            quantize(X, Q, s, fmt, block)
 
         t = time_launches(torch, launch, steps, warmup)
         bytes_ = 5.0 * rows * cols + 4.0 * s.numel()

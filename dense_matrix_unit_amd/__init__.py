@@ -341,6 +341,10 @@ def quantize_fp8(X, Q, scales, fmt: int = E4M3, block=None, stream=None):
     """Q, scales = FP8 quantisation of X (float32 [rows, cols]).  block: None
     (one scale for the tensor), (1, 128) or (128, 128).  Q: uint8 [rows, cols];
     scales: float32 [rows/br, cols/bc] (dequantisation factors)."""
+    return _quantize_fp8("quantize_fp8", X, Q, scales, fmt, block, stream)
+
+
+def _quantize_fp8(fn, X, Q, scales, fmt, block, stream):
     torch = _torch()
     _check_dtype(X, (torch.float32,), "X")
     rows, cols = X.shape
@@ -350,10 +354,10 @@ def quantize_fp8(X, Q, scales, fmt: int = E4M3, block=None, stream=None):
     if scales.numel() < (rows // br) * (cols // bc) or not scales.is_contiguous():
         raise ValueError("scales must be contiguous with one element per block")
     _check_dtype(scales, (torch.float32,), "scales")
-    rc = load_library().quantize_fp8(
+    rc = getattr(load_library(), fn)(
         _dev_ptr(X, "X"), rows, cols, _ld(X, "X"), fmt, br, bc, _fp8_ptr(Q, "Q"), _ld(Q, "Q"),
         _dev_ptr(scales, "scales"), _stream(stream))
-    _check("quantize_fp8", rc)
+    _check(fn, rc)
     return Q, scales
 
 

@@ -141,9 +141,12 @@ int gemm_fp8_scaled(const uint8_t* A, int64_t lda, int fmt_a, const uint8_t* B, 
                                      (hipStream_t)stream));
 }
 
-int quantize_fp8(const float* X, int64_t rows, int64_t cols, int64_t ldx, int fmt,
-                 int64_t block_rows, int64_t block_cols, uint8_t* Q, int64_t ldq, float* scales,
-                 void* stream) {
+namespace {
+
+// Argument checks of quantize_fp8.
+int quantize_args(const float* X, int64_t rows, int64_t cols, int64_t ldx, int fmt,
+                  int64_t block_rows, int64_t block_cols, const uint8_t* Q, int64_t ldq,
+                  const float* scales) {
   if (!X || !Q || !scales || rows < 1 || cols < 1) return DMU_ERR_INVALID_ARG;
   if (fmt != DMU_FP8_E4M3 && fmt != DMU_FP8_E5M2) return DMU_ERR_INVALID_ARG;
   if (ldx < cols || ldq < cols || ldx % 4 || ldq % 16) return DMU_ERR_INVALID_ARG;
@@ -156,9 +159,24 @@ int quantize_fp8(const float* X, int64_t rows, int64_t cols, int64_t ldx, int fm
   if (!tensor && !row128 && !blk128) return DMU_ERR_UNSUPPORTED;
   if (tensor && cols % 4) return DMU_ERR_UNSUPPORTED;
   if ((rows / block_rows) * (cols / block_cols) > INT32_MAX) return DMU_ERR_UNSUPPORTED;
+  return DMU_OK;
+}
+
+}  // namespace
+
+int quantize_fp8(const float* X, int64_t rows, int64_t cols, int64_t ldx, int fmt,
+                 int64_t block_rows, int64_t block_cols, uint8_t* Q, int64_t ldq, float* scales,
+                 void* stream) {
+  int rc = quantize_args(X, rows, cols, ldx, fmt, block_rows, block_cols, Q, ldq, scales);
+  if (rc) return rc;
+  const int64_t slots = dmu::quantize_scratch_slots(rows, cols, ldx, ldq, block_rows, block_cols);
+  if (slots > dmu::kQuantizeScratchSlots) return DMU_ERR_UNSUPPORTED;
   (void)hipGetLastError();
+  hipStream_t s = (hipStream_t)stream;
+  if (slots > 0)  // per tensor: the library's workspace on the stream's GPU
+    return finish(dmu::launch_quantize_fp8_tensor_ws(X, rows, cols, ldx, fmt, Q, ldq, scales, s));
   return finish(dmu::launch_quantize_fp8(X, rows, cols, ldx, fmt, block_rows, block_cols, Q, ldq,
-                                         scales, (hipStream_t)stream));
+                                         scales, nullptr, s));
 }
 
 int gemm_mxfp8(const uint8_t* A, int64_t lda, int fmt_a, const uint8_t* B, int64_t ldb,

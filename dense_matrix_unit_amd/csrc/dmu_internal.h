@@ -84,9 +84,23 @@ hipError_t launch_quantize_mxfp4(const float* X, int64_t rows, int64_t cols, int
                                  hipStream_t s);
 hipError_t launch_quantize_mxfp8(const float* X, int64_t rows, int64_t cols, int64_t ldx, int fmt,
                                  uint8_t* Q, int64_t ldq, uint8_t* S, int64_t lds, hipStream_t s);
+// quantize_fp8: the per-tensor mode writes one uint32 amax partial per
+// pass-1 workgroup to `part` and reads them all in the second pass;
+// quantize_scratch_slots gives how many (at most 512 whatever the tensor's
+// size; 0 for block scales, which need no scratch).
+int64_t quantize_scratch_slots(int64_t rows, int64_t cols, int64_t ldx, int64_t ldq, int64_t br,
+                               int64_t bc);
 hipError_t launch_quantize_fp8(const float* X, int64_t rows, int64_t cols, int64_t ldx, int fmt,
                                int64_t br, int64_t bc, uint8_t* Q, int64_t ldq, float* scales,
-                               hipStream_t s);
+                               uint32_t* part, hipStream_t s);
+constexpr int64_t kQuantizeScratchSlots = 1024;  // slots of the workspace (4 KiB)
+constexpr int kMaxDevices = 64;
+// Per-tensor quantize_fp8 on the library's workspace of the stream's GPU
+// (allocated on first use, calls on different streams ordered by an event).
+hipError_t launch_quantize_fp8_tensor_ws(const float* X, int64_t rows, int64_t cols, int64_t ldx,
+                                         int fmt, uint8_t* Q, int64_t ldq, float* scales,
+                                         hipStream_t s);
+
 
 hipError_t launch_probe_mfma(int kind, int fa, int fb, const void* A, const void* B,
                              const float* C, float* D, int count, hipStream_t s);

@@ -8,11 +8,14 @@
 // product x*m, and the dequantisation factor s = amax / FMAX is stored.
 //
 // Kernels (all HBM-bound streaming; every value is read once per pass):
-//  * per tensor: (1) clear the amax slot, (2) grid-wide amax with one atomic
-//    max per workgroup on the bit pattern of |x| (for non-negative floats the
-//    integer order is the numeric order, and any NaN pattern sorts above
-//    +Inf, so a NaN anywhere yields a NaN amax), (3) encode, (4) replace amax
-//    by the scale.  The amax slot is scales[0] itself.
+//  * per tensor: two passes.  Pass 1: each workgroup writes the max of the
+//    bit patterns of |x| over its grid-stride share to its own scratch slot
+//    (for non-negative floats the integer order is the numeric order, and
+//    any NaN pattern sorts above +Inf, so a NaN anywhere yields a NaN amax).
+//    Pass 2: each workgroup takes the max of all slots (the tensor's amax),
+//    then encodes its share; workgroup 0 stores the scale.  No slot needs
+//    clearing and no atomics are used; the slot count is the pass-1 grid
+//    (at most kTensorSlots, whatever the tensor's size).
 //  * 1 x 128 blocks: 32 lanes per block (16 bytes per lane), half-wave max.
 //  * 128 x 128 blocks: one 256-thread workgroup per block keeps its 64 values
 //    per thread in registers between the amax and the encode (one HBM read).
@@ -30,6 +33,8 @@
 //    signs.  MXFP4 (E2M1, emax = 2) packs the four codes of a lane into 16
 //    bits, element 2i in the low nibble; a NaN/Inf block's elements are
 //    signed zeros (E2M1 has no NaN).
+#include <mutex>
+
 #include "dmu_device.h"
 #include "dmu_internal.h"
 
@@ -80,52 +85,79 @@ __device__ __forceinline__ uint32_t encode4(f32x4_t x, float m) {
 }
 
 // ---- per tensor -----------------------------------------------------------
-// Both passes walk rows: workgroup b takes rows b, b + grid, ...; inside a row
-// each thread takes float4 columns t, t + 256, ..., four at a time so that
-// several loads are in flight per thread.  No per-element division.
-
-__global__ void clear_slot(float* s) { *(uint32_t*)s = 0u; }
 
 __device__ __forceinline__ uint32_t amax4(const f32x4_t& v) {
   return max(max(abs_bits(v[0]), abs_bits(v[1])), max(abs_bits(v[2]), abs_bits(v[3])));
 }
 
-// Workgroup max -> one atomic max on the slot.  Device-scope atomics on one
-// address are serialised across the XCDs, so the flat pass uses few, large
-// workgroups (one per CU).
+// Workgroup-wide max of one value per thread (every thread gets the result).
 template <int NT>
-__device__ __forceinline__ void amax_commit(uint32_t m, float* slot) {
-  m = wave_max(m);
+__device__ __forceinline__ uint32_t block_max(uint32_t m) {
   __shared__ uint32_t red[NT / 64];
+  m = wave_max(m);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t b = 0;
-    for (int w = 0; w < NT / 64; ++w) b = max(b, red[w]);
-    atomicMax((unsigned int*)slot, b);
-  }
+  uint32_t b = 0;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) b = max(b, red[w]);
+  return b;
 }
 
-// Contiguous tensor (ldx == cols): flat grid-stride walk, 8 float4 loads in
-// flight per thread.
-__global__ __launch_bounds__(1024) void amax_flat(const f32x4_t* X, int64_t n4, float* slot) {
+// Contiguous tensor (ldx == ldq == cols): a flat grid-stride walk, 8 float4
+// loads in flight per thread, nontemporal (X is read once per pass).
+constexpr int kFlatThreads = 1024;
+constexpr int kFlatGrid = 256;     // one workgroup per CU
+constexpr int kRowsGrid = 512;     // strided rows: at most this many workgroups
+constexpr int kUnroll = 8;
+
+__global__ __launch_bounds__(kFlatThreads) void amax_flat(const f32x4_t* X, int64_t n4,
+                                                          uint32_t* part) {
   uint32_t m = 0;
-  const int64_t stride = (int64_t)gridDim.x * 1024;
-  int64_t i = (int64_t)blockIdx.x * 1024 + threadIdx.x;
-  for (; i + 7 * stride < n4; i += 8 * stride) {
-    f32x4_t v[8];
+  const int64_t stride = (int64_t)gridDim.x * kFlatThreads;
+  int64_t i = (int64_t)blockIdx.x * kFlatThreads + threadIdx.x;
+  for (; i + (kUnroll - 1) * stride < n4; i += kUnroll * stride) {
+    f32x4_t v[kUnroll];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = __builtin_nontemporal_load(X + i + u * stride);
+    for (int u = 0; u < kUnroll; ++u) v[u] = __builtin_nontemporal_load(X + i + u * stride);
 #pragma unroll
-    for (int u = 0; u < 8; ++u) m = max(m, amax4(v[u]));
+    for (int u = 0; u < kUnroll; ++u) m = max(m, amax4(v[u]));
   }
-  for (; i < n4; i += stride) m = max(m, amax4(X[i]));
-  amax_commit<1024>(m, slot);
+  for (; i < n4; i += stride) m = max(m, amax4(__builtin_nontemporal_load(X + i)));
+  m = block_max<kFlatThreads>(m);
+  if (threadIdx.x == 0) part[blockIdx.x] = m;
 }
 
-// Strided rows.
-__global__ __launch_bounds__(256) void amax_tensor(const float* X, int64_t rows, int64_t cols4,
-                                                   int64_t ldx, float* slot) {
+// The tensor's amax: the max of the nparts slots pass 1 wrote.
+template <int NT>
+__device__ __forceinline__ float gather_amax(const uint32_t* part, int nparts) {
+  uint32_t m = 0;
+  for (int i = threadIdx.x; i < nparts; i += NT) m = max(m, part[i]);
+  return __uint_as_float(block_max<NT>(m));
+}
+
+template <int FMT>
+__global__ __launch_bounds__(kFlatThreads) void encode_flat(const f32x4_t* X, int64_t n4,
+                                                            uint32_t* Q4, const uint32_t* part,
+                                                            int nparts, float* scales) {
+  const float amax = gather_amax<kFlatThreads>(part, nparts);
+  const float m = mult_from_amax<FMT>(amax);
+  if (blockIdx.x == 0 && threadIdx.x == 0) scales[0] = scale_from_amax<FMT>(amax);
+  const int64_t stride = (int64_t)gridDim.x * kFlatThreads;
+  int64_t i = (int64_t)blockIdx.x * kFlatThreads + threadIdx.x;
+  for (; i + (kUnroll - 1) * stride < n4; i += kUnroll * stride) {
+    f32x4_t v[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) v[u] = __builtin_nontemporal_load(X + i + u * stride);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) Q4[i + u * stride] = encode4<FMT>(v[u], m);
+  }
+  for (; i < n4; i += stride) Q4[i] = encode4<FMT>(__builtin_nontemporal_load(X + i), m);
+}
+
+// Strided rows: workgroup b walks rows b, b + grid, ..., threads striding
+// over each row's float4 columns.
+__global__ __launch_bounds__(256) void amax_rows(const float* X, int64_t rows, int64_t cols4,
+                                                 int64_t ldx, uint32_t* part) {
   uint32_t m = 0;
   for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
     const float* row = X + r * ldx;
@@ -139,14 +171,18 @@ __global__ __launch_bounds__(256) void amax_tensor(const float* X, int64_t rows,
     }
     for (; c < cols4; c += 256) m = max(m, amax4(*(const f32x4_t*)(row + 4 * c)));
   }
-  amax_commit<256>(m, slot);
+  m = block_max<256>(m);
+  if (threadIdx.x == 0) part[blockIdx.x] = m;
 }
 
 template <int FMT>
-__global__ __launch_bounds__(256) void encode_tensor(const float* X, int64_t rows, int64_t cols4,
-                                                     int64_t ldx, uint8_t* Q, int64_t ldq,
-                                                     const float* slot) {
-  const float m = mult_from_amax<FMT>(*slot);
+__global__ __launch_bounds__(256) void encode_rows(const float* X, int64_t rows, int64_t cols4,
+                                                   int64_t ldx, uint8_t* Q, int64_t ldq,
+                                                   const uint32_t* part, int nparts,
+                                                   float* scales) {
+  const float amax = gather_amax<256>(part, nparts);
+  const float m = mult_from_amax<FMT>(amax);
+  if (blockIdx.x == 0 && threadIdx.x == 0) scales[0] = scale_from_amax<FMT>(amax);
   for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
     const float* row = X + r * ldx;
     uint8_t* qrow = Q + r * ldq;
@@ -161,11 +197,6 @@ __global__ __launch_bounds__(256) void encode_tensor(const float* X, int64_t row
     for (; c < cols4; c += 256)
       *(uint32_t*)(qrow + 4 * c) = encode4<FMT>(*(const f32x4_t*)(row + 4 * c), m);
   }
-}
-
-template <int FMT>
-__global__ void finalize_tensor(float* slot) {
-  *slot = scale_from_amax<FMT>(*slot);
 }
 
 // ---- 1 x 128 blocks -------------------------------------------------------
@@ -290,23 +321,46 @@ __global__ __launch_bounds__(256) void quant_mx(const float* X, int64_t rows, in
   }
 }
 
+// Per-tensor geometry: contiguous tensors take the flat walk, others rows.
+struct TensorPasses {
+  bool flat;
+  int nparts;  // pass-1 workgroups = scratch slots
+};
+
+TensorPasses tensor_passes(int64_t rows, int64_t cols, int64_t ldx, int64_t ldq) {
+  TensorPasses t;
+  t.flat = ldx == cols && ldq == cols;
+  t.nparts = t.flat ? kFlatGrid : (int)(rows < kRowsGrid ? rows : kRowsGrid);
+  return t;
+}
+
+template <int FMT>
+void launch_tensor(const float* X, int64_t rows, int64_t cols, int64_t ldx, uint8_t* Q,
+                   int64_t ldq, float* scales, uint32_t* part, const TensorPasses& t,
+                   hipStream_t s) {
+  const int64_t cols4 = cols / 4;
+  if (t.flat) {
+    const int64_t n4 = rows * cols4;
+    hipLaunchKernelGGL(amax_flat, dim3((unsigned)t.nparts), dim3(kFlatThreads), 0, s,
+                       (const f32x4_t*)X, n4, part);
+    hipLaunchKernelGGL(encode_flat<FMT>, dim3((unsigned)t.nparts), dim3(kFlatThreads), 0, s,
+                       (const f32x4_t*)X, n4, (uint32_t*)Q, (const uint32_t*)part, t.nparts,
+                       scales);
+  } else {
+    hipLaunchKernelGGL(amax_rows, dim3((unsigned)t.nparts), dim3(256), 0, s, X, rows, cols4,
+                       ldx, part);
+    hipLaunchKernelGGL(encode_rows<FMT>, dim3((unsigned)t.nparts), dim3(256), 0, s, X, rows,
+                       cols4, ldx, Q, ldq, (const uint32_t*)part, t.nparts, scales);
+  }
+}
+
 template <int FMT>
 hipError_t launch_fmt(const float* X, int64_t rows, int64_t cols, int64_t ldx, int64_t br,
-                      int64_t bc, uint8_t* Q, int64_t ldq, float* scales, hipStream_t s) {
+                      int64_t bc, uint8_t* Q, int64_t ldq, float* scales, uint32_t* part,
+                      hipStream_t s) {
   if (br == rows && bc == cols) {
-    const int64_t cols4 = cols / 4;
-    const int64_t grid = rows < 2048 ? rows : 2048;  // 8 workgroups per CU on 256 CUs
-    const int64_t agrid = rows < 512 ? rows : 512;   // strided amax: fewer atomics
-    hipLaunchKernelGGL(clear_slot, dim3(1), dim3(1), 0, s, scales);
-    if (ldx == cols)
-      hipLaunchKernelGGL(amax_flat, dim3(256), dim3(1024), 0, s, (const f32x4_t*)X, rows * cols4,
-                         scales);
-    else
-      hipLaunchKernelGGL(amax_tensor, dim3((unsigned)agrid), dim3(256), 0, s, X, rows, cols4, ldx,
-                         scales);
-    hipLaunchKernelGGL(encode_tensor<FMT>, dim3((unsigned)grid), dim3(256), 0, s, X, rows,
-                       cols4, ldx, Q, ldq, scales);
-    hipLaunchKernelGGL(finalize_tensor<FMT>, dim3(1), dim3(1), 0, s, scales);
+    launch_tensor<FMT>(X, rows, cols, ldx, Q, ldq, scales, part,
+                       tensor_passes(rows, cols, ldx, ldq), s);
   } else if (br == 1 && bc == 128) {
     const int64_t nbc = cols / 128, nblk = rows * nbc;
     hipLaunchKernelGGL(quant_1x128<FMT>, dim3((unsigned)((nblk + 8 * kRounds - 1) / (8 * kRounds))),
@@ -342,11 +396,74 @@ hipError_t launch_quantize_mxfp4(const float* X, int64_t rows, int64_t cols, int
   return hipGetLastError();
 }
 
+int64_t quantize_scratch_slots(int64_t rows, int64_t cols, int64_t ldx, int64_t ldq,
+                               int64_t br, int64_t bc) {
+  if (br != rows || bc != cols) return 0;  // block scales need no scratch
+  return tensor_passes(rows, cols, ldx, ldq).nparts;
+}
+
 hipError_t launch_quantize_fp8(const float* X, int64_t rows, int64_t cols, int64_t ldx, int fmt,
                                int64_t br, int64_t bc, uint8_t* Q, int64_t ldq, float* scales,
-                               hipStream_t s) {
-  if (fmt == 0) return launch_fmt<0>(X, rows, cols, ldx, br, bc, Q, ldq, scales, s);
-  return launch_fmt<1>(X, rows, cols, ldx, br, bc, Q, ldq, scales, s);
+                               uint32_t* part, hipStream_t s) {
+  if (fmt == 0) return launch_fmt<0>(X, rows, cols, ldx, br, bc, Q, ldq, scales, part, s);
+  return launch_fmt<1>(X, rows, cols, ldx, br, bc, Q, ldq, scales, part, s);
+}
+
+// ---- scratch of the per-tensor passes --------------------------------------
+
+int device_of(hipStream_t s, hipError_t* e) {
+  hipDevice_t dev = 0;
+  *e = hipStreamGetDevice(s, &dev);
+  return dev;
+}
+
+// quantize_fp8 (the allocating entry point): one workspace of
+// kQuantizeScratchSlots slots per GPU, allocated on the first per-tensor call
+// on that GPU and kept until the process ends.  Calls on different streams
+// would otherwise share it concurrently, so every call first makes its
+// stream wait for the previous call's completion event, then records its own.
+hipError_t launch_quantize_fp8_tensor_ws(const float* X, int64_t rows, int64_t cols, int64_t ldx,
+                                         int fmt, uint8_t* Q, int64_t ldq, float* scales,
+                                         hipStream_t s) {
+  struct Workspace {
+    uint32_t* slots = nullptr;
+    hipEvent_t done = nullptr;  // recorded after each call's last kernel
+    hipStream_t last = nullptr;
+    bool used = false;
+  };
+  static std::mutex mu;
+  static Workspace ws[kMaxDevices];
+  hipError_t e;
+  const int dev = device_of(s, &e);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  Workspace& w = ws[dev];
+  if (!w.slots) {
+    int cur = -1;
+    if ((e = hipGetDevice(&cur)) != hipSuccess) return e;
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    e = hipMalloc((void**)&w.slots, kQuantizeScratchSlots * sizeof(uint32_t));
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&w.done, hipEventDisableTiming);
+    if (cur != dev) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess) {
+      if (w.slots) (void)hipFree(w.slots);
+      w.slots = nullptr;
+      return e;
+    }
+  }
+  // a call on the stream that used the workspace last is ordered after it
+  // already; another stream waits for that call's completion first
+  if (w.used && s != w.last && (e = hipStreamWaitEvent(s, w.done, 0)) != hipSuccess) return e;
+  e = launch_quantize_fp8(X, rows, cols, ldx, fmt, rows, cols, Q, ldq, scales, w.slots, s);
+  if (e != hipSuccess) return e;
+  if ((e = hipEventRecord(w.done, s)) != hipSuccess) return e;
+  w.used = true;
+  w.last = s;
+  return hipSuccess;
 }
 
 }  // namespace dmu

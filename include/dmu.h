@@ -9,7 +9,8 @@
  * and returns without synchronising; a nonzero status means nothing was
  * enqueued (or, for DMU_ERR_HIP, that the launch itself failed).  Faults
  * inside a kernel surface at the caller's next synchronisation.  Calls are
- * thread-safe; the library holds no mutable global state.
+ * thread-safe.  Nothing is allocated except the per-tensor quantize_fp8
+ * workspace (4 KiB per GPU, once).
  *
  * Matrices are dense with a leading dimension counted in elements: element
  * (r, c) of a row-major matrix X lives at X[r * ldx + c].  Every pointer must
@@ -166,10 +167,17 @@ int gemm_fp8_scaled(const uint8_t* A, int64_t lda, int fmt_a, const uint8_t* B, 
  * (scale NaN, codes NaN); one holding an Inf and no NaN gets amax = +Inf
  * (scale +Inf, finite inputs encode to +-0, infinite ones to NaN).  The result
  * is bit-exact and independent of launch configuration.
- * The per-tensor mode writes amax into scales[0] as scratch before it writes
- * the final scale there, and needs no other workspace.
+ * The per-tensor mode runs two passes: per-workgroup amax partials, then the
+ * encode.  The partials (at most 512 x 4 bytes, whatever the tensor's size)
+ * live in a 4 KiB workspace that the library allocates once per GPU, at the
+ * first per-tensor call on it, and keeps until the process ends; each call
+ * makes its stream wait for the previous per-tensor call on that GPU (an
+ * event), so calls on different streams never share it concurrently.  Block
+ * scales need no workspace.
  * Errors: DMU_ERR_INVALID_ARG for null pointers, bad sizes, leading dimensions
- * or alignment, an unknown format; DMU_ERR_UNSUPPORTED for other block shapes.
+ * or alignment, an unknown format; DMU_ERR_UNSUPPORTED for other block shapes;
+ * DMU_ERR_HIP if the workspace cannot be allocated or a launch fails.
+ * Per-tensor calls on one GPU are ordered with each other across streams.
  */
 int quantize_fp8(const float* X, int64_t rows, int64_t cols, int64_t ldx, int fmt,
                  int64_t block_rows, int64_t block_cols, uint8_t* Q, int64_t ldq, float* scales,

@@ -247,3 +247,19 @@ def test_attention_rejects(kw):
 def test_attention_rejects_heads_past_32_bit_offsets():
     # Q's rows span 2^31 bytes; the output heads are laid out without overlap
     assert call_attention(ldq=1 << 16, Sq=1 << 15, ho=1 << 22) == dmu.DMU_ERR_UNSUPPORTED
+
+
+def call_quantize(fn, **kw):
+    a = dict(X=FAKE, rows=64, cols=128, ldx=128, fmt=0, br=64, bc=128, Q=FAKE, ldq=128, s=FAKE,
+             stream=None)
+    a.update(kw)
+    return getattr(dmu.load_library(), fn)(*a.values())
+
+
+@pytest.mark.parametrize("fn", ["quantize_fp8"])
+@pytest.mark.parametrize("kw", [
+    dict(X=None), dict(Q=None), dict(s=None), dict(rows=0), dict(fmt=2), dict(ldx=126),
+    dict(ldq=120), dict(br=3), dict(X=FAKE + 4), dict(Q=FAKE + 8), dict(s=FAKE + 2),
+])
+def test_quantize_rejects(fn, kw):
+    assert call_quantize(fn, **kw) == dmu.DMU_ERR_INVALID_ARG

@@ -88,3 +88,28 @@ def test_block_sizes_of_block_scaled_workload():
     Xb = wl.normal((7168, 7168), wl.SEED_B)
     Q, s = run_quant(Xb, dmu.E4M3, (128, 128))
     compare(Xb, dmu.E4M3, (128, 128), Q, s)
+
+
+def test_per_tensor_calls_on_two_streams():
+    # per-tensor quantisation keeps its amax partials in a workspace shared by
+    # every stream of the GPU; calls alternating between two streams, each on
+    # its own tensor (one 100x the other), must each get their own amax
+    X1 = wl.normal((2048, 2048), 11)
+    X2 = wl.normal((2048, 2048), 12) * np.float32(100.0)
+    g1, g2 = torch.from_numpy(X1).cuda(), torch.from_numpy(X2).cuda()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    outs = []
+    for it in range(6):
+        st, X = (s1, g1) if it % 2 == 0 else (s2, g2)
+        Q = torch.empty((2048, 2048), dtype=torch.uint8, device="cuda")
+        sc = torch.empty(1, dtype=torch.float32, device="cuda")
+        with torch.cuda.stream(st):
+            dmu.quantize_fp8(X, Q, sc, dmu.E4M3)
+        outs.append((Q, sc))
+    torch.cuda.synchronize()
+    refs = [oracle.quantize_fp8(X, oracle.E4M3) for X in (X1, X2)]
+    for it, (Q, sc) in enumerate(outs):
+        Qr, sr = refs[it % 2]
+        assert np.array_equal(Q.cpu().numpy(), Qr), it
+        assert sc.item() == float(sr[0, 0]), it
