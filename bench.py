@@ -442,9 +442,9 @@ class Bench:
                 "pct_hbm_peak": round(100 * bytes_ / ms / 1e6 / PEAK_HBM_GBS, 1),
                 "algorithmic_MB": round(bytes_ / 1e6, 2), "wall_ms": round(t["wall_ms"], 5)}
 
-    def quantize_leg(self, rows, cols, fmt, block, steps, warmup, outliers=False):
+    def quantize_leg(self, rows, cols, fmt, block, steps, warmup, outliers=False, noalloc=False):
         torch, dmu = self.torch, self.dmu
-        quantize = dmu.quantize_fp8
+        quantize = dmu.quantize_fp8_noalloc if noalloc else dmu.quantize_fp8
         if outliers:
             X, _ = self.wl.normal_with_outlier_rows((rows, cols), 1)
             X = torch.from_numpy(X).to(self.dev)
@@ -666,6 +666,10 @@ def main():
     if want("quantize_e4m3_4096_tensor"):
         legs["quantize_e4m3_4096_tensor"] = b.quantize_leg(4096, 4096, dmu.E4M3, None, S, W)
         log("quantize 4096^2: %s" % legs["quantize_e4m3_4096_tensor"])
+        legs["quantize_e4m3_4096_tensor_noalloc"] = b.quantize_leg(4096, 4096, dmu.E4M3, None, S,
+                                                                   W, noalloc=True)
+        log("quantize 4096^2, allocation-free entry: %s"
+            % legs["quantize_e4m3_4096_tensor_noalloc"])
     if want("fp8_block_8192x7168x7168"):
         legs["fp8_block_8192x7168x7168"] = b.gemm_fp8_leg(8192, 7168, 7168, dmu.E4M3, S4, W4,
                                                            block=True)

@@ -54,6 +54,7 @@ SYMBOLS = {
     "gemm_fp8_scaled": (_I, [_P, _I64, _I, _P, _I64, _I, _P, _P, _I, _P, _I64, _P, _I64, _I,
                              _I64, _I64, _I64, _P]),
     "quantize_fp8": (_I, [_P, _I64, _I64, _I64, _I, _I64, _I64, _P, _I64, _P, _P]),
+    "quantize_fp8_noalloc": (_I, [_P, _I64, _I64, _I64, _I, _I64, _I64, _P, _I64, _P, _P]),
     "gemm_bf16_fused": (_I, [_P, _I64, _P, _I64, _I, _P, _I, _P, _I64, _I, _P, _I64, _I64, _I64,
                              _P]),
     "gemm_fp8_fused": (_I, [_P, _I64, _I, _P, _I64, _I, _P, _P, _P, _I, _P, _I64, _I, _P, _I64,
@@ -342,6 +343,12 @@ def quantize_fp8(X, Q, scales, fmt: int = E4M3, block=None, stream=None):
     (one scale for the tensor), (1, 128) or (128, 128).  Q: uint8 [rows, cols];
     scales: float32 [rows/br, cols/bc] (dequantisation factors)."""
     return _quantize_fp8("quantize_fp8", X, Q, scales, fmt, block, stream)
+
+
+def quantize_fp8_noalloc(X, Q, scales, fmt: int = E4M3, block=None, stream=None):
+    """quantize_fp8 through the entry point that allocates nothing (static
+    scratch; calls overlapping on one GPU race, see include/dmu.h)."""
+    return _quantize_fp8("quantize_fp8_noalloc", X, Q, scales, fmt, block, stream)
 
 
 def _quantize_fp8(fn, X, Q, scales, fmt, block, stream):

@@ -143,7 +143,7 @@ int gemm_fp8_scaled(const uint8_t* A, int64_t lda, int fmt_a, const uint8_t* B, 
 
 namespace {
 
-// Argument checks of quantize_fp8.
+// Checks shared by quantize_fp8 and quantize_fp8_noalloc.
 int quantize_args(const float* X, int64_t rows, int64_t cols, int64_t ldx, int fmt,
                   int64_t block_rows, int64_t block_cols, const uint8_t* Q, int64_t ldq,
                   const float* scales) {
@@ -177,6 +177,21 @@ int quantize_fp8(const float* X, int64_t rows, int64_t cols, int64_t ldx, int fm
     return finish(dmu::launch_quantize_fp8_tensor_ws(X, rows, cols, ldx, fmt, Q, ldq, scales, s));
   return finish(dmu::launch_quantize_fp8(X, rows, cols, ldx, fmt, block_rows, block_cols, Q, ldq,
                                          scales, nullptr, s));
+}
+
+int quantize_fp8_noalloc(const float* X, int64_t rows, int64_t cols, int64_t ldx, int fmt,
+                         int64_t block_rows, int64_t block_cols, uint8_t* Q, int64_t ldq,
+                         float* scales, void* stream) {
+  int rc = quantize_args(X, rows, cols, ldx, fmt, block_rows, block_cols, Q, ldq, scales);
+  if (rc) return rc;
+  const int64_t slots = dmu::quantize_scratch_slots(rows, cols, ldx, ldq, block_rows, block_cols);
+  if (slots > dmu::kQuantizeScratchSlots) return DMU_ERR_UNSUPPORTED;  // beyond the static scratch
+  (void)hipGetLastError();
+  hipStream_t s = (hipStream_t)stream;
+  uint32_t* part = nullptr;
+  if (slots > 0 && dmu::quantize_scratch_address(s, &part) != hipSuccess) return DMU_ERR_HIP;
+  return finish(dmu::launch_quantize_fp8(X, rows, cols, ldx, fmt, block_rows, block_cols, Q, ldq,
+                                         scales, part, s));
 }
 
 int gemm_mxfp8(const uint8_t* A, int64_t lda, int fmt_a, const uint8_t* B, int64_t ldb,

@@ -93,14 +93,17 @@ int64_t quantize_scratch_slots(int64_t rows, int64_t cols, int64_t ldx, int64_t 
 hipError_t launch_quantize_fp8(const float* X, int64_t rows, int64_t cols, int64_t ldx, int fmt,
                                int64_t br, int64_t bc, uint8_t* Q, int64_t ldq, float* scales,
                                uint32_t* part, hipStream_t s);
-constexpr int64_t kQuantizeScratchSlots = 1024;  // slots of the workspace (4 KiB)
+constexpr int64_t kQuantizeScratchSlots = 1024;  // slots of either scratch (4 KiB)
 constexpr int kMaxDevices = 64;
 // Per-tensor quantize_fp8 on the library's workspace of the stream's GPU
 // (allocated on first use, calls on different streams ordered by an event).
 hipError_t launch_quantize_fp8_tensor_ws(const float* X, int64_t rows, int64_t cols, int64_t ldx,
                                          int fmt, uint8_t* Q, int64_t ldq, float* scales,
                                          hipStream_t s);
-
+// The allocation-free variant's scratch: a static device array of
+// kQuantizeScratchSlots partials per GPU; its address on the stream's GPU
+// (looked up once per device, with that device current).
+hipError_t quantize_scratch_address(hipStream_t s, uint32_t** out);
 
 hipError_t launch_probe_mfma(int kind, int fa, int fb, const void* A, const void* B,
                              const float* C, float* D, int count, hipStream_t s);

@@ -466,4 +466,41 @@ hipError_t launch_quantize_fp8_tensor_ws(const float* X, int64_t rows, int64_t c
   return hipSuccess;
 }
 
+// ---- the allocation-free entry point's scratch ----------------------------
+// For callers that cannot allocate device memory (code under graph capture,
+// serving loops, harnesses that forbid hipMalloc): the per-tensor pass-1
+// slots live in this file-scope array, one copy per GPU, held until the
+// process ends.  Host code never passes the array's name to a kernel (on the
+// host it is a stand-in, not a device address): it asks once per device, with
+// that device current, for the array's address on that device and passes
+// that.  Calls that overlap on one GPU share the array and race.
+static __device__ __align__(256) uint32_t scratch[kQuantizeScratchSlots];
+static_assert(kFlatGrid <= kQuantizeScratchSlots && kRowsGrid <= kQuantizeScratchSlots,
+              "every per-tensor pass-1 grid fits the scratch");
+
+hipError_t quantize_scratch_address(hipStream_t s, uint32_t** out) {
+  static std::mutex mu;
+  static uint32_t* addr[kMaxDevices] = {};
+  hipError_t e;
+  const int device = device_of(s, &e);
+  if (e != hipSuccess) return e;
+  if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[device]) {
+    int cur = -1;
+    if ((e = hipGetDevice(&cur)) != hipSuccess) return e;
+    if (cur != device && (e = hipSetDevice(device)) != hipSuccess) return e;
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != device) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess) return e;
+    addr[device] = (uint32_t*)p;
+  }
+  *out = addr[device];
+  return hipSuccess;
+}
+
 }  // namespace dmu

@@ -10,7 +10,7 @@
  * enqueued (or, for DMU_ERR_HIP, that the launch itself failed).  Faults
  * inside a kernel surface at the caller's next synchronisation.  Calls are
  * thread-safe.  Nothing is allocated except the per-tensor quantize_fp8
- * workspace (4 KiB per GPU, once).
+ * workspace (4 KiB per GPU, once); quantize_fp8_noalloc allocates nothing.
  *
  * Matrices are dense with a leading dimension counted in elements: element
  * (r, c) of a row-major matrix X lives at X[r * ldx + c].  Every pointer must
@@ -182,6 +182,24 @@ int gemm_fp8_scaled(const uint8_t* A, int64_t lda, int fmt_a, const uint8_t* B, 
 int quantize_fp8(const float* X, int64_t rows, int64_t cols, int64_t ldx, int fmt,
                  int64_t block_rows, int64_t block_cols, uint8_t* Q, int64_t ldq, float* scales,
                  void* stream);
+
+/*
+ * quantize_fp8_noalloc: quantize_fp8 for callers that cannot allocate device
+ * memory -- code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  Same arguments, results and errors as quantize_fp8
+ * (bit-identical output), but the per-tensor mode's amax partials go to a
+ * static scratch array inside the library (1024 slots of 4 bytes per GPU,
+ * held until the process ends) instead of an allocated workspace: the call
+ * allocates nothing.  Limit: a call needing more slots than the scratch
+ * holds returns DMU_ERR_UNSUPPORTED; the per-tensor passes use at most 512
+ * slots whatever the tensor's size, so no valid tensor is refused.  Every
+ * call on one GPU shares that GPU's scratch: calls that overlap on one GPU
+ * (concurrent streams) race and must be serialised by the caller.  Block
+ * scales use no scratch.
+ */
+int quantize_fp8_noalloc(const float* X, int64_t rows, int64_t cols, int64_t ldx, int fmt,
+                         int64_t block_rows, int64_t block_cols, uint8_t* Q, int64_t ldq,
+                         float* scales, void* stream);
 
 /*
  * Microscaling (MX) FP8: block-scaled operands with one power-of-two scale per

@@ -256,7 +256,7 @@ def call_quantize(fn, **kw):
     return getattr(dmu.load_library(), fn)(*a.values())
 
 
-@pytest.mark.parametrize("fn", ["quantize_fp8"])
+@pytest.mark.parametrize("fn", ["quantize_fp8", "quantize_fp8_noalloc"])
 @pytest.mark.parametrize("kw", [
     dict(X=None), dict(Q=None), dict(s=None), dict(rows=0), dict(fmt=2), dict(ldx=126),
     dict(ldq=120), dict(br=3), dict(X=FAKE + 4), dict(Q=FAKE + 8), dict(s=FAKE + 2),
