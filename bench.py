@@ -268,7 +268,7 @@ class Bench:
         return Xa, Xb, Qa, Qb, sa, sb
 
     def gemm_fp8_leg(self, M, N, K, fmt, steps, warmup, copies=1, block=False, promoted=False,
-                     protocol=False):
+                     protocol=False, protocol_seconds=1.0):
         """promoted: per-tensor operands run through the block-scaled path with
         every scale equal, i.e. partial sums promoted into FP32 every 128 K.
         protocol: also time the kernel with protocol_rounds."""
@@ -291,7 +291,8 @@ class Bench:
         bytes_ = 1.0 * (M * K + N * K) + 2.0 * M * N + 4.0 * (sa.numel() + sb.numel())
         r = self.report(t, flop, bytes_, PEAK_FP8_TFLOPS, copies)
         if protocol:
-            r["protocol"] = protocol_rounds(torch, launch, flop, PEAK_FP8_TFLOPS)
+            r["protocol"] = protocol_rounds(torch, launch, flop, PEAK_FP8_TFLOPS,
+                                            seconds=protocol_seconds)
         return r
 
     def fused_leg(self, kind, steps, warmup, copies):
@@ -567,6 +568,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--legs", default="all", help="all | headline | comma list of leg names")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--protocol-seconds", type=float, default=1.0,
+                    help="length of each of the three timing-protocol rounds (0: no protocol; "
+                         "the per-kernel rate then comes from the timed launches' HIP events)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="only run a device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -613,11 +617,17 @@ def main():
         % (value, S, t["event_mean_ms"]))
     # the per-kernel rate of the roofline: the page's protocol, after the
     # timed region (which stays exactly S launches)
-    proto = protocol_rounds(torch, launch, flop, PEAK_BF16_TFLOPS)
-    achieved = proto["TFLOP_per_s"]
-    log("headline per kernel: %.1f TFLOP/s (%.1f%% of peak), rounds %s, spread %.2f%%, sclk %s MHz"
-        % (achieved, proto["pct_peak"], [r["median_ms"] for r in proto["rounds"]],
-           100 * proto["spread"], proto["sclk_mhz_median"]))
+    proto = None
+    if args.protocol_seconds > 0:
+        proto = protocol_rounds(torch, launch, flop, PEAK_BF16_TFLOPS,
+                                seconds=args.protocol_seconds)
+        achieved, kernel_ms = proto["TFLOP_per_s"], proto["ms"]
+        log("headline per kernel: %.1f TFLOP/s (%.1f%% of peak), rounds %s, spread %.2f%%, "
+            "sclk %s MHz" % (achieved, proto["pct_peak"], [r["median_ms"] for r in proto["rounds"]],
+                             100 * proto["spread"], proto["sclk_mhz_median"]))
+    else:
+        kernel_ms = t["event_mean_ms"]
+        achieved = flop / kernel_ms / 1e9
     del As, Bs, out
 
     legs = {}
@@ -627,7 +637,9 @@ def main():
     for name, fmt in (("fp8_e4m3_4096", dmu.E4M3), ("fp8_e5m2_4096", dmu.E5M2)):
         if want(name):
             legs[name] = b.gemm_fp8_leg(4096, 4096, 4096, fmt, S, W, copies=10,
-                                        protocol=name == "fp8_e4m3_4096")
+                                        protocol=(name == "fp8_e4m3_4096" and
+                                                  args.protocol_seconds > 0),
+                                        protocol_seconds=args.protocol_seconds)
             log("%s: %s" % (name, legs[name]))
     if want("fp8_e4m3_4096_promoted"):
         legs["fp8_e4m3_4096_promoted"] = b.gemm_fp8_leg(4096, 4096, 4096, dmu.E4M3, S, W, copies=10,
@@ -688,6 +700,21 @@ def main():
                 M, 28672, 8192, dmu.B_COL_MAJOR, S if M < 1024 else S4, W4, B=Bllm)
             log("llm M=%d: %s" % (M, legs["bf16_llm_M%d_N28672_K8192" % M]))
         del Bllm
+    if want("bf16_4096_lds_layouts"):
+        # the bank-conflict ablation of the vidyal.ai page, Step 3: the headline
+        # kernel with its XOR-swizzled LDS rows, plain rows and padded rows
+        A = b.normal_bf16((4096, 4096), 1)
+        B = b.normal_bf16((4096, 4096), 2)
+        As, Bs = b.copies(A, 6), b.copies(B, 6)
+        o = torch.empty((4096, 4096), dtype=torch.bfloat16, device="cuda")
+        for lay, nm in ((dmu.LDS_SWIZZLED, "swizzled"), (dmu.LDS_PLAIN, "plain"),
+                        (dmu.LDS_PADDED, "padded")):
+            t_l = time_launches(torch, lambda i: dmu.probe_gemm_bf16_layout(lay, As[i % 6], Bs[i % 6],
+                                                                              o), S, W)
+            legs["bf16_4096_lds_" + nm] = b.report(t_l, 2.0 * 4096 ** 3, 2.0 * 3 * 4096 ** 2,
+                                                   PEAK_BF16_TFLOPS, 6)
+            log("bf16 4096 LDS layout %s: %s" % (nm, legs["bf16_4096_lds_" + nm]))
+        del As, Bs, o
     if want("bf16_256"):
         legs["bf16_256_f32out"] = b.gemm_bf16_leg(256, 256, 256, dmu.B_ROW_MAJOR, S, W,
                                                   out_f32=True, seed_dist="uniform")
@@ -725,7 +752,7 @@ def main():
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic_for("gemm_bf16_4096_tn"),
                      "kernel": "gemm_kernel<kBF16, B col-major, 256x256>",
-                     "kernel_ms": proto["ms"]},
+                     "kernel_ms": round(kernel_ms, 5)},
         "protocol": proto,
         "cpu_baseline": cpu,
         "legs": legs,

@@ -74,6 +74,7 @@ SYMBOLS = {
     "dmu_probe_mfma": (_I, [_I, _I, _I, _P, _P, _P, _P, _P]),
     "dmu_probe_mfma_batch": (_I, [_I, _I, _I, _P, _P, _P, _P, _I, _P]),
     "dmu_probe_lds_load": (_I, [_P, _P, _I, _I, _P]),
+    "dmu_probe_gemm_bf16_layout": (_I, [_I, _P, _I64, _P, _I64, _P, _I64, _I64, _I64, _I64, _P]),
     "dmu_probe_mfma_rate": (_I, [_I, _P, _I, _I, _P, _P]),
     "dmu_probe_cvt_fp8": (_I, [_P, _I64, _I, _I, _P, _P]),
     "dmu_probe_lds_tr16": (_I, [_P, _P, _P, _P]),
@@ -554,6 +555,26 @@ def probe_lds_tr16(src, offsets, out, stream=None):
     rc = load_library().dmu_probe_lds_tr16(_dev_ptr(src, "src"), ctypes.cast(offs, _P),
                                            _dev_ptr(out, "out"), _stream(stream))
     _check("dmu_probe_lds_tr16", rc)
+    return out
+
+
+LDS_SWIZZLED, LDS_PLAIN, LDS_PADDED = 0, 1, 2  # layouts of dmu_probe_gemm_bf16_layout
+
+
+def probe_gemm_bf16_layout(layout: int, A, B, out, stream=None):
+    """gemm_bf16 (B stored N x K, BF16 out) with LDS layout `layout` (see
+    include/dmu_probe.h): A [M][K], B [N][K] BF16, out [M][N] BF16."""
+    torch = _torch()
+    for t, name in ((A, "A"), (B, "B"), (out, "out")):
+        _check_dtype(t, (torch.bfloat16, torch.int16), name)
+    M, K = A.shape
+    N = B.shape[0]
+    if B.shape[1] != K or tuple(out.shape) != (M, N):
+        raise ValueError("shapes")
+    rc = load_library().dmu_probe_gemm_bf16_layout(
+        layout, _dev_ptr(A, "A"), _ld(A, "A"), _dev_ptr(B, "B"), _ld(B, "B"), _dev_ptr(out, "out"),
+        _ld(out, "out"), M, N, K, _stream(stream))
+    _check("dmu_probe_gemm_bf16_layout", rc)
     return out
 
 

@@ -379,6 +379,22 @@ int dmu_probe_mfma(int kind, int fmt_a, int fmt_b, const void* A, const void* B,
   return dmu_probe_mfma_batch(kind, fmt_a, fmt_b, A, B, C, D, 1, stream);
 }
 
+int dmu_probe_gemm_bf16_layout(int layout, const uint16_t* A, int64_t lda, const uint16_t* B,
+                               int64_t ldb, void* D, int64_t ldd, int64_t M, int64_t N, int64_t K,
+                               void* stream) {
+  if (layout < 0 || layout > 2) return DMU_ERR_INVALID_ARG;
+  int rc = check_out(nullptr, 0, D, ldd, DMU_OUT_BF16, M, N);
+  if (rc) return rc;
+  if (!A || !B || K < 64 || K % 64 || K > INT32_MAX) return DMU_ERR_INVALID_ARG;
+  if (lda < K || ldb < K || (lda * 2) % 16 || (ldb * 2) % 16) return DMU_ERR_INVALID_ARG;
+  if (!aligned(A, 16) || !aligned(B, 16)) return DMU_ERR_INVALID_ARG;
+  if (kTileRows * lda * 2 >= kMaxTileBytes || kTileRows * ldb * 2 >= kMaxTileBytes)
+    return DMU_ERR_UNSUPPORTED;
+  dmu::GemmArgs a{A, B, nullptr, D, lda, ldb, 0, ldd, M, N, K, nullptr, nullptr, 1};
+  (void)hipGetLastError();
+  return finish(dmu::launch_gemm_bf16_layout(a, layout, (hipStream_t)stream));
+}
+
 int dmu_probe_lds_load(const void* src, void* dst, int mode, int oob_from, void* stream) {
   if (!src || !dst || (mode != 0 && mode != 1) || oob_from < 0 || oob_from > 64)
     return DMU_ERR_INVALID_ARG;

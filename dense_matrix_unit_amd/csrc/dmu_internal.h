@@ -61,6 +61,9 @@ enum GemmKind { kBF16 = 0, kFP8Tensor = 1, kFP8Block = 2, kMX = 3, kMX4 = 4, kMX
 // Launchers: argument checking is done by the caller; these only pick a
 // kernel configuration and launch it.  They return a hipError_t.
 hipError_t launch_gemm_bf16(const GemmArgs& a, int b_col_major, hipStream_t s);
+// The BF16 kernel (B stored N x K, K a multiple of 64) with LDS layout 0
+// (XOR-swizzled, the one every entry point uses), 1 (plain) or 2 (padded).
+hipError_t launch_gemm_bf16_layout(const GemmArgs& a, int layout, hipStream_t s);
 hipError_t launch_gemm_grouped_bf16(const GemmArgs& a, hipStream_t s);
 hipError_t launch_attention_bf16(const AttnArgs& a, int d, int causal, hipStream_t s);
 // fused epilogue (a.bias / a.act / a.out_fp8 set)

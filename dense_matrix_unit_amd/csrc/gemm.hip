@@ -68,8 +68,13 @@ __device__ __forceinline__ f32x16_t mfma_fp8_32x32x64(const i32x8_t& a, const i3
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FA, FB, 0, 0, 0, 0);
 }
 
+// LDS layouts of a K slice: the XOR-swizzled rows every entry point uses, and
+// two variants kept only for the layout ablation of the BF16 kernel
+// (dmu_probe_gemm_bf16_layout): plain rows, and rows padded by 16 bytes.
+enum LdsLayout { kSwizzled = 0, kPlain = 1, kPadded = 2 };
+
 template <int KIND, int FA, int FB, bool BROW, int BM, int BN, int RB, int S, int kGroupM, int PD,
-          int NW, bool KT>
+          int NW, bool KT, int LAY = kSwizzled>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4))) void
 gemm_kernel(GemmArgs p) {
   constexpr int NT = NW * 64;   // threads; NW waves in a 2 x (NW/2) grid
@@ -79,10 +84,16 @@ gemm_kernel(GemmArgs p) {
   constexpr bool BF = KIND == kBF16 || GRP || KIND == kBF16F;  // BF16 operands
   constexpr bool F8T = KIND == kFP8Tensor || KIND == kFP8TensorF;  // per-tensor FP8
   constexpr int ESZ = BF ? 2 : 1;
-  constexpr int CPR = RB / 16;  // 16-byte chunks per LDS row
+  constexpr int CPR = RB / 16;  // 16-byte chunks of K per LDS row
+  // LDS row stride and 16-byte positions per row: a padded row carries one
+  // unused position after its chunks
+  constexpr int RS = LAY == kPadded ? RB + 16 : RB;
+  constexpr int CPRS = RS / 16;
+  static_assert(LAY == kSwizzled || (KIND == kBF16 && !BROW && !KT),
+                "the plain and padded layouts exist for the BF16 kernel's ablation only");
   constexpr int WM = BM / 2, WN = BN / (NW / 2);
   constexpr int TM = WM / 32, TN = WN / 32;      // 32x32 sub-tiles per wave
-  constexpr int A_BYTES = BM * RB, B_BYTES = BN * RB;
+  constexpr int A_BYTES = BM * RS, B_BYTES = BN * RS;
   constexpr int STAGE = A_BYTES + B_BYTES;
   // MX: scale words are fetched XG slices at a time (4 * XG bytes per tile
   // row) into a two-buffer ring of their own after the stages
@@ -94,11 +105,11 @@ gemm_kernel(GemmArgs p) {
   constexpr int XOFF = S * STAGE;               // ring offset in LDS
   constexpr int XR = MX ? 2 * XBUF : 0;
   constexpr int NSTEP = BF || F4 ? RB / 32 : RB / 64;  // MFMA K-steps per slice
-  constexpr int NLA = BM * CPR / NT;                 // A copies per thread per slice
-  constexpr int NLB = BROW ? 8 : BN * CPR / NT;      // B copies per thread per slice
+  constexpr int NLA = BM * CPRS / NT;                // A copies per thread per slice
+  constexpr int NLB = BROW ? 8 : BN * CPRS / NT;     // B copies per thread per slice
   constexpr int NLS = MX ? 2 : 0;                    // MX scale-group copies (A, B)
   constexpr int NL = NLA + NLB + NLS;
-  static_assert(BM % 64 == 0 && BN % 64 == 0 && (BM * CPR) % NT == 0, "tile");
+  static_assert(BM % 64 == 0 && BN % 64 == 0 && (BM * CPRS) % NT == 0, "tile");
   static_assert(!BROW || ((KIND == kBF16 || KIND == kBF16F) && BN == 256 && RB == 128 && S == 2 &&
                           NW == 4),
                 "row-major B staging");
@@ -157,13 +168,19 @@ gemm_kernel(GemmArgs p) {
   const uint32_t ldaB = (uint32_t)(p.lda * ESZ);
   const __amdgpu_buffer_rsrc_t rA =
       make_rsrc((const uint8_t*)p.A + m0 * p.lda * ESZ, (int64_t)(rowsA - 1) * ldaB + kbytes);
+  // copy `it` of a thread fills LDS position q = it * NT + tid (16 bytes):
+  // row q / CPRS, position q % CPRS, from the global chunk that belongs there
+  // (the XOR applied on the source side; a padding position fetches zeros)
+  auto src_chunk = [&](int row, int pos) __attribute__((always_inline)) -> int {
+    return LAY == kSwizzled ? pos ^ swz<RB>(row) : pos;
+  };
   uint32_t voffA[NLA], cA[NLA];
 #pragma unroll
   for (int it = 0; it < NLA; ++it) {
-    const int q = it * NT + tid, row = q / CPR;
-    const uint32_t c = (uint32_t)(((q % CPR) ^ swz<RB>(row)) << 4);
+    const int q = it * NT + tid, row = q / CPRS, pos = q % CPRS;
+    const uint32_t c = (uint32_t)(src_chunk(row, pos) << 4);
     cA[it] = c;
-    voffA[it] = row < rowsA ? (uint32_t)row * ldaB + c : kOOB;
+    voffA[it] = row < rowsA && pos < CPR ? (uint32_t)row * ldaB + c : kOOB;
   }
 
   // ---- B descriptors
@@ -184,10 +201,10 @@ gemm_kernel(GemmArgs p) {
     rB = make_rsrc((const uint8_t*)p.B + n0 * p.ldb * ESZ, (int64_t)(rowsB - 1) * ldbB + kbytes);
 #pragma unroll
     for (int it = 0; it < NLB; ++it) {
-      const int q = it * NT + tid, row = q / CPR;
-      const uint32_t c = (uint32_t)(((q % CPR) ^ swz<RB>(row)) << 4);
+      const int q = it * NT + tid, row = q / CPRS, pos = q % CPRS;
+      const uint32_t c = (uint32_t)(src_chunk(row, pos) << 4);
       cB[it] = c;
-      voffB[it] = row < rowsB ? (uint32_t)row * ldbB + c : kOOB;
+      voffB[it] = row < rowsB && pos < CPR ? (uint32_t)row * ldbB + c : kOOB;
     }
   }
 
@@ -361,7 +378,7 @@ gemm_kernel(GemmArgs p) {
 
   // 16-byte LDS read of logical chunk c of tile row `row`.
   auto lds16 = [&](const uint8_t* base, int row, int c) __attribute__((always_inline)) -> i32x4_t {
-    return *(const i32x4_t*)(base + row * RB + ((c ^ swz<RB>(row)) << 4));
+    return *(const i32x4_t*)(base + row * RS + ((LAY == kSwizzled ? c ^ swz<RB>(row) : c) << 4));
   };
 
   // ---- prologue: slices 0 .. S-2 in flight, wait for slice 0
@@ -852,6 +869,24 @@ hipError_t launch_gemm_fp8_fused(const GemmArgs& a, int fmt_a, int fmt_b, hipStr
 
 hipError_t launch_gemm_grouped_bf16(const GemmArgs& a, hipStream_t s) {
   return launch<kBF16G, 0, 0, false, 256, 256, 128, 2, 4, kPrefetch, kWavesBF16>(a, s);
+}
+
+hipError_t launch_gemm_bf16_layout(const GemmArgs& a, int layout, hipStream_t s) {
+  // the headline kernel (B stored N x K, whole K slices) with each LDS layout
+  const dim3 grid((unsigned)(((a.M + 255) / 256) * ((a.N + 255) / 256)));
+  if (layout == kPlain)
+    hipLaunchKernelGGL((gemm_kernel<kBF16, 0, 0, false, 256, 256, 128, 2, 4, kPrefetch, kWavesBF16,
+                                    false, kPlain>),
+                       grid, dim3(kWavesBF16 * 64), 0, s, a);
+  else if (layout == kPadded)
+    hipLaunchKernelGGL((gemm_kernel<kBF16, 0, 0, false, 256, 256, 128, 2, 4, kPrefetch, kWavesBF16,
+                                    false, kPadded>),
+                       grid, dim3(kWavesBF16 * 64), 0, s, a);
+  else
+    hipLaunchKernelGGL((gemm_kernel<kBF16, 0, 0, false, 256, 256, 128, 2, 4, kPrefetch, kWavesBF16,
+                                    false, kSwizzled>),
+                       grid, dim3(kWavesBF16 * 64), 0, s, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm_bf16(const GemmArgs& a, int b_col_major, hipStream_t s) {

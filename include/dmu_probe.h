@@ -58,6 +58,20 @@ int dmu_probe_mfma_batch(int kind, int fmt_a, int fmt_b, const void* A, const vo
                          const float* C, float* D, int count, void* stream);
 
 /*
+ * The BF16 GEMM of gemm_bf16 (B stored N x K, BF16 output, no C) with a chosen
+ * LDS layout for its K slices, for the bank-conflict ablation of the vidyal.ai
+ * page, Step 3 ("bank conflicts and the XOR swizzle"): layout 0 is the
+ * XOR-swizzled layout every entry point uses (chunk c of 128-byte row r at
+ * position c ^ ((r ^ r >> 3) & 7)), 1 plain 128-byte rows, 2 rows padded to
+ * 144 bytes (the copies fill the padding position with zeros).  All three
+ * compute the same product.  K % 64 == 0; other arguments as gemm_bf16.
+ * Returns DMU_OK, DMU_ERR_INVALID_ARG, DMU_ERR_UNSUPPORTED or DMU_ERR_HIP.
+ */
+int dmu_probe_gemm_bf16_layout(int layout, const uint16_t* A, int64_t lda, const uint16_t* B,
+                               int64_t ldb, void* D, int64_t ldd, int64_t M, int64_t N, int64_t K,
+                               void* stream);
+
+/*
  * Copy 64 x 16 bytes (mode 0) or 64 x 4 bytes (mode 1) from src into LDS with
  * one buffer load per lane that writes LDS directly (lane l's bytes are
  * expected at LDS offset l*size), lanes >= oob_from using an out-of-range
