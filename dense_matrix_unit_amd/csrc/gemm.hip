@@ -51,11 +51,6 @@
 namespace dmu {
 namespace {
 
-template <int V>
-struct IntConst {
-  static constexpr int value = V;
-};
-
 // K slices between the L2 prefetch of a slice and its use (0 = no prefetch).
 constexpr int kPrefetch = 3;
 constexpr int kWavesBF16 = 4, kWavesFP8 = 4;  // waves per workgroup (4: one per SIMD)

@@ -8,6 +8,13 @@ namespace dmu {
 
 constexpr int kThreads = 256;  // 4 waves, one per SIMD
 
+// A compile-time int passed as a value (loop bodies instantiated per stage,
+// per output type).
+template <int V>
+struct IntConst {
+  static constexpr int value = V;
+};
+
 // LDS position of logical 16-byte chunk c in row r for RB-byte rows.
 template <int RB>
 __device__ __forceinline__ int swz(int r) {
