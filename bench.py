@@ -223,7 +223,7 @@ class Bench:
 
     # ---- legs
     def gemm_bf16_leg(self, M, N, K, layout, steps, warmup, copies=1, out_f32=False,
-                      seed_dist="normal", B=None):
+                      seed_dist="normal", B=None, protocol=False, protocol_seconds=1.0):
         torch, dmu = self.torch, self.dmu
         bshape = (N, K) if layout == dmu.B_COL_MAJOR else (K, N)
         if seed_dist == "uniform":
@@ -243,7 +243,11 @@ class Bench:
         t = time_launches(torch, launch, steps, warmup)
         flop = 2.0 * M * N * K
         bytes_ = 2.0 * (M * K + N * K) + (4.0 if out_f32 else 2.0) * M * N
-        return self.report(t, flop, bytes_, PEAK_BF16_TFLOPS, copies)
+        r = self.report(t, flop, bytes_, PEAK_BF16_TFLOPS, copies)
+        if protocol:
+            r["protocol"] = protocol_rounds(torch, launch, flop, PEAK_BF16_TFLOPS,
+                                            seconds=protocol_seconds)
+        return r
 
     def fp8_operands(self, M, N, K, fmt, block=None):
         torch, dmu = self.torch, self.dmu
@@ -683,8 +687,9 @@ def main():
         log("quantize 4096^2, allocation-free entry: %s"
             % legs["quantize_e4m3_4096_tensor_noalloc"])
     if want("fp8_block_8192x7168x7168"):
-        legs["fp8_block_8192x7168x7168"] = b.gemm_fp8_leg(8192, 7168, 7168, dmu.E4M3, S4, W4,
-                                                           block=True)
+        legs["fp8_block_8192x7168x7168"] = b.gemm_fp8_leg(
+            8192, 7168, 7168, dmu.E4M3, S4, W4, block=True, protocol=args.protocol_seconds > 0,
+            protocol_seconds=args.protocol_seconds)
         log("block-scaled: %s" % legs["fp8_block_8192x7168x7168"])
     if want("quantize_block"):
         legs["quantize_e4m3_8192x7168_1x128"] = b.quantize_leg(8192, 7168, dmu.E4M3, (1, 128),
@@ -697,7 +702,9 @@ def main():
         Bllm = b.normal_bf16((28672, 8192), 2)
         for M in (16, 128, 1024, 8192):
             legs["bf16_llm_M%d_N28672_K8192" % M] = b.gemm_bf16_leg(
-                M, 28672, 8192, dmu.B_COL_MAJOR, S if M < 1024 else S4, W4, B=Bllm)
+                M, 28672, 8192, dmu.B_COL_MAJOR, S if M < 1024 else S4, W4, B=Bllm,
+                protocol=M == 8192 and args.protocol_seconds > 0,
+                protocol_seconds=args.protocol_seconds)
             log("llm M=%d: %s" % (M, legs["bf16_llm_M%d_N28672_K8192" % M]))
         del Bllm
     if want("bf16_4096_lds_layouts"):
