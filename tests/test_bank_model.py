@@ -1,7 +1,8 @@
 """A bank-conflict model of shared memory (LDS), checked first against the
 worked example of the vidyal.ai page, Step 3 ("bank conflicts and the XOR
 swizzle"; tests/golden/bank_groups_step3.json), then applied to the 16-byte
-fragment reads of this library's GEMM kernel (csrc/gemm.hip) on gfx950.
+fragment reads of this library's GEMM kernel (csrc/gemm.hip) and the 8-byte
+transposing V reads of its attention kernel (csrc/attention.hip) on gfx950.
 
 Model: memory is `banks` banks of 4 bytes, word w in bank w mod banks.  An
 access by a group of lanes served together takes as many wavefronts as the
@@ -120,3 +121,51 @@ def test_dma_writes_are_contiguous():
     # swizzle is applied to the global source offsets, not the LDS side)
     for banks, lanes in LDS_MODELS:
         assert wavefronts([16 * l for l in range(64)], 16, banks, lanes) == 64 * 16 // (banks * 4)
+
+
+# ---- gfx950: the attention kernel's transposing reads of V (csrc/attention.hip)
+def vswz(d, j):
+    """Swizzle of V row j's 16-byte chunks: bits 2-3 of the chunk index flipped
+    with the row (d = 128: j % 4; d = 64: bit 1 of j)."""
+    return (j & 3) << 2 if d == 128 else ((j >> 1) & 1) << 2
+
+
+def v_read(d, nt, ks, second, swizzled=True):
+    """Byte addresses of one ds_read_b64_tr_b16 of V (8 bytes per lane): lane
+    l = 32 h + 16 g + i reads row 4h + i/4 (+ 16 ks, + 8 for the step's second
+    read) at 16-bit elements 4 (i % 4) .. +3 of columns 32 nt + 16 (g % 2)."""
+    vrow = 2 * d
+    out = []
+    for lane in range(64):
+        h, g, i = lane >> 5, lane >> 4, lane & 15
+        chunk = 4 * nt + 2 * (g & 1) + ((i & 3) >> 1)
+        if swizzled:
+            chunk ^= vswz(d, i >> 2)
+        out.append(16 * ks * vrow + (8 * vrow if second else 0) + (4 * h + (i >> 2)) * vrow +
+                   (chunk << 4) + ((i & 1) << 3))
+    return out
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_attention_v_reads_conflict_free_with_64_banks(d):
+    # 64 banks serve 32 lanes of 8 bytes at a time: 2 wavefronts at best
+    for nt in range(d // 32):
+        for ks in range(4):
+            for second in (False, True):
+                assert wavefronts(v_read(d, nt, ks, second), 8, 64, 32) == 2
+                # without the swizzle the 4 rows' 64-byte runs share banks
+                assert wavefronts(v_read(d, nt, ks, second, swizzled=False), 8, 64, 32) > 2
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_attention_v_reads_with_32_banks(d):
+    # 32 banks serve 16 lanes of 8 bytes (4 rows x 32 bytes): rows j and j+2
+    # of the swizzle land 128 bytes apart, so the reads are 2-way conflicted
+    # (8 wavefronts, against 4 at best and 16 without the swizzle).  gfx950's
+    # LDS is the 64-bank case: 16-byte reads sustain more than 128 bytes per
+    # clock per CU, which 32 banks of 4 bytes cannot deliver.
+    for nt in range(d // 32):
+        for ks in range(4):
+            for second in (False, True):
+                assert wavefronts(v_read(d, nt, ks, second), 8, 32, 16) == 8
+                assert wavefronts(v_read(d, nt, ks, second, swizzled=False), 8, 32, 16) == 16
