@@ -438,19 +438,22 @@ class Bench:
         fp4 = fmt == dmu.E2M1
         Q = torch.empty((rows, cols // 2 if fp4 else cols), dtype=torch.uint8, device=self.dev)
         S = torch.empty((rows, cols // 32), dtype=torch.uint8, device=self.dev)
+        copies = max(1, -(-320 * 2 ** 20 // (4 * rows * cols)))  # beyond the Infinity Cache
+        Xs = self.copies(X, copies)
 
         def launch(i):
             if fp4:
-                dmu.quantize_mxfp4(X, Q, S)
+                dmu.quantize_mxfp4(Xs[i % copies], Q, S)
             else:
-                dmu.quantize_mxfp8(X, Q, S, fmt)
+                dmu.quantize_mxfp8(Xs[i % copies], Q, S, fmt)
 
         t = time_launches(torch, launch, steps, warmup)
         bytes_ = ((4.5 if fp4 else 5.0) + 1.0 / 32) * rows * cols
         ms = t["event_mean_ms"]
         return {"ms": round(ms, 5), "GB_per_s": round(bytes_ / ms / 1e6, 1),
                 "pct_hbm_peak": round(100 * bytes_ / ms / 1e6 / PEAK_HBM_GBS, 1),
-                "algorithmic_MB": round(bytes_ / 1e6, 2), "wall_ms": round(t["wall_ms"], 5)}
+                "algorithmic_MB": round(bytes_ / 1e6, 2), "wall_ms": round(t["wall_ms"], 5),
+                "input_copies": copies}
 
     def quantize_leg(self, rows, cols, fmt, block, steps, warmup, outliers=False, noalloc=False):
         torch, dmu = self.torch, self.dmu
@@ -463,16 +466,21 @@ class Bench:
         Q = torch.empty((rows, cols), dtype=torch.uint8, device=self.dev)
         br, bc = (rows, cols) if block is None else block
         s = torch.empty(((rows // br) * (cols // bc),), dtype=torch.float32, device=self.dev)
+        # rotate over input copies larger than the 256 MB Infinity Cache, so a
+        # call does not find the previous calls' input there
+        copies = max(1, -(-320 * 2 ** 20 // (4 * rows * cols)))
+        Xs = self.copies(X, copies)
 
         def launch(i):
-            quantize(X, Q, s, fmt, block)
+            quantize(Xs[i % copies], Q, s, fmt, block)
 
         t = time_launches(torch, launch, steps, warmup)
         bytes_ = 5.0 * rows * cols + 4.0 * s.numel()
         ms = t["event_mean_ms"]
         return {"ms": round(ms, 5), "GB_per_s": round(bytes_ / ms / 1e6, 1),
                 "pct_hbm_peak": round(100 * bytes_ / ms / 1e6 / PEAK_HBM_GBS, 1),
-                "algorithmic_MB": round(bytes_ / 1e6, 2), "wall_ms": round(t["wall_ms"], 5)}
+                "algorithmic_MB": round(bytes_ / 1e6, 2), "wall_ms": round(t["wall_ms"], 5),
+                "input_copies": copies}
 
     def mfma_ceiling_leg(self, steps, warmup):
         """Sustained MFMA rate with no memory traffic (dmu_probe_mfma_rate): the

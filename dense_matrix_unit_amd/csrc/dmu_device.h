@@ -96,4 +96,24 @@ __device__ __forceinline__ uint32_t encode_fp8(float y) {
   return sign | n;
 }
 
+// Four FP32 values -> four FP8 codes (byte r = value r), saturating RNE: the
+// hardware conversion (v_cvt_pk_fp8_f32 / v_cvt_pk_bf8_f32) rounds to nearest
+// even but turns values past the largest finite one into NaN / Inf, so they
+// are clamped first (NaN passed through).
+template <int FMT>
+__device__ __forceinline__ uint32_t cvt4_fp8(f32x4_t y) {
+  constexpr float kMax = FMT == 0 ? 448.0f : 57344.0f;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) y[r] = y[r] != y[r] ? y[r] : fminf(fmaxf(y[r], -kMax), kMax);
+  int w;
+  if constexpr (FMT == 0) {
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], w, true);
+  } else {
+    w = __builtin_amdgcn_cvt_pk_bf8_f32(y[0], y[1], 0, false);
+    w = __builtin_amdgcn_cvt_pk_bf8_f32(y[2], y[3], w, true);
+  }
+  return (uint32_t)w;
+}
+
 }  // namespace dmu

@@ -168,22 +168,23 @@ __global__ void probe_mx_kernel(const uint8_t* A, const uint8_t* B, const uint8_
 
 // FP32 -> FP8 with the hardware conversion, two values per instruction:
 // v_cvt_pk_fp8_f32 (E4M3) / v_cvt_pk_bf8_f32 (E5M2), applied to x as it is
-// (CLAMP == 0) or to x clamped to the format's largest finite magnitude with
-// NaN passed through (CLAMP == 1; the instruction takes no clamp modifier on
-// gfx950).  Thread t converts x[2t], x[2t+1] into q[2t], q[2t+1].
+// (CLAMP == 0), or through cvt4_fp8 (CLAMP == 1: x clamped to the format's
+// largest finite magnitude, NaN passed through, then converted; the function
+// the fused epilogue and the quantizers use).  Thread t converts x[2t],
+// x[2t+1] into q[2t], q[2t+1].
 template <int FMT, int CLAMP>
 __global__ void probe_cvt_kernel(const float* x, int64_t npairs, uint8_t* q) {
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (t >= npairs) return;
-  float a = x[2 * t], b = x[2 * t + 1];
+  const float a = x[2 * t], b = x[2 * t + 1];
+  uint32_t r;
   if constexpr (CLAMP) {
-    constexpr float kMax = FMT == 0 ? 448.0f : 57344.0f;
-    a = a != a ? a : fminf(fmaxf(a, -kMax), kMax);
-    b = b != b ? b : fminf(fmaxf(b, -kMax), kMax);
+    r = cvt4_fp8<FMT>(f32x4_t{a, b, 0.0f, 0.0f});
+  } else if constexpr (FMT == 0) {
+    r = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  } else {
+    r = (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(a, b, 0, false);
   }
-  int r;
-  if constexpr (FMT == 0) r = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
-  else r = __builtin_amdgcn_cvt_pk_bf8_f32(a, b, 0, false);
   q[2 * t] = (uint8_t)(r & 0xFF);
   q[2 * t + 1] = (uint8_t)((r >> 8) & 0xFF);
 }

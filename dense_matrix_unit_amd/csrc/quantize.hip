@@ -84,6 +84,16 @@ __device__ __forceinline__ uint32_t encode4(f32x4_t x, float m) {
          (encode_fp8<FMT>(x[2] * m) << 16) | (encode_fp8<FMT>(x[3] * m) << 24);
 }
 
+// When amax and m are both finite, every product x*m of the block is finite
+// and at most about FMAX, and the hardware conversion after a clamp to +-FMAX
+// (cvt4_fp8) is exactly the saturating RNE encoder (pinned against the
+// oracle's encoder by a GPU test) at a few instructions per value.  A block
+// with NaN or Inf, or a subnormal amax (m = FMAX / amax overflows, 0 * m is
+// NaN), keeps the integer encoder.
+__device__ __forceinline__ bool hw_encode_ok(float amax, float m) {
+  return amax < __builtin_huge_valf() && m < __builtin_huge_valf();
+}
+
 // ---- per tensor -----------------------------------------------------------
 
 __device__ __forceinline__ uint32_t amax4(const f32x4_t& v) {
@@ -104,7 +114,9 @@ __device__ __forceinline__ uint32_t block_max(uint32_t m) {
 }
 
 // Contiguous tensor (ldx == ldq == cols): a flat grid-stride walk, 8 float4
-// loads in flight per thread, nontemporal (X is read once per pass).
+// loads in flight per thread.  Pass 1 reads with ordinary loads, so a tensor
+// that fits the 256 MB Infinity Cache is still there for pass 2; pass 2 reads
+// nontemporally (its reads are the last).
 constexpr int kFlatThreads = 1024;
 constexpr int kFlatGrid = 256;     // one workgroup per CU
 constexpr int kRowsGrid = 512;     // strided rows: at most this many workgroups
@@ -118,11 +130,11 @@ __global__ __launch_bounds__(kFlatThreads) void amax_flat(const f32x4_t* X, int6
   for (; i + (kUnroll - 1) * stride < n4; i += kUnroll * stride) {
     f32x4_t v[kUnroll];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) v[u] = __builtin_nontemporal_load(X + i + u * stride);
+    for (int u = 0; u < kUnroll; ++u) v[u] = X[i + u * stride];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) m = max(m, amax4(v[u]));
   }
-  for (; i < n4; i += stride) m = max(m, amax4(__builtin_nontemporal_load(X + i)));
+  for (; i < n4; i += stride) m = max(m, amax4(X[i]));
   m = block_max<kFlatThreads>(m);
   if (threadIdx.x == 0) part[blockIdx.x] = m;
 }
@@ -144,6 +156,17 @@ __global__ __launch_bounds__(kFlatThreads) void encode_flat(const f32x4_t* X, in
   if (blockIdx.x == 0 && threadIdx.x == 0) scales[0] = scale_from_amax<FMT>(amax);
   const int64_t stride = (int64_t)gridDim.x * kFlatThreads;
   int64_t i = (int64_t)blockIdx.x * kFlatThreads + threadIdx.x;
+  if (hw_encode_ok(amax, m)) {
+    for (; i + (kUnroll - 1) * stride < n4; i += kUnroll * stride) {
+      f32x4_t v[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) v[u] = __builtin_nontemporal_load(X + i + u * stride);
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) Q4[i + u * stride] = cvt4_fp8<FMT>(v[u] * m);
+    }
+    for (; i < n4; i += stride) Q4[i] = cvt4_fp8<FMT>(__builtin_nontemporal_load(X + i) * m);
+    return;
+  }
   for (; i + (kUnroll - 1) * stride < n4; i += kUnroll * stride) {
     f32x4_t v[kUnroll];
 #pragma unroll
@@ -183,6 +206,23 @@ __global__ __launch_bounds__(256) void encode_rows(const float* X, int64_t rows,
   const float amax = gather_amax<256>(part, nparts);
   const float m = mult_from_amax<FMT>(amax);
   if (blockIdx.x == 0 && threadIdx.x == 0) scales[0] = scale_from_amax<FMT>(amax);
+  if (hw_encode_ok(amax, m)) {
+    for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
+      const float* row = X + r * ldx;
+      uint8_t* qrow = Q + r * ldq;
+      int64_t c = threadIdx.x;
+      for (; c + 768 < cols4; c += 1024) {
+        f32x4_t v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = *(const f32x4_t*)(row + 4 * (c + 256 * u));
+#pragma unroll
+        for (int u = 0; u < 4; ++u) *(uint32_t*)(qrow + 4 * (c + 256 * u)) = cvt4_fp8<FMT>(v[u] * m);
+      }
+      for (; c < cols4; c += 256)
+        *(uint32_t*)(qrow + 4 * c) = cvt4_fp8<FMT>(*(const f32x4_t*)(row + 4 * c) * m);
+    }
+    return;
+  }
   for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
     const float* row = X + r * ldx;
     uint8_t* qrow = Q + r * ldq;

@@ -508,7 +508,8 @@ def test_hardware_fp8_conversion(fmt):
     # gfx950's v_cvt_pk_{fp8,bf8}_f32 rounds to nearest even but does not
     # saturate: past the largest finite value E4M3 gives NaN and E5M2 gives
     # Inf.  Clamped to +-max first (NaN passed through) it is exactly the
-    # saturating encoder of the oracle -- what the fused epilogue relies on.
+    # saturating encoder of the oracle -- what the fused epilogue and the
+    # quantizers (for blocks with finite amax and multiplier) rely on.
     x = cvt_points(fmt)
     want = oracle.encode_fp8(x, fmt)
     xt = dev(x)
