@@ -266,8 +266,9 @@ __global__ __launch_bounds__(256) void quant_1x128(const float* X, int64_t rows,
     m = half_wave_max(m);
     if (blk[u] < nblk) {
       const float amax = __uint_as_float(m);
+      const float mult = mult_from_amax<FMT>(amax);
       *(uint32_t*)(Q + r[u] * ldq + cb[u] * 128 + 4 * lane) =
-          encode4<FMT>(v[u], mult_from_amax<FMT>(amax));
+          hw_encode_ok(amax, mult) ? cvt4_fp8<FMT>(v[u] * mult) : encode4<FMT>(v[u], mult);
       if (lane == 0) scales[blk[u]] = scale_from_amax<FMT>(amax);
     }
   }
@@ -296,8 +297,15 @@ __global__ __launch_bounds__(256) void quant_128x128(const float* X, int64_t nbc
   const float amax = __uint_as_float(m);
   const float mult = mult_from_amax<FMT>(amax);
   uint8_t* qb = Q + (bi * 128) * ldq + bj * 128 + 4 * c4;
+  if (hw_encode_ok(amax, mult)) {  // uniform over the workgroup
 #pragma unroll
-  for (int i = 0; i < 16; ++i) *(uint32_t*)(qb + (int64_t)(r0 + 8 * i) * ldq) = encode4<FMT>(v[i], mult);
+    for (int i = 0; i < 16; ++i)
+      *(uint32_t*)(qb + (int64_t)(r0 + 8 * i) * ldq) = cvt4_fp8<FMT>(v[i] * mult);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      *(uint32_t*)(qb + (int64_t)(r0 + 8 * i) * ldq) = encode4<FMT>(v[i], mult);
+  }
   if (t == 0) scales[blockIdx.x] = scale_from_amax<FMT>(amax);
 }
 
