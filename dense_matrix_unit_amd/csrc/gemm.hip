@@ -21,10 +21,11 @@
 //  * K advances in 128-byte slices (64 BF16 or 128 FP8 values per row) held
 //    in a 2-stage LDS ring: the copy of slice k+1 is issued while slice k is
 //    multiplied, and an L2 prefetch brings slice k+3 close;
-//  * A and column-major B are copied global -> LDS by buffer loads that write
-//    LDS directly (no VGPR round trip); a row-major B slice goes through VGPRs
-//    and is transposed 8x8 in registers so that LDS always holds K-contiguous
-//    rows;
+//  * A and B are copied global -> LDS by buffer loads that write LDS
+//    directly (no VGPR round trip).  A row-major B slice stays row-major in
+//    LDS (64 K rows of 512 bytes) and its fragments are read with gfx950's
+//    transposing LDS read, which hands each lane 4 consecutive K values of
+//    one column;
 //  * LDS rows are 128 bytes of 16-byte chunks; chunk c of row r is stored at
 //    position c ^ ((r ^ (r >> 3)) & 7).  A wave's 16-byte fragment reads
 //    (consecutive rows, one chunk column) then touch every bank group once per
@@ -68,6 +69,24 @@ __device__ __forceinline__ f32x16_t mfma_fp8_32x32x64(const i32x8_t& a, const i3
 // (dmu_probe_gemm_bf16_layout): plain rows, and rows padded by 16 bytes.
 enum LdsLayout { kSwizzled = 0, kPlain = 1, kPadded = 2 };
 
+// A row-major B slice in LDS is K rows of 512 bytes (256 BF16 columns, 32
+// chunks of 16 bytes); chunk c of K row r is stored at position c ^ bswz(r).
+// One transposing fragment read covers 4 consecutive K rows and 64 bytes of
+// each per 32 lanes; flipping bits 2-3 of the chunk index with r % 4 puts
+// those 4 x 64 bytes in distinct banks.
+__device__ __forceinline__ int bswz(int r) { return (r & 3) << 2; }
+
+// gfx950 transposing LDS read (ds_read_b64_tr_b16): in each group of 16
+// lanes, lane i names row i / 4 and 16-bit elements 4 (i % 4) .. +3 of a
+// row-major 4 x 16 block; lane j receives element j of the 4 rows, in row
+// order.
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint2 lds_read_tr16(const uint8_t* p) {
+  typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+  const i16x4_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)p);
+  return __builtin_bit_cast(uint2, r);
+}
+
 template <int KIND, int FA, int FB, bool BROW, int BM, int BN, int RB, int S, int kGroupM, int PD,
           int NW, bool KT, int LAY = kSwizzled>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4))) void
@@ -101,25 +120,49 @@ gemm_kernel(GemmArgs p) {
   constexpr int XR = MX ? 2 * XBUF : 0;
   constexpr int NSTEP = BF || F4 ? RB / 32 : RB / 64;  // MFMA K-steps per slice
   constexpr int NLA = BM * CPRS / NT;                // A copies per thread per slice
-  constexpr int NLB = BROW ? 8 : BN * CPRS / NT;     // B copies per thread per slice
+  constexpr int NLB = BN * CPRS / NT;                // B copies per thread per slice
   constexpr int NLS = MX ? 2 : 0;                    // MX scale-group copies (A, B)
   constexpr int NL = NLA + NLB + NLS;
   static_assert(BM % 64 == 0 && BN % 64 == 0 && (BM * CPRS) % NT == 0, "tile");
+  // row-major B in LDS: RB / 2 K rows of BROWB bytes (BN BF16 values)
+  constexpr int BROWB = BN * 2;
   static_assert(!BROW || ((KIND == kBF16 || KIND == kBF16F) && BN == 256 && RB == 128 && S == 2 &&
-                          NW == 4),
+                          NW == 4 && LAY == kSwizzled),
                 "row-major B staging");
   static_assert(BF || F8T || MX,
                 "per-block FP32 scales live in gemm_block.hip");
   static_assert(!MX || (!KT && !BROW && RB == 128 && NW == 4 && BM == 256 && BN == 256 && S == 2),
                 "MX: whole 128-K slices, one scale row per thread and operand");
   static_assert(S >= 2 && NL * (S - 2) < 64, "vmcnt range");
-  static_assert(PD == 0 || (S == 2 && !BROW && BM == 256 && BN == 256 && kGroupM == 4 && PD >= 2),
+  static_assert(PD == 0 || (S == 2 && BM == 256 && BN == 256 && kGroupM == 4 && PD >= 2),
                 "L2 prefetch layout");
   // one landing area per wave for the L2 prefetch's 4-byte copies, and for
   // MX scale copies that have nothing to fetch (64 lanes x 4 * XG bytes)
   constexpr int PF_WAVE = MX ? 64 * XROW : 256;
   constexpr int PF_BYTES = PD > 0 || MX ? NW * PF_WAVE : 0;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[S * STAGE + XR + PF_BYTES];
+  // Row-major B: every LDS buffer is an array of its own (A stages sa0, sa1,
+  // B stages sb0, sb1, prefetch area spf).  The compiler cannot tell a
+  // transposing read from the copies still writing LDS unless they touch
+  // different arrays; in one array it would make every such read wait for all
+  // outstanding copies.
+  constexpr int SMEM = BROW ? 16 : S * STAGE + XR + PF_BYTES;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM];
+  __shared__ __attribute__((aligned(1024))) uint8_t sa0[BROW ? A_BYTES : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t sa1[BROW ? A_BYTES : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t sb0[BROW ? B_BYTES : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t sb1[BROW ? B_BYTES : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t spf[BROW && PF_BYTES > 0 ? PF_BYTES : 16];
+  // LDS stage st of A and of B (st is a constant at every call), and the
+  // prefetch landing area
+  auto stage_a = [&](int st) __attribute__((always_inline)) -> uint8_t* {
+    if constexpr (BROW) return st == 0 ? sa0 : sa1;
+    else return smem + st * STAGE;
+  };
+  auto stage_b = [&](int st) __attribute__((always_inline)) -> uint8_t* {
+    if constexpr (BROW) return st == 0 ? sb0 : sb1;
+    else return smem + st * STAGE + A_BYTES;
+  };
+  uint8_t* const pf_area = BROW ? spf : smem + S * STAGE + XR;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int swave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, kept scalar
@@ -179,19 +222,22 @@ gemm_kernel(GemmArgs p) {
   }
 
   // ---- B descriptors
-  const int rowsB = (int)min((int64_t)BN, p.N - n0);
+  const int rowsB = (int)min((int64_t)BN, p.N - n0);  // columns of D this tile covers
   const uint32_t ldbB = (uint32_t)(p.ldb * ESZ);
   __amdgpu_buffer_rsrc_t rB;
-  constexpr int NBV = BROW ? 1 : NLB;
-  uint32_t voffB[NBV], cB[NBV];
-  // row-major B: thread owns an 8 (k) x 8 (n) block of the slice
-  const int kb8 = tid >> 5, nb8 = tid & 31;
-  bool colok = true;
+  // column-major B: as A.  Row-major B: copy `it` fills LDS position q = it *
+  // NT + tid, K row q / 32, position q % 32 of that row's 32 16-byte chunks
+  // (8 columns each), from chunk (q % 32) ^ bswz(row); cB holds the K row.
+  uint32_t voffB[NLB], cB[NLB];
   if constexpr (BROW) {
     rB = make_rsrc((const uint8_t*)p.B + n0 * 2, (p.K * p.ldb - n0) * 2);
-    colok = (int64_t)nb8 * 8 < rowsB;
-    voffB[0] = ((uint32_t)(kb8 * 8) * (uint32_t)p.ldb + (uint32_t)nb8 * 8) * 2;
-    cB[0] = 0;
+#pragma unroll
+    for (int it = 0; it < NLB; ++it) {
+      const int q = it * NT + tid, row = q / (BROWB / 16), pos = q % (BROWB / 16);
+      const int c = pos ^ bswz(row);
+      cB[it] = (uint32_t)row;
+      voffB[it] = c * 8 < rowsB ? (uint32_t)row * ldbB + (uint32_t)(c << 4) : kOOB;
+    }
   } else {
     rB = make_rsrc((const uint8_t*)p.B + n0 * p.ldb * ESZ, (int64_t)(rowsB - 1) * ldbB + kbytes);
 #pragma unroll
@@ -233,7 +279,7 @@ gemm_kernel(GemmArgs p) {
     if constexpr (MX) {
       const bool act = on && G < ngroups;
       uint8_t* dst = act ? smem + XOFF + (G & 1) * XBUF + which * BM * XROW + swave * 64 * XROW
-                         : smem + S * STAGE + XR + swave * PF_WAVE;
+                         : pf_area + swave * PF_WAVE;
       const uint32_t koff = act ? (uint32_t)G * XROW : 0u;
       const __amdgpu_buffer_rsrc_t r = act ? (which == 0 ? rXA : rXB) : rNull;
       const uint32_t v = which == 0 ? voffXA : voffXB;
@@ -251,8 +297,12 @@ gemm_kernel(GemmArgs p) {
   // (tile_coords), so each A panel is shared by 8 of them and each B panel
   // by kGroupM: each workgroup fetches 1/8 of its A rows (wave 0) and
   // 1/kGroupM of its B rows (waves 1 and 2), so every line is fetched once.
+  // Row-major B: a slice is RB / 2 K rows of BN columns, and each workgroup
+  // fetches 1/kGroupM of those rows, 64 bytes per lane; prow is the K row
+  // within the slice and pfs the byte distance between slices (RB for A).
   __amdgpu_buffer_rsrc_t rP = rA;
   uint32_t voffP = kOOB, cP = 0;
+  uint32_t pfs = RB, prow = 0;
   if constexpr (PD > 0) {
     const int half = lane & 1;
     cP = (uint32_t)half * 64;
@@ -261,31 +311,65 @@ gemm_kernel(GemmArgs p) {
       voffP = row < rowsA ? (uint32_t)row * ldaB + cP : kOOB;
     } else if (swave <= 2) {
       rP = rB;
-      const int row = (tm & (kGroupM - 1)) * (BN / kGroupM) + (swave - 1) * 32 + (lane >> 1);
-      voffP = row < rowsB ? (uint32_t)row * ldbB + cP : kOOB;
+      if constexpr (BROW) {
+        constexpr int RPW = RB / 2 / kGroupM / 2;  // K rows per fetching wave
+        constexpr int LPR = BROWB / 64;            // lanes per K row
+        static_assert(RPW * LPR == 64, "one 64-byte fetch per lane");
+        const int row = (tm & (kGroupM - 1)) * (2 * RPW) + (swave - 1) * RPW + lane / LPR;
+        const int col = (lane % LPR) * 64;  // bytes
+        prow = (uint32_t)row;
+        pfs = (uint32_t)(RB / 2) * ldbB;
+        voffP = col / 2 < rowsB ? (uint32_t)row * ldbB + (uint32_t)col : kOOB;
+      } else {
+        const int row = (tm & (kGroupM - 1)) * (BN / kGroupM) + (swave - 1) * 32 + (lane >> 1);
+        voffP = row < rowsB ? (uint32_t)row * ldbB + cP : kOOB;
+      }
     }
   }
   auto issue_pf = [&](int kt) __attribute__((always_inline)) {
     if constexpr (PD > 0) {
       const bool active = kt < nkt;
-      const uint32_t koff = active ? (uint32_t)kt * RB : 0u;
-      if constexpr (KT) {
-        const uint32_t v = active && koff + cP < (uint32_t)kbytes ? voffP : kOOB;
-        buffer_load_lds4(rP, smem + S * STAGE + XR + swave * PF_WAVE, v, koff);
+      if constexpr (BROW) {
+        const uint32_t koff = active ? (uint32_t)kt * pfs : 0u;
+        if constexpr (KT) {
+          // past the end of K: the byte along A's row, or B's K row
+          const bool in = swave == 0 ? koff + cP < (uint32_t)kbytes
+                                     : (int64_t)kt * (RB / 2) + prow < p.K;
+          buffer_load_lds4(rP, pf_area + swave * PF_WAVE, active && in ? voffP : kOOB, koff);
+        } else {
+          buffer_load_lds4(active ? rP : rNull, pf_area + swave * PF_WAVE, voffP, koff);
+        }
       } else {
-        buffer_load_lds4(active ? rP : rNull, smem + S * STAGE + XR + swave * PF_WAVE, voffP, koff);
+        const uint32_t koff = active ? (uint32_t)kt * RB : 0u;
+        if constexpr (KT) {
+          const uint32_t v = active && koff + cP < (uint32_t)kbytes ? voffP : kOOB;
+          buffer_load_lds4(rP, pf_area + swave * PF_WAVE, v, koff);
+        } else {
+          buffer_load_lds4(active ? rP : rNull, pf_area + swave * PF_WAVE, voffP, koff);
+        }
       }
     }
   };
 
-  u32x4_t breg[BROW ? 8 : 1];  // row-major B staging registers
+  // Row-major B: copy `it` of slice kt into B stage sB.  The slice is RB / 2
+  // K rows from row kt * RB / 2; rows past K read zeros.
+  auto issue_brow = [&](uint8_t* sB, int kt, bool active, int it) __attribute__((always_inline)) {
+    uint8_t* dst = sB + (it * NT + swave * 64) * 16;
+    const uint32_t soff = active ? (uint32_t)kt * (uint32_t)(RB / 2) * ldbB : 0u;
+    if constexpr (KT) {
+      const bool in = active && (int64_t)kt * (RB / 2) + cB[it] < p.K;
+      buffer_load_lds16(rB, dst, in ? voffB[it] : kOOB, soff);
+    } else {
+      buffer_load_lds16(active ? rB : rNull, dst, voffB[it], soff);
+    }
+  };
 
   // Copy K slice `kt` into LDS stage `st`.  With active == false every lane
   // gets an out-of-range offset (slices after the last one), so the
   // instruction stream is the same on every iteration.
   auto issue_loads = [&](int kt, int st, bool active) __attribute__((always_inline)) {
-    uint8_t* sA = smem + st * STAGE;
-    uint8_t* sB = sA + A_BYTES;
+    uint8_t* sA = stage_a(st);
+    uint8_t* sB = stage_b(st);
     // chunks at byte position >= klim along K are fetched as zeros: the K
     // tail of the last slice, or everything when inactive
     const uint32_t koff = active ? (uint32_t)kt * RB : 0u;
@@ -296,12 +380,8 @@ gemm_kernel(GemmArgs p) {
       buffer_load_lds16(rA, sA + (it * NT + swave * 64) * 16, v, koff);
     }
     if constexpr (BROW) {
-      const int k0 = kt * 64 + kb8 * 8;
-      const bool ok = active && colok && k0 < p.K;
-      const uint32_t soff = active ? (uint32_t)kt * 64u * (uint32_t)p.ldb * 2u : 0u;
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        breg[i] = buffer_load16(rB, ok ? voffB[0] + (uint32_t)(i * p.ldb * 2) : kOOB, soff);
+      for (int it = 0; it < NLB; ++it) issue_brow(sB, kt, active, it);
     } else {
 #pragma unroll
       for (int it = 0; it < NLB; ++it) {
@@ -325,8 +405,8 @@ gemm_kernel(GemmArgs p) {
       issue_xgroup(cur / XG + 1, idx - NLA - NLB, cur % XG == 0);
       return;
     }
-    uint8_t* sA = smem + st * STAGE;
-    uint8_t* sB = sA + A_BYTES;
+    uint8_t* sA = stage_a(st);
+    uint8_t* sB = stage_b(st);
     const uint32_t koff = active ? (uint32_t)kt * RB : 0u;
     const uint32_t klim = active ? (uint32_t)kbytes : 0u;
     if (idx < NLA) {
@@ -337,10 +417,7 @@ gemm_kernel(GemmArgs p) {
         buffer_load_lds16(active ? rA : rNull, sA + (idx * NT + swave * 64) * 16, voffA[idx], koff);
       }
     } else if constexpr (BROW) {
-      const int i = idx - NLA;
-      const bool ok = active && colok && kt * 64 + kb8 * 8 < p.K;
-      const uint32_t soff = active ? (uint32_t)kt * 64u * (uint32_t)p.ldb * 2u : 0u;
-      breg[i] = buffer_load16(rB, ok ? voffB[0] + (uint32_t)(i * p.ldb * 2) : kOOB, soff);
+      issue_brow(sB, kt, active, idx - NLA);
     } else {
       const int it = idx - NLA;
       if constexpr (KT) {
@@ -348,25 +425,6 @@ gemm_kernel(GemmArgs p) {
         buffer_load_lds16(rB, sB + (it * NT + swave * 64) * 16, v, koff);
       } else {
         buffer_load_lds16(active ? rB : rNull, sB + (it * NT + swave * 64) * 16, voffB[it], koff);
-      }
-    }
-  };
-
-  // row-major B: transpose the thread's 8x8 block in registers and store the
-  // eight 16-byte K-chunks (one per n) into the swizzled K-contiguous layout.
-  auto store_brow = [&](int st) __attribute__((always_inline)) {
-    if constexpr (BROW) {
-      uint8_t* sB = smem + st * STAGE + A_BYTES;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        u32x4_t w;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const uint32_t lo = breg[2 * q][j >> 1], hi = breg[2 * q + 1][j >> 1];
-          w[q] = (j & 1) ? ((lo >> 16) | (hi & 0xFFFF0000u)) : ((lo & 0xFFFFu) | (hi << 16));
-        }
-        const int n = nb8 * 8 + j;
-        *(u32x4_t*)(sB + n * RB + ((kb8 ^ swz<RB>(n)) << 4)) = w;
       }
     }
   };
@@ -385,13 +443,7 @@ gemm_kernel(GemmArgs p) {
 #pragma unroll
   for (int t = 1; t < PD; ++t) issue_pf(t);
   constexpr int NPF = PD > 0 ? 1 : 0;  // prefetches per slice per thread
-  if constexpr (BROW) {
-    __builtin_amdgcn_s_waitcnt(0);
-    store_brow(0);
-  } else {
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<NL * (S - 2) + (PD > 1 ? PD - 1 : 0)>());
-  }
-  if constexpr (BROW) __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<0>());  // store_brow's LDS writes
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<NL * (S - 2) + (PD > 1 ? PD - 1 : 0)>());
   stage_barrier();
 
   {
@@ -443,9 +495,34 @@ gemm_kernel(GemmArgs p) {
         }
       }
     };
+    // Row-major B: the step-s fragment of sub-tile j (lane l: column l % 32,
+    // K values 16 s + 8 (l / 32) + 0..7, as the A fragment's chunk) is two
+    // transposing reads, K rows 16 s + 8 (l / 32) + 0..3 and + 4..7.  Lane i
+    // of 16-lane group g names K row i / 4 of the four and columns
+    // 16 (g % 2) + 4 (i % 4) .. +3 of the sub-tile; bswz of those rows is
+    // (i / 4) << 2, so each sub-tile has one per-lane offset.
+    uint32_t bro[BROW ? TN : 1];
+    if constexpr (BROW) {
+      const int i = lane & 15, g = (lane >> 4) & 1;
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int c = (wn * WN + j * 32) / 8 + 2 * g + ((i & 3) >> 1);  // 16-byte chunk
+        bro[j] = (uint32_t)((8 * hl + (i >> 2)) * BROWB + ((c ^ ((i >> 2) << 2)) << 4) +
+                            ((i & 1) << 3));
+      }
+    }
+    auto rd_b = [&](const uint8_t* sB, int j, int s, int h) __attribute__((always_inline)) -> i32x4_t {
+      if constexpr (BROW) {
+        const uint8_t* q = sB + bro[j] + 16 * s * BROWB;
+        const uint2 lo = lds_read_tr16(q), hi = lds_read_tr16(q + 4 * BROWB);
+        return i32x4_t{(int)lo.x, (int)lo.y, (int)hi.x, (int)hi.y};
+      } else {
+        return lds16(sB, wn * WN + j * 32 + rl, chunk(s, h));
+      }
+    };
     auto load_step = [&](int st, int s, int buf) __attribute__((always_inline)) {
-      const uint8_t* sA = smem + st * STAGE;
-      const uint8_t* sB = sA + A_BYTES;
+      const uint8_t* sA = stage_a(st);
+      const uint8_t* sB = stage_b(st);
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -454,8 +531,7 @@ gemm_kernel(GemmArgs p) {
 #pragma unroll
       for (int j = 0; j < TN; ++j)
 #pragma unroll
-        for (int h = 0; h < CPL; ++h)
-          fb[buf][j][h] = lds16(sB, wn * WN + j * 32 + rl, chunk(s, h));
+        for (int h = 0; h < CPL; ++h) fb[buf][j][h] = rd_b(sB, j, s, h);
     };
     // Fragment read k (0 <= k < NR) of step s, in the order the step's MFMAs
     // first need them: A fragment 0, B fragments 0 .. TN-1, A fragments
@@ -464,14 +540,14 @@ gemm_kernel(GemmArgs p) {
     // next step's first MFMAs never wait on a burst of reads.
     constexpr int NR = (TM + TN) * CPL;
     auto read_one = [&](int st, int s, int buf, int k) __attribute__((always_inline)) {
-      const uint8_t* sA = smem + st * STAGE;
-      const uint8_t* sB = sA + A_BYTES;
+      const uint8_t* sA = stage_a(st);
+      const uint8_t* sB = stage_b(st);
       const int c = chunk(s, k % CPL);
       const int slot = k / CPL, h = k % CPL;
       if (slot == 0)
         fa[buf][0][h] = lds16(sA, wm * WM + rl, c);
       else if (slot <= TN)
-        fb[buf][slot - 1][h] = lds16(sB, wn * WN + (slot - 1) * 32 + rl, c);
+        fb[buf][slot - 1][h] = rd_b(sB, slot - 1, s, h);
       else
         fa[buf][slot - TN][h] = lds16(sA, wm * WM + (slot - TN) * 32 + rl, c);
     };
@@ -566,10 +642,6 @@ gemm_kernel(GemmArgs p) {
       // slice kt+1 has landed; only the prefetch issued in this slice may
       // still be in flight (vector memory operations complete in order)
       __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<NL * (S - 2) + NPF>());
-      if constexpr (BROW) {
-        store_brow(ld_st);  // row-major B: registers of slice kt+1 -> LDS (S == 2)
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<0>());  // LDS writes done before the barrier
-      }
       stage_barrier();
       __builtin_amdgcn_sched_barrier(0);
       read_scales(kt + 1);  // next slice's scale words; this slice's stay in xa / xb
@@ -616,6 +688,16 @@ gemm_kernel(GemmArgs p) {
     if constexpr (F8T) alpha = p.sa[0] * p.sb[0];
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();  // every wave is done reading the K-slice stages
+    // the wave's staging region of `bytes`; with row-major B the regions are
+    // the two A stages and the two B stages, 32 KB each
+    auto region = [&](int bytes) __attribute__((always_inline)) -> uint8_t* {
+      if constexpr (BROW) {
+        static_assert(NW == 4 && A_BYTES == 32768 && B_BYTES == 32768, "four 32 KB regions");
+        return swave == 0 ? sa0 : swave == 1 ? sa1 : swave == 2 ? sb0 : sb1;
+      } else {
+        return smem + swave * bytes;
+      }
+    };
     if constexpr (EPI) {
       // Fused epilogue (the fused entry points take no C): scale, bias,
       // activation and conversion on the accumulators, one 32-row block row
@@ -674,7 +756,8 @@ gemm_kernel(GemmArgs p) {
         static_assert(NW * 32 * RBS <= S * STAGE && RBS % 16 == 0 && 64 % UPS == 0,
                       "block staging fits in LDS");
         const float m = EB == 1 ? 1.0f / p.out_scale[0] : 1.0f;
-        uint8_t* wb = smem + swave * (32 * RBS);
+        static_assert(!BROW || 32 * RBS <= 32768, "staging region");
+        uint8_t* wb = region(32 * RBS);
 #pragma unroll 1
         for (int i = 0; i < TM; ++i) {
           f32x16_t cur[TN];
@@ -766,7 +849,8 @@ gemm_kernel(GemmArgs p) {
       // staged row r sits at u ^ (r % 16): the 8-byte writes of 16 rows at
       // one column then fall in distinct bank groups.  Each read instruction
       // covers 4 rows x 256 B and each store writes 16 B (8 columns) per lane.
-      uint8_t* wbase = smem + swave * (TM * 32 * WN * 2);
+      static_assert(!BROW || TM * 32 * WN * 2 <= 32768, "staging region");
+      uint8_t* wbase = region(TM * 32 * WN * 2);
       constexpr int RB16 = WN * 2;    // staged row bytes
       constexpr int UPR = RB16 / 16;  // 16-byte units per row
 #pragma unroll
@@ -802,7 +886,8 @@ gemm_kernel(GemmArgs p) {
         }
       }
     } else {
-      float* band = (float*)smem + swave * 32 * ROWW;
+      static_assert(!BROW || 32 * ROWW * 4 <= 32768, "staging region");
+      float* band = (float*)region(32 * ROWW * 4);
       constexpr int LPR = WN / 4;       // lanes per band row on the read side
       constexpr int RPI = 64 / LPR;     // band rows per read instruction
 #pragma unroll
@@ -850,7 +935,7 @@ hipError_t launch(const GemmArgs& a, hipStream_t s) {
 
 hipError_t launch_gemm_bf16_fused(const GemmArgs& a, int b_col_major, hipStream_t s) {
   if (b_col_major) return launch<kBF16F, 0, 0, false, 256, 256, 128, 2, 4, kPrefetch, kWavesBF16>(a, s);
-  return launch<kBF16F, 0, 0, true, 256, 256, 128, 2, 4>(a, s);
+  return launch<kBF16F, 0, 0, true, 256, 256, 128, 2, 4, kPrefetch, kWavesBF16>(a, s);
 }
 
 hipError_t launch_gemm_fp8_fused(const GemmArgs& a, int fmt_a, int fmt_b, hipStream_t s) {
@@ -887,7 +972,7 @@ hipError_t launch_gemm_bf16_layout(const GemmArgs& a, int layout, hipStream_t s)
 hipError_t launch_gemm_bf16(const GemmArgs& a, int b_col_major, hipStream_t s) {
   if (b_col_major && skinny_applies(a)) return launch_gemm_bf16_skinny(a, s);
   if (b_col_major) return launch<kBF16, 0, 0, false, 256, 256, 128, 2, 4, kPrefetch, kWavesBF16>(a, s);
-  return launch<kBF16, 0, 0, true, 256, 256, 128, 2, 4>(a, s);
+  return launch<kBF16, 0, 0, true, 256, 256, 128, 2, 4, kPrefetch, kWavesBF16>(a, s);
 }
 
 template <int FA, int FB>

@@ -169,3 +169,61 @@ def test_attention_v_reads_with_32_banks(d):
             for second in (False, True):
                 assert wavefronts(v_read(d, nt, ks, second), 8, 32, 16) == 8
                 assert wavefronts(v_read(d, nt, ks, second, swizzled=False), 8, 32, 16) == 16
+
+
+# ---- gfx950: the GEMM kernel's transposing reads of a row-major B slice
+# (csrc/gemm.hip, B stored K x N): 64 K rows of 512 bytes (256 BF16 columns,
+# 32 chunks of 16 bytes), chunk c of K row r at position c ^ ((r % 4) << 2)
+def brow_read(wn, j, s, second, swizzled=True):
+    """Byte addresses of one ds_read_b64_tr_b16 of sub-tile j of wave column
+    wn at K step s (8 bytes per lane): lane l = 32 h + 16 g + i reads K row
+    16 s + 8 h + i/4 (+ 4 for the second read) at 16-bit elements
+    4 (i % 4) .. +3 of columns 128 wn + 32 j + 16 (g % 2)."""
+    out = []
+    for lane in range(64):
+        h, g, i = lane >> 5, lane >> 4, lane & 15
+        row = 16 * s + 8 * h + (4 if second else 0) + (i >> 2)
+        chunk = (128 * wn + 32 * j) // 8 + 2 * (g & 1) + ((i & 3) >> 1)
+        if swizzled:
+            chunk ^= (row & 3) << 2
+        out.append(row * 512 + (chunk << 4) + ((i & 1) << 3))
+    return out
+
+
+def test_row_major_b_reads_conflict_free_with_64_banks():
+    # every read of every wave column, sub-tile and step: 2 wavefronts, the
+    # minimum for 512 bytes; unswizzled, the 4 K rows of a 16-lane group share
+    # one 64-byte bank run (512-byte rows)
+    for wn in range(2):
+        for j in range(4):
+            for s in range(4):
+                for second in (False, True):
+                    assert wavefronts(brow_read(wn, j, s, second), 8, 64, 32) == 2
+                    assert wavefronts(brow_read(wn, j, s, second, swizzled=False), 8, 64, 32) == 8
+
+
+def test_row_major_b_reads_cover_the_fragment():
+    # lane l of the two reads gets column l % 32 of the sub-tile and K values
+    # 8 (l / 32) + 0..7 of the step, the K run its A fragment holds (one
+    # 16-byte chunk per lane); each read's 16-lane group names 4 K rows x 16
+    # columns, element e of lane i's 8 bytes being column 4 (i % 4) + e
+    for wn in range(2):
+        for j in range(4):
+            for s in range(4):
+                got = {}
+                for second in (False, True):
+                    addrs = brow_read(wn, j, s, second)
+                    for lane in range(64):
+                        g, i = lane >> 4, lane & 15
+                        for e in range(4):
+                            a = addrs[lane] + 2 * e
+                            row, pos = a // 512, (a % 512) // 16
+                            col = 8 * (pos ^ ((row & 3) << 2)) + (a % 16) // 2
+                            # the transposed result: lane 16 g + t of the group
+                            # receives column t of the 4 rows named by i / 4
+                            t = 4 * (i & 3) + e
+                            got.setdefault((16 * g + t, row), col)
+                for lane in range(64):
+                    rows = sorted(r for (l, r) in got if l == lane)
+                    assert rows == [16 * s + 8 * (lane >> 5) + k for k in range(8)]
+                    assert {got[(lane, r)] for r in rows} == {128 * wn + 32 * j + lane % 32}

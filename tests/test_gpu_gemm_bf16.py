@@ -11,7 +11,8 @@ import torch
 import oracle
 import dense_matrix_unit_amd as dmu
 from dense_matrix_unit_amd import workloads as wl
-from gpu_helpers import (assert_within_bound, bf16, dev, out_to_f64, round_out, run_gemm_bf16)
+from gpu_helpers import (assert_within_bound, bf16, dev, empty_padded, out_to_f64, round_out,
+                         run_gemm_bf16)
 
 pytestmark = pytest.mark.gpu
 LAYOUTS = [dmu.B_ROW_MAJOR, dmu.B_COL_MAJOR]
@@ -93,6 +94,27 @@ def test_strided_operands():
                                np.ascontiguousarray(Bbig[:, :K]), dmu.B_COL_MAJOR)
     assert_within_bound(out.cpu().numpy().astype(np.float64), Dref, S, False, "strided")
     assert torch.all(out_big[:, N:] == 0)
+
+
+@pytest.mark.parametrize("out_dtype", OUTS)
+@pytest.mark.parametrize("shape", [(300, 200, 264), (513, 257, 1032), (64, 520, 4104),
+                                   (40, 1000, 8)])
+def test_row_major_b_reads_nothing_outside_the_view(out_dtype, shape):
+    # B (K x N, row-major) is a view into a larger buffer whose other rows and
+    # columns hold NaN: neither the rows past K (the K tail of the last
+    # slice) nor the columns past N may reach D
+    M, N, K = shape
+    A = bf16(wl.normal((M, K), 41))
+    B = bf16(wl.normal((K, N), 42))
+    ldb = (N + 7) // 8 * 8 + 8
+    big = torch.full((K + 64, ldb), float("nan"), dtype=torch.bfloat16, device="cuda")
+    big[:K, :N] = dev(B)
+    out = empty_padded(M, N, out_dtype)
+    dmu.gemm_bf16(dev(A), big[:K, :N], out, dmu.B_ROW_MAJOR)
+    torch.cuda.synchronize()
+    Dref, S = oracle.gemm_bf16(A, B, dmu.B_ROW_MAJOR)
+    assert_within_bound(out_to_f64(out), Dref, S, out_dtype == torch.bfloat16,
+                        "row-major B view %s" % (shape,))
 
 
 @pytest.mark.parametrize("layout", LAYOUTS)
