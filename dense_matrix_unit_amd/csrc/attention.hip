@@ -23,9 +23,11 @@
 //    gfx950's transposing LDS read, ds_read_b64_tr_b16, gives each lane four
 //    keys of its column from four rows, so V is never transposed in
 //    registers; two such reads, of keys 4h..4h+3 and 8+4h..8+4h+3 of a 16-key
-//    step, match the order of the weights in the score registers.  They are
-//    issued as inline assembly with explicit LDS-counter waits, so they do
-//    not wait for the copies of later blocks;
+//    step, match the order of the weights in the score registers;
+//  * each stage of K and of V is an LDS array of its own: the compiler then
+//    sees that a stage's reads and the copies into the other stage touch
+//    different arrays, and waits only for the reads (in one array it would
+//    make every transposing read wait for all copies in flight);
 //  * two stages of K and V (64 KB for d = 128), so two workgroups share a
 //    CU and one wave's softmax arithmetic can run beside another's MFMAs;
 //    alternate runs of 256 workgroup ids run at a higher wave priority, which
@@ -59,27 +61,14 @@ __device__ __forceinline__ int vswz(int j) {
 }
 
 // gfx950 transposing LDS read (ds_read_b64_tr_b16): in each group of 16
-// lanes, lane i names row i / 4, 16-bit elements 4 (i % 4) .. +3 of a
+// lanes, lane i names row i / 4 and 16-bit elements 4 (i % 4) .. +3 of a
 // row-major 4 x 16 block; lane j receives element j of the 4 rows, in row
-// order.  Issued as inline assembly, at LDS byte address addr + OFF: given
-// the compiler's builtin, the compiler cannot tell which LDS bytes the read
-// touches and makes it wait for every outstanding global -> LDS copy (the
-// next blocks' K and V), which stalls the wave in the middle of each block.
-// The caller waits on the LDS counter itself before using the result.
-template <int OFF>
-__device__ __forceinline__ uint2 read_tr16_at(uint32_t addr) {
-  static_assert(OFF >= 0 && OFF < 65536, "ds offset field");
-  uint2 r;
-  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
-  return r;
-}
-
-// s_waitcnt for the LDS counter alone: at most N LDS (or scalar-load)
-// operations outstanding.
-template <int N>
-constexpr int waitcnt_lgkm() {
-  static_assert(N >= 0 && N < 16, "lgkmcnt range");
-  return 0xF | (0x7 << 4) | (N << 8) | (0x3 << 14);
+// order.
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint2 read_tr16(const uint8_t* q) {
+  typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+  const i16x4_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)q);
+  return __builtin_bit_cast(uint2, r);
 }
 
 // Compile-time loop: f(Idx<0>{}), ..., f(Idx<N-1>{}), so that an index can
@@ -149,9 +138,11 @@ attention_kernel(AttnArgs p) {
   constexpr int CPR = D / 8;                 // 16-byte chunks of a V row
   constexpr int OB = 32 * D * 2;             // one wave's staged output rows
   static_assert(4 * OB <= 2 * K_BYTES + 2 * V_BYTES, "output staging fits");
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * K_BYTES + 2 * V_BYTES];
-  uint8_t* const sK = smem;
-  uint8_t* const sV = smem + 2 * K_BYTES;
+  __shared__ __attribute__((aligned(1024))) uint8_t sK0[K_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t sK1[K_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t sV0[V_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t sV1[V_BYTES];
+  static_assert(2 * OB == K_BYTES, "two waves' output rows per K stage");
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -222,11 +213,11 @@ attention_kernel(AttnArgs p) {
     const __amdgpu_buffer_rsrc_t rK = make_rsrc(Kh + k0 * p.ldk, ((rows - 1) * p.ldk + D) * 2);
 #pragma unroll
     for (int it = 0; it < KCOPY; ++it)
-      buffer_load_lds16(rK, sK + stage * K_BYTES + (it * kThreads + wave * 64) * 16, kvo[it], 0);
+      buffer_load_lds16(rK, (stage ? sK1 : sK0) + (it * kThreads + wave * 64) * 16, kvo[it], 0);
     const __amdgpu_buffer_rsrc_t rV = make_rsrc(Vh + k0 * p.ldv, ((rows - 1) * p.ldv + D) * 2);
 #pragma unroll
     for (int it = 0; it < VCOPY; ++it)
-      buffer_load_lds16(rV, sV + stage * V_BYTES + (it * kThreads + wave * 64) * 16, vvo[it], 0);
+      buffer_load_lds16(rV, (stage ? sV1 : sV0) + (it * kThreads + wave * 64) * 16, vvo[it], 0);
   };
   // ---- prologue: block 0 staged, block 1 in flight
   issue_block(0, 0);
@@ -249,19 +240,15 @@ attention_kernel(AttnArgs p) {
   // V operand of output tile nt: lane i of 16-lane group g reads row 4h + i/4
   // (+ the step's first key, + 8 for the second read), columns
   // 32 nt + 16 (g % 2) + 4 (i % 4) .. +3; the swizzle depends on the row only
-  // through i / 4, so each tile has one per-lane offset.
-  // Kept as LDS byte addresses of V stage 0; stage, key step and half go in
-  // the read's immediate offset.
-  uint32_t vaddr[NT];
+  // through i / 4, so each tile has one per-lane offset (bytes into a V
+  // stage); key step and half are constants added to it.
+  int voff[NT];
   {
-    typedef __attribute__((address_space(3))) uint8_t lds_u8;
-    const uint32_t vbase = (uint32_t)(size_t)(lds_u8*)sV;
     const int g = lane >> 4, i = lane & 15;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
-      vaddr[nt] = vbase + (uint32_t)((4 * hl + (i >> 2)) * VROW +
-                                     (((4 * nt + 2 * (g & 1) + ((i & 3) >> 1)) ^ vswz<D>(i >> 2)) << 4) +
-                                     ((i & 1) << 3));
+      voff[nt] = (4 * hl + (i >> 2)) * VROW +
+                 (((4 * nt + 2 * (g & 1) + ((i & 3) >> 1)) ^ vswz<D>(i >> 2)) << 4) + ((i & 1) << 3);
   }
 
   const float c = p.scale * kLog2e;  // exp(scale * x) = exp2(c * x)
@@ -285,7 +272,7 @@ attention_kernel(AttnArgs p) {
     if (visible) {
       // ---- scores S^T = K Q^T, two 32-key tiles
       // (fragment reads run two MFMAs ahead of their use: a ring of three)
-      const uint8_t* kb = sK + stage * K_BYTES;
+      const uint8_t* kb = stage ? sK1 : sK0;
       auto kread = [&](int x) __attribute__((always_inline)) {
         const int s = x >> 1, jt = x & 1;  // d step, key tile
         const int half = s >> 2, k = ((2 * s) ^ (4 * jt)) & 7;
@@ -344,30 +331,23 @@ attention_kernel(AttnArgs p) {
         for (int nt = 0; nt < NT; ++nt) o[nt] *= alpha;
       }
       // ---- O^T += V^T P^T, four 16-key steps
-      // (reads two MFMAs ahead, each fragment two transposing reads; the LDS
-      // counter is drained first, so the waits below count these reads only)
+      // (reads two MFMAs ahead, each fragment two transposing reads)
+      const uint8_t* vb = stage ? sV1 : sV0;
       auto vread = [&](auto X) __attribute__((always_inline)) {
         constexpr int x = decltype(X)::value;
         constexpr int ks = x / NT, nt = x % NT;  // key step, output tile
-        constexpr int off = stage * V_BYTES + ks * 16 * VROW;
-        const uint2 lo = read_tr16_at<off>(vaddr[nt]);
-        const uint2 hi = read_tr16_at<off + 8 * VROW>(vaddr[nt]);
+        const uint8_t* q = vb + voff[nt] + ks * 16 * VROW;
+        const uint2 lo = read_tr16(q), hi = read_tr16(q + 8 * VROW);
         return u32x4_t{lo.x, lo.y, hi.x, hi.y};
       };
-      __builtin_amdgcn_sched_barrier(0);
-      __builtin_amdgcn_s_waitcnt(waitcnt_lgkm<0>());
-      __builtin_amdgcn_sched_barrier(0);
       u32x4_t vq[3];
       vq[0] = vread(Idx<0>{});
       vq[1] = vread(Idx<1>{});
       unroll_n<4 * NT>([&](auto X) __attribute__((always_inline)) {
         constexpr int x = decltype(X)::value;
         if constexpr (x + 2 < 4 * NT) vq[(x + 2) % 3] = vread(Idx<x + 2>{});
-        constexpr int ahead = x + 2 < 4 * NT ? 2 : x + 1 < 4 * NT ? 1 : 0;  // fragments after x
         constexpr int ks = x / NT, nt = x % NT, jt = ks >> 1, w0 = (ks & 1) * 4;
         const u32x4_t pf = {pk[jt][w0], pk[jt][w0 + 1], pk[jt][w0 + 2], pk[jt][w0 + 3]};
-        __builtin_amdgcn_sched_barrier(0);
-        __builtin_amdgcn_s_waitcnt(waitcnt_lgkm<2 * ahead>());
         __builtin_amdgcn_sched_barrier(0);
         o[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vq[x % 3]),
                                                         __builtin_bit_cast(bf16x8_t, pf), o[nt], 0,
@@ -375,15 +355,23 @@ attention_kernel(AttnArgs p) {
         __builtin_amdgcn_sched_barrier(0);
       });
     }
-    // ---- block t+1's copies are in; then start block t+2
-    if (t + 1 < nblk) __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<0>());
+    // ---- block t+1's copies are in; then start block t+2.  The wait is
+    // unconditional (nothing is in flight after the last block), so the
+    // compiler knows no copy is outstanding past the barrier but those
+    // issued after it, into the stage the next block does not read.
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<0>());
     stage_barrier();  // block t's stage is free; block t+1's is complete
     if (t + 2 < nblk) issue_block(t + 2, stage);
   };
-  for (int t = 0; t < nblk; t += 2) {
+  // Blocks in pairs, so that every pass round the loop has run both stages:
+  // the copies in flight at the top of the loop are then only those into
+  // stage 1, which the compiler can see (an odd last block runs after it).
+  int t = 0;
+  for (; t + 1 < nblk; t += 2) {
     blk(t, Idx<0>{});
-    if (t + 1 < nblk) blk(t + 1, Idx<1>{});
+    blk(t + 1, Idx<1>{});
   }
+  if (t < nblk) blk(t, Idx<0>{});
 
   // ---- epilogue: O / l, rounded to BF16, staged per wave and stored in row segments
   l = half_sum(l);
@@ -392,7 +380,7 @@ attention_kernel(AttnArgs p) {
     constexpr int RB = D * 2;       // staged row bytes
     constexpr int UPR = RB / 16;    // 16-byte units per row
     constexpr int RPI = 64 / UPR;   // rows per read instruction
-    uint8_t* wb = smem + wave * OB;
+    uint8_t* wb = (wave < 2 ? sK0 : sK1) + (wave & 1) * OB;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
