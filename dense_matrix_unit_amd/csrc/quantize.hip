@@ -16,7 +16,8 @@
 //    then encodes its share; workgroup 0 stores the scale.  No slot needs
 //    clearing and no atomics are used; the slot count is the pass-1 grid
 //    (at most kTensorSlots, whatever the tensor's size).
-//  * 1 x 128 blocks: 32 lanes per block (16 bytes per lane), half-wave max.
+//  * 1 x 128 blocks: 32 lanes per block (16 bytes per lane), half-wave max,
+//    rows walked by the grid's y dimension.
 //  * 128 x 128 blocks: one 256-thread workgroup per block keeps its 64 values
 //    per thread in registers between the amax and the encode (one HBM read).
 //  * MX (1 x 32 blocks, E8M0 scales; "How Blackwell's Tensor Memory Actually
@@ -240,36 +241,39 @@ __global__ __launch_bounds__(256) void encode_rows(const float* X, int64_t rows,
 }
 
 // ---- 1 x 128 blocks -------------------------------------------------------
-// 32 lanes own one block (4 values each); a 256-thread workgroup covers 8
-// blocks per round and does kRounds rounds, loads of all rounds issued first.
+// Workgroup (x, y) walks rows y, y + gridDim.y, ...; in each it covers
+// kRounds chunks of 1024 columns starting at x * 1024 * kRounds, thread t
+// taking columns 4t .. 4t+3 of every chunk, so the 32 lanes of a half-wave
+// own one block and no division is needed.  Loads of all rounds are issued
+// first; X is read once, with nontemporal loads.
 constexpr int kRounds = 4;
 template <int FMT>
-__global__ __launch_bounds__(256) void quant_1x128(const float* X, int64_t rows, int64_t nbc,
+__global__ __launch_bounds__(256) void quant_1x128(const float* X, int64_t rows, int64_t cols,
                                                    int64_t ldx, uint8_t* Q, int64_t ldq,
                                                    float* scales) {
   const int lane = threadIdx.x & 31;
-  const int64_t nblk = rows * nbc;
-  f32x4_t v[kRounds];
-  int64_t blk[kRounds], r[kRounds], cb[kRounds];
+  const int64_t nbc = cols / 128;
+  const int64_t c0 = (int64_t)blockIdx.x * (1024 * kRounds) + 4 * threadIdx.x;
+  for (int64_t r = blockIdx.y; r < rows; r += gridDim.y) {
+    const float* xr = X + r * ldx;
+    f32x4_t v[kRounds];
 #pragma unroll
-  for (int u = 0; u < kRounds; ++u) {
-    blk[u] = ((int64_t)blockIdx.x * kRounds + u) * 8 + (threadIdx.x >> 5);
-    v[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    r[u] = blk[u] / nbc;
-    cb[u] = blk[u] - r[u] * nbc;
-    if (blk[u] < nblk) v[u] = *(const f32x4_t*)(X + r[u] * ldx + cb[u] * 128 + 4 * lane);
-  }
+    for (int u = 0; u < kRounds; ++u) {
+      const int64_t c = c0 + u * 1024;
+      v[u] = c < cols ? __builtin_nontemporal_load((const f32x4_t*)(xr + c))
+                      : f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
 #pragma unroll
-  for (int u = 0; u < kRounds; ++u) {
-    uint32_t m = max(max(abs_bits(v[u][0]), abs_bits(v[u][1])),
-                     max(abs_bits(v[u][2]), abs_bits(v[u][3])));
-    m = half_wave_max(m);
-    if (blk[u] < nblk) {
-      const float amax = __uint_as_float(m);
-      const float mult = mult_from_amax<FMT>(amax);
-      *(uint32_t*)(Q + r[u] * ldq + cb[u] * 128 + 4 * lane) =
-          hw_encode_ok(amax, mult) ? cvt4_fp8<FMT>(v[u] * mult) : encode4<FMT>(v[u], mult);
-      if (lane == 0) scales[blk[u]] = scale_from_amax<FMT>(amax);
+    for (int u = 0; u < kRounds; ++u) {
+      const int64_t c = c0 + u * 1024;
+      const uint32_t m = half_wave_max(amax4(v[u]));
+      if (c < cols) {  // cols % 128 == 0: a block is entirely in or out
+        const float amax = __uint_as_float(m);
+        const float mult = mult_from_amax<FMT>(amax);
+        *(uint32_t*)(Q + r * ldq + c) =
+            hw_encode_ok(amax, mult) ? cvt4_fp8<FMT>(v[u] * mult) : encode4<FMT>(v[u], mult);
+        if (lane == 0) scales[r * nbc + c / 128] = scale_from_amax<FMT>(amax);
+      }
     }
   }
 }
@@ -356,7 +360,9 @@ __global__ __launch_bounds__(256) void quant_mx(const float* X, int64_t rows, in
 #pragma unroll
             for (int e = 0; e < 4; ++e) q |= encode_fp4(v[u][e] * mult) << (4 * e);
           } else {
-            q = encode4<FMT>(v[u], mult);
+            // finite block, normal power-of-two multiplier: every product is
+            // finite, where the clamped hardware conversion is the encoder
+            q = cvt4_fp8<FMT>(v[u] * mult);
           }
         }
         if constexpr (FMT == 4)
@@ -410,9 +416,9 @@ hipError_t launch_fmt(const float* X, int64_t rows, int64_t cols, int64_t ldx, i
     launch_tensor<FMT>(X, rows, cols, ldx, Q, ldq, scales, part,
                        tensor_passes(rows, cols, ldx, ldq), s);
   } else if (br == 1 && bc == 128) {
-    const int64_t nbc = cols / 128, nblk = rows * nbc;
-    hipLaunchKernelGGL(quant_1x128<FMT>, dim3((unsigned)((nblk + 8 * kRounds - 1) / (8 * kRounds))),
-                       dim3(256), 0, s, X, rows, nbc, ldx, Q, ldq, scales);
+    const dim3 grid((unsigned)((cols + 1024 * kRounds - 1) / (1024 * kRounds)),
+                    (unsigned)(rows < 65535 ? rows : 65535));
+    hipLaunchKernelGGL(quant_1x128<FMT>, grid, dim3(256), 0, s, X, rows, cols, ldx, Q, ldq, scales);
   } else {
     const int64_t nbc = cols / 128, nblk = (rows / 128) * nbc;
     hipLaunchKernelGGL(quant_128x128<FMT>, dim3((unsigned)nblk), dim3(256), 0, s, X, nbc, ldx, Q,
