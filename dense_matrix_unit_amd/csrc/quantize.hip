@@ -34,6 +34,8 @@
 //    signs.  MXFP4 (E2M1, emax = 2) packs the four codes of a lane into 16
 //    bits, element 2i in the low nibble; a NaN/Inf block's elements are
 //    signed zeros (E2M1 has no NaN).
+#include <hip/hip_ext.h>
+
 #include <mutex>
 
 #include "dmu_device.h"
@@ -388,33 +390,37 @@ TensorPasses tensor_passes(int64_t rows, int64_t cols, int64_t ldx, int64_t ldq)
   return t;
 }
 
+// The two per-tensor passes.  `done`, when given, is recorded by the second
+// kernel's own completion (hipExtLaunchKernelGGL's stop event): a separate
+// event record between two calls would put a gap of its own between them.
 template <int FMT>
 void launch_tensor(const float* X, int64_t rows, int64_t cols, int64_t ldx, uint8_t* Q,
                    int64_t ldq, float* scales, uint32_t* part, const TensorPasses& t,
-                   hipStream_t s) {
+                   hipStream_t s, hipEvent_t done) {
   const int64_t cols4 = cols / 4;
   if (t.flat) {
     const int64_t n4 = rows * cols4;
     hipLaunchKernelGGL(amax_flat, dim3((unsigned)t.nparts), dim3(kFlatThreads), 0, s,
                        (const f32x4_t*)X, n4, part);
-    hipLaunchKernelGGL(encode_flat<FMT>, dim3((unsigned)t.nparts), dim3(kFlatThreads), 0, s,
-                       (const f32x4_t*)X, n4, (uint32_t*)Q, (const uint32_t*)part, t.nparts,
-                       scales);
+    hipExtLaunchKernelGGL(encode_flat<FMT>, dim3((unsigned)t.nparts), dim3(kFlatThreads), 0, s,
+                          nullptr, done, 0, (const f32x4_t*)X, n4, (uint32_t*)Q,
+                          (const uint32_t*)part, t.nparts, scales);
   } else {
     hipLaunchKernelGGL(amax_rows, dim3((unsigned)t.nparts), dim3(256), 0, s, X, rows, cols4,
                        ldx, part);
-    hipLaunchKernelGGL(encode_rows<FMT>, dim3((unsigned)t.nparts), dim3(256), 0, s, X, rows,
-                       cols4, ldx, Q, ldq, (const uint32_t*)part, t.nparts, scales);
+    hipExtLaunchKernelGGL(encode_rows<FMT>, dim3((unsigned)t.nparts), dim3(256), 0, s, nullptr,
+                          done, 0, X, rows, cols4, ldx, Q, ldq, (const uint32_t*)part, t.nparts,
+                          scales);
   }
 }
 
 template <int FMT>
 hipError_t launch_fmt(const float* X, int64_t rows, int64_t cols, int64_t ldx, int64_t br,
                       int64_t bc, uint8_t* Q, int64_t ldq, float* scales, uint32_t* part,
-                      hipStream_t s) {
+                      hipStream_t s, hipEvent_t done = nullptr) {
   if (br == rows && bc == cols) {
     launch_tensor<FMT>(X, rows, cols, ldx, Q, ldq, scales, part,
-                       tensor_passes(rows, cols, ldx, ldq), s);
+                       tensor_passes(rows, cols, ldx, ldq), s, done);
   } else if (br == 1 && bc == 128) {
     const dim3 grid((unsigned)((cols + 1024 * kRounds - 1) / (1024 * kRounds)),
                     (unsigned)(rows < 65535 ? rows : 65535));
@@ -475,7 +481,8 @@ int device_of(hipStream_t s, hipError_t* e) {
 // kQuantizeScratchSlots slots per GPU, allocated on the first per-tensor call
 // on that GPU and kept until the process ends.  Calls on different streams
 // would otherwise share it concurrently, so every call first makes its
-// stream wait for the previous call's completion event, then records its own.
+// stream wait for the previous call's completion event; its own second pass
+// records that event when it completes.
 hipError_t launch_quantize_fp8_tensor_ws(const float* X, int64_t rows, int64_t cols, int64_t ldx,
                                          int fmt, uint8_t* Q, int64_t ldq, float* scales,
                                          hipStream_t s) {
@@ -498,7 +505,7 @@ hipError_t launch_quantize_fp8_tensor_ws(const float* X, int64_t rows, int64_t c
     if ((e = hipGetDevice(&cur)) != hipSuccess) return e;
     if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
     e = hipMalloc((void**)&w.slots, kQuantizeScratchSlots * sizeof(uint32_t));
-    if (e == hipSuccess) e = hipEventCreateWithFlags(&w.done, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreate(&w.done);
     if (cur != dev) {
       const hipError_t e2 = hipSetDevice(cur);
       if (e == hipSuccess) e = e2;
@@ -512,9 +519,9 @@ hipError_t launch_quantize_fp8_tensor_ws(const float* X, int64_t rows, int64_t c
   // a call on the stream that used the workspace last is ordered after it
   // already; another stream waits for that call's completion first
   if (w.used && s != w.last && (e = hipStreamWaitEvent(s, w.done, 0)) != hipSuccess) return e;
-  e = launch_quantize_fp8(X, rows, cols, ldx, fmt, rows, cols, Q, ldq, scales, w.slots, s);
+  e = fmt == 0 ? launch_fmt<0>(X, rows, cols, ldx, rows, cols, Q, ldq, scales, w.slots, s, w.done)
+               : launch_fmt<1>(X, rows, cols, ldx, rows, cols, Q, ldq, scales, w.slots, s, w.done);
   if (e != hipSuccess) return e;
-  if ((e = hipEventRecord(w.done, s)) != hipSuccess) return e;
   w.used = true;
   w.last = s;
   return hipSuccess;
