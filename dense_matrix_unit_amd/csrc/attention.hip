@@ -33,7 +33,11 @@
 //    alternate runs of 256 workgroup ids run at a higher wave priority, which
 //    keeps the two on a CU from running in step;
 //  * the copies of block t+2 go out right after the barrier that ends block
-//    t, one barrier per block.
+//    t, one barrier per block;
+//  * with the causal mask a workgroup takes two query blocks, the i-th from
+//    the end and the i-th from the start of its head, one after the other:
+//    their key counts add up to the same for every pair, so all workgroups
+//    carry the same work.
 #include <utility>
 
 #include "dmu_device.h"
@@ -154,40 +158,27 @@ attention_kernel(AttnArgs p) {
   // keeps them out of step: 2-4% faster across the measured shapes.
   if (((blockIdx.x >> 8) & 1) != 0) __builtin_amdgcn_s_setprio(2);
 
-  // Workgroup -> (head, query block).  Dispatch goes round robin over the 8
+  // Workgroup -> (head, work item).  Dispatch goes round robin over the 8
   // XCDs; give each XCD a contiguous run of ids, so the query blocks of one
-  // head (which read the same K and V) share an L2.  Causal: the longest
-  // query blocks of a head first.
+  // head (which read the same K and V) share an L2.  A work item is one query
+  // block; with the causal mask it is a pair, blocks nqb-1-pb and pb, whose
+  // key counts add up to the same for every pair, so every workgroup has the
+  // same work (an odd middle block runs alone).
   const int nqb = (int)((p.Sq + kBM - 1) / kBM);
+  const int npq = CAUSAL ? (nqb + 1) / 2 : nqb;  // work items per head
   int logical;
   {
     const int b = blockIdx.x, T = gridDim.x;
     const int x = b & 7, per = T >> 3, rem = T & 7;
     logical = __builtin_amdgcn_readfirstlane(x * per + (x < rem ? x : rem) + (b >> 3));
   }
-  const int64_t bh = logical / nqb;
-  int qb = logical - (int)(bh * nqb);
-  if constexpr (CAUSAL) qb = nqb - 1 - qb;
-  const int64_t q0 = (int64_t)qb * kBM;
-  const int64_t i0 = q0 + wave * 32;  // the wave's first query row
-  const int64_t off = p.Sk - p.Sq;    // causal: row i sees keys j <= i + off
-  int64_t kend = p.Sk;
-  if constexpr (CAUSAL) kend = min(p.Sk, q0 + kBM + off);
-  const int nblk = (int)((kend + kBN - 1) / kBN);
+  const int64_t bh = logical / npq;
+  const int pb = logical - (int)(bh * npq);
+  const int64_t off = p.Sk - p.Sq;  // causal: row i sees keys j <= i + off
 
   const uint16_t* Qh = p.Q + bh * p.hq;
   const uint16_t* Kh = p.K + bh * p.hk;
   const uint16_t* Vh = p.V + bh * p.hv;
-
-  // ---- Q rows of this wave, in registers: lane holds row i0 + l%32, d = 16s + 8h .. +7
-  u32x4_t qf[NSTEP];
-  {
-    const __amdgpu_buffer_rsrc_t rQ = make_rsrc(Qh, ((p.Sq - 1) * p.ldq + D) * 2);
-    const int64_t i = i0 + rl;
-    const uint32_t vo = i < p.Sq ? (uint32_t)(i * p.ldq * 2) + (uint32_t)hl * 16u : kOOB;
-#pragma unroll
-    for (int s = 0; s < NSTEP; ++s) qf[s] = buffer_load16(rQ, vo, (uint32_t)s * 32u);
-  }
 
   // ---- per-thread parts of the block copies (the block start moves the resource base)
   // K: copy unit u = it * 256 + tid -> half st = u / 512, row j, slot c of that
@@ -219,16 +210,6 @@ attention_kernel(AttnArgs p) {
     for (int it = 0; it < VCOPY; ++it)
       buffer_load_lds16(rV, (stage ? sV1 : sV0) + (it * kThreads + wave * 64) * 16, vvo[it], 0);
   };
-  // ---- prologue: block 0 staged, block 1 in flight
-  issue_block(0, 0);
-  if (nblk > 1) {
-    issue_block(1, 1);
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<KCOPY + VCOPY>());  // block 0 (and Q) in
-  } else {
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<0>());
-  }
-  stage_barrier();
-
   // Fragment reads.  Row 32t + l%32 of a K half-tile has
   // aswz = aswz(l%32) ^ (4t & 7), and the chunk a lane half h reads at d step
   // s is (2s + h) ^ aswz = ((2s ^ 4t) & 7) ^ (h ^ aswz(l%32)): one of four
@@ -248,165 +229,200 @@ attention_kernel(AttnArgs p) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
       voff[nt] = (4 * hl + (i >> 2)) * VROW +
-                 (((4 * nt + 2 * (g & 1) + ((i & 3) >> 1)) ^ vswz<D>(i >> 2)) << 4) + ((i & 1) << 3);
+                 (((4 * nt + 2 * (g & 1) + ((i & 3) >> 1)) ^ vswz<D>(i >> 2)) << 4) +
+                 ((i & 1) << 3);
   }
 
   const float c = p.scale * kLog2e;  // exp(scale * x) = exp2(c * x)
-  f32x16_t o[NT];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) o[nt] = f32x16_t{};
-  float m = kMinusBig;  // running row maximum of the raw scores (both lane halves agree)
-  float l = 0.0f;       // this lane's part of the running row sum
-  const int64_t irow = i0 + rl;
-  const int64_t lim_row = CAUSAL ? min(p.Sk - 1, irow + off) : p.Sk - 1;  // last key the row sees
 
-  // One block; ST (0 or 1) is its stage, a constant, so every LDS offset is.
-  auto blk = [&](int t, auto ST) __attribute__((always_inline)) {
-    constexpr int stage = decltype(ST)::value;
-    const int64_t k0 = (int64_t)t * kBN;
-    bool visible = true, masked = k0 + kBN > p.Sk;
-    if constexpr (CAUSAL) {
-      visible = k0 <= i0 + 31 + off;
-      masked = masked || k0 + kBN - 1 > i0 + off;
-    }
-    if (visible) {
-      // ---- scores S^T = K Q^T, two 32-key tiles
-      // (fragment reads run two MFMAs ahead of their use: a ring of three)
-      const uint8_t* kb = stage ? sK1 : sK0;
-      auto kread = [&](int x) __attribute__((always_inline)) {
-        const int s = x >> 1, jt = x & 1;  // d step, key tile
-        const int half = s >> 2, k = ((2 * s) ^ (4 * jt)) & 7;
-        return *(const u32x4_t*)(kb + foff[k >> 1] + half * (kBN * KROW) + jt * 32 * KROW);
-      };
-      f32x16_t sc[2] = {f32x16_t{}, f32x16_t{}};
-      u32x4_t kr[3];
-      kr[0] = kread(0);
-      kr[1] = kread(1);
+  const int npass = CAUSAL && 2 * pb + 1 < nqb ? 2 : 1;
+#pragma unroll 1
+  for (int pass = 0; pass < npass; ++pass) {
+    const int qb = CAUSAL ? (pass == 0 ? nqb - 1 - pb : pb) : pb;  // the longer block first
+    const int64_t q0 = (int64_t)qb * kBM;
+    const int64_t i0 = q0 + wave * 32;  // the wave's first query row
+    int64_t kend = p.Sk;
+    if constexpr (CAUSAL) kend = min(p.Sk, q0 + kBM + off);
+    const int nblk = (int)((kend + kBN - 1) / kBN);
+    if (pass > 0) __syncthreads();  // every wave has read its output staging back
+
+    // ---- Q rows of this wave, in registers: lane holds row i0 + l%32, d = 16s + 8h .. +7
+    u32x4_t qf[NSTEP];
+    {
+      const __amdgpu_buffer_rsrc_t rQ = make_rsrc(Qh, ((p.Sq - 1) * p.ldq + D) * 2);
+      const int64_t i = i0 + rl;
+      const uint32_t vo = i < p.Sq ? (uint32_t)(i * p.ldq * 2) + (uint32_t)hl * 16u : kOOB;
 #pragma unroll
-      for (int x = 0; x < 2 * NSTEP; ++x) {
-        if (x + 2 < 2 * NSTEP) kr[(x + 2) % 3] = kread(x + 2);
-        __builtin_amdgcn_sched_barrier(0);
-        sc[x & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kr[x % 3]),
-                                                            __builtin_bit_cast(bf16x8_t, qf[x >> 1]),
-                                                            sc[x & 1], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
+      for (int s = 0; s < NSTEP; ++s) qf[s] = buffer_load16(rQ, vo, (uint32_t)s * 32u);
+    }
+
+    // ---- prologue: block 0 staged, block 1 in flight
+    issue_block(0, 0);
+    if (nblk > 1) {
+      issue_block(1, 1);
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<KCOPY + VCOPY>());  // block 0 (and Q) in
+    } else {
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<0>());
+    }
+    stage_barrier();
+
+    f32x16_t o[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) o[nt] = f32x16_t{};
+    float m = kMinusBig;  // running row maximum of the raw scores (both lane halves agree)
+    float l = 0.0f;       // this lane's part of the running row sum
+    const int64_t irow = i0 + rl;
+    const int64_t lim_row = CAUSAL ? min(p.Sk - 1, irow + off) : p.Sk - 1;  // last key the row sees
+
+    // One block; ST (0 or 1) is its stage, a constant, so every LDS offset is.
+    auto blk = [&](int t, auto ST) __attribute__((always_inline)) {
+      constexpr int stage = decltype(ST)::value;
+      const int64_t k0 = (int64_t)t * kBN;
+      bool visible = true, masked = k0 + kBN > p.Sk;
+      if constexpr (CAUSAL) {
+        visible = k0 <= i0 + 31 + off;
+        masked = masked || k0 + kBN - 1 > i0 + off;
       }
-      // ---- keys past the end, or past the row's causal limit
-      if (masked) {
-        const int lim = (int)max(min(lim_row - k0, (int64_t)kBN), (int64_t)-1);
+      if (visible) {
+        // ---- scores S^T = K Q^T, two 32-key tiles
+        // (fragment reads run two MFMAs ahead of their use: a ring of three)
+        const uint8_t* kb = stage ? sK1 : sK0;
+        auto kread = [&](int x) __attribute__((always_inline)) {
+          const int s = x >> 1, jt = x & 1;  // d step, key tile
+          const int half = s >> 2, k = ((2 * s) ^ (4 * jt)) & 7;
+          return *(const u32x4_t*)(kb + foff[k >> 1] + half * (kBN * KROW) + jt * 32 * KROW);
+        };
+        f32x16_t sc[2] = {f32x16_t{}, f32x16_t{}};
+        u32x4_t kr[3];
+        kr[0] = kread(0);
+        kr[1] = kread(1);
+#pragma unroll
+        for (int x = 0; x < 2 * NSTEP; ++x) {
+          if (x + 2 < 2 * NSTEP) kr[(x + 2) % 3] = kread(x + 2);
+          __builtin_amdgcn_sched_barrier(0);
+          sc[x & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8_t, kr[x % 3]), __builtin_bit_cast(bf16x8_t, qf[x >> 1]),
+              sc[x & 1], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        // ---- keys past the end, or past the row's causal limit
+        if (masked) {
+          const int lim = (int)max(min(lim_row - k0, (int64_t)kBN), (int64_t)-1);
+#pragma unroll
+          for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              const int j = jt * 32 + (v >> 2) * 8 + hl * 4 + (v & 3);
+              if (j > lim) sc[jt][v] = -__builtin_huge_valf();
+            }
+        }
+        // ---- online softmax: row maximum over both lane halves
+        float mx = sc[0][0];
 #pragma unroll
         for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int j = jt * 32 + (v >> 2) * 8 + hl * 4 + (v & 3);
-            if (j > lim) sc[jt][v] = -__builtin_huge_valf();
+          for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sc[jt][v]);
+        mx = half_max(mx);
+        const bool move = (mx - m) * c > kRescaleSlack;  // false for an all-masked row (-inf)
+        const float mnew = move ? mx : m;
+        const float alpha = move ? __builtin_amdgcn_exp2f((m - mnew) * c) : 1.0f;
+        m = mnew;
+        const float mc = mnew * c;
+        uint32_t pk[2][8];
+        float rs = 0.0f;
+#pragma unroll
+        for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+          for (int w = 0; w < 8; ++w) {
+            const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[jt][2 * w], c, -mc));
+            const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[jt][2 * w + 1], c, -mc));
+            rs += p0 + p1;
+            pk[jt][w] = pack_bf16(p0, p1);
           }
-      }
-      // ---- online softmax: row maximum over both lane halves
-      float mx = sc[0][0];
+        l = l * alpha + rs;
+        if (__builtin_amdgcn_ballot_w64(move)) {
 #pragma unroll
-      for (int jt = 0; jt < 2; ++jt)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sc[jt][v]);
-      mx = half_max(mx);
-      const bool move = (mx - m) * c > kRescaleSlack;  // false for an all-masked row (-inf)
-      const float mnew = move ? mx : m;
-      const float alpha = move ? __builtin_amdgcn_exp2f((m - mnew) * c) : 1.0f;
-      m = mnew;
-      const float mc = mnew * c;
-      uint32_t pk[2][8];
-      float rs = 0.0f;
-#pragma unroll
-      for (int jt = 0; jt < 2; ++jt)
-#pragma unroll
-        for (int w = 0; w < 8; ++w) {
-          const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[jt][2 * w], c, -mc));
-          const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[jt][2 * w + 1], c, -mc));
-          rs += p0 + p1;
-          pk[jt][w] = pack_bf16(p0, p1);
+          for (int nt = 0; nt < NT; ++nt) o[nt] *= alpha;
         }
-      l = l * alpha + rs;
-      if (__builtin_amdgcn_ballot_w64(move)) {
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) o[nt] *= alpha;
+        // ---- O^T += V^T P^T, four 16-key steps
+        // (reads two MFMAs ahead, each fragment two transposing reads)
+        const uint8_t* vb = stage ? sV1 : sV0;
+        auto vread = [&](auto X) __attribute__((always_inline)) {
+          constexpr int x = decltype(X)::value;
+          constexpr int ks = x / NT, nt = x % NT;  // key step, output tile
+          const uint8_t* q = vb + voff[nt] + ks * 16 * VROW;
+          const uint2 lo = read_tr16(q), hi = read_tr16(q + 8 * VROW);
+          return u32x4_t{lo.x, lo.y, hi.x, hi.y};
+        };
+        u32x4_t vq[3];
+        vq[0] = vread(Idx<0>{});
+        vq[1] = vread(Idx<1>{});
+        unroll_n<4 * NT>([&](auto X) __attribute__((always_inline)) {
+          constexpr int x = decltype(X)::value;
+          if constexpr (x + 2 < 4 * NT) vq[(x + 2) % 3] = vread(Idx<x + 2>{});
+          constexpr int ks = x / NT, nt = x % NT, jt = ks >> 1, w0 = (ks & 1) * 4;
+          const u32x4_t pf = {pk[jt][w0], pk[jt][w0 + 1], pk[jt][w0 + 2], pk[jt][w0 + 3]};
+          __builtin_amdgcn_sched_barrier(0);
+          o[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vq[x % 3]),
+                                                          __builtin_bit_cast(bf16x8_t, pf), o[nt],
+                                                          0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        });
       }
-      // ---- O^T += V^T P^T, four 16-key steps
-      // (reads two MFMAs ahead, each fragment two transposing reads)
-      const uint8_t* vb = stage ? sV1 : sV0;
-      auto vread = [&](auto X) __attribute__((always_inline)) {
-        constexpr int x = decltype(X)::value;
-        constexpr int ks = x / NT, nt = x % NT;  // key step, output tile
-        const uint8_t* q = vb + voff[nt] + ks * 16 * VROW;
-        const uint2 lo = read_tr16(q), hi = read_tr16(q + 8 * VROW);
-        return u32x4_t{lo.x, lo.y, hi.x, hi.y};
-      };
-      u32x4_t vq[3];
-      vq[0] = vread(Idx<0>{});
-      vq[1] = vread(Idx<1>{});
-      unroll_n<4 * NT>([&](auto X) __attribute__((always_inline)) {
-        constexpr int x = decltype(X)::value;
-        if constexpr (x + 2 < 4 * NT) vq[(x + 2) % 3] = vread(Idx<x + 2>{});
-        constexpr int ks = x / NT, nt = x % NT, jt = ks >> 1, w0 = (ks & 1) * 4;
-        const u32x4_t pf = {pk[jt][w0], pk[jt][w0 + 1], pk[jt][w0 + 2], pk[jt][w0 + 3]};
-        __builtin_amdgcn_sched_barrier(0);
-        o[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vq[x % 3]),
-                                                        __builtin_bit_cast(bf16x8_t, pf), o[nt], 0,
-                                                        0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-      });
+      // ---- block t+1's copies are in; then start block t+2.  The wait is
+      // unconditional (nothing is in flight after the last block), so the
+      // compiler knows no copy is outstanding past the barrier but those
+      // issued after it, into the stage the next block does not read.
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<0>());
+      stage_barrier();  // block t's stage is free; block t+1's is complete
+      if (t + 2 < nblk) issue_block(t + 2, stage);
+    };
+    // Blocks in pairs, so that every pass round the loop has run both stages:
+    // the copies in flight at the top of the loop are then only those into
+    // stage 1, which the compiler can see (an odd last block runs after it).
+    int t = 0;
+    for (; t + 1 < nblk; t += 2) {
+      blk(t, Idx<0>{});
+      blk(t + 1, Idx<1>{});
     }
-    // ---- block t+1's copies are in; then start block t+2.  The wait is
-    // unconditional (nothing is in flight after the last block), so the
-    // compiler knows no copy is outstanding past the barrier but those
-    // issued after it, into the stage the next block does not read.
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<0>());
-    stage_barrier();  // block t's stage is free; block t+1's is complete
-    if (t + 2 < nblk) issue_block(t + 2, stage);
-  };
-  // Blocks in pairs, so that every pass round the loop has run both stages:
-  // the copies in flight at the top of the loop are then only those into
-  // stage 1, which the compiler can see (an odd last block runs after it).
-  int t = 0;
-  for (; t + 1 < nblk; t += 2) {
-    blk(t, Idx<0>{});
-    blk(t + 1, Idx<1>{});
-  }
-  if (t < nblk) blk(t, Idx<0>{});
+    if (t < nblk) blk(t, Idx<0>{});
 
-  // ---- epilogue: O / l, rounded to BF16, staged per wave and stored in row segments
-  l = half_sum(l);
-  const float inv = 1.0f / l;
-  {
-    constexpr int RB = D * 2;       // staged row bytes
-    constexpr int UPR = RB / 16;    // 16-byte units per row
-    constexpr int RPI = 64 / UPR;   // rows per read instruction
-    uint8_t* wb = (wave < 2 ? sK0 : sK1) + (wave & 1) * OB;
+    // ---- epilogue: O / l, rounded to BF16, staged per wave and stored in row segments
+    l = half_sum(l);
+    const float inv = 1.0f / l;
+    {
+      constexpr int RB = D * 2;       // staged row bytes
+      constexpr int UPR = RB / 16;    // 16-byte units per row
+      constexpr int RPI = 64 / UPR;   // rows per read instruction
+      uint8_t* wb = (wave < 2 ? sK0 : sK1) + (wave & 1) * OB;
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
+      for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const f32x4_t x = {o[nt][4 * q] * inv, o[nt][4 * q + 1] * inv, o[nt][4 * q + 2] * inv,
-                           o[nt][4 * q + 3] * inv};
-        const int u = nt * 4 + q;  // unit of columns 8u .. 8u+7; this lane half's are 8u + 4h ..
-        *(uint2*)(wb + rl * RB + ((u ^ (rl & (UPR - 1))) << 4) + hl * 8) =
-            make_uint2(pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3]));
+        for (int q = 0; q < 4; ++q) {
+          const f32x4_t x = {o[nt][4 * q] * inv, o[nt][4 * q + 1] * inv, o[nt][4 * q + 2] * inv,
+                             o[nt][4 * q + 3] * inv};
+          const int u = nt * 4 + q;  // unit of columns 8u .. 8u+7; this lane half's are 8u + 4h ..
+          *(uint2*)(wb + rl * RB + ((u ^ (rl & (UPR - 1))) << 4) + hl * 8) =
+              make_uint2(pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3]));
+        }
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<63>());  // own region: no barrier
+      uint16_t* Oh = p.O + bh * p.ho;
+#pragma unroll
+      for (int it = 0; it < 32 / RPI; ++it) {
+        const int r = it * RPI + lane / UPR, u = lane % UPR;
+        const u32x4_t v = *(const u32x4_t*)(wb + r * RB + ((u ^ (r & (UPR - 1))) << 4));
+        const int64_t i = i0 + r;
+        if (i < p.Sq) *(u32x4_t*)(Oh + i * p.ldo + u * 8) = v;
       }
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<63>());  // own region: no barrier
-    uint16_t* Oh = p.O + bh * p.ho;
-#pragma unroll
-    for (int it = 0; it < 32 / RPI; ++it) {
-      const int r = it * RPI + lane / UPR, u = lane % UPR;
-      const u32x4_t v = *(const u32x4_t*)(wb + r * RB + ((u ^ (r & (UPR - 1))) << 4));
-      const int64_t i = i0 + r;
-      if (i < p.Sq) *(u32x4_t*)(Oh + i * p.ldo + u * 8) = v;
     }
-  }
-  if (p.lse && hl == 0 && irow < p.Sq) p.lse[bh * p.Sq + irow] = m * p.scale + __logf(l);
+    if (p.lse && hl == 0 && irow < p.Sq) p.lse[bh * p.Sq + irow] = m * p.scale + __logf(l);
+  }  // pass
 }
 
 template <int D, bool CAUSAL>
 hipError_t launch(const AttnArgs& a, hipStream_t s) {
-  const int64_t wgs = (a.Sq + kBM - 1) / kBM * a.BH;
+  const int64_t nqb = (a.Sq + kBM - 1) / kBM;
+  const int64_t wgs = (CAUSAL ? (nqb + 1) / 2 : nqb) * a.BH;
   hipLaunchKernelGGL((attention_kernel<D, CAUSAL>), dim3((unsigned)wgs), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }

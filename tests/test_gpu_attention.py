@@ -72,10 +72,12 @@ def run(Q, K, V, scale, causal, with_lse=True):
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("shape", [(1, 128, 128, 128), (2, 200, 300, 128), (3, 65, 130, 64),
                                    (2, 256, 256, 64), (1, 1, 1, 128), (1, 3, 700, 128),
-                                   (2, 129, 129, 128)])
+                                   (2, 129, 129, 128), (2, 640, 700, 128)])
 def test_attention_matches_oracle(shape, causal):
     # ragged query blocks (Sq % 128) and key blocks (Sk % 64), one-row and
-    # one-key heads, Sq < Sk under the causal mask
+    # one-key heads, Sq < Sk under the causal mask; with the mask a workgroup
+    # takes a pair of query blocks, and an odd count leaves a middle block
+    # alone (Sq = 300, 640)
     heads, Sq, Sk, d = shape
     Q, K, V = bf16((heads, Sq, d), 1), bf16((heads, Sk, d), 2), bf16((heads, Sk, d), 3)
     scale = 1.0 / np.sqrt(d)
