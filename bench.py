@@ -17,7 +17,8 @@ kernel, the metric's other half, gets the same protocol in its leg.  The other w
 block-scaled 8192x7168x7168 GEMM and its quantizers, the LLM-shaped sweep,
 256^3) are timed the same way in the same process and reported under "legs",
 with "mfma_ceiling": the sustained matrix-unit rate with no memory traffic,
-for N(0,1) and for constant operands.
+for N(0,1) and for constant operands, and "bf16_4096_operand_data": the
+headline kernel itself on N(0,1), all-ones and all-zero operands.
 
 Operands are resident in HBM before timing starts.  The 4096^3 legs rotate
 over several operand copies whose total exceeds the 256 MB Infinity Cache, so
@@ -743,6 +744,25 @@ def main():
                                                   out_f32=True, seed_dist="uniform")
         log("256^3: %s" % legs["bf16_256_f32out"])
 
+    if want("bf16_4096_operand_data"):
+        # the headline kernel, unchanged, on operands that draw less power per
+        # MFMA: the same instructions and memory traffic, a different clock
+        for dist in ("normal", "ones", "zeros"):
+            fill = {"normal": None, "ones": 1.0, "zeros": 0.0}[dist]
+            if fill is None:
+                Ad, Bd = b.normal_bf16((4096, 4096), 1), b.normal_bf16((4096, 4096), 2)
+            else:
+                Ad = torch.full((4096, 4096), fill, dtype=torch.bfloat16, device="cuda")
+                Bd = Ad.clone()
+            As, Bs = b.copies(Ad, 6), b.copies(Bd, 6)
+            o = torch.empty((4096, 4096), dtype=torch.bfloat16, device="cuda")
+            t_d = time_launches(torch, lambda i: dmu.gemm_bf16(As[i % 6], Bs[i % 6], o,
+                                                                dmu.B_COL_MAJOR), S, W)
+            legs["bf16_4096_operands_" + dist] = b.report(t_d, 2.0 * 4096 ** 3,
+                                                          2.0 * 3 * 4096 ** 2,
+                                                          PEAK_BF16_TFLOPS, 6)
+            log("bf16 4096 operands %s: %s" % (dist, legs["bf16_4096_operands_" + dist]))
+            del As, Bs, o, Ad, Bd
     if want("mfma_ceiling"):
         legs["mfma_ceiling"] = b.mfma_ceiling_leg(S4, W4)
         log("mfma ceiling (no memory traffic): %s" % legs["mfma_ceiling"])
