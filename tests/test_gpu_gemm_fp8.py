@@ -166,3 +166,44 @@ def test_promotion_every_128_k_vs_fast_accumulation(K):
     e_fast, e_prom = oracle.rel_rms(Dfast, Dref), oracle.rel_rms(Dprom, Dref2)
     print("E4M3 K=%d rel-RMS from the sums: fast %.3e, promoted every 128 K %.3e" % (K, e_fast, e_prom))
     assert e_prom > e_fast / 4 and e_prom < e_fast * 4
+
+
+@pytest.mark.parametrize("K", [256, 4096, 65536])
+def test_promotion_interval_64_128_256(K):
+    # Promotion every P K for P = 64, 128 and 256 (the vidyal.ai page, Step 5,
+    # promotes every 64), assembled from the library's own products: each K
+    # chunk of P is one gemm_fp8_scaled call with unit scales, whose MFMA chain
+    # starts from zero, so its FP32 output is the chunk's partial sum exactly;
+    # the partial sums are added in K order in FP32 and scaled once at the end.
+    # That is the arithmetic of a kernel that promotes every P K.  Every
+    # interval must meet the bound, with the same error as no promotion.
+    Af = wl.normal((256, K), wl.SEED_A)
+    Bf = wl.normal((256, K), wl.SEED_B)
+    A, sa = quant(Af, dmu.E4M3)
+    B, sb = quant(Bf, dmu.E4M3)
+    Dref, S = oracle.gemm_fp8(A, B, 0, 0, sa, sb, dmu.SCALE_TENSOR)
+
+    def within(D, what):
+        ok, _ = within_fp8_bound(D, Dref, S, False,
+                                 lambda r: fp8_loss(A, B, 0, 0, sa, sb, dmu.SCALE_TENSOR, r))
+        assert ok.all(), "%s, K=%d: %d outside the bound" % (what, K, (~ok).sum())
+        return oracle.rel_rms(D, Dref)
+
+    Dfast = run_fp8(A, B, 0, 0, sa, sb, dmu.SCALE_TENSOR, torch.float32)
+    e_fast = within(Dfast, "fast")
+    dA, dB = padded(A, 16), padded(B, 16)
+    one = dev(np.ones(1, np.float32))
+    alpha = float(np.float32(sa[0]) * np.float32(sb[0]))
+    part = torch.empty((256, 256), dtype=torch.float32, device="cuda")
+    line = ["E4M3 K=%d rel-RMS from the sums: fast %.3e" % (K, e_fast)]
+    for P in (64, 128, 256):
+        acc = torch.zeros((256, 256), dtype=torch.float32, device="cuda")
+        for k0 in range(0, K, P):
+            dmu.gemm_fp8_scaled(dA[:, k0:k0 + P], dB[:, k0:k0 + P], one, one, part, 0, 0,
+                                dmu.SCALE_TENSOR)
+            acc += part
+        D = (acc * alpha).cpu().numpy().astype(np.float64)
+        e = within(D, "promotion every %d K" % P)
+        line.append("every %d K %.3e (%d elements differ from fast)" % (P, e, (D != Dfast).sum()))
+        assert e_fast / 4 < e < e_fast * 4
+    print(", ".join(line))
