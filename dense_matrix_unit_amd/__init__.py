@@ -77,6 +77,7 @@ SYMBOLS = {
     "dmu_probe_gemm_bf16_layout": (_I, [_I, _P, _I64, _P, _I64, _P, _I64, _I64, _I64, _I64, _P]),
     "dmu_probe_mfma_rate": (_I, [_I, _P, _I, _I, _P, _P]),
     "dmu_probe_cvt_fp8": (_I, [_P, _I64, _I, _I, _P, _P]),
+    "dmu_probe_quantize_tensor_resident": (_I, [_P, _I64, _I64, _I, _P, _P, _I, _P]),
     "dmu_probe_lds_tr16": (_I, [_P, _P, _P, _P]),
     "dmu_probe_mfma_mx": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P]),
 }
@@ -540,6 +541,25 @@ def probe_cvt_fp8(x, q, fmt: int = E4M3, clamp: int = 1, stream=None):
                                           _dev_ptr(q, "q"), _stream(stream))
     _check("dmu_probe_cvt_fp8", rc)
     return q
+
+
+def probe_quantize_tensor_resident(X, Q, scale, fmt: int = E4M3, spin_limit: int = 0,
+                                   stream=None):
+    """Per-tensor quantize_fp8 of a contiguous X (float32 [rows, cols]) into
+    Q (uint8, same shape) and scale (one float32) through the one-pass kernel
+    with the given wait bound; see include/dmu_probe.h."""
+    torch = _torch()
+    _check_dtype(X, (torch.float32,), "X")
+    _check_dtype(Q, (torch.uint8,), "Q")
+    _check_dtype(scale, (torch.float32,), "scale")
+    if X.dim() != 2 or tuple(Q.shape) != tuple(X.shape) or not (X.is_contiguous() and
+                                                                Q.is_contiguous()):
+        raise ValueError("X and Q: contiguous, same 2-D shape")
+    rc = load_library().dmu_probe_quantize_tensor_resident(
+        _dev_ptr(X, "X"), X.shape[0], X.shape[1], fmt, _dev_ptr(Q, "Q"),
+        _dev_ptr(scale, "scale"), spin_limit, _stream(stream))
+    _check("dmu_probe_quantize_tensor_resident", rc)
+    return Q, scale
 
 
 def probe_lds_tr16(src, offsets, out, stream=None):

@@ -434,6 +434,18 @@ int dmu_probe_lds_tr16(const uint16_t* src, const uint32_t* offsets, uint16_t* o
   return finish(dmu::launch_probe_tr16(src, offsets, out, (hipStream_t)stream));
 }
 
+int dmu_probe_quantize_tensor_resident(const float* X, int64_t rows, int64_t cols, int fmt,
+                                       uint8_t* Q, float* scale, int spin_limit, void* stream) {
+  const int rc = quantize_args(X, rows, cols, cols, fmt, rows, cols, Q, cols, scale);
+  if (rc) return rc;
+  if (spin_limit < 0) return DMU_ERR_INVALID_ARG;
+  (void)hipGetLastError();
+  const hipError_t e = dmu::launch_probe_quantize_resident(X, rows, cols, fmt, Q, scale,
+                                                           spin_limit, (hipStream_t)stream);
+  if (e == hipErrorInvalidValue) return DMU_ERR_UNSUPPORTED;
+  return finish(e);
+}
+
 int dmu_probe_cvt_fp8(const float* x, int64_t n, int fmt, int clamp, uint8_t* q, void* stream) {
   if (!x || !q || n < 2 || n % 2 || n > ((int64_t)1 << 31)) return DMU_ERR_INVALID_ARG;
   if ((fmt != 0 && fmt != 1) || (clamp != 0 && clamp != 1) || !aligned(x, 8))

@@ -87,16 +87,22 @@ hipError_t launch_quantize_mxfp4(const float* X, int64_t rows, int64_t cols, int
                                  hipStream_t s);
 hipError_t launch_quantize_mxfp8(const float* X, int64_t rows, int64_t cols, int64_t ldx, int fmt,
                                  uint8_t* Q, int64_t ldq, uint8_t* S, int64_t lds, hipStream_t s);
-// quantize_fp8: the per-tensor mode writes one uint32 amax partial per
-// pass-1 workgroup to `part` and reads them all in the second pass;
-// quantize_scratch_slots gives how many (at most 512 whatever the tensor's
-// size; 0 for block scales, which need no scratch).
+// quantize_fp8: the per-tensor mode uses a scratch of kQuantizeScratchSlots
+// + kQuantizeSyncSlots words at `part`.  The two-pass walk writes one uint32
+// amax partial per pass-1 workgroup to the first kQuantizeScratchSlots words
+// and reads them all in the second pass; quantize_scratch_slots gives how many
+// (at most 512 whatever the tensor's size; 0 for block scales, which need no
+// scratch).  The one-pass kernel for tensors its grid holds in registers
+// synchronises through the last kQuantizeSyncSlots words, which must be zero
+// before the first call on a scratch and which every call leaves zero.
 int64_t quantize_scratch_slots(int64_t rows, int64_t cols, int64_t ldx, int64_t ldq, int64_t br,
                                int64_t bc);
 hipError_t launch_quantize_fp8(const float* X, int64_t rows, int64_t cols, int64_t ldx, int fmt,
                                int64_t br, int64_t bc, uint8_t* Q, int64_t ldq, float* scales,
                                uint32_t* part, hipStream_t s);
-constexpr int64_t kQuantizeScratchSlots = 1024;  // slots of either scratch (4 KiB)
+constexpr int64_t kQuantizeScratchSlots = 1024;  // pass-1 partial slots of either scratch
+constexpr int64_t kQuantizeSyncSlots = 3072;     // the one-pass kernel's words after them
+constexpr int64_t kQuantizeScratchWords = kQuantizeScratchSlots + kQuantizeSyncSlots;  // 16 KiB
 constexpr int kMaxDevices = 64;
 // Per-tensor quantize_fp8 on the library's workspace of the stream's GPU
 // (allocated on first use, calls on different streams ordered by an event).
@@ -104,9 +110,14 @@ hipError_t launch_quantize_fp8_tensor_ws(const float* X, int64_t rows, int64_t c
                                          int fmt, uint8_t* Q, int64_t ldq, float* scales,
                                          hipStream_t s);
 // The allocation-free variant's scratch: a static device array of
-// kQuantizeScratchSlots partials per GPU; its address on the stream's GPU
+// kQuantizeScratchWords words per GPU; its address on the stream's GPU
 // (looked up once per device, with that device current).
 hipError_t quantize_scratch_address(hipStream_t s, uint32_t** out);
+// The one-pass per-tensor kernel with a chosen wait bound (diagnostic);
+// hipErrorInvalidValue when the tensor does not take the one-pass kernel.
+hipError_t launch_probe_quantize_resident(const float* X, int64_t rows, int64_t cols, int fmt,
+                                          uint8_t* Q, float* scale, int spin_limit,
+                                          hipStream_t s);
 
 hipError_t launch_probe_mfma(int kind, int fa, int fb, const void* A, const void* B,
                              const float* C, float* D, int count, hipStream_t s);

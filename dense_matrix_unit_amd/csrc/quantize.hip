@@ -36,12 +36,17 @@
 //    signed zeros (E2M1 has no NaN).
 #include <hip/hip_ext.h>
 
+#include <atomic>
 #include <mutex>
 
 #include "dmu_device.h"
 #include "dmu_internal.h"
 
 namespace dmu {
+
+int device_of(hipStream_t s, hipError_t* e);
+int compute_units(hipStream_t s);
+
 namespace {
 
 __device__ __forceinline__ uint32_t abs_bits(float x) { return __float_as_uint(x) & 0x7FFFFFFFu; }
@@ -178,6 +183,180 @@ __global__ __launch_bounds__(kFlatThreads) void encode_flat(const f32x4_t* X, in
     for (int u = 0; u < kUnroll; ++u) Q4[i + u * stride] = encode4<FMT>(v[u], m);
   }
   for (; i < n4; i += stride) Q4[i] = encode4<FMT>(__builtin_nontemporal_load(X + i), m);
+}
+
+// One pass for a contiguous tensor that the grid can hold in registers
+// (kResident float4 per thread, the grid at most one workgroup per compute
+// unit).  Each workgroup loads its share once and keeps it, stores the max of
+// its |x| bit patterns in its own 64-bit slot tagged with the call's epoch,
+// and counts itself in: first in the counter of its group of kGroupSize
+// workgroups, and the group's last arrival then in the top counter (two
+// short chains of increments on one address each instead of one as long as
+// the grid).  The workgroup that completes the top count reads every slot,
+// waiting for each to carry this call's tag, takes the tensor's amax, stores
+// the scale, advances the epoch, and releases each other workgroup by
+// swapping its state word from kWaiting (0) to kReleased with the amax in the
+// upper half; each then encodes the share it still holds.  X is read once.
+// Nothing that passes between workgroups relies on the order of two
+// different words becoming visible: the amax travels in tagged slots and in
+// the state words, so no fence is needed (an agent-scope fence writes back
+// and invalidates the XCD's L2; one per arrival cost about 3 us here), and
+// the counters take plain increments (compare-and-swap loops on one word,
+// contended by 32 workgroups, cost more than the fences).
+//
+// The grid is sized so that every workgroup can be resident at once, but
+// nothing guarantees it (another kernel may hold compute units).  So every
+// wait is bounded: a workgroup that sees no release after spin_limit polls
+// swaps kWaiting for kGaveUp and exits, and the last arrival, whose swap then
+// fails, encodes that workgroup's share from X itself.  Each state word has
+// one swap that succeeds, so every share is encoded exactly once, and every
+// workgroup exits.  A slot whose tag never arrives (which the counters rule
+// out) would count as NaN, so such a failure could not pass unseen.
+//
+// The sync area is zero before the first call.  Every call leaves the
+// counters and state words zero (each counter is cleared by the arrival that
+// completes it, a released workgroup clears its own state word, the last
+// arrival those of the workgroups that gave up) and the epoch advanced; a
+// slot's tag is the epoch plus one, so the zeroed slots never match.  32-bit
+// word offsets: top counter 0, epoch 1, group g's counter kSyncGroup + 16 g
+// (64 bytes apart), workgroup w's slot kSyncSlot + 2 w and state
+// kSyncState + 2 w.
+constexpr int kResident = 16;           // float4 per thread held in registers
+constexpr int kGroupSize = 32;          // workgroups per first-level counter
+constexpr int kMaxResidentGrid = 512;
+constexpr int kSyncGroup = 16;
+constexpr int kSyncSlot = kSyncGroup + 16 * (kMaxResidentGrid / kGroupSize);
+constexpr int kSyncState = kSyncSlot + 2 * kMaxResidentGrid;
+static_assert(kSyncSlot % 2 == 0 && kSyncState % 2 == 0 &&
+                  kSyncState + 2 * kMaxResidentGrid <= kQuantizeSyncSlots,
+              "sync area");
+constexpr uint64_t kWaiting = 0, kReleased = 2, kGaveUp = 3;
+constexpr int kSpinLimit = 4096;        // polls before a waiting workgroup gives up
+constexpr int kSlotPolls = 1 << 16;     // polls of one slot by the last arrival
+
+template <int FMT>
+__global__ __launch_bounds__(kFlatThreads) void quant_tensor_resident(const f32x4_t* X,
+                                                                      int64_t n4, uint32_t* Q4,
+                                                                      uint32_t* sync,
+                                                                      float* scales,
+                                                                      int spin_limit) {
+  constexpr int kScope = __HIP_MEMORY_SCOPE_AGENT;
+  uint32_t epoch = 0;
+  if (threadIdx.x == 0) epoch = __hip_atomic_load(&sync[1], __ATOMIC_RELAXED, kScope);
+  const int64_t stride = (int64_t)gridDim.x * kFlatThreads;
+  const int64_t i0 = (int64_t)blockIdx.x * kFlatThreads + threadIdx.x;
+  f32x4_t v[kResident];
+#pragma unroll
+  for (int u = 0; u < kResident; ++u) {
+    const int64_t i = i0 + u * stride;
+    v[u] = i < n4 ? __builtin_nontemporal_load(X + i) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  uint32_t mx = 0;
+#pragma unroll
+  for (int u = 0; u < kResident; ++u) mx = max(mx, amax4(v[u]));
+  mx = block_max<kFlatThreads>(mx);
+
+  uint64_t* slot = (uint64_t*)(sync + kSyncSlot);
+  uint64_t* state = (uint64_t*)(sync + kSyncState);
+  __shared__ uint32_t s_last, s_run, s_amax, s_ngone, s_tag;
+  __shared__ uint32_t s_gone[kMaxResidentGrid];
+  if (threadIdx.x == 0) {
+    const uint32_t w = blockIdx.x, grid = gridDim.x, tag = epoch + 1;
+    __hip_atomic_store(&slot[w], ((uint64_t)tag << 32) | mx, __ATOMIC_RELAXED, kScope);
+    const uint32_t g = w / kGroupSize, in_g = min(grid - g * kGroupSize, (uint32_t)kGroupSize);
+    uint32_t* gc = &sync[kSyncGroup + 16 * g];
+    bool last = false;
+    if (__hip_atomic_fetch_add(gc, 1u, __ATOMIC_RELAXED, kScope) == in_g - 1) {
+      __hip_atomic_store(gc, 0u, __ATOMIC_RELAXED, kScope);
+      const uint32_t groups = (grid + kGroupSize - 1) / kGroupSize;
+      last = __hip_atomic_fetch_add(&sync[0], 1u, __ATOMIC_RELAXED, kScope) == groups - 1;
+      if (last) {
+        __hip_atomic_store(&sync[0], 0u, __ATOMIC_RELAXED, kScope);
+        __hip_atomic_store(&sync[1], tag, __ATOMIC_RELAXED, kScope);  // the next call's epoch
+      }
+    }
+    s_last = last;
+    s_tag = tag;
+    s_ngone = 0;
+  }
+  __syncthreads();
+  if (s_last) {
+    // every workgroup has counted itself in after storing its slot; a slot
+    // still showing an older tag is a store not yet visible here
+    uint32_t a = 0;
+    for (uint32_t w = threadIdx.x; w < gridDim.x; w += kFlatThreads) {
+      uint64_t sv = __hip_atomic_load(&slot[w], __ATOMIC_RELAXED, kScope);
+      for (int it = 0; it < kSlotPolls && (uint32_t)(sv >> 32) != s_tag; ++it) {
+        __builtin_amdgcn_s_sleep(1);
+        sv = __hip_atomic_load(&slot[w], __ATOMIC_RELAXED, kScope);
+      }
+      a = max(a, (uint32_t)(sv >> 32) == s_tag ? (uint32_t)sv : 0x7FC00000u);
+    }
+    a = block_max<kFlatThreads>(a);
+    if (threadIdx.x == 0) {
+      scales[0] = scale_from_amax<FMT>(__uint_as_float(a));
+      s_amax = a;  // read after the barrier below
+    }
+    const uint64_t rel = kReleased | ((uint64_t)a << 32);
+    for (uint32_t w = threadIdx.x; w < gridDim.x; w += kFlatThreads) {
+      if (w == blockIdx.x) continue;
+      uint64_t expect = kWaiting;
+      if (!__hip_atomic_compare_exchange_strong(&state[w], &expect, rel, __ATOMIC_RELAXED,
+                                                __ATOMIC_RELAXED, kScope)) {
+        // it gave up and exited: its share is encoded here
+        s_gone[atomicAdd(&s_ngone, 1u)] = w;
+        __hip_atomic_store(&state[w], kWaiting, __ATOMIC_RELAXED, kScope);
+      }
+    }
+    __syncthreads();
+    const float amax = __uint_as_float(a);
+    const float m = mult_from_amax<FMT>(amax);
+    const bool hw = hw_encode_ok(amax, m);
+    for (uint32_t g = 0; g < s_ngone; ++g) {
+      const int64_t j0 = (int64_t)s_gone[g] * kFlatThreads + threadIdx.x;
+      for (int u = 0; u < kResident; ++u) {
+        const int64_t i = j0 + u * stride;
+        if (i < n4) Q4[i] = hw ? cvt4_fp8<FMT>(X[i] * m) : encode4<FMT>(X[i], m);
+      }
+    }
+  } else {
+    if (threadIdx.x == 0) {
+      uint64_t st = kWaiting;
+      for (int it = 0; it < spin_limit && st == kWaiting; ++it) {
+        __builtin_amdgcn_s_sleep(2);
+        st = __hip_atomic_load(&state[blockIdx.x], __ATOMIC_RELAXED, kScope);
+      }
+      if (st == kWaiting) {
+        uint64_t expect = kWaiting;
+        st = __hip_atomic_compare_exchange_strong(&state[blockIdx.x], &expect, kGaveUp,
+                                                  __ATOMIC_RELAXED, __ATOMIC_RELAXED, kScope)
+                 ? kGaveUp
+                 : expect;  // released after the last poll
+      }
+      // a released workgroup clears its own state word; a given-up one is
+      // cleared by the last arrival
+      if (st != kGaveUp) __hip_atomic_store(&state[blockIdx.x], kWaiting, __ATOMIC_RELAXED, kScope);
+      s_run = st != kGaveUp;
+      s_amax = (uint32_t)(st >> 32);
+    }
+    __syncthreads();
+    if (!s_run) return;
+  }
+  const float amax = __uint_as_float(s_amax);
+  const float m = mult_from_amax<FMT>(amax);
+  if (hw_encode_ok(amax, m)) {
+#pragma unroll
+    for (int u = 0; u < kResident; ++u) {
+      const int64_t i = i0 + u * stride;
+      if (i < n4) Q4[i] = cvt4_fp8<FMT>(v[u] * m);
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < kResident; ++u) {
+      const int64_t i = i0 + u * stride;
+      if (i < n4) Q4[i] = encode4<FMT>(v[u], m);
+    }
+  }
 }
 
 // Strided rows: workgroup b walks rows b, b + grid, ..., threads striding
@@ -393,13 +572,29 @@ TensorPasses tensor_passes(int64_t rows, int64_t cols, int64_t ldx, int64_t ldq)
 // The two per-tensor passes.  `done`, when given, is recorded by the second
 // kernel's own completion (hipExtLaunchKernelGGL's stop event): a separate
 // event record between two calls would put a gap of its own between them.
+// The one-pass kernel's grid for n4 float4, or 0 when the tensor is not
+// contiguous or more than the resident grid can hold.
+int64_t resident_grid(const TensorPasses& t, int64_t n4, hipStream_t s) {
+  if (!t.flat || n4 < 1) return 0;
+  const int64_t cus = compute_units(s), need = (n4 + kFlatThreads - 1) / kFlatThreads;
+  const int64_t grid = need < cus ? need : cus;
+  if (grid < 1 || grid > kMaxResidentGrid || n4 > grid * kFlatThreads * kResident) return 0;
+  return grid;
+}
+
 template <int FMT>
 void launch_tensor(const float* X, int64_t rows, int64_t cols, int64_t ldx, uint8_t* Q,
                    int64_t ldq, float* scales, uint32_t* part, const TensorPasses& t,
-                   hipStream_t s, hipEvent_t done) {
+                   hipStream_t s, hipEvent_t done, int spin_limit) {
   const int64_t cols4 = cols / 4;
   if (t.flat) {
     const int64_t n4 = rows * cols4;
+    if (const int64_t grid = resident_grid(t, n4, s)) {
+      hipExtLaunchKernelGGL(quant_tensor_resident<FMT>, dim3((unsigned)grid), dim3(kFlatThreads),
+                            0, s, nullptr, done, 0, (const f32x4_t*)X, n4, (uint32_t*)Q,
+                            part + kQuantizeScratchSlots, scales, spin_limit);
+      return;
+    }
     hipLaunchKernelGGL(amax_flat, dim3((unsigned)t.nparts), dim3(kFlatThreads), 0, s,
                        (const f32x4_t*)X, n4, part);
     hipExtLaunchKernelGGL(encode_flat<FMT>, dim3((unsigned)t.nparts), dim3(kFlatThreads), 0, s,
@@ -417,10 +612,10 @@ void launch_tensor(const float* X, int64_t rows, int64_t cols, int64_t ldx, uint
 template <int FMT>
 hipError_t launch_fmt(const float* X, int64_t rows, int64_t cols, int64_t ldx, int64_t br,
                       int64_t bc, uint8_t* Q, int64_t ldq, float* scales, uint32_t* part,
-                      hipStream_t s, hipEvent_t done = nullptr) {
+                      hipStream_t s, hipEvent_t done = nullptr, int spin_limit = kSpinLimit) {
   if (br == rows && bc == cols) {
     launch_tensor<FMT>(X, rows, cols, ldx, Q, ldq, scales, part,
-                       tensor_passes(rows, cols, ldx, ldq), s, done);
+                       tensor_passes(rows, cols, ldx, ldq), s, done, spin_limit);
   } else if (br == 1 && bc == 128) {
     const dim3 grid((unsigned)((cols + 1024 * kRounds - 1) / (1024 * kRounds)),
                     (unsigned)(rows < 65535 ? rows : 65535));
@@ -477,12 +672,27 @@ int device_of(hipStream_t s, hipError_t* e) {
   return dev;
 }
 
+// Compute units of the stream's GPU, looked up once per device; 0 if the
+// query fails (the per-tensor quantizer then takes its two-pass walk).
+int compute_units(hipStream_t s) {
+  static std::atomic<int> cached[kMaxDevices];
+  hipError_t e;
+  const int dev = device_of(s, &e);
+  if (e != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cached[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
 // quantize_fp8 (the allocating entry point): one workspace of
-// kQuantizeScratchSlots slots per GPU, allocated on the first per-tensor call
-// on that GPU and kept until the process ends.  Calls on different streams
-// would otherwise share it concurrently, so every call first makes its
-// stream wait for the previous call's completion event; its own second pass
-// records that event when it completes.
+// kQuantizeScratchWords words per GPU, allocated and zeroed on the first
+// per-tensor call on that GPU and kept until the process ends.  Calls on
+// different streams would otherwise share it concurrently, so every call
+// first makes its stream wait for the previous call's completion event; its
+// last kernel records that event when it completes.
 hipError_t launch_quantize_fp8_tensor_ws(const float* X, int64_t rows, int64_t cols, int64_t ldx,
                                          int fmt, uint8_t* Q, int64_t ldq, float* scales,
                                          hipStream_t s) {
@@ -504,7 +714,9 @@ hipError_t launch_quantize_fp8_tensor_ws(const float* X, int64_t rows, int64_t c
     int cur = -1;
     if ((e = hipGetDevice(&cur)) != hipSuccess) return e;
     if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
-    e = hipMalloc((void**)&w.slots, kQuantizeScratchSlots * sizeof(uint32_t));
+    e = hipMalloc((void**)&w.slots, kQuantizeScratchWords * sizeof(uint32_t));
+    // the one-pass kernel's sync words start at zero (every call leaves them so)
+    if (e == hipSuccess) e = hipMemset(w.slots, 0, kQuantizeScratchWords * sizeof(uint32_t));
     if (e == hipSuccess) e = hipEventCreate(&w.done);
     if (cur != dev) {
       const hipError_t e2 = hipSetDevice(cur);
@@ -530,12 +742,13 @@ hipError_t launch_quantize_fp8_tensor_ws(const float* X, int64_t rows, int64_t c
 // ---- the allocation-free entry point's scratch ----------------------------
 // For callers that cannot allocate device memory (code under graph capture,
 // serving loops, harnesses that forbid hipMalloc): the per-tensor pass-1
-// slots live in this file-scope array, one copy per GPU, held until the
-// process ends.  Host code never passes the array's name to a kernel (on the
+// slots and the one-pass kernel's sync words live in this file-scope array,
+// one copy per GPU, zero when the library loads and held until the process
+// ends.  Host code never passes the array's name to a kernel (on the
 // host it is a stand-in, not a device address): it asks once per device, with
 // that device current, for the array's address on that device and passes
 // that.  Calls that overlap on one GPU share the array and race.
-static __device__ __align__(256) uint32_t scratch[kQuantizeScratchSlots];
+static __device__ __align__(256) uint32_t scratch[kQuantizeScratchWords];  // zero at load
 static_assert(kFlatGrid <= kQuantizeScratchSlots && kRowsGrid <= kQuantizeScratchSlots,
               "every per-tensor pass-1 grid fits the scratch");
 
@@ -562,6 +775,23 @@ hipError_t quantize_scratch_address(hipStream_t s, uint32_t** out) {
   }
   *out = addr[device];
   return hipSuccess;
+}
+
+// The one-pass per-tensor kernel with a chosen wait bound, on the
+// allocation-free scratch.  Diagnostic: a bound of 0 makes waiting
+// workgroups give up at once, so the last arrival encodes their shares.
+hipError_t launch_probe_quantize_resident(const float* X, int64_t rows, int64_t cols, int fmt,
+                                          uint8_t* Q, float* scale, int spin_limit,
+                                          hipStream_t s) {
+  if (!resident_grid(tensor_passes(rows, cols, cols, cols), rows * (cols / 4), s))
+    return hipErrorInvalidValue;
+  uint32_t* part = nullptr;
+  const hipError_t e = quantize_scratch_address(s, &part);
+  if (e != hipSuccess) return e;
+  return fmt == 0 ? launch_fmt<0>(X, rows, cols, cols, rows, cols, Q, cols, scale, part, s,
+                                  nullptr, spin_limit)
+                  : launch_fmt<1>(X, rows, cols, cols, rows, cols, Q, cols, scale, part, s,
+                                  nullptr, spin_limit);
 }
 
 }  // namespace dmu

@@ -10,7 +10,7 @@
  * enqueued (or, for DMU_ERR_HIP, that the launch itself failed).  Faults
  * inside a kernel surface at the caller's next synchronisation.  Calls are
  * thread-safe.  Nothing is allocated except the per-tensor quantize_fp8
- * workspace (4 KiB per GPU, once); quantize_fp8_noalloc allocates nothing.
+ * workspace (16 KiB per GPU, once); quantize_fp8_noalloc allocates nothing.
  *
  * Matrices are dense with a leading dimension counted in elements: element
  * (r, c) of a row-major matrix X lives at X[r * ldx + c].  Every pointer must
@@ -195,13 +195,16 @@ int gemm_fp8_scaled(const uint8_t* A, int64_t lda, int fmt_a, const uint8_t* B, 
  * (scale NaN, codes NaN); one holding an Inf and no NaN gets amax = +Inf
  * (scale +Inf, finite inputs encode to +-0, infinite ones to NaN).  The result
  * is bit-exact and independent of launch configuration.
- * The per-tensor mode runs two passes: per-workgroup amax partials, then the
- * encode.  The partials (at most 512 x 4 bytes, whatever the tensor's size)
- * live in a 4 KiB workspace that the library allocates once per GPU, at the
- * first per-tensor call on it, and keeps until the process ends; each call
- * makes its stream wait for the previous per-tensor call on that GPU (an
- * event), so calls on different streams never share it concurrently.  Block
- * scales need no workspace.
+ * The per-tensor mode reads a contiguous tensor (ldx == ldq == cols) of up to
+ * 16384 values per compute unit once, with one kernel whose workgroups keep
+ * their share in registers and exchange their amax partials through the
+ * workspace; larger or strided tensors take two passes (per-workgroup amax
+ * partials, then the encode).  The workspace (16 KiB: partial slots and the
+ * one-pass kernel's counters) is allocated and zeroed by the library once per
+ * GPU, at the first per-tensor call on it, and kept until the process ends;
+ * each call makes its stream wait for the previous per-tensor call on that
+ * GPU (an event), so calls on different streams never share it concurrently.
+ * Block scales need no workspace.
  * Errors: DMU_ERR_INVALID_ARG for null pointers, bad sizes, leading dimensions
  * or alignment, an unknown format; DMU_ERR_UNSUPPORTED for other block shapes;
  * DMU_ERR_HIP if the workspace cannot be allocated or a launch fails.
@@ -215,15 +218,16 @@ int quantize_fp8(const float* X, int64_t rows, int64_t cols, int64_t ldx, int fm
  * quantize_fp8_noalloc: quantize_fp8 for callers that cannot allocate device
  * memory -- code under HIP graph capture, tight serving loops, harnesses that
  * forbid hipMalloc.  Same arguments, results and errors as quantize_fp8
- * (bit-identical output), but the per-tensor mode's amax partials go to a
- * static scratch array inside the library (1024 slots of 4 bytes per GPU,
- * held until the process ends) instead of an allocated workspace: the call
- * allocates nothing.  Limit: a call needing more slots than the scratch
- * holds returns DMU_ERR_UNSUPPORTED; the per-tensor passes use at most 512
- * slots whatever the tensor's size, so no valid tensor is refused.  Every
- * call on one GPU shares that GPU's scratch: calls that overlap on one GPU
- * (concurrent streams) race and must be serialised by the caller.  Block
- * scales use no scratch.
+ * (bit-identical output), but the per-tensor mode's amax partials and the
+ * one-pass kernel's counters go to a static scratch array inside the library
+ * (16 KiB per GPU: 1024 partial slots and 3072 counter words, zero when the
+ * library loads, held until the process ends) instead of an allocated
+ * workspace: the call allocates nothing.  Limit: a call needing more partial
+ * slots than the scratch holds returns DMU_ERR_UNSUPPORTED; the per-tensor
+ * passes use at most 512 slots whatever the tensor's size, so no valid tensor
+ * is refused.  Every call on one GPU shares that GPU's scratch: calls that
+ * overlap on one GPU (concurrent streams) race and must be serialised by the
+ * caller.  Block scales use no scratch.
  */
 int quantize_fp8_noalloc(const float* X, int64_t rows, int64_t cols, int64_t ldx, int fmt,
                          int64_t block_rows, int64_t block_cols, uint8_t* Q, int64_t ldq,

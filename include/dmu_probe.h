@@ -144,6 +144,22 @@ int dmu_probe_cvt_fp8(const float* x, int64_t n, int fmt, int clamp, uint8_t* q,
 int dmu_probe_lds_tr16(const uint16_t* src, const uint32_t* offsets, uint16_t* out,
                        void* stream);
 
+/*
+ * Per-tensor quantize_fp8 of a contiguous rows x cols tensor (X and Q
+ * row-major with no padding, scale one float) through the one-pass kernel,
+ * with the bound on how many times a waiting workgroup polls for the tensor's
+ * amax before it gives up and leaves its share to the last workgroup to
+ * arrive.  quantize_fp8 uses a bound long enough that the fallback only runs
+ * when the grid's workgroups are not all resident at once; spin_limit = 0
+ * makes every waiting workgroup give up, so the tests can check that
+ * fallback's codes (they must equal quantize_fp8's).  Uses the allocation-free
+ * entry point's scratch, so it must not overlap such a call on the same GPU.
+ * Returns DMU_ERR_UNSUPPORTED when the tensor is too large for the one-pass
+ * kernel, DMU_ERR_INVALID_ARG as quantize_fp8 does or for spin_limit < 0.
+ */
+int dmu_probe_quantize_tensor_resident(const float* X, int64_t rows, int64_t cols, int fmt,
+                                       uint8_t* Q, float* scale, int spin_limit, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -113,3 +113,56 @@ def test_per_tensor_calls_on_two_streams():
         Qr, sr = refs[it % 2]
         assert np.array_equal(Q.cpu().numpy(), Qr), it
         assert sc.item() == float(sr[0, 0]), it
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_per_tensor_every_walk(fmt):
+    # A contiguous tensor that the grid can hold in registers takes the
+    # one-pass kernel, a strided one the two-pass row walk, and a contiguous
+    # one larger than 64 MB the two-pass flat walk; all must equal the oracle.
+    X = wl.normal((1024, 1024), 21)
+    Q, s = run_quant(X, fmt, None)                       # one pass
+    compare(X, fmt, None, Q, s)
+    Xbig = np.zeros((1024, 1040), np.float32)
+    Xbig[:, :1024] = X
+    Q, s = run_quant(dev(Xbig)[:, :1024], fmt, None)     # rows, two passes
+    compare(X, fmt, None, Q, s)
+    X = wl.normal((8192, 4096), 22)
+    X[5000, 7] = 300.0                                   # amax far from the first rows
+    Q, s = run_quant(X, fmt, None)                       # flat, two passes
+    compare(X, fmt, None, Q, s)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("shape", [(1, 16), (3, 64), (384, 640), (4096, 4096)])
+def test_one_pass_fallback_when_workgroups_give_up(fmt, shape):
+    # With a wait bound of 0 a waiting workgroup gives up at once and the last
+    # one to arrive encodes its share from X (the path taken when the grid's
+    # workgroups are not all resident); which workgroups give up depends on
+    # timing, and the codes must not.  Then quantize_fp8_noalloc on the same
+    # scratch: the one-pass kernel must have left its sync words cleared.
+    X = wl.normal(shape, 23)
+    X.flat[len(X.flat) // 2] = -77.0
+    g = dev(X)
+    for limit in (0, 0, 1 << 30):
+        Q = torch.full(shape, 0x5A, dtype=torch.uint8, device="cuda")
+        sc = torch.full((1,), -7.0, dtype=torch.float32, device="cuda")
+        dmu.probe_quantize_tensor_resident(g, Q, sc, fmt, spin_limit=limit)
+        torch.cuda.synchronize()
+        compare(X, fmt, None, Q.cpu().numpy(), sc.cpu().numpy().reshape(1, 1))
+    Q = torch.full(shape, 0x5A, dtype=torch.uint8, device="cuda")
+    sc = torch.full((1,), -7.0, dtype=torch.float32, device="cuda")
+    dmu.quantize_fp8_noalloc(g, Q, sc, fmt)
+    torch.cuda.synchronize()
+    compare(X, fmt, None, Q.cpu().numpy(), sc.cpu().numpy().reshape(1, 1))
+
+
+def test_one_pass_nonfinite_tensor():
+    # NaN anywhere makes the amax NaN; an Inf (no NaN) makes it Inf; both keep
+    # the integer encoder, on the one-pass kernel as on the two-pass walks
+    for bad in (np.nan, np.inf, -np.inf):
+        X = wl.normal((512, 512), 24)
+        X[100, 200] = bad
+        for fmt in FMTS:
+            Q, s = run_quant(X, fmt, None)
+            compare(X, fmt, None, Q, s)
