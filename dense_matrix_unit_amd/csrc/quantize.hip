@@ -316,7 +316,8 @@ __global__ __launch_bounds__(kFlatThreads) void quant_tensor_resident(const f32x
       const int64_t j0 = (int64_t)s_gone[g] * kFlatThreads + threadIdx.x;
       for (int u = 0; u < kResident; ++u) {
         const int64_t i = j0 + u * stride;
-        if (i < n4) Q4[i] = hw ? cvt4_fp8<FMT>(X[i] * m) : encode4<FMT>(X[i], m);
+        if (i < n4)
+          __builtin_nontemporal_store(hw ? cvt4_fp8<FMT>(X[i] * m) : encode4<FMT>(X[i], m), Q4 + i);
       }
     }
   } else {
@@ -342,19 +343,22 @@ __global__ __launch_bounds__(kFlatThreads) void quant_tensor_resident(const f32x
     __syncthreads();
     if (!s_run) return;
   }
+  // Q is written with streaming stores: its 16.8 MB (at 4096^2) would
+  // otherwise sit dirty in the L2s and be written back at the kernel's end,
+  // after the last encode (2.1 us more per call here)
   const float amax = __uint_as_float(s_amax);
   const float m = mult_from_amax<FMT>(amax);
   if (hw_encode_ok(amax, m)) {
 #pragma unroll
     for (int u = 0; u < kResident; ++u) {
       const int64_t i = i0 + u * stride;
-      if (i < n4) Q4[i] = cvt4_fp8<FMT>(v[u] * m);
+      if (i < n4) __builtin_nontemporal_store(cvt4_fp8<FMT>(v[u] * m), Q4 + i);
     }
   } else {
 #pragma unroll
     for (int u = 0; u < kResident; ++u) {
       const int64_t i = i0 + u * stride;
-      if (i < n4) Q4[i] = encode4<FMT>(v[u], m);
+      if (i < n4) __builtin_nontemporal_store(encode4<FMT>(v[u], m), Q4 + i);
     }
   }
 }
