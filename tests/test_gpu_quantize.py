@@ -134,7 +134,7 @@ def test_per_tensor_every_walk(fmt):
 
 
 @pytest.mark.parametrize("fmt", FMTS)
-@pytest.mark.parametrize("shape", [(1, 16), (3, 64), (384, 640), (4096, 4096)])
+@pytest.mark.parametrize("shape", [(1, 16), (3, 64), (384, 640), (1000, 1008), (4096, 4096)])
 def test_one_pass_fallback_when_workgroups_give_up(fmt, shape):
     # With a wait bound of 0 a waiting workgroup gives up at once and the last
     # one to arrive encodes its share from X (the path taken when the grid's
