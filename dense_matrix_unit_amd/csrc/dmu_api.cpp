@@ -438,7 +438,7 @@ int dmu_probe_quantize_tensor_resident(const float* X, int64_t rows, int64_t col
                                        uint8_t* Q, float* scale, int spin_limit, void* stream) {
   const int rc = quantize_args(X, rows, cols, cols, fmt, rows, cols, Q, cols, scale);
   if (rc) return rc;
-  if (spin_limit < 0) return DMU_ERR_INVALID_ARG;
+  if (spin_limit < 0 || spin_limit > (1 << 16)) return DMU_ERR_INVALID_ARG;  // every wait stays short
   (void)hipGetLastError();
   const hipError_t e = dmu::launch_probe_quantize_resident(X, rows, cols, fmt, Q, scale,
                                                            spin_limit, (hipStream_t)stream);

@@ -155,7 +155,8 @@ int dmu_probe_lds_tr16(const uint16_t* src, const uint32_t* offsets, uint16_t* o
  * fallback's codes (they must equal quantize_fp8's).  Uses the allocation-free
  * entry point's scratch, so it must not overlap such a call on the same GPU.
  * Returns DMU_ERR_UNSUPPORTED when the tensor is too large for the one-pass
- * kernel, DMU_ERR_INVALID_ARG as quantize_fp8 does or for spin_limit < 0.
+ * kernel, DMU_ERR_INVALID_ARG as quantize_fp8 does or for spin_limit outside
+ * [0, 65536] (quantize_fp8 itself uses 4096).
  */
 int dmu_probe_quantize_tensor_resident(const float* X, int64_t rows, int64_t cols, int fmt,
                                        uint8_t* Q, float* scale, int spin_limit, void* stream);

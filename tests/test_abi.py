@@ -269,7 +269,8 @@ def test_quantize_rejects(fn, kw):
     (dict(X=None), dmu.DMU_ERR_INVALID_ARG), (dict(Q=None), dmu.DMU_ERR_INVALID_ARG),
     (dict(s=None), dmu.DMU_ERR_INVALID_ARG), (dict(rows=0), dmu.DMU_ERR_INVALID_ARG),
     (dict(cols=120), dmu.DMU_ERR_INVALID_ARG), (dict(fmt=2), dmu.DMU_ERR_INVALID_ARG),
-    (dict(spin=-1), dmu.DMU_ERR_INVALID_ARG), (dict(X=FAKE + 4), dmu.DMU_ERR_INVALID_ARG),
+    (dict(spin=-1), dmu.DMU_ERR_INVALID_ARG), (dict(spin=(1 << 16) + 1), dmu.DMU_ERR_INVALID_ARG),
+    (dict(X=FAKE + 4), dmu.DMU_ERR_INVALID_ARG),
 ])
 def test_probe_quantize_resident_rejects(kw, rc):
     a = dict(X=FAKE, rows=256, cols=128, fmt=0, Q=FAKE, s=FAKE, spin=0, stream=None)
