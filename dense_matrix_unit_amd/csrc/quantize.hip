@@ -8,14 +8,17 @@
 // product x*m, and the dequantisation factor s = amax / FMAX is stored.
 //
 // Kernels (all HBM-bound streaming; every value is read once per pass):
-//  * per tensor: two passes.  Pass 1: each workgroup writes the max of the
-//    bit patterns of |x| over its grid-stride share to its own scratch slot
-//    (for non-negative floats the integer order is the numeric order, and
-//    any NaN pattern sorts above +Inf, so a NaN anywhere yields a NaN amax).
-//    Pass 2: each workgroup takes the max of all slots (the tensor's amax),
-//    then encodes its share; workgroup 0 stores the scale.  No slot needs
-//    clearing and no atomics are used; the slot count is the pass-1 grid
-//    (at most kTensorSlots, whatever the tensor's size).
+//  * per tensor, contiguous and small enough for the grid's registers: one
+//    pass (quant_tensor_resident, described at the kernel).  Amaxes are
+//    compared as the bit patterns of |x|: for non-negative floats the
+//    integer order is the numeric order, and any NaN pattern sorts above
+//    +Inf, so a NaN anywhere yields a NaN amax.
+//  * per tensor, otherwise: two passes.  Pass 1: each workgroup writes the
+//    max of the |x| bit patterns over its grid-stride share to its own
+//    scratch slot.  Pass 2: each workgroup takes the max of all slots (the
+//    tensor's amax), then encodes its share; workgroup 0 stores the scale.
+//    No slot needs clearing and no atomics are used; the slot count is the
+//    pass-1 grid (at most 512, whatever the tensor's size).
 //  * 1 x 128 blocks: 32 lanes per block (16 bytes per lane), half-wave max,
 //    rows walked by the grid's y dimension.
 //  * 128 x 128 blocks: one 256-thread workgroup per block keeps its 64 values
