@@ -166,3 +166,33 @@ def test_one_pass_nonfinite_tensor():
         for fmt in FMTS:
             Q, s = run_quant(X, fmt, None)
             compare(X, fmt, None, Q, s)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_one_pass_under_graph_replay(fmt):
+    # The allocation-free entry point captured once in a HIP graph and replayed
+    # on new contents of the same input buffer, with eager copies and
+    # synchronisations between replays: the one-pass kernel keeps no state
+    # across calls but what it clears itself, so every replay must match the
+    # oracle, and so must an eager call after the replays.
+    shape = (2048, 1024)
+    Xs = [wl.normal(shape, 30 + k) * np.float32(10.0 ** (k - 1)) for k in range(3)]
+    Xg = torch.from_numpy(Xs[0]).cuda()
+    Q = torch.empty(shape, dtype=torch.uint8, device="cuda")
+    sc = torch.empty(1, dtype=torch.float32, device="cuda")
+    dmu.quantize_fp8_noalloc(Xg, Q, sc, fmt)      # outside the capture first
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        dmu.quantize_fp8_noalloc(Xg, Q, sc, fmt)
+    torch.cuda.synchronize()
+    for rep in range(6):
+        X = Xs[rep % 3]
+        Xg.copy_(torch.from_numpy(X))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        compare(X, fmt, None, Q.cpu().numpy(), sc.cpu().numpy().reshape(1, 1))
+    dmu.quantize_fp8_noalloc(Xg, Q, sc, fmt)
+    torch.cuda.synchronize()
+    compare(Xs[5 % 3], fmt, None, Q.cpu().numpy(), sc.cpu().numpy().reshape(1, 1))
