@@ -531,12 +531,14 @@ def probe_mfma_mx(shape: int, A, B, SA, SB, C, D, fmt_a: int = E4M3, fmt_b: int 
 
 def probe_cvt_fp8(x, q, fmt: int = E4M3, clamp: int = 1, stream=None):
     """Hardware FP32 -> FP8 conversion of x (float32, even length) into q
-    (uint8, same length); see include/dmu_probe.h."""
+    (uint8, same length; half the length for fmt E2M1, two codes per byte);
+    see include/dmu_probe.h."""
     torch = _torch()
     _check_dtype(x, (torch.float32,), "x")
     _check_dtype(q, (torch.uint8,), "q")
-    if x.numel() != q.numel() or not (x.is_contiguous() and q.is_contiguous()):
-        raise ValueError("x and q: contiguous, same length")
+    want = x.numel() // 2 if fmt == E2M1 else x.numel()
+    if q.numel() != want or not (x.is_contiguous() and q.is_contiguous()):
+        raise ValueError("x and q: contiguous, q of %d bytes" % want)
     rc = load_library().dmu_probe_cvt_fp8(_dev_ptr(x, "x"), x.numel(), fmt, clamp,
                                           _dev_ptr(q, "q"), _stream(stream))
     _check("dmu_probe_cvt_fp8", rc)

@@ -448,7 +448,7 @@ int dmu_probe_quantize_tensor_resident(const float* X, int64_t rows, int64_t col
 
 int dmu_probe_cvt_fp8(const float* x, int64_t n, int fmt, int clamp, uint8_t* q, void* stream) {
   if (!x || !q || n < 2 || n % 2 || n > ((int64_t)1 << 31)) return DMU_ERR_INVALID_ARG;
-  if ((fmt != 0 && fmt != 1) || (clamp != 0 && clamp != 1) || !aligned(x, 8))
+  if ((fmt != 0 && fmt != 1 && fmt != 4) || (clamp != 0 && clamp != 1) || !aligned(x, 8))
     return DMU_ERR_INVALID_ARG;
   (void)hipGetLastError();
   return finish(dmu::launch_probe_cvt(x, n, fmt, clamp, q, (hipStream_t)stream));

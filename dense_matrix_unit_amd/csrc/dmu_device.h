@@ -116,4 +116,17 @@ __device__ __forceinline__ uint32_t cvt4_fp8(f32x4_t y) {
   return (uint32_t)w;
 }
 
+// Four FP32 values -> four E2M1 codes in 16 bits (value r in nibble r), round
+// to nearest even, saturating at +-6: gfx950's v_cvt_scalef32_pk_fp4_f32 with
+// a scale operand of 1 (no scaling), two values per instruction into byte
+// `sel` of its result, after a clamp to +-6.  Only for finite values (the
+// quantizer sends blocks with NaN or Inf elsewhere).
+__device__ __forceinline__ uint32_t cvt4_fp4(f32x4_t y) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r) y[r] = fminf(fmaxf(y[r], -6.0f), 6.0f);
+  uint32_t w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, y[0], y[1], 1.0f, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[2], y[3], 1.0f, 1);
+  return w & 0xFFFFu;
+}
+
 }  // namespace dmu

@@ -171,14 +171,22 @@ __global__ void probe_mx_kernel(const uint8_t* A, const uint8_t* B, const uint8_
 // (CLAMP == 0), or through cvt4_fp8 (CLAMP == 1: x clamped to the format's
 // largest finite magnitude, NaN passed through, then converted; the function
 // the fused epilogue and the quantizers use).  Thread t converts x[2t],
-// x[2t+1] into q[2t], q[2t+1].
+// x[2t+1] into q[2t], q[2t+1].  FMT 4: E2M1 by v_cvt_scalef32_pk_fp4_f32 with
+// scale 1 (CLAMP == 1: through cvt4_fp4, clamped to +-6), both codes of the
+// pair into byte q[t].
 template <int FMT, int CLAMP>
 __global__ void probe_cvt_kernel(const float* x, int64_t npairs, uint8_t* q) {
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (t >= npairs) return;
   const float a = x[2 * t], b = x[2 * t + 1];
   uint32_t r;
-  if constexpr (CLAMP) {
+  if constexpr (FMT == 4) {
+    // E2M1: both codes in one byte
+    r = CLAMP ? cvt4_fp4(f32x4_t{a, b, 0.0f, 0.0f})
+              : (uint32_t)__builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, a, b, 1.0f, 0);
+    q[t] = (uint8_t)(r & 0xFF);
+    return;
+  } else if constexpr (CLAMP) {
     r = cvt4_fp8<FMT>(f32x4_t{a, b, 0.0f, 0.0f});
   } else if constexpr (FMT == 0) {
     r = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
@@ -399,6 +407,8 @@ hipError_t launch_probe_cvt(const float* x, int64_t n, int fmt, int clamp, uint8
 #define DMU_CVT(F, C) hipLaunchKernelGGL((probe_cvt_kernel<F, C>), grid, dim3(256), 0, s, x, np, q)
   if (fmt == 0 && !clamp) DMU_CVT(0, 0);
   else if (fmt == 0) DMU_CVT(0, 1);
+  else if (fmt == 4 && !clamp) DMU_CVT(4, 0);
+  else if (fmt == 4) DMU_CVT(4, 1);
   else if (!clamp) DMU_CVT(1, 0);
   else DMU_CVT(1, 1);
 #undef DMU_CVT

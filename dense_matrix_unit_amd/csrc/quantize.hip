@@ -54,19 +54,6 @@ namespace {
 
 __device__ __forceinline__ uint32_t abs_bits(float x) { return __float_as_uint(x) & 0x7FFFFFFFu; }
 
-// FP32 -> E2M1 (FP4: magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6), round to nearest
-// with ties to the even code, saturating at 6, sign kept.  The magnitude code
-// counts the rounding boundaries |y| has passed: a boundary between codes
-// c and c + 1 is their midpoint, which itself rounds up exactly when c + 1 is
-// even (>=) and down when c + 1 is odd (>).
-__device__ __forceinline__ uint32_t encode_fp4(float y) {
-  const float a = fabsf(y);
-  const uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
-                     (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
-                     (uint32_t)(a > 5.0f);
-  return c | ((__float_as_uint(y) >> 28) & 8u);
-}
-
 __device__ __forceinline__ uint32_t wave_max(uint32_t v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, 64));
@@ -543,15 +530,12 @@ __global__ __launch_bounds__(256) void quant_mx(const float* X, int64_t rows, in
           const uint32_t eb = m >> 23;  // biased exponent of amax (0: zero or subnormal)
           code = eb > kEmax ? eb - kEmax : 0u;
           const float mult = __uint_as_float((254u - code) << 23);
-          if constexpr (FMT == 4) {
-            q = 0;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) q |= encode_fp4(v[u][e] * mult) << (4 * e);
-          } else {
-            // finite block, normal power-of-two multiplier: every product is
-            // finite, where the clamped hardware conversion is the encoder
+          // finite block, normal power-of-two multiplier: every product is
+          // finite, where the clamped hardware conversion is the encoder
+          if constexpr (FMT == 4)
+            q = cvt4_fp4(v[u] * mult);
+          else
             q = cvt4_fp8<FMT>(v[u] * mult);
-          }
         }
         if constexpr (FMT == 4)
           *(uint16_t*)(Q + r * ldq + c / 2) = (uint16_t)q;

@@ -127,8 +127,11 @@ int dmu_probe_mfma_mx(int shape, int fmt_a, int fmt_b, int opsel, const void* A,
  * v_cvt_pk_bf8_f32 for fmt 1 = E5M2), two values per instruction, on x as
  * given (clamp = 0) or on x clamped to +-the format's largest finite value
  * with NaN passed through (clamp = 1).  x and q
- * are device arrays of n floats / n bytes.  Exists so the tests can pin the
- * conversion's rounding, saturation and special values against the oracle.
+ * are device arrays of n floats / n bytes.  fmt 4 = E2M1 uses
+ * v_cvt_scalef32_pk_fp4_f32 with scale 1 (clamp = 1: x clamped to +-6 first)
+ * and writes the pair x[2i], x[2i+1] as byte i of q (n / 2 bytes).  Exists so
+ * the tests can pin the conversion's rounding, saturation and special values
+ * against the oracle.
  */
 int dmu_probe_cvt_fp8(const float* x, int64_t n, int fmt, int clamp, uint8_t* q, void* stream);
 

@@ -530,6 +530,36 @@ def test_hardware_fp8_conversion(fmt):
     assert np.array_equal(out[0][inrange], want[inrange])
 
 
+def test_hardware_fp4_conversion():
+    # gfx950's v_cvt_scalef32_pk_fp4_f32 (scale 1) after a clamp to +-6 is the
+    # oracle's saturating round-to-nearest-even E2M1 encoder on every finite
+    # input: every code value, every midpoint and one FP32 step either side,
+    # signed zeros, FP32 subnormals, values past 6 and random values.  The MX
+    # quantizer relies on it for blocks with a finite amax.  The pair
+    # x[2i], x[2i+1] lands in one byte, the first value in the low nibble.
+    rng = np.random.default_rng(4)
+    vals = oracle.decode_fp4(np.arange(16, dtype=np.uint8))
+    fin = np.sort(np.unique(np.abs(vals)))
+    mids = ((fin[1:] + fin[:-1]) / 2).astype(np.float32)
+    up, dn = np.nextafter(mids, np.float32(np.inf)), np.nextafter(mids, np.float32(0))
+    special = np.float32([0.0, -0.0, 1e-45, -1e-45, 1e-38, -1e-38, 6.5, -7.0, 7.99, 1e30, -1e30,
+                          np.inf, -np.inf, 0.25, -0.25, 0.2500001, 5.0, -5.0])
+    x = np.concatenate([special, fin, -fin, mids, -mids, up, -up, dn, -dn,
+                        rng.uniform(-8, 8, 100000),
+                        np.exp(rng.uniform(-30, 2.1, 100000)) * rng.choice([-1, 1], 100000)])
+    x = x.astype(np.float32)
+    if x.size % 2:
+        x = np.append(x, np.float32(0))
+    want = oracle.encode_fp4(x).astype(np.uint8)
+    q = torch.empty(x.size // 2, dtype=torch.uint8, device="cuda")
+    dmu.probe_cvt_fp8(dev(x), q, dmu.E2M1, 1)
+    torch.cuda.synchronize()
+    got = q.cpu().numpy()
+    lo, hi = got & 0xF, got >> 4
+    assert np.array_equal(lo, want[0::2]), np.flatnonzero(lo != want[0::2])[:8]
+    assert np.array_equal(hi, want[1::2]), np.flatnonzero(hi != want[1::2])[:8]
+
+
 def run_tr16(offsets):
     src = torch.arange(1024, dtype=torch.int16, device="cuda")
     out = torch.full((256,), -1, dtype=torch.int16, device="cuda")
