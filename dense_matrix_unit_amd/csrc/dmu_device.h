@@ -52,6 +52,14 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
   return __builtin_bit_cast(uint16_t, h);
 }
 
+// Two FP32 values -> two BF16 (round to nearest even), lo in the low half:
+// one v_cvt_pk_bf16_f32, where two f32_to_bf16_bits and an OR take three.
+typedef __bf16 dmu_bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float dmu_f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(dmu_f32x2_t{lo, hi}, dmu_bf16x2_t));
+}
+
 // FP8 formats (OCP): E4M3 (FN: no Inf, S.1111.111 NaN, max 448) and E5M2.
 template <int FMT>
 struct Fp8Fmt;

@@ -794,9 +794,9 @@ gemm_kernel(GemmArgs p) {
                 *(f32x4_t*)(row + ((u ^ (rl & (UPS - 1))) << 4)) = x;
               } else if constexpr (EB == 2) {
                 const uint32_t lo =
-                    f32_to_bf16_bits(x[0]) | ((uint32_t)f32_to_bf16_bits(x[1]) << 16);
+                    pack2_bf16(x[0], x[1]);
                 const uint32_t hi =
-                    f32_to_bf16_bits(x[2]) | ((uint32_t)f32_to_bf16_bits(x[3]) << 16);
+                    pack2_bf16(x[2], x[3]);
                 const int u = j * 4 + q;
                 *(uint2*)(row + ((u ^ (rl & (UPS - 1))) << 4) + hl * 8) = make_uint2(lo, hi);
               } else {
@@ -862,8 +862,8 @@ gemm_kernel(GemmArgs p) {
             f32x4_t x = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
                          acc[i][j][4 * q + 3]};
             if constexpr (F8T) x *= alpha;
-            const uint32_t lo = f32_to_bf16_bits(x[0]) | ((uint32_t)f32_to_bf16_bits(x[1]) << 16);
-            const uint32_t hi = f32_to_bf16_bits(x[2]) | ((uint32_t)f32_to_bf16_bits(x[3]) << 16);
+            const uint32_t lo = pack2_bf16(x[0], x[1]);
+            const uint32_t hi = pack2_bf16(x[2], x[3]);
             const int u = j * 4 + q;  // 16-byte unit of the staged row
             *(uint2*)(wbase + (i * 32 + rl) * RB16 + ((u ^ (rl & (UPR - 1))) << 4) + hl * 8) =
                 make_uint2(lo, hi);

@@ -327,8 +327,8 @@ gemm_fp8_block_kernel(GemmArgs p) {
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
         const f32x4_t x = acc[i][j];
-        const uint32_t lo = f32_to_bf16_bits(x[0]) | ((uint32_t)f32_to_bf16_bits(x[1]) << 16);
-        const uint32_t hi = f32_to_bf16_bits(x[2]) | ((uint32_t)f32_to_bf16_bits(x[3]) << 16);
+        const uint32_t lo = pack2_bf16(x[0], x[1]);
+        const uint32_t hi = pack2_bf16(x[2], x[3]);
         const int r = i * 16 + r16, u = 2 * j + (g16 >> 1);
         *(uint2*)(wbase + r * RBY + ((u ^ (r & (UPR - 1))) << 4) + (g16 & 1) * 8) =
             make_uint2(lo, hi);

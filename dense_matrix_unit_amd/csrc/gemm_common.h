@@ -112,8 +112,8 @@ __device__ __forceinline__ void store4(const GemmArgs& p, int64_t row, int64_t c
   }
   if (p.out_bf16) {
     uint16_t* d = (uint16_t*)p.D + row * p.ldd + col;
-    const uint32_t lo = f32_to_bf16_bits(x[0]) | ((uint32_t)f32_to_bf16_bits(x[1]) << 16);
-    const uint32_t hi = f32_to_bf16_bits(x[2]) | ((uint32_t)f32_to_bf16_bits(x[3]) << 16);
+    const uint32_t lo = pack2_bf16(x[0], x[1]);
+    const uint32_t hi = pack2_bf16(x[2], x[3]);
     if (full) {
       *(uint2*)d = make_uint2(lo, hi);
     } else {

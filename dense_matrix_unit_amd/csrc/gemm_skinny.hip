@@ -160,8 +160,8 @@ __global__ __launch_bounds__(kThreads) void gemm_skinny_kernel(GemmArgs p) {
     if (p.out_bf16) {
       uint16_t* d = (uint16_t*)p.D + row * p.ldd + col;
       if (full) {
-        *(uint2*)d = make_uint2(f32_to_bf16_bits(x[0]) | ((uint32_t)f32_to_bf16_bits(x[1]) << 16),
-                                f32_to_bf16_bits(x[2]) | ((uint32_t)f32_to_bf16_bits(x[3]) << 16));
+        *(uint2*)d = make_uint2(pack2_bf16(x[0], x[1]),
+                                pack2_bf16(x[2], x[3]));
       } else {
         for (int r = 0; r < 4; ++r)
           if (col + r < p.N) d[r] = f32_to_bf16_bits(x[r]);
