@@ -227,7 +227,9 @@ int quantize_fp8(const float* X, int64_t rows, int64_t cols, int64_t ldx, int fm
  * passes use at most 512 slots whatever the tensor's size, so no valid tensor
  * is refused.  Every call on one GPU shares that GPU's scratch: calls that
  * overlap on one GPU (concurrent streams) race and must be serialised by the
- * caller.  Block scales use no scratch.
+ * caller.  A race can also leave the one-pass kernel's counters inconsistent,
+ * after which per-tensor results of later calls on that GPU are undefined as
+ * well.  Block scales use no scratch.
  */
 int quantize_fp8_noalloc(const float* X, int64_t rows, int64_t cols, int64_t ldx, int fmt,
                          int64_t block_rows, int64_t block_cols, uint8_t* Q, int64_t ldq,
