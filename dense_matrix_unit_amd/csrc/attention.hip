@@ -90,14 +90,6 @@ __device__ __forceinline__ void unroll_n(F&& f) {
   unroll_seq(f, std::make_integer_sequence<int, N>{});
 }
 
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-
-// Two FP32 values -> two BF16 (round to nearest even) in one v_cvt_pk_bf16_f32.
-__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
-}
-
 // The reference maximum of a row moves only when a block's maximum exceeds
 // it by more than this (in exp2 units): weights then stay below 2^8, and the
 // output is rescaled rarely instead of after nearly every block.
@@ -337,7 +329,7 @@ attention_kernel(AttnArgs p) {
             const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[jt][2 * w], c, -mc));
             const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[jt][2 * w + 1], c, -mc));
             rs += p0 + p1;
-            pk[jt][w] = pack_bf16(p0, p1);
+            pk[jt][w] = pack2_bf16(p0, p1);
           }
         l = l * alpha + rs;
         if (__builtin_amdgcn_ballot_w64(move)) {
@@ -403,7 +395,7 @@ attention_kernel(AttnArgs p) {
                              o[nt][4 * q + 3] * inv};
           const int u = nt * 4 + q;  // unit of columns 8u .. 8u+7; this lane half's are 8u + 4h ..
           *(uint2*)(wb + rl * RB + ((u ^ (rl & (UPR - 1))) << 4) + hl * 8) =
-              make_uint2(pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3]));
+              make_uint2(pack2_bf16(x[0], x[1]), pack2_bf16(x[2], x[3]));
         }
       __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0<63>());  // own region: no barrier
       uint16_t* Oh = p.O + bh * p.ho;
