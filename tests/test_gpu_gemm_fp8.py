@@ -193,7 +193,7 @@ def test_promotion_interval_64_128_256(K):
     e_fast = within(Dfast, "fast")
     dA, dB = padded(A, 16), padded(B, 16)
     one = dev(np.ones(1, np.float32))
-    alpha = float(np.float32(sa[0]) * np.float32(sb[0]))
+    alpha = float(np.float32(np.ravel(sa)[0]) * np.float32(np.ravel(sb)[0]))
     part = torch.empty((256, 256), dtype=torch.float32, device="cuda")
     line = ["E4M3 K=%d rel-RMS from the sums: fast %.3e" % (K, e_fast)]
     for P in (64, 128, 256):
