@@ -1,7 +1,6 @@
 """The C-ABI library loads on the CPU host, exports every function the public
 headers declare, and rejects bad arguments before launching anything (every
 call below fails validation, so no GPU is touched)."""
-import ctypes
 import glob
 import os
 import re

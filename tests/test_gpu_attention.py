@@ -21,7 +21,6 @@ import torch
 import dense_matrix_unit_amd as dmu
 import oracle
 from dense_matrix_unit_amd import workloads as wl
-from gpu_helpers import dev
 
 pytestmark = pytest.mark.gpu
 

@@ -17,7 +17,7 @@ import torch
 import oracle
 import dense_matrix_unit_amd as dmu
 from dense_matrix_unit_amd import workloads as wl
-from gpu_helpers import dev, empty_padded, out_to_f64, padded, round_out, within_fp8_bound
+from gpu_helpers import empty_padded, out_to_f64, padded, round_out, within_fp8_bound
 
 pytestmark = pytest.mark.gpu
 FMT_PAIRS = [(0, 0), (0, 1), (1, 0), (1, 1)]
