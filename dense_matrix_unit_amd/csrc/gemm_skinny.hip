@@ -13,9 +13,13 @@
 //    gives exactly 256 workgroups, one per CU;
 //  * every wave streams its own 16 rows of B straight into registers (no LDS
 //    round trip), 16 bytes per lane per 32-wide K step, in a ring of three
-//    128-wide K chunks (two in flight while one is multiplied);
-//  * A (at most 128 x K) is shared by the workgroup through LDS, one 128-wide
-//    K chunk per stage, copied with buffer loads that write LDS directly; its
+//    K chunks (two in flight while one is multiplied).  A chunk is 256 K wide
+//    for M <= 64 and 128 wide for M = 128, whose A stages would not fit in
+//    LDS at 256: the longer run of each B row per chunk took M = 16 from 97.4
+//    to 94.4 us and M = 64 from 101.1 to 97.4 us (N = 28672, K = 8192,
+//    bit-identical output); 512 wide was slower again at M = 16;
+//  * A (at most 128 x K) is shared by the workgroup through LDS, one K chunk
+//    per stage, copied with buffer loads that write LDS directly; its
 //    16-byte chunks are XOR-swizzled with the row index so the MFMA fragment
 //    reads are bank-conflict free.  There is one A stage more than the ring
 //    holds chunks, so the copy of chunk c + 3 goes into the stage of chunk
@@ -34,19 +38,18 @@ namespace {
 constexpr int kWaves = 7;
 constexpr int kThreads = kWaves * 64;
 constexpr int kBN = kWaves * 16;  // columns of D per workgroup
-constexpr int kKC = 128;          // K elements per chunk
-constexpr int kRowB = kKC * 2;    // bytes per A row per chunk
-constexpr int kSteps = kKC / 32;  // 16x16x32 MFMA steps per chunk
-
-// LDS position of 16-byte chunk c (0..15) of A row r (256-byte rows): flip
-// the four bits of c with the row, so 16 consecutive rows at the same c hit
-// 16 distinct 16-byte bank groups.
-__device__ __forceinline__ int aswz(int r, int c) { return c ^ (r & (kRowB / 16 - 1) & 15); }
 
 // kNB: chunks in the ring (kNB-1 in flight while one is multiplied); enough
 // bytes must be in flight per CU to cover HBM latency at full bandwidth.
-template <int MB, int kNB>
+// kKC: K elements per chunk.
+template <int MB, int kNB, int kKC>
 __global__ __launch_bounds__(kThreads) void gemm_skinny_kernel(GemmArgs p) {
+  constexpr int kRowB = kKC * 2;    // bytes per A row per chunk
+  constexpr int kSteps = kKC / 32;  // 16x16x32 MFMA steps per chunk
+  // LDS position of 16-byte chunk c of A row r: flip the low four bits of c
+  // with the row, so 16 consecutive rows at the same c hit 16 distinct
+  // 16-byte bank groups.
+  auto aswz = [](int r, int c) { return c ^ (r & (kRowB / 16 - 1) & 15); };
   static_assert(MB % 16 == 0 && MB <= 128, "rows");
   constexpr int MT = MB / 16;                  // 16-row MFMA blocks
   constexpr int A_STAGE = MB * kRowB;          // bytes of one A chunk
@@ -184,10 +187,10 @@ __global__ __launch_bounds__(kThreads) void gemm_skinny_kernel(GemmArgs p) {
   }
 }
 
-template <int MB, int NB>
+template <int MB, int NB, int KC>
 hipError_t launch_mb(const GemmArgs& a, hipStream_t s) {
   const int64_t wgs = (a.N + kBN - 1) / kBN;
-  hipLaunchKernelGGL((gemm_skinny_kernel<MB, NB>), dim3((unsigned)wgs), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL((gemm_skinny_kernel<MB, NB, KC>), dim3((unsigned)wgs), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
@@ -199,10 +202,10 @@ bool skinny_applies(const GemmArgs& a) {
 }
 
 hipError_t launch_gemm_bf16_skinny(const GemmArgs& a, hipStream_t s) {
-  if (a.M <= 16) return launch_mb<16, 3>(a, s);
-  if (a.M <= 32) return launch_mb<32, 3>(a, s);
-  if (a.M <= 64) return launch_mb<64, 3>(a, s);
-  return launch_mb<128, 3>(a, s);
+  if (a.M <= 16) return launch_mb<16, 3, 256>(a, s);
+  if (a.M <= 32) return launch_mb<32, 3, 256>(a, s);
+  if (a.M <= 64) return launch_mb<64, 3, 256>(a, s);
+  return launch_mb<128, 3, 128>(a, s);
 }
 
 }  // namespace dmu
