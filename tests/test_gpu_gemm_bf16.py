@@ -151,7 +151,8 @@ def test_accuracy_vs_k(K):
 
 @pytest.mark.parametrize("out_dtype", OUTS)
 @pytest.mark.parametrize("shape", [(1, 113, 8), (5, 1000, 264), (33, 250, 520), (100, 3000, 1032),
-                                   (128, 224, 4096), (16, 2000, 8192)])
+                                   (128, 224, 4096), (16, 2000, 8192),
+                                   (24, 700, 776), (64, 900, 1800)])
 def test_skinny_m(out_dtype, shape):
     # M <= 128 with B stored N x K takes the bandwidth-bound skinny kernel
     M, N, K = shape
