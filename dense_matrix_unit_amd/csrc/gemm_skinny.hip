@@ -12,17 +12,18 @@
 //  * a workgroup of 7 waves owns 112 columns of D (16 per wave), so N = 28672
 //    gives exactly 256 workgroups, one per CU;
 //  * every wave streams its own 16 rows of B straight into registers (no LDS
-//    round trip), 16 bytes per lane per 32-wide K step, in a ring of three
-//    K chunks (two in flight while one is multiplied).  A chunk is 256 K wide
-//    for M <= 64 and 128 wide for M = 128, whose A stages would not fit in
-//    LDS at 256: the longer run of each B row per chunk took M = 16 from 97.4
-//    to 94.4 us and M = 64 from 101.1 to 97.4 us (N = 28672, K = 8192,
-//    bit-identical output); 512 wide was slower again at M = 16;
+//    round trip), 16 bytes per lane per 32-wide K step, in a ring of K
+//    chunks.  For M <= 64 a chunk is 256 K wide and the ring holds two (one
+//    in flight while one is multiplied); M = 128, whose A stages would not
+//    fit in LDS at 256, takes three 128-wide chunks.  The longer run of each
+//    B row per chunk took M = 16 from 97.4 to 94.4 us and M = 64 from 101.1
+//    to 97.4 us (N = 28672, K = 8192, bit-identical output), and the shorter
+//    ring another 1-2%; 512-wide chunks were slower at M = 16;
 //  * A (at most 128 x K) is shared by the workgroup through LDS, one K chunk
 //    per stage, copied with buffer loads that write LDS directly; its
 //    16-byte chunks are XOR-swizzled with the row index so the MFMA fragment
 //    reads are bank-conflict free.  There is one A stage more than the ring
-//    holds chunks, so the copy of chunk c + 3 goes into the stage of chunk
+//    holds chunks, so the copy of chunk c + ring goes into the stage of chunk
 //    c - 1, which every wave has finished reading by the barrier that opens
 //    chunk c: one barrier per chunk instead of two, and the copy leaves before
 //    chunk c is multiplied (128.3 -> 117.6 us at M = 128, N = 28672,
@@ -202,9 +203,9 @@ bool skinny_applies(const GemmArgs& a) {
 }
 
 hipError_t launch_gemm_bf16_skinny(const GemmArgs& a, hipStream_t s) {
-  if (a.M <= 16) return launch_mb<16, 3, 256>(a, s);
-  if (a.M <= 32) return launch_mb<32, 3, 256>(a, s);
-  if (a.M <= 64) return launch_mb<64, 3, 256>(a, s);
+  if (a.M <= 16) return launch_mb<16, 2, 256>(a, s);
+  if (a.M <= 32) return launch_mb<32, 2, 256>(a, s);
+  if (a.M <= 64) return launch_mb<64, 2, 256>(a, s);
   return launch_mb<128, 3, 128>(a, s);
 }
 
